@@ -1,0 +1,181 @@
+/*
+ * gqa_decode.h -- C ABI of the MI355X (gfx950) split-KV grouped-query-attention
+ * decode library (libgqa_decode.so).
+ *
+ * The operation (kernbench2 page "_gqa_attention_decode_long.py": the kernel
+ * docstring, the "Tile 0" block, the tile loop over 1024-key tiles with
+ * `_merge_running`, and the final normalise-and-store block):
+ *
+ *   for every sequence b < batch and query head h < h_q, with G = h_q / h_kv,
+ *   kv head j = h / G, S = seq_lens[b] (negative counts as 0) and
+ *   base = seq_lens[0] + ... + seq_lens[b-1]:
+ *
+ *     s_t      = scale * sum_i q[b,h,i] * k[base+t, j, i]        t < S
+ *     o[b,h,:] = sum_t softmax(s)_t * v[base+t, j, :]           (S = 0 gives 0)
+ *
+ * computed as a sweep over the key axis: the keys of every (sequence, kv head)
+ * are cut into ranges, each range is reduced to a partial online-softmax triple
+ * (m, l, O) for all G query heads of that kv head at once, and the triples are
+ * combined with the log-sum-exp merge (m = max of both; each side rescaled by
+ * exp(its m - m); l and O summed), then O / l is stored.  The page's reduction
+ * across ranks of a device mesh becomes, on one GPU, the ranges of one kernel
+ * grid plus a merge kernel.
+ *
+ * Readings where the page is silent: `scale` multiplies the raw dot product
+ * (the page applies none; scale = 1 reproduces it); K is used truly transposed;
+ * query head h reads kv head h / G; K/V of the sequences are packed back to
+ * back; the accumulator, partials and merge are fp32; bf16 output is the
+ * nearest-even rounding of the fp32 result.
+ *
+ * Tensor layouts (row-major, contiguous, all in device memory of the current
+ * HIP device, owned by the caller; the library never frees or keeps them):
+ *   q         [batch, h_q, d_head]            in_dtype
+ *   k, v      [sum(seq_lens), h_kv, d_head]   in_dtype, sequences packed back to back
+ *   o         [batch, h_q, d_head]            out_dtype (written)
+ *   seq_lens  int32[batch]  (device memory; read by the kernels, never by the host,
+ *             so a call needs no host synchronisation)
+ *
+ * Supported: d_head in {64, 128}; G = h_q / h_kv in 1..16; (in, out) dtypes
+ * (bf16, bf16), (f32, f32) and (bf16, f32).  q, k, v, o must be 16-byte aligned,
+ * seq_lens 4-byte aligned.
+ *
+ * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns without synchronising.  Errors found on the host
+ * return before anything is enqueued, and then `o` is untouched.
+ *
+ * Errors: every entry point returns GQA_OK (0) or a positive gqa_status code;
+ * gqa_last_error_message() gives a thread-local description of the last error.
+ * No C++ exception crosses this interface.
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+#define GQA_DTYPE_BF16 0
+#define GQA_DTYPE_F32 1
+
+/* Status codes. */
+typedef enum gqa_status {
+    GQA_OK = 0,
+    GQA_ERR_NULL = 1,        /* a required pointer is NULL                              */
+    GQA_ERR_SHAPE = 2,       /* batch, h_q or h_kv <= 0, or h_q not a multiple of h_kv  */
+    GQA_ERR_UNSUPPORTED = 3, /* d_head not 64/128, G > 16, or dtype pair not supported  */
+    GQA_ERR_ALIGN = 4,       /* q/k/v/o not 16-byte aligned or seq_lens not 4-byte      */
+    GQA_ERR_SCALE = 5,       /* scale is not finite                                     */
+    GQA_ERR_WORKSPACE = 6,   /* caller workspace too small or not 256-byte aligned      */
+    GQA_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed              */
+    GQA_ERR_ARG = 8          /* a tuning field is out of range                          */
+} gqa_status;
+
+/*
+ * gqa_decode -- bf16 q/k/v in, bf16 o out, fp32 accumulation.
+ * Arguments as in the layouts above.  `scale` is usually 1/sqrt(d_head).
+ * Uses a library-owned workspace (see gqa_decode_ex), so the first call on a
+ * (device, stream) pair may allocate device memory.
+ */
+int gqa_decode(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
+               int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale,
+               void *stream);
+
+/* gqa_decode_f32 -- the same operation with fp32 q/k/v in and fp32 o out. */
+int gqa_decode_f32(const void *q, const void *k, const void *v, void *o,
+                   const int32_t *seq_lens, int32_t batch, int32_t h_q, int32_t h_kv,
+                   int32_t d_head, float scale, void *stream);
+
+/*
+ * Full argument block.  Zero-initialise it, then set the fields.
+ *
+ * num_chunks  The flattened key axis -- every (sequence, kv head) pair's keys laid
+ *             end to end, h_kv * sum(seq_lens) keys in all -- is cut into equal
+ *             ranges of `chunk` keys, one range per wavefront, where
+ *               chunk = max(min_chunk, ceil(total / num_chunks))
+ *             is computed on the device from seq_lens.  A range that covers a whole
+ *             (sequence, kv head) writes o directly; the pieces of a pair that spans
+ *             several ranges are merged by a second kernel.  0 = automatic (compute
+ *             units x resident wavefronts per compute unit).  Range: 0..2^24.
+ * min_chunk   Smallest range in keys; 0 = automatic.  Range: 0..2^30.
+ *             min_chunk = 1024 with a large num_chunks reproduces the page's
+ *             1024-key tiles as the split granularity.
+ * workspace   Device scratch for the partial triples, at least
+ *             gqa_decode_workspace_bytes() bytes, 256-byte aligned, owned by the
+ *             caller and not used concurrently by another call.  NULL = a
+ *             library-owned buffer per (device, stream), grown with hipMalloc on
+ *             demand and freed by gqa_release(); callers that capture HIP graphs
+ *             must pass their own.
+ */
+typedef struct gqa_decode_args {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    const int32_t *seq_lens;
+    int32_t batch;
+    int32_t h_q;
+    int32_t h_kv;
+    int32_t d_head;
+    float scale;
+    int32_t in_dtype;  /* GQA_DTYPE_BF16 or GQA_DTYPE_F32 */
+    int32_t out_dtype; /* GQA_DTYPE_BF16 or GQA_DTYPE_F32 */
+    int32_t num_chunks;
+    int32_t min_chunk;
+    void *workspace;
+    size_t workspace_bytes;
+    void *stream; /* hipStream_t */
+} gqa_decode_args;
+
+/* gqa_decode_ex -- the operation with every field of `args` (see above). */
+int gqa_decode_ex(const gqa_decode_args *args);
+
+/*
+ * gqa_decode_validate -- the host-side argument checks of gqa_decode_ex alone
+ * (pointers, shapes, support, alignment, scale, tuning ranges; the workspace
+ * size is checked only when num_chunks is given, since the automatic value needs
+ * the device).  Touches no device and enqueues nothing.  Returns the status
+ * gqa_decode_ex would return for these arguments before launching.
+ */
+int gqa_decode_validate(const gqa_decode_args *args);
+
+/*
+ * Resolved launch plan of a call (pure host arithmetic, no device access).
+ * num_cus and waves_per_cu describe the device: the automatic num_chunks is
+ * num_cus * waves_per_cu.  Returns GQA_OK or the validation status.
+ */
+typedef struct gqa_decode_plan {
+    int32_t num_chunks;      /* wavefronts launched = ranges of the key axis       */
+    int32_t min_chunk;       /* smallest range in keys                             */
+    int32_t split_blocks;    /* workgroups of the partial kernel (4 wavefronts)    */
+    int32_t merge_blocks;    /* workgroups of the merge kernel (batch * h_kv)      */
+    size_t workspace_bytes;  /* partial-triple scratch the call needs              */
+} gqa_decode_plan;
+
+int gqa_decode_make_plan(const gqa_decode_args *args, int32_t num_cus, int32_t waves_per_cu,
+                         gqa_decode_plan *plan);
+
+/*
+ * gqa_decode_workspace_bytes -- bytes of workspace a gqa_decode_ex call with these
+ * arguments needs, in *bytes.  With num_chunks = 0 it queries the current
+ * device's compute-unit count.  Returns a status.
+ */
+int gqa_decode_workspace_bytes(const gqa_decode_args *args, size_t *bytes);
+
+/* Text of a status code (static storage). */
+const char *gqa_status_str(int status);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char *gqa_last_error_message(void);
+
+/* Frees every library-owned workspace after synchronising its device. */
+void gqa_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H */
