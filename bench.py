@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the split-KV GQA decode library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+
+One step is one gqa_decode_ex call -- the sweep (partial) kernel and the merge
+kernel -- over the whole batch, with q, k, v and seq_lens already resident in
+HBM.  The default workload is the 70B-shaped ragged batch: batch 64, h_q 64,
+h_kv 8, d_head 128, per-sequence lengths uniform in [1024, 32768], bf16 in and
+out, fp32 accumulation, synthetic seeded data.
+
+Prints one JSON line:
+  value          K/V bytes read once per step / step time (GB/s), whole job
+  us_per_step    mean step time (HIP events around the K timed steps)
+  roofline       the sweep kernel: algorithmic K+V bytes per launch / its mean
+                 duration (HIP events recorded by the library around that kernel
+                 on the launch stream), against MI355X's 8 TB/s HBM peak;
+                 traffic = HBM bytes per launch from the committed rocprofv3
+                 counter summary if it was taken on the current kernel source
+  cpu_baseline   the fp64 CPU oracle on the same inputs, on the host cores
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "µs/decode step + K/V HBM GB/s (% of peak), GQA h_q=64 h_kv=8 d=128 @32K"
+KERNEL_SRC = os.path.join(ROOT, "gqa_split_kv_amd", "csrc", "decode_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_kernel_70b_ragged_traffic.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (events), through ctypes."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError("%s failed (%d)" % (what, rc))
+
+    def event(self):
+        e = ctypes.c_void_p()
+        self._ok(self.lib.hipEventCreate(ctypes.byref(e)), "hipEventCreate")
+        return e.value
+
+    def record(self, ev, stream):
+        self._ok(self.lib.hipEventRecord(ev, stream), "hipEventRecord")
+
+    def sync(self, ev):
+        self._ok(self.lib.hipEventSynchronize(ev), "hipEventSynchronize")
+
+    def ms(self, a, b):
+        t = ctypes.c_float()
+        self._ok(self.lib.hipEventElapsedTime(ctypes.byref(t), a, b), "hipEventElapsedTime")
+        return float(t.value)
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def committed_traffic():
+    """(bytes per launch, note) from the committed counter summary, or (None, why)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary committed"
+    text = open(TRAFFIC_FILE).read()
+    h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t:
+        return None, "counter summary unreadable"
+    if h.group(1) != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return float(t.group(1)), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-kernel scaled"
+
+
+def cpu_baseline(d, w, budget_s: float):
+    """Times the fp64 oracle on the host over whole sequences of the same inputs."""
+    import numpy as np
+    import oracle
+    from gqa_split_kv_amd.inputs import to_host_bits
+    sl = d.seq_lens_host
+    # Sample: the first n sequences whose estimated oracle time fits the budget
+    # (rate measured on the first sequence).
+    log("cpu baseline: copying inputs to the host")
+    qh, kh, vh = to_host_bits(d.q), to_host_bits(d.k), to_host_bits(d.v)
+    rows0 = int(sl[0])
+    t = time.perf_counter()
+    oracle.gqa_decode_f64(qh[:1], kh[:rows0], vh[:rows0], sl[:1], d.scale)
+    rate = rows0 / max(time.perf_counter() - t, 1e-6)            # rows (all kv heads) per second
+    n = 1
+    rows = rows0
+    while n < len(sl) and (rows + int(sl[n])) / rate < budget_s:
+        rows += int(sl[n])
+        n += 1
+    log("cpu baseline: oracle over %d of %d sequences (%d keys)" % (n, len(sl), rows))
+    t = time.perf_counter()
+    oracle.gqa_decode_f64(qh[:n], kh[:rows], vh[:rows], sl[:n], d.scale)
+    dt = time.perf_counter() - t
+    nbytes = rows * w.h_kv * w.d * 2 * 2
+    return {
+        "value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+        "seconds": dt,
+        "sample": "first %d of %d sequences (%d keys, %.3g GB of K+V), same seeded inputs, "
+                  "fp64 direct softmax(qK^T*scale)V per head, OpenMP over (sequence, kv head)"
+                  % (n, len(sl), rows, nbytes / 1e9),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=4, help="workload number 1..5 (default 4)")
+    ap.add_argument("--num-chunks", type=int, default=0)
+    ap.add_argument("--min-chunk", type=int, default=0)
+    ap.add_argument("--rotate", type=int, default=1,
+                    help="independent copies of q/k/v cycled through (defeats the 256 MiB "
+                         "last-level cache on small workloads)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (profiler calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path runs on a single MI355X and has no "
+              "multi-GPU mode (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gqa_split_kv_amd as gqa
+    from gqa_split_kv_amd.inputs import WORKLOADS, device_workload
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    hip = Hip()
+    log("generating workload %d (%s)" % (w.cfg, w.name))
+    sets = [device_workload(w) if r == 0 else None for r in range(args.rotate)]
+    d = sets[0]
+    for r in range(1, args.rotate):
+        sets[r] = type(d)(d.q.clone(), d.k.clone(), d.v.clone(), d.seq_lens.clone(), d.seq_lens_host,
+                          d.scale, d.dtype)
+    torch.cuda.synchronize()
+    kv_bytes = w.kv_bytes(d.seq_lens_host)
+    out = torch.empty((w.batch, w.h_q, w.d), dtype=d.q.dtype, device="cuda")
+    stream = int(torch.cuda.current_stream().cuda_stream)
+    dt_code = gqa.GQA_DTYPE_BF16 if w.dtype == "bf16" else gqa.GQA_DTYPE_F32
+    probe = gqa.make_args(d.q, d.k, d.v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale,
+                          dt_code, dt_code, args.num_chunks, args.min_chunk, stream=stream)
+    ws_bytes = gqa.gqa_decode_workspace_bytes(probe)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    ev_steps = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    ev_all = (hip.event(), hip.event())
+
+    def step(i, events=None):
+        s = sets[i % args.rotate]
+        a = gqa.make_args(s.q, s.k, s.v, out, s.seq_lens, w.batch, w.h_q, w.h_kv, w.d, s.scale,
+                          dt_code, dt_code, args.num_chunks, args.min_chunk, ws, ws_bytes, stream,
+                          sweep_events=events)
+        gqa.gqa_decode_ex(a)
+
+    log("warmup %d steps" % args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    t0 = time.perf_counter()
+    hip.record(ev_all[0], stream)
+    for i in range(args.steps):
+        step(i, ev_steps[i])
+    hip.record(ev_all[1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    hip.sync(ev_all[1])
+    total_ms = hip.ms(*ev_all)
+    sweep_ms = sum(hip.ms(a, b) for a, b in ev_steps) / args.steps
+    ms_per_step = total_ms / args.steps
+    value = kv_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = kv_bytes / (sweep_ms / 1e3) / 1e9
+    traffic, traffic_note = committed_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_peak_hbm": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "wall_s_timed_region": round(wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "accumulate": "fp32",
+        "data": "synthetic (seeded N(0,1), rounded to bf16)",
+        "config": {
+            "workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv, "d_head": w.d,
+            "seq_lens": ("uniform [%d, %d] seed %d, sum %d" % (w.ragged[0], w.ragged[1], w.seed,
+                         int(d.seq_lens_host.sum()))) if w.ragged else "%d each" % w.seq_len,
+            "kv_bytes_per_step": kv_bytes, "rotate": args.rotate,
+            "num_chunks": args.num_chunks or "auto", "min_chunk": args.min_chunk or "auto",
+            "workspace_bytes": ws_bytes,
+        },
+        "roofline": {
+            "kernel": "split_kernel (key sweep)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "traffic_note": traffic_note,
+            "kernel_us": round(sweep_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = n
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(d, w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

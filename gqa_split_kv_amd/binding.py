@@ -1,0 +1,247 @@
+"""ctypes binding of libgqa_decode.so (include/gqa_decode.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, and every step of the decode runs in the HIP
+kernels behind the C ABI.  There is no fallback: if the library is missing or
+was not built, calls raise.
+
+Functions with the C names take raw pointers or tensors exactly as the C ABI
+does; `decode` is the convenience wrapper that allocates the output tensor.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgqa_decode.so")
+
+GQA_DTYPE_BF16 = 0
+GQA_DTYPE_F32 = 1
+
+GQA_OK = 0
+GQA_ERR_NULL = 1
+GQA_ERR_SHAPE = 2
+GQA_ERR_UNSUPPORTED = 3
+GQA_ERR_ALIGN = 4
+GQA_ERR_SCALE = 5
+GQA_ERR_WORKSPACE = 6
+GQA_ERR_HIP = 7
+GQA_ERR_ARG = 8
+
+# Every function the header declares, in header order.
+EXPORTS = ("gqa_decode", "gqa_decode_f32", "gqa_decode_ex", "gqa_decode_validate",
+           "gqa_decode_make_plan", "gqa_decode_workspace_bytes", "gqa_status_str",
+           "gqa_last_error_message", "gqa_release")
+
+
+class GqaArgs(ctypes.Structure):
+    """Mirror of gqa_decode_args."""
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+        ("d_head", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("num_chunks", ctypes.c_int32), ("min_chunk", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+        ("sweep_events", ctypes.c_void_p * 2),
+    ]
+
+
+class GqaPlan(ctypes.Structure):
+    """Mirror of gqa_decode_plan."""
+    _fields_ = [
+        ("num_chunks", ctypes.c_int32), ("min_chunk", ctypes.c_int32),
+        ("split_blocks", ctypes.c_int32), ("merge_blocks", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (status_str(status), message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it was not built (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgqa_decode.so is not built: run `python -m gqa_split_kv_amd.build` "
+                           "(or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    sig = [P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float, P]
+    L.gqa_decode.argtypes = sig
+    L.gqa_decode.restype = ctypes.c_int
+    L.gqa_decode_f32.argtypes = sig
+    L.gqa_decode_f32.restype = ctypes.c_int
+    L.gqa_decode_ex.argtypes = [ctypes.POINTER(GqaArgs)]
+    L.gqa_decode_ex.restype = ctypes.c_int
+    L.gqa_decode_validate.argtypes = [ctypes.POINTER(GqaArgs)]
+    L.gqa_decode_validate.restype = ctypes.c_int
+    L.gqa_decode_make_plan.argtypes = [ctypes.POINTER(GqaArgs), i32, i32, ctypes.POINTER(GqaPlan)]
+    L.gqa_decode_make_plan.restype = ctypes.c_int
+    L.gqa_decode_workspace_bytes.argtypes = [ctypes.POINTER(GqaArgs), ctypes.POINTER(ctypes.c_size_t)]
+    L.gqa_decode_workspace_bytes.restype = ctypes.c_int
+    L.gqa_status_str.argtypes = [ctypes.c_int]
+    L.gqa_status_str.restype = ctypes.c_char_p
+    L.gqa_last_error_message.argtypes = []
+    L.gqa_last_error_message.restype = ctypes.c_char_p
+    L.gqa_release.argtypes = []
+    L.gqa_release.restype = None
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().gqa_status_str(int(status)).decode()
+
+
+def last_error_message() -> str:
+    return lib().gqa_last_error_message().decode()
+
+
+def _check(status: int) -> None:
+    if status != GQA_OK:
+        raise GqaError(status, last_error_message())
+
+
+def _ptr(x) -> Optional[int]:
+    """A tensor's device address, an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GQA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return GQA_DTYPE_F32
+    raise TypeError("q/k/v/o must be bfloat16 or float32 tensors, got %s" % t.dtype)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+# ------------------------------------------------------------------ the C names
+
+
+def gqa_decode(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_head: int, scale: float,
+               stream=None) -> int:
+    """bf16 in / bf16 out.  Raises GqaError on a non-zero status; returns 0."""
+    st = lib().gqa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens), batch, h_q, h_kv,
+                          d_head, float(scale), _stream(stream))
+    _check(st)
+    return st
+
+
+def gqa_decode_f32(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_head: int,
+                   scale: float, stream=None) -> int:
+    """fp32 in / fp32 out."""
+    st = lib().gqa_decode_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens), batch, h_q, h_kv,
+                              d_head, float(scale), _stream(stream))
+    _check(st)
+    return st
+
+
+def make_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, in_dtype, out_dtype,
+              num_chunks=0, min_chunk=0, workspace=None, workspace_bytes=0, stream=0,
+              sweep_events=None) -> GqaArgs:
+    a = GqaArgs()
+    a.q, a.k, a.v, a.o, a.seq_lens = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens)
+    a.batch, a.h_q, a.h_kv, a.d_head = int(batch), int(h_q), int(h_kv), int(d_head)
+    a.scale = float(scale)
+    a.in_dtype, a.out_dtype = int(in_dtype), int(out_dtype)
+    a.num_chunks, a.min_chunk = int(num_chunks), int(min_chunk)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = int(workspace_bytes)
+    a.stream = stream
+    if sweep_events is not None:
+        a.sweep_events[0] = int(sweep_events[0])
+        a.sweep_events[1] = int(sweep_events[1])
+    return a
+
+
+def gqa_decode_ex(args: GqaArgs) -> int:
+    st = lib().gqa_decode_ex(ctypes.byref(args))
+    _check(st)
+    return st
+
+
+def gqa_decode_validate(args: GqaArgs) -> int:
+    """Host-side checks only; returns the status (does not raise)."""
+    return int(lib().gqa_decode_validate(ctypes.byref(args)))
+
+
+def gqa_decode_make_plan(args: GqaArgs, num_cus: int, waves_per_cu: int):
+    """(status, GqaPlan) -- pure host arithmetic."""
+    plan = GqaPlan()
+    st = lib().gqa_decode_make_plan(ctypes.byref(args), int(num_cus), int(waves_per_cu),
+                                    ctypes.byref(plan))
+    return int(st), plan
+
+
+def gqa_decode_workspace_bytes(args: GqaArgs) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().gqa_decode_workspace_bytes(ctypes.byref(args), ctypes.byref(n)))
+    return int(n.value)
+
+
+def gqa_status_str(status: int) -> str:
+    return status_str(status)
+
+
+def gqa_last_error_message() -> str:
+    return last_error_message()
+
+
+def gqa_release() -> None:
+    lib().gqa_release()
+
+
+# ------------------------------------------------------------------ convenience
+
+
+def decode(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype=None,
+           num_chunks: int = 0, min_chunk: int = 0, workspace=None, stream=None):
+    """o = GQA decode of q [batch, h_q, d] against packed k, v [sum(seq_lens), h_kv, d].
+
+    seq_lens is an int32 device tensor.  out_dtype defaults to q's dtype; pass
+    torch.float32 with bf16 inputs for the fp32 result.  Returns `out`.
+    """
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [batch, h_q, d]; k, v [sum(seq_lens), h_kv, d]")
+    batch, h_q, d = q.shape
+    h_kv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty((batch, h_q, d), dtype=out_dtype or q.dtype, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    args = make_args(q, k, v, out, seq_lens, batch, h_q, h_kv, d, scale, _dtype_code(q),
+                     _dtype_code(out), num_chunks, min_chunk, workspace, ws_bytes, _stream(stream))
+    gqa_decode_ex(args)
+    return out

@@ -1,0 +1,259 @@
+// api.cpp -- the extern "C" entry points of libgqa_decode.so (declared in
+// include/gqa_decode.h): validation, planning, the library-owned workspace
+// cache, and the launch.  No C++ exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "host.h"
+#include "kernels.h"
+
+namespace gqa {
+const char *last_error();
+}
+
+namespace {
+
+struct OwnedWorkspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_mu;
+std::map<int, int> g_num_cus;                                   // device -> compute units
+std::map<std::pair<int, int>, int> g_waves_per_cu;               // (device, variant) -> waves
+std::map<std::pair<int, uintptr_t>, OwnedWorkspace> g_workspaces; // (device, stream)
+
+int variant_id(int in_bf16, int out_bf16, int D) { return (in_bf16 << 2) | (out_bf16 << 1) | (D == 128); }
+
+int device_shape(int dev, int in_bf16, int out_bf16, int D, int *num_cus, int *waves_per_cu) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_num_cus.find(dev);
+    if (it == g_num_cus.end()) {
+        int n = 0;
+        hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || n <= 0)
+            return gqa::fail(GQA_ERR_HIP, "hipDeviceGetAttribute(compute units) failed: %s",
+                             hipGetErrorString(e));
+        it = g_num_cus.emplace(dev, n).first;
+    }
+    *num_cus = it->second;
+    const auto key = std::make_pair(dev, variant_id(in_bf16, out_bf16, D));
+    auto wt = g_waves_per_cu.find(key);
+    if (wt == g_waves_per_cu.end()) {
+        int blocks = 0;
+        hipError_t e = gqa::split_occupancy(in_bf16, out_bf16, D, &blocks);
+        if (e != hipSuccess || blocks <= 0)
+            return gqa::fail(GQA_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
+        wt = g_waves_per_cu.emplace(key, blocks * gqa::kWavesPerBlock).first;
+    }
+    *waves_per_cu = wt->second;
+    return GQA_OK;
+}
+
+int owned_workspace(int dev, hipStream_t stream, size_t need, void **out) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    OwnedWorkspace &w = g_workspaces[std::make_pair(dev, reinterpret_cast<uintptr_t>(stream))];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            // Work already enqueued on this stream may still read the old buffer.
+            hipError_t e = hipStreamSynchronize(stream);
+            if (e != hipSuccess)
+                return gqa::fail(GQA_ERR_HIP, "hipStreamSynchronize failed: %s", hipGetErrorString(e));
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        const size_t grow = ((need + need / 4) + (1u << 20) - 1) & ~static_cast<size_t>((1u << 20) - 1);
+        hipError_t e = hipMalloc(&w.ptr, grow);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return gqa::fail(GQA_ERR_HIP, "hipMalloc(%zu) for the workspace failed: %s", grow,
+                             hipGetErrorString(e));
+        }
+        w.bytes = grow;
+    }
+    *out = w.ptr;
+    return GQA_OK;
+}
+
+int decode_ex(const gqa_decode_args *a) {
+    gqa::clear_error();
+    int st = gqa::validate(a);
+    if (st != GQA_OK) return st;
+    const int in_bf16 = a->in_dtype == GQA_DTYPE_BF16;
+    const int out_bf16 = a->out_dtype == GQA_DTYPE_BF16;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    int num_cus = 0, waves_per_cu = 0;
+    st = device_shape(dev, in_bf16, out_bf16, a->d_head, &num_cus, &waves_per_cu);
+    if (st != GQA_OK) return st;
+    gqa_decode_plan plan;
+    st = gqa::make_plan(a, num_cus, waves_per_cu, &plan);
+    if (st != GQA_OK) return st;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(a->stream);
+    void *ws = a->workspace;
+    if (!ws) {
+        st = owned_workspace(dev, stream, plan.workspace_bytes, &ws);
+        if (st != GQA_OK) return st;
+    }
+    const int G = a->h_q / a->h_kv;
+    const gqa::WorkspaceLayout L = gqa::workspace_layout(plan.num_chunks, G, a->d_head);
+    gqa::DecodeParams P;
+    P.q = static_cast<const uint8_t *>(a->q);
+    P.k = static_cast<const uint8_t *>(a->k);
+    P.v = static_cast<const uint8_t *>(a->v);
+    P.o = static_cast<uint8_t *>(a->o);
+    P.seq_lens = a->seq_lens;
+    P.ws_o = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + L.o_offset);
+    P.ws_ml = reinterpret_cast<float2 *>(static_cast<uint8_t *>(ws) + L.ml_offset);
+    P.batch = a->batch;
+    P.h_q = a->h_q;
+    P.h_kv = a->h_kv;
+    P.G = G;
+    P.num_chunks = plan.num_chunks;
+    P.min_chunk = plan.min_chunk;
+    P.scale_log2 = static_cast<float>(static_cast<double>(a->scale) * 1.4426950408889634074);
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    if (a->sweep_events[0] && a->sweep_events[1]) {
+        ev0 = reinterpret_cast<hipEvent_t>(a->sweep_events[0]);
+        ev1 = reinterpret_cast<hipEvent_t>(a->sweep_events[1]);
+    }
+    e = gqa::launch_decode(P, in_bf16, out_bf16, a->d_head, plan.split_blocks, plan.merge_blocks,
+                           stream, ev0, ev1);
+    if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return GQA_OK;
+}
+
+gqa_decode_args make_args(const void *q, const void *k, const void *v, void *o,
+                          const int32_t *seq_lens, int32_t batch, int32_t h_q, int32_t h_kv,
+                          int32_t d_head, float scale, void *stream, int dtype) {
+    gqa_decode_args a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.seq_lens = seq_lens;
+    a.batch = batch;
+    a.h_q = h_q;
+    a.h_kv = h_kv;
+    a.d_head = d_head;
+    a.scale = scale;
+    a.in_dtype = dtype;
+    a.out_dtype = dtype;
+    a.stream = stream;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_decode_ex(const gqa_decode_args *args) {
+    try {
+        return decode_ex(args);
+    } catch (...) {
+        return gqa::fail(GQA_ERR_HIP, "internal error");
+    }
+}
+
+int gqa_decode(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
+               int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream) {
+    const gqa_decode_args a =
+        make_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, stream, GQA_DTYPE_BF16);
+    return gqa_decode_ex(&a);
+}
+
+int gqa_decode_f32(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
+                   int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale,
+                   void *stream) {
+    const gqa_decode_args a =
+        make_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, stream, GQA_DTYPE_F32);
+    return gqa_decode_ex(&a);
+}
+
+int gqa_decode_validate(const gqa_decode_args *args) {
+    try {
+        gqa::clear_error();
+        return gqa::validate(args);
+    } catch (...) {
+        return gqa::fail(GQA_ERR_HIP, "internal error");
+    }
+}
+
+int gqa_decode_make_plan(const gqa_decode_args *args, int32_t num_cus, int32_t waves_per_cu,
+                         gqa_decode_plan *plan) {
+    try {
+        gqa::clear_error();
+        return gqa::make_plan(args, num_cus, waves_per_cu, plan);
+    } catch (...) {
+        return gqa::fail(GQA_ERR_HIP, "internal error");
+    }
+}
+
+int gqa_decode_workspace_bytes(const gqa_decode_args *args, size_t *bytes) {
+    try {
+        gqa::clear_error();
+        if (!bytes) return gqa::fail(GQA_ERR_NULL, "bytes is NULL");
+        int st = gqa::validate(args);
+        if (st != GQA_OK) return st;
+        int num_cus = 1, waves_per_cu = 1;
+        if (args->num_chunks == 0) {
+            int dev = 0;
+            hipError_t e = hipGetDevice(&dev);
+            if (e != hipSuccess)
+                return gqa::fail(GQA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+            st = device_shape(dev, args->in_dtype == GQA_DTYPE_BF16, args->out_dtype == GQA_DTYPE_BF16,
+                              args->d_head, &num_cus, &waves_per_cu);
+            if (st != GQA_OK) return st;
+        }
+        gqa_decode_plan plan;
+        st = gqa::make_plan(args, num_cus, waves_per_cu, &plan);
+        if (st != GQA_OK) return st;
+        *bytes = plan.workspace_bytes;
+        return GQA_OK;
+    } catch (...) {
+        return gqa::fail(GQA_ERR_HIP, "internal error");
+    }
+}
+
+const char *gqa_status_str(int status) {
+    switch (status) {
+        case GQA_OK: return "GQA_OK";
+        case GQA_ERR_NULL: return "GQA_ERR_NULL";
+        case GQA_ERR_SHAPE: return "GQA_ERR_SHAPE";
+        case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED";
+        case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN";
+        case GQA_ERR_SCALE: return "GQA_ERR_SCALE";
+        case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE";
+        case GQA_ERR_HIP: return "GQA_ERR_HIP";
+        case GQA_ERR_ARG: return "GQA_ERR_ARG";
+        default: return "GQA_ERR_UNKNOWN";
+    }
+}
+
+const char *gqa_last_error_message(void) { return gqa::last_error(); }
+
+void gqa_release(void) {
+    try {
+        std::lock_guard<std::mutex> lock(g_mu);
+        int cur = 0;
+        const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+        for (auto &kv : g_workspaces) {
+            if (!kv.second.ptr) continue;
+            if (hipSetDevice(kv.first.first) == hipSuccess) {
+                (void)hipDeviceSynchronize();
+                (void)hipFree(kv.second.ptr);
+            }
+        }
+        g_workspaces.clear();
+        if (have_cur) (void)hipSetDevice(cur);
+    } catch (...) {
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// host.h -- internal host-side declarations shared by the C-ABI layer (api.cpp),
+// the pure-C++ validation/planning (plan.cpp) and the kernel launcher
+// (decode_kernels.hip).  Not part of the public interface.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gqa_decode.h"
+
+namespace gqa {
+
+constexpr int kWavesPerBlock = 4;   // wavefronts per workgroup of the partial kernel
+constexpr int kThreads = 64 * kWavesPerBlock;
+constexpr int kMaxG = 16;           // query heads per kv head held by one 16-wide MFMA tile
+constexpr int kMaxChunks = 1 << 24;
+constexpr int kMaxHeadsKv = 1 << 16;   // keeps 16 key rows of lane offsets within 32 bits
+constexpr int kMaxMinChunk = 1 << 30;
+constexpr int kAutoMinChunk = 32;   // default smallest key range per wavefront
+
+// Sets the thread-local error message and returns `status`.
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Argument checks in a fixed order (null, shape, support, alignment, scale,
+// tuning ranges, and the caller workspace when num_chunks is explicit).
+int validate(const gqa_decode_args *a);
+
+// Workspace layout for `num_chunks` wavefronts: two partial-triple slots per
+// wavefront, each G rows of (O[D] fp32) plus (m, l) fp32.
+struct WorkspaceLayout {
+    size_t o_offset;    // float  [num_chunks][2][G][D]
+    size_t ml_offset;   // float2 [num_chunks][2][G]
+    size_t bytes;
+};
+WorkspaceLayout workspace_layout(int64_t num_chunks, int G, int D);
+
+int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decode_plan *plan);
+
+}  // namespace gqa

@@ -1,0 +1,33 @@
+// kernels.h -- parameters and launchers of the gfx950 decode kernels
+// (decode_kernels.hip).  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "host.h"
+
+namespace gqa {
+
+struct DecodeParams {
+    const uint8_t *q;          // [batch, h_q, D] in_dtype
+    const uint8_t *k;          // [sum(seq_lens), h_kv, D] in_dtype
+    const uint8_t *v;
+    uint8_t *o;                // [batch, h_q, D] out_dtype
+    const int32_t *seq_lens;   // [batch]
+    float *ws_o;               // [num_chunks][2][G][D]   unnormalised O of a piece
+    float2 *ws_ml;             // [num_chunks][2][G]      (m in log2 units, l)
+    int32_t batch, h_q, h_kv, G;
+    int32_t num_chunks, min_chunk;
+    float scale_log2;          // scale * log2(e)
+};
+
+// Enqueues the partial kernel and the merge kernel on `stream`.
+// ev_begin/ev_end (may be null) are recorded around the partial kernel.
+hipError_t launch_decode(const DecodeParams &P, int in_bf16, int out_bf16, int D, int split_blocks,
+                         int merge_blocks, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
+
+// Resident workgroups of the partial kernel per compute unit.
+hipError_t split_occupancy(int in_bf16, int out_bf16, int D, int *blocks_per_cu);
+
+}  // namespace gqa

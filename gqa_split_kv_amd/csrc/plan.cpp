@@ -1,0 +1,128 @@
+// plan.cpp -- argument validation and launch planning.  Pure C++: no HIP
+// header, no device access, so every rule here is testable on a host without a
+// GPU through gqa_decode_validate / gqa_decode_make_plan.
+//
+// The rules follow the launch-argument checks of the pages' kernels: reject
+// bad arguments before any work is enqueued (kernbench2 page
+// "_gqa_attention_decode_long.py", the `sub_w` check that raises before the
+// kernel body; sglang page "tp_qknorm.cuh", the host launcher's shape, dtype and
+// 16-byte alignment checks).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "host.h"
+
+namespace gqa {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+const char *last_error() { return g_last_error.c_str(); }
+
+static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+WorkspaceLayout workspace_layout(int64_t num_chunks, int G, int D) {
+    WorkspaceLayout L;
+    const size_t slots = static_cast<size_t>(num_chunks) * 2 * static_cast<size_t>(G);
+    L.o_offset = 0;
+    L.ml_offset = round_up(slots * static_cast<size_t>(D) * sizeof(float), 256);
+    L.bytes = round_up(L.ml_offset + slots * 2 * sizeof(float), 256);
+    return L;
+}
+
+static int check_basic(const gqa_decode_args *a) {
+    if (!a) return fail(GQA_ERR_NULL, "args is NULL");
+    if (!a->q || !a->k || !a->v || !a->o || !a->seq_lens)
+        return fail(GQA_ERR_NULL, "q, k, v, o and seq_lens must be non-NULL");
+    if (a->batch <= 0 || a->h_q <= 0 || a->h_kv <= 0)
+        return fail(GQA_ERR_SHAPE, "batch (%d), h_q (%d) and h_kv (%d) must be positive", a->batch,
+                    a->h_q, a->h_kv);
+    if (a->h_q % a->h_kv != 0)
+        return fail(GQA_ERR_SHAPE, "h_q (%d) is not a multiple of h_kv (%d)", a->h_q, a->h_kv);
+    if (static_cast<int64_t>(a->batch) * a->h_kv > 0x7fffffff)
+        return fail(GQA_ERR_SHAPE, "batch * h_kv exceeds 2^31-1");
+    if (a->h_kv > kMaxHeadsKv)
+        return fail(GQA_ERR_UNSUPPORTED, "h_kv %d exceeds %d", a->h_kv, kMaxHeadsKv);
+    const int G = a->h_q / a->h_kv;
+    if (G > kMaxG)
+        return fail(GQA_ERR_UNSUPPORTED, "G = h_q/h_kv = %d exceeds %d", G, kMaxG);
+    if (a->d_head != 64 && a->d_head != 128)
+        return fail(GQA_ERR_UNSUPPORTED, "d_head %d not supported (64 or 128)", a->d_head);
+    const bool pair_ok = (a->in_dtype == GQA_DTYPE_BF16 && a->out_dtype == GQA_DTYPE_BF16) ||
+                         (a->in_dtype == GQA_DTYPE_F32 && a->out_dtype == GQA_DTYPE_F32) ||
+                         (a->in_dtype == GQA_DTYPE_BF16 && a->out_dtype == GQA_DTYPE_F32);
+    if (!pair_ok)
+        return fail(GQA_ERR_UNSUPPORTED, "dtype pair (in %d, out %d) not supported", a->in_dtype,
+                    a->out_dtype);
+    if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->o, 16))
+        return fail(GQA_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+    if (!aligned(a->seq_lens, 4)) return fail(GQA_ERR_ALIGN, "seq_lens must be 4-byte aligned");
+    if (!std::isfinite(a->scale)) return fail(GQA_ERR_SCALE, "scale is not finite");
+    if (a->num_chunks < 0 || a->num_chunks > kMaxChunks)
+        return fail(GQA_ERR_ARG, "num_chunks %d out of range [0, %d]", a->num_chunks, kMaxChunks);
+    if (a->min_chunk < 0 || a->min_chunk > kMaxMinChunk)
+        return fail(GQA_ERR_ARG, "min_chunk %d out of range [0, %d]", a->min_chunk, kMaxMinChunk);
+    return GQA_OK;
+}
+
+static int check_workspace(const gqa_decode_args *a, size_t need) {
+    if (!a->workspace) return GQA_OK;
+    if (!aligned(a->workspace, 256)) return fail(GQA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (a->workspace_bytes < need)
+        return fail(GQA_ERR_WORKSPACE, "workspace holds %zu bytes, the call needs %zu",
+                    a->workspace_bytes, need);
+    return GQA_OK;
+}
+
+int validate(const gqa_decode_args *a) {
+    int st = check_basic(a);
+    if (st != GQA_OK) return st;
+    if (a->num_chunks > 0) {
+        const WorkspaceLayout L = workspace_layout(a->num_chunks, a->h_q / a->h_kv, a->d_head);
+        st = check_workspace(a, L.bytes);
+        if (st != GQA_OK) return st;
+    }
+    return GQA_OK;
+}
+
+int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decode_plan *plan) {
+    int st = check_basic(a);
+    if (st != GQA_OK) return st;
+    if (!plan) return fail(GQA_ERR_NULL, "plan is NULL");
+    int64_t chunks = a->num_chunks;
+    if (chunks == 0) {
+        if (num_cus <= 0 || waves_per_cu <= 0)
+            return fail(GQA_ERR_ARG, "automatic num_chunks needs num_cus (%d) and waves_per_cu (%d) > 0",
+                        num_cus, waves_per_cu);
+        chunks = static_cast<int64_t>(num_cus) * waves_per_cu;
+        if (chunks > kMaxChunks) chunks = kMaxChunks;
+    }
+    const WorkspaceLayout L = workspace_layout(chunks, a->h_q / a->h_kv, a->d_head);
+    st = check_workspace(a, L.bytes);
+    if (st != GQA_OK) return st;
+    plan->num_chunks = static_cast<int32_t>(chunks);
+    plan->min_chunk = a->min_chunk > 0 ? a->min_chunk : kAutoMinChunk;
+    plan->split_blocks = static_cast<int32_t>((chunks + kWavesPerBlock - 1) / kWavesPerBlock);
+    plan->merge_blocks = a->batch * a->h_kv;
+    plan->workspace_bytes = L.bytes;
+    return GQA_OK;
+}
+
+}  // namespace gqa

@@ -109,6 +109,7 @@ int gqa_decode_f32(const void *q, const void *k, const void *v, void *o,
  *             library-owned buffer per (device, stream), grown with hipMalloc on
  *             demand and freed by gqa_release(); callers that capture HIP graphs
  *             must pass their own.
+ * sweep_events  See the field's comment; leave NULL outside profiling.
  */
 typedef struct gqa_decode_args {
     const void *q;
@@ -128,6 +129,11 @@ typedef struct gqa_decode_args {
     void *workspace;
     size_t workspace_bytes;
     void *stream; /* hipStream_t */
+    /* Optional profiling hook: two hipEvent_t created by the caller.  When both
+     * are non-NULL, the first is recorded on `stream` just before the partial
+     * (sweep) kernel and the second just after it, so its duration can be read
+     * with hipEventElapsedTime without a profiler.  NULL = not recorded. */
+    void *sweep_events[2];
 } gqa_decode_args;
 
 /* gqa_decode_ex -- the operation with every field of `args` (see above). */

@@ -1,0 +1,157 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every function
+include/gqa_decode.h declares, and its host-side validation and planning follow
+the documented rules.  Nothing here launches a kernel.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from gqa_split_kv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_decode.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from gqa_split_kv_amd import build
+        build.build()
+    return B.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|void|size_t|char)\s*\*?\s*(gqa_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(B.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def _args(**kw):
+    base = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, seq_lens=0x50000, batch=4, h_q=32,
+                h_kv=8, d_head=128, scale=0.088, in_dtype=B.GQA_DTYPE_BF16,
+                out_dtype=B.GQA_DTYPE_BF16)
+    base.update(kw)
+    return B.make_args(**base)
+
+
+def _validate(**kw):
+    return B.gqa_decode_validate(_args(**kw))
+
+
+def test_valid_arguments_pass(lib):
+    assert _validate() == B.GQA_OK
+    assert _validate(in_dtype=B.GQA_DTYPE_F32, out_dtype=B.GQA_DTYPE_F32, d_head=64) == B.GQA_OK
+    assert _validate(out_dtype=B.GQA_DTYPE_F32) == B.GQA_OK
+    for G, h_kv in [(1, 8), (2, 4), (4, 8), (8, 8), (16, 1), (3, 2), (5, 1)]:
+        assert _validate(h_q=G * h_kv, h_kv=h_kv) == B.GQA_OK
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "seq_lens"])
+def test_null_pointer(lib, field):
+    assert _validate(**{field: None}) == B.GQA_ERR_NULL
+    assert field in B.last_error_message() or "NULL" in B.last_error_message()
+
+
+def test_null_args_block(lib):
+    assert lib.gqa_decode_validate(None) == B.GQA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(batch=-1), dict(h_q=0), dict(h_kv=0),
+                                dict(h_q=30, h_kv=8), dict(h_q=7, h_kv=2)])
+def test_shape_errors(lib, kw):
+    assert _validate(**kw) == B.GQA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(d_head=96), dict(d_head=256), dict(d_head=0),
+                                dict(h_q=32 * 8, h_kv=8), dict(h_q=17, h_kv=1),
+                                dict(in_dtype=B.GQA_DTYPE_F32, out_dtype=B.GQA_DTYPE_BF16),
+                                dict(in_dtype=7), dict(out_dtype=3), dict(h_q=70000, h_kv=70000)])
+def test_unsupported(lib, kw):
+    assert _validate(**kw) == B.GQA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o"])
+def test_alignment_16_bytes(lib, field):
+    assert _validate(**{field: 0x10008}) == B.GQA_ERR_ALIGN
+    assert _validate(**{field: 0x10010}) == B.GQA_OK
+
+
+def test_seq_lens_alignment(lib):
+    assert _validate(seq_lens=0x50002) == B.GQA_ERR_ALIGN
+    assert _validate(seq_lens=0x50004) == B.GQA_OK
+
+
+@pytest.mark.parametrize("scale", [math.inf, -math.inf, math.nan])
+def test_non_finite_scale(lib, scale):
+    assert _validate(scale=scale) == B.GQA_ERR_SCALE
+
+
+@pytest.mark.parametrize("kw", [dict(num_chunks=-1), dict(min_chunk=-5), dict(num_chunks=(1 << 24) + 1),
+                                dict(min_chunk=(1 << 30) + 1)])
+def test_tuning_ranges(lib, kw):
+    assert _validate(**kw) == B.GQA_ERR_ARG
+
+
+def test_workspace_size_checked_with_explicit_chunks(lib):
+    st, plan = B.gqa_decode_make_plan(_args(num_chunks=100), 256, 8)
+    assert st == B.GQA_OK
+    need = plan.workspace_bytes
+    G, D = 4, 128
+    assert need >= 100 * 2 * G * (D + 2) * 4
+    assert need % 256 == 0
+    assert _validate(num_chunks=100, workspace=0x100000, workspace_bytes=need) == B.GQA_OK
+    assert _validate(num_chunks=100, workspace=0x100000, workspace_bytes=need - 1) == B.GQA_ERR_WORKSPACE
+    assert _validate(num_chunks=100, workspace=0x100010, workspace_bytes=need) == B.GQA_ERR_WORKSPACE
+    # automatic num_chunks: the size needs the device, so validation skips it
+    assert _validate(workspace=0x100000, workspace_bytes=1) == B.GQA_OK
+
+
+def test_plan_automatic_and_explicit(lib):
+    st, plan = B.gqa_decode_make_plan(_args(), 256, 8)
+    assert st == B.GQA_OK
+    assert plan.num_chunks == 256 * 8
+    assert plan.split_blocks == (256 * 8 + 3) // 4
+    assert plan.merge_blocks == 4 * 8
+    assert plan.min_chunk > 0
+    st, plan = B.gqa_decode_make_plan(_args(num_chunks=7, min_chunk=1024), 256, 8)
+    assert st == B.GQA_OK
+    assert (plan.num_chunks, plan.min_chunk, plan.split_blocks) == (7, 1024, 2)
+    st, _ = B.gqa_decode_make_plan(_args(), 0, 8)
+    assert st == B.GQA_ERR_ARG
+    st, _ = B.gqa_decode_make_plan(_args(h_q=30), 256, 8)
+    assert st == B.GQA_ERR_SHAPE
+
+
+def test_status_strings(lib):
+    names = {B.GQA_OK: "GQA_OK", B.GQA_ERR_NULL: "GQA_ERR_NULL", B.GQA_ERR_SHAPE: "GQA_ERR_SHAPE",
+             B.GQA_ERR_UNSUPPORTED: "GQA_ERR_UNSUPPORTED", B.GQA_ERR_ALIGN: "GQA_ERR_ALIGN",
+             B.GQA_ERR_SCALE: "GQA_ERR_SCALE", B.GQA_ERR_WORKSPACE: "GQA_ERR_WORKSPACE",
+             B.GQA_ERR_HIP: "GQA_ERR_HIP", B.GQA_ERR_ARG: "GQA_ERR_ARG"}
+    for code, name in names.items():
+        assert B.status_str(code) == name
+    assert B.status_str(99) == "GQA_ERR_UNKNOWN"
+
+
+def test_error_message_is_cleared_on_success(lib):
+    assert _validate(batch=0) == B.GQA_ERR_SHAPE
+    assert B.last_error_message() != ""
+    assert _validate() == B.GQA_OK
+    assert B.last_error_message() == ""
+
+
+def test_struct_mirrors_match_header_sizes(lib):
+    # gqa_decode_args: 5 pointers, 6 int32 + float, 2 more int32, pointer, size_t, pointer
+    assert ctypes.sizeof(B.GqaArgs) == 5 * 8 + 4 * 4 + 4 + 4 * 4 + 4 + 8 + 8 + 8 + 2 * 8
+    assert ctypes.sizeof(B.GqaPlan) == 4 * 4 + 8

@@ -1,0 +1,250 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle, on an MI355X.
+
+Every test calls libgqa_decode.so via the ctypes binding and compares with
+oracle.gqa_decode_f64 on the same seeded inputs:
+  * fp32 results: max |err| <= 2e-3 and relative L2 <= 1e-3;
+  * bf16 results: every element within one bf16 ulp of the nearest-even bf16
+    rounding of the oracle, and relative L2 <= 1e-3 against that rounding.
+Outputs are NaN-poisoned before each call so an unwritten element fails.
+"""
+import numpy as np
+import pytest
+
+from gqa_split_kv_amd import binding as B
+from gqa_split_kv_amd.inputs import (WORKLOADS, device_workload, host_case, host_workload,
+                                     to_host_bits)
+
+from helpers import compare, oracle_of, run_hip, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "these tests need an MI355X GPU"
+    B.lib()   # raises if the library is not built: there is no fallback path
+    yield
+    B.gqa_release()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ the named workloads
+
+
+def test_tiny_fp32_workload():
+    w = WORKLOADS[1]
+    c = host_workload(w)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    for nc, mc in [(0, 0), (1, 1), (16, 1), (4096, 1), (7, 33)]:
+        _say("tiny fp32, num_chunks", nc, "min_chunk", mc)
+        out = run_hip(q, k, v, sl, c.scale, num_chunks=nc, min_chunk=mc)
+        e, r = compare(out, ref, "cfg1 nc=%d mc=%d" % (nc, mc))
+        assert e < 1e-5 and r < 1e-5, (e, r)   # fp32 in and out: fp32-level agreement
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_single_sequence_bf16_workloads(cfg):
+    import torch
+    w = WORKLOADS[cfg]
+    c = host_workload(w)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    plans = [(0, 0), (0, 1024), (1 << 16, 1024), (333, 1)]
+    for nc, mc in plans:
+        _say("cfg", cfg, "num_chunks", nc, "min_chunk", mc)
+        out32 = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=mc)
+        e, r = compare(out32, ref, "cfg%d f32 out" % cfg)
+        assert e < 1e-4 and r < 1e-4, (e, r)
+        out16 = run_hip(q, k, v, sl, c.scale, num_chunks=nc, min_chunk=mc)
+        compare(out16, ref, "cfg%d bf16 out" % cfg)
+
+
+def _full_size(cfg):
+    import torch
+    w = WORKLOADS[cfg]
+    _say("generating", w.name)
+    d = device_workload(w)
+    torch.cuda.synchronize()
+    _say("decode (automatic plan, as the benchmark runs it)")
+    out16 = run_hip(d.q, d.k, d.v, d.seq_lens, d.scale)
+    out32 = run_hip(d.q, d.k, d.v, d.seq_lens, d.scale, out_dtype=torch.float32)
+    _say("copying inputs to the host and running the oracle")
+    qh, kh, vh = to_host_bits(d.q), to_host_bits(d.k), to_host_bits(d.v)
+    import oracle
+    ref = oracle.gqa_decode_f64(qh, kh, vh, d.seq_lens_host, d.scale)
+    return out16, out32, ref
+
+
+def test_70b_shaped_ragged_workload_full_size():
+    out16, out32, ref = _full_size(4)
+    e, r = compare(out32, ref, "cfg4 f32 out")
+    _say("cfg4 fp32 out: max|err| %.3g rel-L2 %.3g" % (e, r))
+    u, r16, r16raw = compare(out16, ref, "cfg4 bf16 out")
+    _say("cfg4 bf16 out: max ulps %d rel-L2 vs bf16(oracle) %.3g vs oracle %.3g" % (u, r16, r16raw))
+
+
+def test_long_context_peaked_workload_full_size():
+    out16, out32, ref = _full_size(5)
+    e, r = compare(out32, ref, "cfg5 f32 out")
+    _say("cfg5 fp32 out: max|err| %.3g rel-L2 %.3g" % (e, r))
+    compare(out16, ref, "cfg5 bf16 out")
+
+
+# ------------------------------------------------------------------ shapes and plans
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G,h_kv", [(1, 4), (2, 2), (3, 1), (4, 2), (8, 1), (8, 2), (16, 1), (5, 3)])
+@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
+def test_heads_dims_dtypes(d, G, h_kv, dtype, out):
+    import torch
+    lens = [37, 0, 300, 16, 1]
+    c = host_case(len(lens), G * h_kv, h_kv, d, lens, dtype, seed=G * 100 + h_kv * 10 + d)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    for nc, mc in [(0, 0), (5, 1), (64, 16)]:
+        o = run_hip(q, k, v, sl, c.scale, out_dtype=odt, num_chunks=nc, min_chunk=mc)
+        compare(o, ref, "G=%d h_kv=%d d=%d %s->%s nc=%d mc=%d" % (G, h_kv, d, dtype, out, nc, mc))
+
+
+@pytest.mark.parametrize("lens", [[0], [1], [15], [16], [17], [31], [33], [1024], [1025],
+                                  [0, 0, 5], [-2, 3], [0, 0], [5, 0, 0, 0, 7], list(range(0, 70))])
+def test_edge_lengths(lens):
+    import torch
+    c = host_case(len(lens), 8, 2, 128, lens, "bf16", seed=len(lens) + 7)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    for nc, mc in [(0, 0), (1, 1), (3, 1), (1000, 1), (2, 16)]:
+        o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=mc)
+        compare(o, ref, "lens=%s nc=%d mc=%d" % (lens[:8], nc, mc))
+        for b, L in enumerate(lens):
+            if L <= 0:
+                assert (o[b] == 0).all().item()
+
+
+@pytest.mark.parametrize("nc,mc", [(1, 1), (2, 1), (3, 7), (64, 1), (4096, 1), (100000, 1),
+                                   (7, 1024), (1 << 20, 16), (0, 17)])
+def test_forced_chunking_ragged_batch(nc, mc):
+    import torch
+    lens = [513, 1, 2000, 0, 77, 1024, 16, 3333]
+    c = host_case(len(lens), 64, 8, 128, lens, "bf16", seed=55)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=mc)
+    compare(o, ref, "nc=%d mc=%d" % (nc, mc))
+    o16 = run_hip(q, k, v, sl, c.scale, num_chunks=nc, min_chunk=mc)
+    compare(o16, ref, "bf16 nc=%d mc=%d" % (nc, mc))
+
+
+def test_peaked_keys_exercise_running_max():
+    import torch
+    lens = [4096, 8192]
+    c = host_case(2, 16, 2, 128, lens, "bf16", seed=77, peaked_frac=0.001, peak_factor=8.0)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    for nc, mc in [(0, 0), (257, 1), (9, 16)]:
+        o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=mc)
+        compare(o, ref, "peaked nc=%d mc=%d" % (nc, mc))
+
+
+def test_scale_one_is_the_pages_unscaled_kernel():
+    import torch
+    c = host_case(1, 8, 1, 64, [256], "f32", seed=3, scale=1.0)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    o = run_hip(q, k, v, sl, 1.0, out_dtype=torch.float32)
+    compare(o, ref, "scale 1")
+
+
+# ------------------------------------------------------------------ boundary behaviour
+
+
+def test_caller_workspace_poisoned_and_reused():
+    import torch
+    lens = [900, 50, 3000]
+    c = host_case(3, 32, 8, 128, lens, "bf16", seed=91)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    args = B.make_args(q, k, v, q, sl, 3, 32, 8, 128, c.scale, 0, 1, num_chunks=300, min_chunk=1)
+    nbytes = B.gqa_decode_workspace_bytes(args)
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=300, min_chunk=1,
+                    workspace=ws)
+        compare(o, ref, "caller workspace")
+
+
+def test_too_small_workspace_is_rejected_and_output_untouched():
+    import torch
+    c = host_case(1, 8, 1, 128, [100], "bf16", seed=92)
+    q, k, v, sl = upload(c)
+    ws = torch.zeros(64, dtype=torch.float32, device="cuda")
+    o = torch.full((1, 8, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.GqaError) as ei:
+        B.decode(q, k, v, sl, out=o, num_chunks=10, workspace=ws)
+    assert ei.value.status == B.GQA_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert (o == 7.0).all().item()
+
+
+def test_invalid_arguments_leave_output_untouched():
+    import torch
+    c = host_case(1, 8, 2, 128, [10], "bf16", seed=93)
+    q, k, v, sl = upload(c)
+    o = torch.full((1, 8, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    for kw, status in [(dict(h_q=7), B.GQA_ERR_SHAPE), (dict(d_head=96), B.GQA_ERR_UNSUPPORTED),
+                       (dict(scale=float("nan")), B.GQA_ERR_SCALE)]:
+        base = dict(q=q, k=k, v=v, o=o, seq_lens=sl, batch=1, h_q=8, h_kv=2, d_head=128,
+                    scale=c.scale, in_dtype=0, out_dtype=0)
+        base.update(kw)
+        args = B.make_args(**base)
+        with pytest.raises(B.GqaError) as ei:
+            B.gqa_decode_ex(args)
+        assert ei.value.status == status
+    torch.cuda.synchronize()
+    assert (o == 3.0).all().item()
+
+
+def test_c_names_and_f32_entry_point():
+    import torch
+    c = host_case(2, 8, 2, 64, [40, 9], "f32", seed=94)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    o = torch.full((2, 8, 64), float("nan"), dtype=torch.float32, device="cuda")
+    B.gqa_decode_f32(q, k, v, o, sl, 2, 8, 2, 64, c.scale)
+    torch.cuda.synchronize()
+    compare(o, ref, "gqa_decode_f32")
+    cb = host_case(2, 8, 2, 64, [40, 9], "bf16", seed=95)
+    refb = oracle_of(cb)
+    q, k, v, sl = upload(cb)
+    ob = torch.full((2, 8, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.gqa_decode(q, k, v, ob, sl, 2, 8, 2, 64, cb.scale)
+    torch.cuda.synchronize()
+    compare(ob, refb, "gqa_decode")
+
+
+def test_runs_on_the_given_stream_and_is_deterministic():
+    import torch
+    lens = [5000, 123, 7001]
+    c = host_case(3, 64, 8, 128, lens, "bf16", seed=96)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    s = torch.cuda.Stream()
+    outs = []
+    for _ in range(2):
+        o = torch.full((3, 64, 128), float("nan"), dtype=torch.float32, device="cuda")
+        torch.cuda.current_stream().synchronize()
+        with torch.cuda.stream(s):
+            B.decode(q, k, v, sl, out=o, stream=s)
+            ev = torch.cuda.Event()
+            ev.record(s)
+        ev.synchronize()
+        outs.append(o.clone())
+    compare(outs[0], ref, "side stream")
+    assert torch.equal(outs[0], outs[1])
