@@ -245,11 +245,27 @@ def main():
         },
         "cpu_baseline": None,
     }
+    # Achievable read bandwidth on this machine: the plain read probe over the
+    # same K and V bytes, timed the same way.
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    reps = 10
+    for i in range(2):
+        gqa.gqa_probe_read(d.k, d.k.numel() * d.k.element_size(), sink, stream)
+    ev_p = (hip.event(), hip.event())
+    hip.record(ev_p[0], stream)
+    for i in range(reps):
+        gqa.gqa_probe_read(d.k, d.k.numel() * d.k.element_size(), sink, stream)
+        gqa.gqa_probe_read(d.v, d.v.numel() * d.v.element_size(), sink, stream)
+    hip.record(ev_p[1], stream)
+    hip.sync(ev_p[1])
+    probe_gbs = kv_bytes * reps / (hip.ms(*ev_p) / 1e3) / 1e9
+    result["roofline"]["probe_read_gbs"] = round(probe_gbs, 1)
+    result["roofline"]["frac_of_probe_read"] = round(achieved / probe_gbs, 4)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        gqa.gqa_probe_copy(src, dst, n, stream)
         torch.cuda.synchronize()
         result["copy_probe_bytes"] = n
     if not args.no_cpu_baseline:

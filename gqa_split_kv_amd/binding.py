@@ -30,10 +30,10 @@ GQA_ERR_WORKSPACE = 6
 GQA_ERR_HIP = 7
 GQA_ERR_ARG = 8
 
-# Every function the header declares, in header order.
+# Every function include/gqa_decode.h and include/gqa_probe.h declare.
 EXPORTS = ("gqa_decode", "gqa_decode_f32", "gqa_decode_ex", "gqa_decode_validate",
            "gqa_decode_make_plan", "gqa_decode_workspace_bytes", "gqa_status_str",
-           "gqa_last_error_message", "gqa_release")
+           "gqa_last_error_message", "gqa_release", "gqa_probe_copy", "gqa_probe_read")
 
 
 class GqaArgs(ctypes.Structure):
@@ -99,6 +99,10 @@ def lib() -> ctypes.CDLL:
     L.gqa_last_error_message.restype = ctypes.c_char_p
     L.gqa_release.argtypes = []
     L.gqa_release.restype = None
+    L.gqa_probe_copy.argtypes = [P, P, ctypes.c_size_t, P]
+    L.gqa_probe_copy.restype = ctypes.c_int
+    L.gqa_probe_read.argtypes = [P, ctypes.c_size_t, P, P]
+    L.gqa_probe_read.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -245,3 +249,19 @@ def decode(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype
                      _dtype_code(out), num_chunks, min_chunk, workspace, ws_bytes, _stream(stream))
     gqa_decode_ex(args)
     return out
+
+
+def gqa_probe_copy(src, dst, nbytes: int, stream=None) -> int:
+    """Plain device copy of nbytes (measurement reference)."""
+    st = lib().gqa_probe_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_probe_copy failed")
+    return st
+
+
+def gqa_probe_read(src, nbytes: int, sink, stream=None) -> int:
+    """Plain device read of nbytes folded into *sink (measurement reference)."""
+    st = lib().gqa_probe_read(_ptr(src), int(nbytes), _ptr(sink), _stream(stream))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_probe_read failed")
+    return st

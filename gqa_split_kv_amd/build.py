@@ -43,6 +43,12 @@ def build(verbose: bool = False) -> str:
     _run([HIPCC, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *NO_PACKED_FP32, *DEVICE_FLAGS,
           "-c", src, "-o", obj], verbose)
     objs.append(obj)
+    # Measurement probes (plain copy / read kernels).
+    src = os.path.join(CSRC, "probe_kernels.hip")
+    obj = os.path.join(BUILD, "probe_kernels.o")
+    _run([HIPCC, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *NO_PACKED_FP32, "-c", src, "-o", obj],
+         verbose)
+    objs.append(obj)
     # C ABI layer: HIP runtime host API only.
     src = os.path.join(CSRC, "api.cpp")
     obj = os.path.join(BUILD, "api.o")

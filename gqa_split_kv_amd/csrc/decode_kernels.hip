@@ -9,22 +9,27 @@
 // and the owner stores O / l ("Final normalise + store").
 //
 // Mapping to one MI355X:
-//   * The page's ranks become wavefronts.  The flattened key axis -- the keys of
-//     all (sequence, kv head) pairs end to end -- is cut into equal ranges, one
-//     per wavefront (stream-K style), so ragged lengths cost no load imbalance.
-//     A range that covers a whole pair stores o itself; a pair cut across ranges
-//     leaves one partial triple per piece in a workspace, merged by merge_kernel.
-//   * A wavefront sweeps its piece in 16-key blocks.  Q K^T for the block is one
-//     to four v_mfma_f32_16x16x32_bf16 (or 16x16x4_f32 for fp32 input) with the
-//     16 keys as the M axis and the (up to 16) query heads as the N axis; K rows
-//     are loaded straight into the MFMA A-operand layout with 16-byte loads, so
-//     no LDS round trip is needed.  The d axis of the contraction is permuted
-//     (the same permutation on Q and K) so each load instruction reads 64
-//     contiguous bytes of 16 key rows.
-//   * P V runs as v_mfma_f32_16x16x4_f32 with V^T as the A operand and P^T as the
-//     B operand: each lane contributes one key per MFMA, so V rows need no
-//     transpose and P stays in fp32 (no rounding of the softmax weights).  The
-//     V loads read 4 whole key rows per instruction.
+//   * The page's ranks become wavefronts.  The flattened token axis -- the key
+//     rows of all sequences end to end -- is cut into equal ranges (stream-K
+//     style), and each range is swept by h_kv consecutive wavefronts, one per kv
+//     head, so ragged lengths cost no load imbalance and the wavefronts of one
+//     range read the adjacent kv-head slices of the same rows at the same time
+//     (contiguous DRAM traffic).  A range that covers a whole sequence stores o
+//     itself; a sequence cut across ranges leaves one partial triple per piece
+//     and kv head in a workspace, merged by merge_kernel.
+//   * A wavefront sweeps its piece in steps of 32 keys (bf16) or 16 keys (fp32).
+//     Q K^T is v_mfma_f32_16x16x32_bf16 (16x16x4_f32 for fp32 input) with the 16
+//     keys of a block as the M axis and the (up to 16) query heads as the N axis;
+//     K rows are loaded straight into the MFMA A-operand layout with 16-byte
+//     buffer loads, so no LDS round trip is needed.  The d axis of the
+//     contraction is permuted (the same permutation on Q and K) so each load
+//     instruction reads 64 contiguous bytes of 16 key rows.
+//   * P V runs on the matrix cores too, with V^T as the A operand and the keys
+//     as the contraction: for bf16 input each lane loads 16 bytes of 8 key rows
+//     (whole rows per load instruction) and repacks them in registers, and P is
+//     split into bf16 high and low parts issued as two products (so P keeps about
+//     16 significant bits); for fp32 input v_mfma_f32_16x16x4_f32 takes one key
+//     per lane and stays in fp32.
 //   * The softmax state of query head g lives in lanes with lane % 16 == g; the
 //     block maximum is reduced across the 4 lane groups with two cross-lane
 //     exchanges, l is kept per lane and reduced once per piece.  Scores are kept
@@ -33,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace gqa {
@@ -40,9 +47,23 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kBlockKeys = 16;
+constexpr int kMergeThreads = 256;
+#ifndef GQA_SWEEP_DEPTH
+#define GQA_SWEEP_DEPTH 2
+#endif
+constexpr int kSweepDepth = GQA_SWEEP_DEPTH;   // register buffers in the sweep pipeline
+// Cache policy of the K/V stream loads (buffer-instruction cache-policy bits).
+// K and V are read exactly once, so they are loaded non-temporally (nt) and do
+// not displace the partials, q and seq_lens from the caches.
+#ifndef GQA_KV_CPOL
+#define GQA_KV_CPOL 2
+#endif
+constexpr int kKvCachePolicy = GQA_KV_CPOL;
 
 // ------------------------------------------------------------------ wave helpers
 
@@ -148,37 +169,34 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return u >> 16;
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// ------------------------------------------------------------------ per-type shape
+// ------------------------------------------------------------------ loads
 
-template <bool kBf16In, int D>
-struct Shape {
-    static constexpr int ES = kBf16In ? 2 : 4;   // input element bytes
-    static constexpr int ROWB = D * ES;          // one key row of one kv head
-    static constexpr int NKP = ROWB / 64;        // 16-byte K pieces per lane per block
-    static constexpr int VEC = D / 16;           // V elements per lane per key row
-    static constexpr int VW = VEC * ES / 4;      // V 32-bit words per lane per key row
-    static constexpr int QOPS = kBf16In ? NKP : NKP * 4;   // MFMAs for Q K^T per block
-};
+// Buffer resource over `bytes` bytes at `base` (raw, stride 0): loads at offsets
+// at or beyond `bytes` return zero without touching memory.  Both inputs are
+// wave-uniform; readfirstlane makes that visible to the compiler so the resource
+// lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t *base, uint32_t bytes) {
+    const int64_t a = uniform64(reinterpret_cast<int64_t>(base));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<uint8_t *>(a), 0,
+                                             uniform32(static_cast<int>(bytes)), 0x00020000);
+}
 
-template <bool kBf16In, int D>
-struct Block {
-    uint4 k[Shape<kBf16In, D>::NKP];
-    uint32_t v[4][Shape<kBf16In, D>::VW];
-};
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kKvCachePolicy);
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
 
 template <int NW>
-__device__ __forceinline__ void load_words(uint32_t (&dst)[NW], const uint8_t *p) {
+__device__ __forceinline__ void load_words(uint32_t (&dst)[NW], __amdgpu_buffer_rsrc_t r, uint32_t off) {
     if constexpr (NW == 2) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(p);
-        dst[0] = x.x;
-        dst[1] = x.y;
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kKvCachePolicy);
+        dst[0] = x[0];
+        dst[1] = x[1];
     } else {
 #pragma unroll
         for (int i = 0; i < NW / 4; ++i) {
-            const uint4 x = *reinterpret_cast<const uint4 *>(p + 16 * i);
+            const uint4 x = load16(r, off + 16 * i);
             dst[4 * i + 0] = x.x;
             dst[4 * i + 1] = x.y;
             dst[4 * i + 2] = x.z;
@@ -187,109 +205,192 @@ __device__ __forceinline__ void load_words(uint32_t (&dst)[NW], const uint8_t *p
     }
 }
 
-// Loads one 16-key block (keys [16*blk, 16*blk + 16) of the piece, clamped to the
-// last valid key so every address stays inside the piece).  The block base is
-// wave-uniform and the lane offsets are 32-bit, so the loads take the
-// scalar-base + vector-offset form.
-template <bool kBf16In, int D>
-__device__ __forceinline__ void load_block(Block<kBf16In, D> &B, const uint8_t *kbase,
-                                           const uint8_t *vbase, int rowstride, int blk, int nkeys) {
-    using S = Shape<kBf16In, D>;
-    const int lane = lane_id();
-    const int m = lane & 15;
-    const int kg = lane >> 4;
-    const int last = min(kBlockKeys, nkeys - blk * kBlockKeys) - 1;
-    const int64_t boff = static_cast<int64_t>(blk) * kBlockKeys * rowstride;
-    const uint8_t *kb = kbase + boff;
-    const uint8_t *vb = vbase + boff;
-    // K: lane -> key m of the block, bytes [64p + 16kg, +16) of the row.
-    const uint32_t koff = static_cast<uint32_t>(min(m, last) * rowstride + 16 * kg);
+// Online-softmax update of one step's scores (the page's running merge of the
+// step's (m, l, O) into the state): the scores of head lane%16 are reduced
+// across the four lane groups, the state is rescaled by 2^(m_old - m_new) and
+// p = 2^(s - m_new) is returned in place of s.
+template <int N, int VEC>
+__device__ __forceinline__ void softmax_step(float (&sv)[N], float &m_run, float &l_run,
+                                             f32x4_t (&acc)[VEC]) {
+    float mx = sv[0];
 #pragma unroll
-    for (int p = 0; p < S::NKP; ++p) B.k[p] = *reinterpret_cast<const uint4 *>(kb + koff + 64 * p);
-    // V: lane -> key 4kg + r of the block, elements [VEC*m, VEC*m + VEC) of the row.
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint32_t voff = static_cast<uint32_t>(min(4 * kg + r, last) * rowstride + m * S::VEC * S::ES);
-        load_words<S::VW>(B.v[r], vb + voff);
-    }
-}
-
-// Q K^T of one block: s[q] = score of key 4*kg + q against query head lane%16.
-template <bool kBf16In, int D>
-__device__ __forceinline__ f32x4_t qk_block(const Block<kBf16In, D> &B,
-                                            const uint4 (&qop)[Shape<kBf16In, D>::NKP]) {
-    using S = Shape<kBf16In, D>;
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < S::NKP; ++p) {
-        if constexpr (kBf16In) {
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, B.k[p]),
-                                                        __builtin_bit_cast(bf16x8_t, qop[p]), s, 0,
-                                                        0, 0);
-        } else {
-            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(B.k[p].x),
-                                                     __uint_as_float(qop[p].x), s, 0, 0, 0);
-            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(B.k[p].y),
-                                                     __uint_as_float(qop[p].y), s, 0, 0, 0);
-            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(B.k[p].z),
-                                                     __uint_as_float(qop[p].z), s, 0, 0, 0);
-            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(B.k[p].w),
-                                                     __uint_as_float(qop[p].w), s, 0, 0, 0);
-        }
-    }
-    return s;
-}
-
-// O[c] += V^T P^T for one block: acc[c][q] holds O[g = lane%16][d = VEC*(4kg+q) + c].
-template <bool kBf16In, int D>
-__device__ __forceinline__ void pv_block(const Block<kBf16In, D> &B, const float (&p)[4],
-                                         f32x4_t (&acc)[Shape<kBf16In, D>::VEC]) {
-    using S = Shape<kBf16In, D>;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        float vf[S::VEC];
-        if constexpr (kBf16In) {
-#pragma unroll
-            for (int w = 0; w < S::VW; ++w) {
-                vf[2 * w] = bf16_lo(B.v[r][w]);
-                vf[2 * w + 1] = bf16_hi(B.v[r][w]);
-            }
-        } else {
-#pragma unroll
-            for (int w = 0; w < S::VW; ++w) vf[w] = __uint_as_float(B.v[r][w]);
-        }
-#pragma unroll
-        for (int c = 0; c < S::VEC; ++c)
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[c], p[r], acc[c], 0, 0, 0);
-    }
-}
-
-// One block of the sweep: scores, online-softmax update (the page's running
-// merge of the block's (m, l, O) into the state), and P V.
-template <bool kBf16In, int D>
-__device__ __forceinline__ void block_step(const Block<kBf16In, D> &B,
-                                           const uint4 (&qop)[Shape<kBf16In, D>::NKP], int nvalid,
-                                           int kg, float sl2, float &m_run, float &l_run,
-                                           f32x4_t (&acc)[Shape<kBf16In, D>::VEC]) {
-    using S = Shape<kBf16In, D>;
-    const f32x4_t s = qk_block<kBf16In, D>(B, qop);
-    float sv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sv[q] = (4 * kg + q < nvalid) ? s[q] * sl2 : -INFINITY;
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    for (int i = 1; i < N; ++i) mx = fmaxf(mx, sv[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first block
-    float p[4];
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first step
+    float sum = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) p[q] = __builtin_amdgcn_exp2f(sv[q] - m_new);
-    l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    for (int i = 0; i < N; ++i) {
+        sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
+        sum += sv[i];
+    }
+    l_run = l_run * alpha + sum;
 #pragma unroll
-    for (int c = 0; c < S::VEC; ++c) acc[c] *= alpha;
+    for (int c = 0; c < VEC; ++c) acc[c] *= alpha;
     m_run = m_new;
-    pv_block<kBf16In, D>(B, p, acc);
 }
+
+// ------------------------------------------------------------------ bf16 steps
+//
+// One step = 32 keys.  Q K^T: two v_mfma_f32_16x16x32_bf16 groups (16 keys each)
+// with K rows as the A operand (M = keys) and Q^T as B (N = query heads); lane l
+// of QK block b loads key row 8*(m/4) + 4b + m%4 (m = l%16), so that after the
+// product lane l holds the scores of keys 8*kg + i (kg = l/16, i = 0..7) of its
+// head -- exactly the eight keys it contributes to the P V product below.
+//
+// P V: O^T[d][g] += V^T[d][key] P^T[key][g] as v_mfma_f32_16x16x32_bf16 with
+// the 32 keys as the contraction.  Lane l loads 16 bytes (8 d) of key rows
+// 8*kg + i, i = 0..7 (each load instruction reads four whole rows), and repacks
+// them in registers so its A operand for column c holds d = VEC*(l%16) + c of its
+// eight keys.  P is split into a bf16 high part (round to nearest) and a bf16
+// low part (the rounded remainder) and the product is issued twice, so P keeps
+// ~16 significant bits; V, Q and K are exact in bf16.
+template <int D>
+struct Bf16Step {
+    static constexpr int kKeys = 32;
+    static constexpr int ES = 2;
+    static constexpr int ROWB = D * ES;
+    static constexpr int NKP = ROWB / 64;   // 16-byte K pieces per lane per 16-key block
+    static constexpr int VEC = D / 16;      // d elements per lane per key row
+    static constexpr int VW = VEC / 2;      // 32-bit words per lane per V row
+    struct Buf {
+        uint4 k[2][NKP];
+        uint32_t v[8][VW];
+    };
+    struct Lanes {
+        uint32_t k[2];   // + 64p: K row of block b, bytes [16kg + 64p, +16)
+        uint32_t v[8];   // V row 8kg + i, elements [VEC*m, VEC*m + VEC)
+        __device__ __forceinline__ explicit Lanes(int rowstride) {
+            const int lane = lane_id();
+            const int m = lane & 15;
+            const int kg = lane >> 4;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                k[b] = static_cast<uint32_t>((8 * (m >> 2) + 4 * b + (m & 3)) * rowstride + 16 * kg);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = static_cast<uint32_t>((8 * kg + i) * rowstride + m * VEC * ES);
+        }
+    };
+    __device__ __forceinline__ static void load(Buf &B, __amdgpu_buffer_rsrc_t rk,
+                                                __amdgpu_buffer_rsrc_t rv, const Lanes &lo) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int p = 0; p < NKP; ++p) B.k[b][p] = load16(rk, lo.k[b] + 64 * p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) load_words<VW>(B.v[i], rv, lo.v[i]);
+    }
+    __device__ __forceinline__ static void compute(const Buf &B, const uint4 (&qop)[NKP], int nvalid,
+                                                   int kg, float sl2, float &m_run, float &l_run,
+                                                   f32x4_t (&acc)[VEC]) {
+        float sv[8];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < NKP; ++p)
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, B.k[b][p]),
+                                                            __builtin_bit_cast(bf16x8_t, qop[p]), s,
+                                                            0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                sv[4 * b + q] = (8 * kg + 4 * b + q < nvalid) ? s[q] * sl2 : -INFINITY;
+        }
+        softmax_step<8, VEC>(sv, m_run, l_run, acc);
+        // P = hi + lo, both bf16, packed two keys per word (key 2w in the low half).
+        uint32_t phi[4], plo[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const f32x2_t pw = {sv[2 * w], sv[2 * w + 1]};
+            const bf16x2_t h = __builtin_convertvector(pw, bf16x2_t);
+            const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+            const f32x2_t r = {pw[0] - __uint_as_float(hb << 16), pw[1] - __uint_as_float(hb & 0xffff0000u)};
+            phi[w] = hb;
+            plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+        }
+        const bf16x8_t bhi = __builtin_bit_cast(bf16x8_t, make_uint4(phi[0], phi[1], phi[2], phi[3]));
+        const bf16x8_t blo = __builtin_bit_cast(bf16x8_t, make_uint4(plo[0], plo[1], plo[2], plo[3]));
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+            // A operand of column c: element i = V[key 8kg + i][d = VEC*m + c].
+            uint32_t a[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x = B.v[2 * w][c >> 1];
+                const uint32_t y = B.v[2 * w + 1][c >> 1];
+                a[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+            }
+            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(a[0], a[1], a[2], a[3]));
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bhi, acc[c], 0, 0, 0);
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, blo, acc[c], 0, 0, 0);
+        }
+    }
+};
+
+// ------------------------------------------------------------------ fp32 steps
+//
+// One step = 16 keys.  Q K^T as v_mfma_f32_16x16x4_f32 (K rows as A, M = keys;
+// lane l loads key m = l%16), P V as v_mfma_f32_16x16x4_f32 with V^T as A and
+// P^T as B: lane l loads key rows 4*kg + r and contributes one key per product,
+// so neither operand needs a transpose and everything stays in fp32.
+template <int D>
+struct F32Step {
+    static constexpr int kKeys = 16;
+    static constexpr int ES = 4;
+    static constexpr int ROWB = D * ES;
+    static constexpr int NKP = ROWB / 64;   // 16-byte K pieces per lane per step
+    static constexpr int VEC = D / 16;
+    static constexpr int VW = VEC;          // 32-bit words per lane per V row
+    struct Buf {
+        uint4 k[NKP];
+        uint32_t v[4][VW];
+    };
+    struct Lanes {
+        uint32_t k;
+        uint32_t v[4];
+        __device__ __forceinline__ explicit Lanes(int rowstride) {
+            const int lane = lane_id();
+            const int m = lane & 15;
+            const int kg = lane >> 4;
+            k = static_cast<uint32_t>(m * rowstride + 16 * kg);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = static_cast<uint32_t>((4 * kg + r) * rowstride + m * VEC * ES);
+        }
+    };
+    __device__ __forceinline__ static void load(Buf &B, __amdgpu_buffer_rsrc_t rk,
+                                                __amdgpu_buffer_rsrc_t rv, const Lanes &lo) {
+#pragma unroll
+        for (int p = 0; p < NKP; ++p) B.k[p] = load16(rk, lo.k + 64 * p);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) load_words<VW>(B.v[r], rv, lo.v[r]);
+    }
+    __device__ __forceinline__ static void compute(const Buf &B, const uint4 (&qop)[NKP], int nvalid,
+                                                   int kg, float sl2, float &m_run, float &l_run,
+                                                   f32x4_t (&acc)[VEC]) {
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < NKP; ++p) {
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(B.k[p].x), __uint_as_float(qop[p].x), s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(B.k[p].y), __uint_as_float(qop[p].y), s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(B.k[p].z), __uint_as_float(qop[p].z), s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(B.k[p].w), __uint_as_float(qop[p].w), s, 0, 0, 0);
+        }
+        float sv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sv[q] = (4 * kg + q < nvalid) ? s[q] * sl2 : -INFINITY;
+        softmax_step<4, VEC>(sv, m_run, l_run, acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < VEC; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(B.v[r][c]), sv[r], acc[c], 0, 0, 0);
+    }
+};
+
+template <bool kBf16In, int D>
+using Step = typename std::conditional<kBf16In, Bf16Step<D>, F32Step<D>>::type;
 
 template <bool kBf16Out>
 __device__ __forceinline__ void store_row(uint8_t *dst, const float *x, int n);
@@ -314,17 +415,19 @@ __device__ __forceinline__ void store_row<false>(uint8_t *dst, const float *x, i
 }
 
 // One piece: keys [t0, t1) of (sequence b, kv head j); off = keys before b.
-template <bool kBf16In, bool kBf16Out, int D>
+template <bool kBf16In, bool kBf16Out, int D, int kDepth>
 __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int j, int64_t off,
                                               int t0, int t1, int len, int w) {
-    using S = Shape<kBf16In, D>;
+    using S = Step<kBf16In, D>;
+    constexpr int VEC = S::VEC;
     const int lane = lane_id();
     const int g = lane & 15;
     const int kg = lane >> 4;
     const int G = P.G;
     const int rowstride = P.h_kv * S::ROWB;
 
-    // Q operand: query head j*G + g, bytes [64p + 16kg, +16) of its row (zero for g >= G).
+    // Q operand: query head j*G + g, bytes [64p + 16kg, +16) of its row (zero for g >= G):
+    // the same d permutation as the K rows, so the contraction covers every d once.
     uint4 qop[S::NKP];
     {
         const int gq = g < G ? g : G - 1;
@@ -336,152 +439,198 @@ __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int 
         }
     }
 
-    f32x4_t acc[S::VEC];
+    f32x4_t acc[VEC];
 #pragma unroll
-    for (int c = 0; c < S::VEC; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < VEC; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY;
     float l_run = 0.f;
 
     const int nkeys = t1 - t0;
-    const int nblk = (nkeys + kBlockKeys - 1) / kBlockKeys;
+    const int nstep = (nkeys + S::kKeys - 1) / S::kKeys;
     const int64_t row0 = (off + t0) * P.h_kv + j;
     const uint8_t *kbase = P.k + row0 * S::ROWB;
     const uint8_t *vbase = P.v + row0 * S::ROWB;
     const float sl2 = P.scale_log2;
+    const typename S::Lanes lo(rowstride);
 
-    // Software pipeline over two register buffers: the loads of block blk+1 are in
-    // flight while block blk is computed.  The prefetch index is clamped so the
-    // loads are unconditional (the last block is fetched twice, from cache).
-    Block<kBf16In, D> bufA, bufB;
-    load_block<kBf16In, D>(bufA, kbase, vbase, rowstride, 0, nkeys);
-    int blk = 0;
+    // Step st covers keys [kKeys*st, kKeys*st + kKeys) of the piece; its buffer
+    // resources span exactly its valid rows, so rows past the piece read as zero
+    // (and their scores are masked to -inf).
+    auto load_step = [&](typename S::Buf &B, int st) {
+        const int nvalid = min(S::kKeys, nkeys - st * S::kKeys);
+        const int64_t boff = static_cast<int64_t>(st) * S::kKeys * rowstride;
+        const uint32_t bytes = static_cast<uint32_t>(nvalid * rowstride);
+        S::load(B, buffer_rsrc(kbase + boff, bytes), buffer_rsrc(vbase + boff, bytes), lo);
+    };
+
+    // Software pipeline over kDepth register buffers: the loads of the next
+    // kDepth-1 steps are in flight while a step is computed.  Prefetch indices
+    // are clamped so every load is unconditional (the last step is fetched again,
+    // from cache, instead of branching).
+    typename S::Buf buf[kDepth];
+#pragma unroll
+    for (int u = 0; u + 1 < kDepth; ++u) load_step(buf[u], min(u, nstep - 1));
+    int st = 0;
     while (true) {
-        load_block<kBf16In, D>(bufB, kbase, vbase, rowstride, min(blk + 1, nblk - 1), nkeys);
-        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
-        block_step<kBf16In, D>(bufA, qop, min(kBlockKeys, nkeys - blk * kBlockKeys), kg, sl2, m_run,
-                               l_run, acc);
-        if (++blk == nblk) break;
-        load_block<kBf16In, D>(bufA, kbase, vbase, rowstride, min(blk + 1, nblk - 1), nkeys);
-        __builtin_amdgcn_sched_barrier(0);
-        block_step<kBf16In, D>(bufB, qop, min(kBlockKeys, nkeys - blk * kBlockKeys), kg, sl2, m_run,
-                               l_run, acc);
-        if (++blk == nblk) break;
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+            load_step(buf[(u + kDepth - 1) % kDepth], min(st + kDepth - 1, nstep - 1));
+            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
+            S::compute(buf[u], qop, min(S::kKeys, nkeys - st * S::kKeys), kg, sl2, m_run, l_run, acc);
+            if (++st == nstep) goto swept;
+        }
     }
+swept:
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
 
-    // The lane's outputs: d in [4*VEC*kg, 4*VEC*kg + 4*VEC), index q*VEC + c.
-    float out[4 * S::VEC];
+    // The lane's outputs: O[g][d] for d in [4*VEC*kg, 4*VEC*kg + 4*VEC), index q*VEC + c.
+    float out[4 * VEC];
     if (t0 == 0 && t1 == len) {
-        // The whole (sequence, kv head) was in this range: normalise and store.
+        // The whole sequence was in this range: normalise and store.
         const float inv = 1.0f / l_tot;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int c = 0; c < S::VEC; ++c) out[q * S::VEC + c] = acc[c][q] * inv;
+            for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[c][q] * inv;
         if (g < G) {
             const int64_t orow = static_cast<int64_t>(b) * P.h_q + j * G + g;
-            uint8_t *dst = P.o + (orow * D + 4 * S::VEC * kg) * (kBf16Out ? 2 : 4);
-            store_row<kBf16Out>(dst, out, 4 * S::VEC);
+            uint8_t *dst = P.o + (orow * D + 4 * VEC * kg) * (kBf16Out ? 2 : 4);
+            store_row<kBf16Out>(dst, out, 4 * VEC);
         }
     } else {
-        // Slot 0: a piece of a pair that began before this range; slot 1: the
-        // first piece of a pair that continues past it.
+        // Slot 0: a piece of a sequence that began before this range; slot 1: the
+        // first piece of a sequence that continues past it.
         const int slot = (t0 > 0) ? 0 : 1;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int c = 0; c < S::VEC; ++c) out[q * S::VEC + c] = acc[c][q];
+            for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[c][q];
         if (g < G) {
             const int64_t srow = (static_cast<int64_t>(w) * 2 + slot) * G + g;
-            store_row<false>(reinterpret_cast<uint8_t *>(P.ws_o + srow * D + 4 * S::VEC * kg), out,
-                             4 * S::VEC);
+            store_row<false>(reinterpret_cast<uint8_t *>(P.ws_o + srow * D + 4 * VEC * kg), out, 4 * VEC);
             if (kg == 0) P.ws_ml[srow] = make_float2(m_run, l_tot);
         }
     }
 }
 
-template <bool kBf16In, bool kBf16Out, int D>
+template <bool kBf16In, bool kBf16Out, int D, int kDepth>
 __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
     const int w = uniform32(static_cast<int>(blockIdx.x) * kWavesPerBlock +
                             static_cast<int>(threadIdx.x) / kWave);
     if (w >= P.num_chunks) return;
-    const int64_t total = static_cast<int64_t>(P.h_kv) * total_len(P.seq_lens, P.batch);
-    const int64_t chunk = chunk_keys(total, P.num_chunks, P.min_chunk);
-    int64_t pos = static_cast<int64_t>(w) * chunk;
+    // Wavefront w sweeps kv head j over token range c of the flattened token axis;
+    // the h_kv wavefronts of one range are consecutive, so they stream the
+    // adjacent kv-head slices of the same key rows at the same time.
+    const int j = w % P.h_kv;
+    const int c = w / P.h_kv;
+    const int64_t total = total_len(P.seq_lens, P.batch);
+    const int64_t chunk = chunk_keys(total, P.num_chunks / P.h_kv, P.min_chunk);
+    int64_t pos = static_cast<int64_t>(c) * chunk;
     if (pos >= total) return;
     const int64_t end = pos + chunk < total ? pos + chunk : total;
     int b, len;
     int64_t off;
-    locate(P.seq_lens, P.batch, P.h_kv, pos, b, off, len);
+    locate(P.seq_lens, P.batch, 1, pos, b, off, len);
     while (true) {
-        const int64_t seq_start = off * P.h_kv;
-        const int j = uniform32(static_cast<int>((pos - seq_start) / len));
-        const int64_t ustart = seq_start + static_cast<int64_t>(j) * len;
-        const int t0 = uniform32(static_cast<int>(pos - ustart));
-        const int64_t lim = end - ustart;
+        const int t0 = uniform32(static_cast<int>(pos - off));
+        const int64_t lim = end - off;
         const int t1 = uniform32(static_cast<int>(lim < len ? lim : len));
-        process_piece<kBf16In, kBf16Out, D>(P, b, j, off, t0, t1, len, w);
-        pos = ustart + t1;
+        process_piece<kBf16In, kBf16Out, D, kDepth>(P, b, j, off, t0, t1, len, w);
+        pos = off + t1;
         if (pos >= end) break;
-        if (j + 1 == P.h_kv) {   // next non-empty sequence (one exists: pos < total)
-            off += len;
-            do {
-                ++b;
-                len = uniform32(seq_len_at(P.seq_lens, b));
-            } while (len == 0);
-        }
+        off += len;   // next non-empty sequence (one exists: pos < total)
+        do {
+            ++b;
+            len = uniform32(seq_len_at(P.seq_lens, b));
+        } while (len == 0);
     }
 }
 
 // Merge of the pieces of one (sequence, kv head): for every query head g and
 // element d, M = max m_s, L = sum l_s 2^(m_s - M), o = sum O_s 2^(m_s - M) / L,
-// pieces in ascending order.  Also writes zeros for an empty sequence.
+// with the pieces taken in ascending order, eight at a time (their loads in
+// flight together) and folded into a running (M, L, acc) with the same
+// rescaling rule.  Each thread owns four consecutive d of one head (16-byte
+// loads).  Also writes zeros for an empty sequence.
 template <bool kBf16Out, int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams P) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams P) {
+    constexpr int kPieces = 8;
     const int b = static_cast<int>(blockIdx.x) / P.h_kv;
     const int j = static_cast<int>(blockIdx.x) % P.h_kv;
     const int G = P.G;
     const int len = uniform32(seq_len_at(P.seq_lens, b));
     uint8_t *obase = P.o + (static_cast<int64_t>(b) * P.h_q + j * G) * D * (kBf16Out ? 2 : 4);
-    const int n = G * D;
+    const int n4 = G * D / 4;
     if (len == 0) {
-        for (int e = threadIdx.x; e < n; e += kThreads) {
+        for (int e = threadIdx.x; e < n4; e += kMergeThreads) {
             if constexpr (kBf16Out)
-                reinterpret_cast<uint16_t *>(obase)[e] = 0;
+                reinterpret_cast<uint2 *>(obase)[e] = make_uint2(0, 0);
             else
-                reinterpret_cast<float *>(obase)[e] = 0.f;
+                reinterpret_cast<float4 *>(obase)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
         return;
     }
-    const int64_t total = static_cast<int64_t>(P.h_kv) * total_len(P.seq_lens, P.batch);
-    const int64_t chunk = chunk_keys(total, P.num_chunks, P.min_chunk);
-    const int64_t ustart = prefix_len(P.seq_lens, b) * P.h_kv + static_cast<int64_t>(j) * len;
-    const int64_t wa = ustart / chunk;
-    const int64_t wb = (ustart + len - 1) / chunk;
-    if (wa == wb) return;   // written whole by the partial kernel
-    for (int e = threadIdx.x; e < n; e += kThreads) {
-        const int g = e / D;
-        const int d = e - g * D;
-        float M = -INFINITY;
-        for (int64_t s = wa; s <= wb; ++s) {
-            const int64_t srow = (s * 2 + (s == wa ? 1 : 0)) * G + g;
-            M = fmaxf(M, P.ws_ml[srow].x);
+    const int64_t total = total_len(P.seq_lens, P.batch);
+    const int64_t chunk = chunk_keys(total, P.num_chunks / P.h_kv, P.min_chunk);
+    const int64_t ustart = prefix_len(P.seq_lens, b);
+    const int64_t ca = ustart / chunk;              // token ranges holding this sequence
+    const int64_t cb = (ustart + len - 1) / chunk;
+    if (ca == cb) return;   // written whole by the partial kernel
+    for (int e = threadIdx.x; e < n4; e += kMergeThreads) {
+        const int g = (4 * e) / D;
+        const int d = 4 * e - g * D;
+        float M = -INFINITY, L = 0.f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int64_t s0 = ca; s0 <= cb; s0 += kPieces) {
+            float2 ml[kPieces];
+            float4 ov[kPieces];
+#pragma unroll
+            for (int i = 0; i < kPieces; ++i) {
+                const int64_t s = s0 + i;
+                if (s <= cb) {
+                    // range s was swept by wavefront s*h_kv + j; the first piece sits
+                    // in slot 1 of its wavefront, the others in slot 0
+                    const int64_t wv = s * P.h_kv + j;
+                    const int64_t srow = (wv * 2 + (s == ca ? 1 : 0)) * G + g;
+                    ml[i] = P.ws_ml[srow];
+                    ov[i] = *reinterpret_cast<const float4 *>(P.ws_o + srow * D + d);
+                } else {
+                    ml[i] = make_float2(-INFINITY, 0.f);
+                    ov[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+            float mb = ml[0].x;
+#pragma unroll
+            for (int i = 1; i < kPieces; ++i) mb = fmaxf(mb, ml[i].x);
+            const float Mn = fmaxf(M, mb);
+            const float a = __builtin_amdgcn_exp2f(M - Mn);
+            L *= a;
+            acc.x *= a;
+            acc.y *= a;
+            acc.z *= a;
+            acc.w *= a;
+#pragma unroll
+            for (int i = 0; i < kPieces; ++i) {
+                const float f = __builtin_amdgcn_exp2f(ml[i].x - Mn);
+                L += f * ml[i].y;
+                acc.x += f * ov[i].x;
+                acc.y += f * ov[i].y;
+                acc.z += f * ov[i].z;
+                acc.w += f * ov[i].w;
+            }
+            M = Mn;
         }
-        float L = 0.f, acc = 0.f;
-        for (int64_t s = wa; s <= wb; ++s) {
-            const int64_t srow = (s * 2 + (s == wa ? 1 : 0)) * G + g;
-            const float2 ml = P.ws_ml[srow];
-            const float f = __builtin_amdgcn_exp2f(ml.x - M);
-            L += f * ml.y;
-            acc += f * P.ws_o[srow * D + d];
+        const float inv = 1.0f / L;
+        if constexpr (kBf16Out) {
+            reinterpret_cast<uint2 *>(obase)[e] =
+                make_uint2(bf16_rne(acc.x * inv) | (bf16_rne(acc.y * inv) << 16),
+                           bf16_rne(acc.z * inv) | (bf16_rne(acc.w * inv) << 16));
+        } else {
+            reinterpret_cast<float4 *>(obase)[e] =
+                make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
         }
-        const float r = acc / L;
-        if constexpr (kBf16Out)
-            reinterpret_cast<uint16_t *>(obase)[e] = static_cast<uint16_t>(bf16_rne(r));
-        else
-            reinterpret_cast<float *>(obase)[e] = r;
     }
 }
 
@@ -490,19 +639,19 @@ hipError_t launch_variant(const DecodeParams &P, int split_blocks, int merge_blo
                           hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
     hipError_t e;
     if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL((split_kernel<kBf16In, kBf16Out, D>), dim3(split_blocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL((split_kernel<kBf16In, kBf16Out, D, kSweepDepth>), dim3(split_blocks), dim3(kThreads), 0,
                        stream, P);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_kernel<kBf16Out, D>), dim3(merge_blocks), dim3(kThreads), 0, stream, P);
+    hipLaunchKernelGGL((merge_kernel<kBf16Out, D>), dim3(merge_blocks), dim3(kMergeThreads), 0, stream, P);
     return hipGetLastError();
 }
 
 template <bool kBf16In, bool kBf16Out, int D>
 hipError_t occupancy_variant(int *blocks_per_cu) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu,
-                                                        split_kernel<kBf16In, kBf16Out, D>, kThreads, 0);
+                                                        split_kernel<kBf16In, kBf16Out, D, kSweepDepth>, kThreads, 0);
 }
 
 }  // namespace

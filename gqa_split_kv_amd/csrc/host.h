@@ -10,13 +10,24 @@
 
 namespace gqa {
 
-constexpr int kWavesPerBlock = 4;   // wavefronts per workgroup of the partial kernel
+#ifndef GQA_SWEEP_WAVES
+#define GQA_SWEEP_WAVES 4
+#endif
+// Wavefronts per workgroup of the sweep kernel.
+constexpr int kWavesPerBlock = GQA_SWEEP_WAVES;
 constexpr int kThreads = 64 * kWavesPerBlock;
 constexpr int kMaxG = 16;           // query heads per kv head held by one 16-wide MFMA tile
 constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxHeadsKv = 1 << 16;   // keeps 16 key rows of lane offsets within 32 bits
 constexpr int kMaxMinChunk = 1 << 30;
-constexpr int kAutoMinChunk = 32;   // default smallest key range per wavefront
+constexpr int kAutoMinChunk = 32;   // default smallest token range
+// Automatic plan: at most this many sweep wavefronts per compute unit, i.e. one
+// per SIMD.  Measured on MI355X (70B-shaped ragged batch): with the MFMA-based
+// step the SIMD is lightly loaded, one wavefront per SIMD with one step of
+// prefetch saturates HBM, and a second wavefront on the same SIMD only competes
+// for issue (the younger one is served later, which leaves a tail at the end of
+// the equal-work stream-K sweep).
+constexpr int kAutoWavesPerCu = 4;
 
 // Sets the thread-local error message and returns `status`.
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));

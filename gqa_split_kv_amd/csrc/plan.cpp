@@ -95,7 +95,9 @@ int validate(const gqa_decode_args *a) {
     int st = check_basic(a);
     if (st != GQA_OK) return st;
     if (a->num_chunks > 0) {
-        const WorkspaceLayout L = workspace_layout(a->num_chunks, a->h_q / a->h_kv, a->d_head);
+        int64_t chunks = static_cast<int64_t>(a->num_chunks) / a->h_kv * a->h_kv;
+        if (chunks < a->h_kv) chunks = a->h_kv;
+        const WorkspaceLayout L = workspace_layout(chunks, a->h_q / a->h_kv, a->d_head);
         st = check_workspace(a, L.bytes);
         if (st != GQA_OK) return st;
     }
@@ -111,9 +113,13 @@ int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decod
         if (num_cus <= 0 || waves_per_cu <= 0)
             return fail(GQA_ERR_ARG, "automatic num_chunks needs num_cus (%d) and waves_per_cu (%d) > 0",
                         num_cus, waves_per_cu);
-        chunks = static_cast<int64_t>(num_cus) * waves_per_cu;
+        chunks = static_cast<int64_t>(num_cus) * (waves_per_cu < kAutoWavesPerCu ? waves_per_cu : kAutoWavesPerCu);
         if (chunks > kMaxChunks) chunks = kMaxChunks;
     }
+    // One wavefront per kv head of every token range: a multiple of h_kv.
+    chunks = chunks / a->h_kv * a->h_kv;
+    if (chunks < a->h_kv) chunks = a->h_kv;
+    if (chunks > kMaxChunks) return fail(GQA_ERR_ARG, "h_kv %d needs more than %d wavefronts", a->h_kv, kMaxChunks);
     const WorkspaceLayout L = workspace_layout(chunks, a->h_q / a->h_kv, a->d_head);
     st = check_workspace(a, L.bytes);
     if (st != GQA_OK) return st;

@@ -92,15 +92,17 @@ int gqa_decode_f32(const void *q, const void *k, const void *v, void *o,
 /*
  * Full argument block.  Zero-initialise it, then set the fields.
  *
- * num_chunks  The flattened key axis -- every (sequence, kv head) pair's keys laid
- *             end to end, h_kv * sum(seq_lens) keys in all -- is cut into equal
- *             ranges of `chunk` keys, one range per wavefront, where
- *               chunk = max(min_chunk, ceil(total / num_chunks))
- *             is computed on the device from seq_lens.  A range that covers a whole
- *             (sequence, kv head) writes o directly; the pieces of a pair that spans
- *             several ranges are merged by a second kernel.  0 = automatic (compute
- *             units x resident wavefronts per compute unit).  Range: 0..2^24.
- * min_chunk   Smallest range in keys; 0 = automatic.  Range: 0..2^30.
+ * num_chunks  Wavefronts of the sweep.  The token axis -- the key rows of all
+ *             sequences end to end, sum(seq_lens) rows -- is cut into
+ *             num_chunks / h_kv equal ranges of `chunk` rows, where
+ *               chunk = max(min_chunk, ceil(sum(seq_lens) / (num_chunks / h_kv)))
+ *             is computed on the device from seq_lens, and each range is swept by
+ *             h_kv wavefronts, one per kv head.  A range that holds a whole
+ *             sequence writes its o rows directly; the pieces of a sequence that
+ *             spans several ranges are merged by a second kernel.  Rounded down to
+ *             a multiple of h_kv (at least h_kv).  0 = automatic (compute units x
+ *             resident wavefronts per compute unit).  Range: 0..2^24.
+ * min_chunk   Smallest range in key rows; 0 = automatic.  Range: 0..2^30.
  *             min_chunk = 1024 with a large num_chunks reproduces the page's
  *             1024-key tiles as the split granularity.
  * workspace   Device scratch for the partial triples, at least
@@ -154,8 +156,8 @@ int gqa_decode_validate(const gqa_decode_args *args);
  * num_cus * waves_per_cu.  Returns GQA_OK or the validation status.
  */
 typedef struct gqa_decode_plan {
-    int32_t num_chunks;      /* wavefronts launched = ranges of the key axis       */
-    int32_t min_chunk;       /* smallest range in keys                             */
+    int32_t num_chunks;      /* wavefronts launched (h_kv per token range)         */
+    int32_t min_chunk;       /* smallest token range in key rows                   */
     int32_t split_blocks;    /* workgroups of the partial kernel (4 wavefronts)    */
     int32_t merge_blocks;    /* workgroups of the merge kernel (batch * h_kv)      */
     size_t workspace_bytes;  /* partial-triple scratch the call needs              */

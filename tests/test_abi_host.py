@@ -12,7 +12,8 @@ import pytest
 from gqa_split_kv_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gqa_decode.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -24,10 +25,12 @@ def lib():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?(?:int|void|size_t|char)\s*\*?\s*(gqa_\w+)\s*\(", text, flags=re.M)
-    return sorted(set(names))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?(?:int|void|size_t|char)\s*\*?\s*(gqa_\w+)\s*\(",
+                                text, flags=re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function(lib):
@@ -109,7 +112,8 @@ def test_workspace_size_checked_with_explicit_chunks(lib):
     assert st == B.GQA_OK
     need = plan.workspace_bytes
     G, D = 4, 128
-    assert need >= 100 * 2 * G * (D + 2) * 4
+    assert plan.num_chunks == 96          # rounded down to a multiple of h_kv = 8
+    assert need >= 96 * 2 * G * (D + 2) * 4
     assert need % 256 == 0
     assert _validate(num_chunks=100, workspace=0x100000, workspace_bytes=need) == B.GQA_OK
     assert _validate(num_chunks=100, workspace=0x100000, workspace_bytes=need - 1) == B.GQA_ERR_WORKSPACE
@@ -121,13 +125,19 @@ def test_workspace_size_checked_with_explicit_chunks(lib):
 def test_plan_automatic_and_explicit(lib):
     st, plan = B.gqa_decode_make_plan(_args(), 256, 8)
     assert st == B.GQA_OK
-    assert plan.num_chunks == 256 * 8
-    assert plan.split_blocks == (256 * 8 + 3) // 4
+    assert plan.num_chunks == 256 * 4                       # one wavefront per SIMD
+    assert plan.split_blocks == 256                         # 4-wave workgroups
     assert plan.merge_blocks == 4 * 8
     assert plan.min_chunk > 0
     st, plan = B.gqa_decode_make_plan(_args(num_chunks=7, min_chunk=1024), 256, 8)
     assert st == B.GQA_OK
-    assert (plan.num_chunks, plan.min_chunk, plan.split_blocks) == (7, 1024, 2)
+    assert (plan.num_chunks, plan.min_chunk, plan.split_blocks) == (8, 1024, 2)   # at least h_kv
+    st, plan = B.gqa_decode_make_plan(_args(num_chunks=7, h_kv=1, h_q=8), 256, 8)
+    assert (st, plan.num_chunks, plan.split_blocks) == (B.GQA_OK, 7, 2)
+    st, plan = B.gqa_decode_make_plan(_args(h_kv=6, h_q=48), 256, 12)
+    assert st == B.GQA_OK and plan.num_chunks == 1024 // 6 * 6     # capped at 4 waves per CU
+    st, plan = B.gqa_decode_make_plan(_args(), 256, 2)
+    assert st == B.GQA_OK and plan.num_chunks == 512                # occupancy below the cap
     st, _ = B.gqa_decode_make_plan(_args(), 0, 8)
     assert st == B.GQA_ERR_ARG
     st, _ = B.gqa_decode_make_plan(_args(h_q=30), 256, 8)

@@ -248,3 +248,20 @@ def test_runs_on_the_given_stream_and_is_deterministic():
         outs.append(o.clone())
     compare(outs[0], ref, "side stream")
     assert torch.equal(outs[0], outs[1])
+
+
+# ------------------------------------------------------------------ measurement probes
+
+
+def test_probe_copy_and_read_are_exact():
+    import torch
+    n = (37 << 20) + 48
+    src = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.gqa_probe_copy(src, dst, n)
+    B.gqa_probe_read(src, n, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    want = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(want)
