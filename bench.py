@@ -35,7 +35,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "µs/decode step + K/V HBM GB/s (% of peak), GQA h_q=64 h_kv=8 d=128 @32K"
-KERNEL_SRC = os.path.join(ROOT, "gqa_split_kv_amd", "csrc", "decode_kernels.hip")
+# Sources that define the sweep kernel's code (its counter data is tied to them).
+KERNEL_SRCS = [os.path.join(ROOT, "gqa_split_kv_amd", "csrc", f)
+               for f in ("sweep_kernel.hip", "device_common.h", "kernels.h", "host.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_kernel_70b_ragged_traffic.md")
 
 
@@ -80,8 +82,11 @@ class Hip:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def committed_traffic():

@@ -38,11 +38,12 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     # Device + host code of the kernels.
-    src = os.path.join(CSRC, "decode_kernels.hip")
-    obj = os.path.join(BUILD, "decode_kernels.o")
-    _run([HIPCC, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *NO_PACKED_FP32, *DEVICE_FLAGS,
-          "-c", src, "-o", obj], verbose)
-    objs.append(obj)
+    for name in ("sweep_kernel", "merge_kernel"):
+        src = os.path.join(CSRC, name + ".hip")
+        obj = os.path.join(BUILD, name + ".o")
+        _run([HIPCC, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *NO_PACKED_FP32, *DEVICE_FLAGS,
+              "-c", src, "-o", obj], verbose)
+        objs.append(obj)
     # Measurement probes (plain copy / read kernels).
     src = os.path.join(CSRC, "probe_kernels.hip")
     obj = os.path.join(BUILD, "probe_kernels.o")

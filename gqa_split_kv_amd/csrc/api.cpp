@@ -45,7 +45,7 @@ int device_shape(int dev, int in_bf16, int out_bf16, int D, int *num_cus, int *w
     auto wt = g_waves_per_cu.find(key);
     if (wt == g_waves_per_cu.end()) {
         int blocks = 0;
-        hipError_t e = gqa::split_occupancy(in_bf16, out_bf16, D, &blocks);
+        hipError_t e = gqa::sweep_occupancy(in_bf16, out_bf16, D, &blocks);
         if (e != hipSuccess || blocks <= 0)
             return gqa::fail(GQA_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
         wt = g_waves_per_cu.emplace(key, blocks * gqa::kWavesPerBlock).first;
@@ -123,9 +123,14 @@ int decode_ex(const gqa_decode_args *a) {
         ev0 = reinterpret_cast<hipEvent_t>(a->sweep_events[0]);
         ev1 = reinterpret_cast<hipEvent_t>(a->sweep_events[1]);
     }
-    e = gqa::launch_decode(P, in_bf16, out_bf16, a->d_head, plan.split_blocks, plan.merge_blocks,
-                           stream, ev0, ev1);
-    if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess)
+        return gqa::fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+    e = gqa::launch_sweep(P, in_bf16, out_bf16, a->d_head, plan.split_blocks, stream);
+    if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "sweep kernel launch failed: %s", hipGetErrorString(e));
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess)
+        return gqa::fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+    e = gqa::launch_merge(P, out_bf16, a->d_head, plan.merge_blocks, plan.merge_threads, stream);
+    if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
     return GQA_OK;
 }
 

@@ -1,0 +1,124 @@
+// device_common.h -- device helpers shared by the sweep and merge kernels:
+// wavefront scans over seq_lens, the stream-K range arithmetic both kernels
+// must agree on, and bf16 rounding.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+namespace dev {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
+
+__device__ __forceinline__ int64_t shfl64(int64_t x, int src) {
+    const int lo = __shfl(static_cast<int>(static_cast<uint32_t>(x)), src);
+    const int hi = __shfl(static_cast<int>(x >> 32), src);
+    return (static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo);
+}
+
+__device__ __forceinline__ int64_t shfl_up64(int64_t x, int d) {
+    const int lo = __shfl_up(static_cast<int>(static_cast<uint32_t>(x)), d);
+    const int hi = __shfl_up(static_cast<int>(x >> 32), d);
+    return (static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo);
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(x)));
+    const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(x >> 32));
+    return (static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo);
+}
+
+__device__ __forceinline__ int uniform32(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ int64_t inclusive_scan64(int64_t x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int64_t y = shfl_up64(x, d);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ int seq_len_at(const int32_t *seq_lens, int i) {
+    const int v = seq_lens[i];
+    return v > 0 ? v : 0;   // a negative length counts as empty
+}
+
+// Sum of the (clamped) sequence lengths; the same value in every lane.
+__device__ int64_t total_len(const int32_t *seq_lens, int batch) {
+    const int lane = lane_id();
+    int64_t acc = 0;
+    for (int base = 0; base < batch; base += kWave) {
+        const int i = base + lane;
+        const int64_t len = (i < batch) ? seq_len_at(seq_lens, i) : 0;
+        acc += shfl64(inclusive_scan64(len), kWave - 1);
+    }
+    return uniform64(acc);
+}
+
+// Sum of the lengths of sequences [0, b).
+__device__ int64_t prefix_len(const int32_t *seq_lens, int b) {
+    const int lane = lane_id();
+    int64_t acc = 0;
+    for (int base = 0; base < b; base += kWave) {
+        const int i = base + lane;
+        const int64_t len = (i < b) ? seq_len_at(seq_lens, i) : 0;
+        acc += shfl64(inclusive_scan64(len), kWave - 1);
+    }
+    return uniform64(acc);
+}
+
+// The sequence b holding flat key `pos` (0 <= pos < h_kv * total), with
+// off = lengths before b and len = its length.
+__device__ void locate(const int32_t *seq_lens, int batch, int h_kv, int64_t pos, int &b,
+                       int64_t &off, int &len) {
+    const int lane = lane_id();
+    int64_t run = 0;
+    for (int base = 0; base < batch; base += kWave) {
+        const int i = base + lane;
+        const int64_t li = (i < batch) ? seq_len_at(seq_lens, i) : 0;
+        const int64_t incl = inclusive_scan64(li);
+        const bool hit = (i < batch) && ((run + incl) * h_kv > pos);
+        const unsigned long long mask = __ballot(hit);
+        if (mask) {
+            const int src = __ffsll(static_cast<long long>(mask)) - 1;
+            b = base + src;
+            const int64_t inc_s = shfl64(incl, src);
+            const int64_t len_s = shfl64(li, src);
+            off = uniform64(run + inc_s - len_s);
+            len = uniform32(static_cast<int>(len_s));
+            return;
+        }
+        run += shfl64(incl, kWave - 1);
+    }
+    b = batch;
+    off = run;
+    len = 0;
+}
+
+// Keys per range: max(min_chunk, ceil(total / num_chunks)).  The partial and the
+// merge kernel must agree on it exactly.
+__device__ __forceinline__ int64_t chunk_keys(int64_t total, int num_chunks, int min_chunk) {
+    const int64_t c = (total + num_chunks - 1) / num_chunks;
+    return c > min_chunk ? c : static_cast<int64_t>(min_chunk);
+}
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+
+}  // namespace dev
+}  // namespace gqa

@@ -16,6 +16,11 @@ namespace gqa {
 // Wavefronts per workgroup of the sweep kernel.
 constexpr int kWavesPerBlock = GQA_SWEEP_WAVES;
 constexpr int kThreads = 64 * kWavesPerBlock;
+// Merge kernel workgroup sizes: narrow (8 piece lanes at d_head 128) when a
+// sequence is expected to be cut into few pieces, wide (32 lanes) when into many.
+constexpr int kMergeThreadsNarrow = 256;
+constexpr int kMergeThreadsWide = 1024;
+constexpr int kWideMergePieces = 32;   // expected pieces per sequence above which the merge is wide
 constexpr int kMaxG = 16;           // query heads per kv head held by one 16-wide MFMA tile
 constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxHeadsKv = 1 << 16;   // keeps 16 key rows of lane offsets within 32 bits

@@ -1,5 +1,5 @@
 // kernels.h -- parameters and launchers of the gfx950 decode kernels
-// (decode_kernels.hip).  Internal to the library.
+// (sweep_kernel.hip, merge_kernel.hip).  Internal to the library.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,11 +23,16 @@ struct DecodeParams {
 };
 
 // Enqueues the partial kernel and the merge kernel on `stream`.
-// ev_begin/ev_end (may be null) are recorded around the partial kernel.
-hipError_t launch_decode(const DecodeParams &P, int in_bf16, int out_bf16, int D, int split_blocks,
-                         int merge_blocks, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
+// Enqueues the sweep (partial) kernel: `blocks` workgroups of kThreads.
+hipError_t launch_sweep(const DecodeParams &P, int in_bf16, int out_bf16, int D, int blocks,
+                        hipStream_t stream);
 
-// Resident workgroups of the partial kernel per compute unit.
-hipError_t split_occupancy(int in_bf16, int out_bf16, int D, int *blocks_per_cu);
+// Resident workgroups of the sweep kernel per compute unit.
+hipError_t sweep_occupancy(int in_bf16, int out_bf16, int D, int *blocks_per_cu);
+
+// Enqueues the merge kernel: `blocks` = batch * h_kv * G workgroups of `threads`
+// (kMergeThreadsNarrow or kMergeThreadsWide).
+hipError_t launch_merge(const DecodeParams &P, int out_bf16, int D, int blocks, int threads,
+                        hipStream_t stream);
 
 }  // namespace gqa

@@ -1,0 +1,171 @@
+// merge_kernel.hip -- log-sum-exp merge of the partial triples a sequence left in
+// the workspace when its keys were cut across several sweep ranges.
+//
+// For query head g of (sequence b, kv head j) with pieces s = ca .. cb (range s
+// was swept by wavefront s*h_kv + j; the first piece sits in slot 1 of its
+// wavefront, the rest in slot 0):
+//   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s O_s 2^(m_s - M) / L
+// (kernbench2 page "_gqa_attention_decode_long.py", `_merge_running`: the
+// pairwise rule applied to all pieces at once with their common maximum, which
+// is the same reduction its chain and centre-root trees compute), then the final
+// normalise and store.  m is in log2 units (the sweep folds log2 e into the
+// scale), so the weights are exp2.
+//
+// Layout: a workgroup covers (sequence, kv head) and a group of query heads.
+// Thread (pl, h, eq) owns four consecutive elements d = 4eq .. 4eq+3 of head h
+// and the pieces s = ca + pl, ca + pl + PL, ...; it loads eight pieces at a time
+// and folds them into a running (M, L, acc) with the merge rule; the piece lanes
+// are then folded through LDS in ascending order, so the result is
+// deterministic.  The narrow layout (one piece lane, up to 8 heads per
+// workgroup at d 128) serves sequences cut into few pieces; the wide one (one
+// head, 32 piece lanes at d 128) serves a long sequence cut into many.  Also
+// writes zeros for an empty sequence.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace gqa {
+namespace {
+
+using namespace dev;
+
+template <bool kBf16Out>
+__device__ __forceinline__ void store_quad(uint8_t *row, int eq, float4 x) {
+    if constexpr (kBf16Out)
+        reinterpret_cast<uint2 *>(row)[eq] =
+            make_uint2(bf16_rne(x.x) | (bf16_rne(x.y) << 16), bf16_rne(x.z) | (bf16_rne(x.w) << 16));
+    else
+        reinterpret_cast<float4 *>(row)[eq] = x;
+}
+
+// Folds a batch of pieces into a running (M, L, acc) with the merge rule: the new
+// maximum, both sides rescaled by 2^(old - new), sums added.
+struct Running {
+    float M, L;
+    float4 acc;
+};
+
+__device__ __forceinline__ void fold(Running &r, float m, float l, float4 o) {
+    const float Mn = fmaxf(r.M, m);
+    const float a = __builtin_amdgcn_exp2f(r.M - Mn);   // 0 when r is empty
+    const float f = __builtin_amdgcn_exp2f(m - Mn);     // 0 for an empty side
+    r.L = r.L * a + l * f;
+    r.acc.x = r.acc.x * a + o.x * f;
+    r.acc.y = r.acc.y * a + o.y * f;
+    r.acc.z = r.acc.z * a + o.z * f;
+    r.acc.w = r.acc.w * a + o.w * f;
+    r.M = Mn;
+}
+
+// Workgroup layout: kHeads query heads x PL piece lanes x QD element quads.
+template <bool kBf16Out, int D, int kThreadsM, int kHeads>
+__global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
+    constexpr int QD = D / 4;                        // element quads per head
+    constexpr int PL = kThreadsM / (QD * kHeads);    // piece lanes
+    constexpr int kBatch = 8;                        // pieces in flight per thread
+    static_assert(PL >= 1 && PL * QD * kHeads == kThreadsM, "layout");
+    __shared__ Running s_run[PL > 1 ? PL : 1][kHeads][QD];
+
+    const int G = P.G;
+    const int groups = (G + kHeads - 1) / kHeads;
+    const int unit = static_cast<int>(blockIdx.x) / groups;
+    const int g0 = (static_cast<int>(blockIdx.x) - unit * groups) * kHeads;
+    const int b = unit / P.h_kv;
+    const int j = unit - b * P.h_kv;
+    const int t = static_cast<int>(threadIdx.x);
+    const int eq = t % QD;
+    const int hh = (t / QD) % kHeads;
+    const int pl = t / (QD * kHeads);
+    const int g = g0 + hh;
+    const bool active = g < G;
+    const int len = uniform32(seq_len_at(P.seq_lens, b));
+    uint8_t *orow = P.o + (static_cast<int64_t>(b) * P.h_q + j * G + g) * D * (kBf16Out ? 2 : 4);
+    if (len == 0) {
+        if (pl == 0 && active) store_quad<kBf16Out>(orow, eq, make_float4(0.f, 0.f, 0.f, 0.f));
+        return;
+    }
+    const int64_t total = total_len(P.seq_lens, P.batch);
+    const int64_t chunk = chunk_keys(total, P.num_chunks / P.h_kv, P.min_chunk);
+    const int64_t ustart = prefix_len(P.seq_lens, b);
+    const int64_t ca = ustart / chunk;   // token ranges holding this sequence
+    const int64_t cb = (ustart + len - 1) / chunk;
+    if (ca == cb) return;                // written whole by the sweep kernel
+
+    Running r = {-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+    if (active) {
+        for (int64_t s0 = ca + pl; s0 <= cb; s0 += static_cast<int64_t>(PL) * kBatch) {
+            float2 ml[kBatch];
+            float4 ov[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int64_t s = s0 + static_cast<int64_t>(i) * PL;
+                if (s <= cb) {
+                    const int64_t row = ((s * P.h_kv + j) * 2 + (s == ca ? 1 : 0)) * G + g;
+                    ml[i] = P.ws_ml[row];
+                    ov[i] = reinterpret_cast<const float4 *>(P.ws_o + row * D)[eq];
+                } else {
+                    ml[i] = make_float2(-INFINITY, 0.f);
+                    ov[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+            float mb = ml[0].x;
+#pragma unroll
+            for (int i = 1; i < kBatch; ++i) mb = fmaxf(mb, ml[i].x);
+            // One rescale per batch: fold the batch at its own maximum, then into r.
+            Running bt = {mb, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const float f = __builtin_amdgcn_exp2f(ml[i].x - mb);   // 0 for the padding
+                bt.L += f * ml[i].y;
+                bt.acc.x += f * ov[i].x;
+                bt.acc.y += f * ov[i].y;
+                bt.acc.z += f * ov[i].z;
+                bt.acc.w += f * ov[i].w;
+            }
+            fold(r, bt.M, bt.L, bt.acc);
+        }
+    }
+    if constexpr (PL > 1) {
+        s_run[pl][hh][eq] = r;
+        __syncthreads();
+        if (pl != 0) return;
+#pragma unroll
+        for (int i = 1; i < PL; ++i) {
+            const Running x = s_run[i][hh][eq];
+            fold(r, x.M, x.L, x.acc);
+        }
+    }
+    if (active) {
+        const float inv = 1.0f / r.L;
+        store_quad<kBf16Out>(orow, eq, make_float4(r.acc.x * inv, r.acc.y * inv, r.acc.z * inv, r.acc.w * inv));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const DecodeParams &P, int out_bf16, int D, int blocks, int threads,
+                        hipStream_t stream) {
+    // Narrow: 256 threads covering 256/(D/4) heads with one piece lane each
+    // (few pieces per sequence).  Wide: 1024 threads, one head, 1024/(D/4) piece lanes.
+#define GQA_MERGE(O, DD, T, H) \
+    hipLaunchKernelGGL((merge_kernel<O, DD, T, H>), dim3(blocks), dim3(T), 0, stream, P)
+    if (threads == kMergeThreadsWide) {
+        if (out_bf16) {
+            if (D == 128) GQA_MERGE(true, 128, kMergeThreadsWide, 1); else GQA_MERGE(true, 64, kMergeThreadsWide, 1);
+        } else {
+            if (D == 128) GQA_MERGE(false, 128, kMergeThreadsWide, 1); else GQA_MERGE(false, 64, kMergeThreadsWide, 1);
+        }
+    } else {
+        if (out_bf16) {
+            if (D == 128) GQA_MERGE(true, 128, kMergeThreadsNarrow, 8); else GQA_MERGE(true, 64, kMergeThreadsNarrow, 16);
+        } else {
+            if (D == 128) GQA_MERGE(false, 128, kMergeThreadsNarrow, 8); else GQA_MERGE(false, 64, kMergeThreadsNarrow, 16);
+        }
+    }
+#undef GQA_MERGE
+    return hipGetLastError();
+}
+
+}  // namespace gqa

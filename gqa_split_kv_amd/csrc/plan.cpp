@@ -56,8 +56,8 @@ static int check_basic(const gqa_decode_args *a) {
                     a->h_q, a->h_kv);
     if (a->h_q % a->h_kv != 0)
         return fail(GQA_ERR_SHAPE, "h_q (%d) is not a multiple of h_kv (%d)", a->h_q, a->h_kv);
-    if (static_cast<int64_t>(a->batch) * a->h_kv > 0x7fffffff)
-        return fail(GQA_ERR_SHAPE, "batch * h_kv exceeds 2^31-1");
+    if (static_cast<int64_t>(a->batch) * a->h_q > 0x7fffffff)
+        return fail(GQA_ERR_SHAPE, "batch * h_q exceeds 2^31-1");
     if (a->h_kv > kMaxHeadsKv)
         return fail(GQA_ERR_UNSUPPORTED, "h_kv %d exceeds %d", a->h_kv, kMaxHeadsKv);
     const int G = a->h_q / a->h_kv;
@@ -126,7 +126,13 @@ int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decod
     plan->num_chunks = static_cast<int32_t>(chunks);
     plan->min_chunk = a->min_chunk > 0 ? a->min_chunk : kAutoMinChunk;
     plan->split_blocks = static_cast<int32_t>((chunks + kWavesPerBlock - 1) / kWavesPerBlock);
-    plan->merge_blocks = a->batch * a->h_kv;
+    // Expected pieces per sequence: token ranges per sequence on average.
+    const int64_t ranges = chunks / a->h_kv;
+    const int G = a->h_q / a->h_kv;
+    const bool wide = ranges / a->batch > kWideMergePieces;
+    plan->merge_threads = wide ? kMergeThreadsWide : kMergeThreadsNarrow;
+    const int heads_per_block = wide ? 1 : kMergeThreadsNarrow / (a->d_head / 4);
+    plan->merge_blocks = a->batch * a->h_kv * ((G + heads_per_block - 1) / heads_per_block);
     plan->workspace_bytes = L.bytes;
     return GQA_OK;
 }

@@ -40,19 +40,14 @@
 
 #include <type_traits>
 
+#include "device_common.h"
 #include "kernels.h"
 
 namespace gqa {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+using namespace dev;
 
-constexpr int kWave = 64;
-constexpr int kBlockKeys = 16;
-constexpr int kMergeThreads = 256;
 #ifndef GQA_SWEEP_DEPTH
 #define GQA_SWEEP_DEPTH 2
 #endif
@@ -64,111 +59,6 @@ constexpr int kSweepDepth = GQA_SWEEP_DEPTH;   // register buffers in the sweep 
 #define GQA_KV_CPOL 2
 #endif
 constexpr int kKvCachePolicy = GQA_KV_CPOL;
-
-// ------------------------------------------------------------------ wave helpers
-
-__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
-
-__device__ __forceinline__ int64_t shfl64(int64_t x, int src) {
-    const int lo = __shfl(static_cast<int>(static_cast<uint32_t>(x)), src);
-    const int hi = __shfl(static_cast<int>(x >> 32), src);
-    return (static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo);
-}
-
-__device__ __forceinline__ int64_t shfl_up64(int64_t x, int d) {
-    const int lo = __shfl_up(static_cast<int>(static_cast<uint32_t>(x)), d);
-    const int hi = __shfl_up(static_cast<int>(x >> 32), d);
-    return (static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo);
-}
-
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-    const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(x)));
-    const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(x >> 32));
-    return (static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo);
-}
-
-__device__ __forceinline__ int uniform32(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-__device__ __forceinline__ int64_t inclusive_scan64(int64_t x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int64_t y = shfl_up64(x, d);
-        if (lane >= d) x += y;
-    }
-    return x;
-}
-
-__device__ __forceinline__ int seq_len_at(const int32_t *seq_lens, int i) {
-    const int v = seq_lens[i];
-    return v > 0 ? v : 0;   // a negative length counts as empty
-}
-
-// Sum of the (clamped) sequence lengths; the same value in every lane.
-__device__ int64_t total_len(const int32_t *seq_lens, int batch) {
-    const int lane = lane_id();
-    int64_t acc = 0;
-    for (int base = 0; base < batch; base += kWave) {
-        const int i = base + lane;
-        const int64_t len = (i < batch) ? seq_len_at(seq_lens, i) : 0;
-        acc += shfl64(inclusive_scan64(len), kWave - 1);
-    }
-    return uniform64(acc);
-}
-
-// Sum of the lengths of sequences [0, b).
-__device__ int64_t prefix_len(const int32_t *seq_lens, int b) {
-    const int lane = lane_id();
-    int64_t acc = 0;
-    for (int base = 0; base < b; base += kWave) {
-        const int i = base + lane;
-        const int64_t len = (i < b) ? seq_len_at(seq_lens, i) : 0;
-        acc += shfl64(inclusive_scan64(len), kWave - 1);
-    }
-    return uniform64(acc);
-}
-
-// The sequence b holding flat key `pos` (0 <= pos < h_kv * total), with
-// off = lengths before b and len = its length.
-__device__ void locate(const int32_t *seq_lens, int batch, int h_kv, int64_t pos, int &b,
-                       int64_t &off, int &len) {
-    const int lane = lane_id();
-    int64_t run = 0;
-    for (int base = 0; base < batch; base += kWave) {
-        const int i = base + lane;
-        const int64_t li = (i < batch) ? seq_len_at(seq_lens, i) : 0;
-        const int64_t incl = inclusive_scan64(li);
-        const bool hit = (i < batch) && ((run + incl) * h_kv > pos);
-        const unsigned long long mask = __ballot(hit);
-        if (mask) {
-            const int src = __ffsll(static_cast<long long>(mask)) - 1;
-            b = base + src;
-            const int64_t inc_s = shfl64(incl, src);
-            const int64_t len_s = shfl64(li, src);
-            off = uniform64(run + inc_s - len_s);
-            len = uniform32(static_cast<int>(len_s));
-            return;
-        }
-        run += shfl64(incl, kWave - 1);
-    }
-    b = batch;
-    off = run;
-    len = 0;
-}
-
-// Keys per range: max(min_chunk, ceil(total / num_chunks)).  The partial and the
-// merge kernel must agree on it exactly.
-__device__ __forceinline__ int64_t chunk_keys(int64_t total, int num_chunks, int min_chunk) {
-    const int64_t c = (total + num_chunks - 1) / num_chunks;
-    return c > min_chunk ? c : static_cast<int64_t>(min_chunk);
-}
-
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-
 
 // ------------------------------------------------------------------ loads
 
@@ -548,137 +438,30 @@ __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
     }
 }
 
-// Merge of the pieces of one (sequence, kv head): for every query head g and
-// element d, M = max m_s, L = sum l_s 2^(m_s - M), o = sum O_s 2^(m_s - M) / L,
-// with the pieces taken in ascending order, eight at a time (their loads in
-// flight together) and folded into a running (M, L, acc) with the same
-// rescaling rule.  Each thread owns four consecutive d of one head (16-byte
-// loads).  Also writes zeros for an empty sequence.
-template <bool kBf16Out, int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams P) {
-    constexpr int kPieces = 8;
-    const int b = static_cast<int>(blockIdx.x) / P.h_kv;
-    const int j = static_cast<int>(blockIdx.x) % P.h_kv;
-    const int G = P.G;
-    const int len = uniform32(seq_len_at(P.seq_lens, b));
-    uint8_t *obase = P.o + (static_cast<int64_t>(b) * P.h_q + j * G) * D * (kBf16Out ? 2 : 4);
-    const int n4 = G * D / 4;
-    if (len == 0) {
-        for (int e = threadIdx.x; e < n4; e += kMergeThreads) {
-            if constexpr (kBf16Out)
-                reinterpret_cast<uint2 *>(obase)[e] = make_uint2(0, 0);
-            else
-                reinterpret_cast<float4 *>(obase)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        return;
-    }
-    const int64_t total = total_len(P.seq_lens, P.batch);
-    const int64_t chunk = chunk_keys(total, P.num_chunks / P.h_kv, P.min_chunk);
-    const int64_t ustart = prefix_len(P.seq_lens, b);
-    const int64_t ca = ustart / chunk;              // token ranges holding this sequence
-    const int64_t cb = (ustart + len - 1) / chunk;
-    if (ca == cb) return;   // written whole by the partial kernel
-    for (int e = threadIdx.x; e < n4; e += kMergeThreads) {
-        const int g = (4 * e) / D;
-        const int d = 4 * e - g * D;
-        float M = -INFINITY, L = 0.f;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int64_t s0 = ca; s0 <= cb; s0 += kPieces) {
-            float2 ml[kPieces];
-            float4 ov[kPieces];
-#pragma unroll
-            for (int i = 0; i < kPieces; ++i) {
-                const int64_t s = s0 + i;
-                if (s <= cb) {
-                    // range s was swept by wavefront s*h_kv + j; the first piece sits
-                    // in slot 1 of its wavefront, the others in slot 0
-                    const int64_t wv = s * P.h_kv + j;
-                    const int64_t srow = (wv * 2 + (s == ca ? 1 : 0)) * G + g;
-                    ml[i] = P.ws_ml[srow];
-                    ov[i] = *reinterpret_cast<const float4 *>(P.ws_o + srow * D + d);
-                } else {
-                    ml[i] = make_float2(-INFINITY, 0.f);
-                    ov[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-            }
-            float mb = ml[0].x;
-#pragma unroll
-            for (int i = 1; i < kPieces; ++i) mb = fmaxf(mb, ml[i].x);
-            const float Mn = fmaxf(M, mb);
-            const float a = __builtin_amdgcn_exp2f(M - Mn);
-            L *= a;
-            acc.x *= a;
-            acc.y *= a;
-            acc.z *= a;
-            acc.w *= a;
-#pragma unroll
-            for (int i = 0; i < kPieces; ++i) {
-                const float f = __builtin_amdgcn_exp2f(ml[i].x - Mn);
-                L += f * ml[i].y;
-                acc.x += f * ov[i].x;
-                acc.y += f * ov[i].y;
-                acc.z += f * ov[i].z;
-                acc.w += f * ov[i].w;
-            }
-            M = Mn;
-        }
-        const float inv = 1.0f / L;
-        if constexpr (kBf16Out) {
-            reinterpret_cast<uint2 *>(obase)[e] =
-                make_uint2(bf16_rne(acc.x * inv) | (bf16_rne(acc.y * inv) << 16),
-                           bf16_rne(acc.z * inv) | (bf16_rne(acc.w * inv) << 16));
-        } else {
-            reinterpret_cast<float4 *>(obase)[e] =
-                make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-        }
-    }
-}
+}  // namespace
 
-template <bool kBf16In, bool kBf16Out, int D>
-hipError_t launch_variant(const DecodeParams &P, int split_blocks, int merge_blocks,
-                          hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
-    hipError_t e;
-    if (ev_begin && (e = hipEventRecord(ev_begin, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL((split_kernel<kBf16In, kBf16Out, D, kSweepDepth>), dim3(split_blocks), dim3(kThreads), 0,
-                       stream, P);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (ev_end && (e = hipEventRecord(ev_end, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_kernel<kBf16Out, D>), dim3(merge_blocks), dim3(kMergeThreads), 0, stream, P);
+hipError_t launch_sweep(const DecodeParams &P, int in_bf16, int out_bf16, int D, int blocks,
+                        hipStream_t stream) {
+#define GQA_LAUNCH(I, O, DD)                                                                        \
+    hipLaunchKernelGGL((split_kernel<I, O, DD, kSweepDepth>), dim3(blocks), dim3(kThreads), 0, stream, P)
+    if (in_bf16 && out_bf16) {
+        if (D == 128) GQA_LAUNCH(true, true, 128); else GQA_LAUNCH(true, true, 64);
+    } else if (in_bf16) {
+        if (D == 128) GQA_LAUNCH(true, false, 128); else GQA_LAUNCH(true, false, 64);
+    } else {
+        if (D == 128) GQA_LAUNCH(false, false, 128); else GQA_LAUNCH(false, false, 64);
+    }
+#undef GQA_LAUNCH
     return hipGetLastError();
 }
 
-template <bool kBf16In, bool kBf16Out, int D>
-hipError_t occupancy_variant(int *blocks_per_cu) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu,
-                                                        split_kernel<kBf16In, kBf16Out, D, kSweepDepth>, kThreads, 0);
-}
-
-}  // namespace
-
-hipError_t launch_decode(const DecodeParams &P, int in_bf16, int out_bf16, int D, int split_blocks,
-                         int merge_blocks, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
-    if (in_bf16 && out_bf16) {
-        return D == 128 ? launch_variant<true, true, 128>(P, split_blocks, merge_blocks, stream, ev_begin, ev_end)
-                        : launch_variant<true, true, 64>(P, split_blocks, merge_blocks, stream, ev_begin, ev_end);
-    }
-    if (in_bf16) {
-        return D == 128 ? launch_variant<true, false, 128>(P, split_blocks, merge_blocks, stream, ev_begin, ev_end)
-                        : launch_variant<true, false, 64>(P, split_blocks, merge_blocks, stream, ev_begin, ev_end);
-    }
-    return D == 128 ? launch_variant<false, false, 128>(P, split_blocks, merge_blocks, stream, ev_begin, ev_end)
-                    : launch_variant<false, false, 64>(P, split_blocks, merge_blocks, stream, ev_begin, ev_end);
-}
-
-hipError_t split_occupancy(int in_bf16, int out_bf16, int D, int *blocks_per_cu) {
-    if (in_bf16 && out_bf16)
-        return D == 128 ? occupancy_variant<true, true, 128>(blocks_per_cu)
-                        : occupancy_variant<true, true, 64>(blocks_per_cu);
-    if (in_bf16)
-        return D == 128 ? occupancy_variant<true, false, 128>(blocks_per_cu)
-                        : occupancy_variant<true, false, 64>(blocks_per_cu);
-    return D == 128 ? occupancy_variant<false, false, 128>(blocks_per_cu)
-                    : occupancy_variant<false, false, 64>(blocks_per_cu);
+hipError_t sweep_occupancy(int in_bf16, int out_bf16, int D, int *blocks_per_cu) {
+#define GQA_OCC(I, O, DD) \
+    hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, split_kernel<I, O, DD, kSweepDepth>, kThreads, 0)
+    if (in_bf16 && out_bf16) return D == 128 ? GQA_OCC(true, true, 128) : GQA_OCC(true, true, 64);
+    if (in_bf16) return D == 128 ? GQA_OCC(true, false, 128) : GQA_OCC(true, false, 64);
+    return D == 128 ? GQA_OCC(false, false, 128) : GQA_OCC(false, false, 64);
+#undef GQA_OCC
 }
 
 }  // namespace gqa

@@ -65,7 +65,8 @@ extern "C" {
 typedef enum gqa_status {
     GQA_OK = 0,
     GQA_ERR_NULL = 1,        /* a required pointer is NULL                              */
-    GQA_ERR_SHAPE = 2,       /* batch, h_q or h_kv <= 0, or h_q not a multiple of h_kv  */
+    GQA_ERR_SHAPE = 2,       /* batch, h_q or h_kv <= 0, h_q not a multiple of h_kv,    *
+                              * or batch * h_q above 2^31-1                             */
     GQA_ERR_UNSUPPORTED = 3, /* d_head not 64/128, G > 16, or dtype pair not supported  */
     GQA_ERR_ALIGN = 4,       /* q/k/v/o not 16-byte aligned or seq_lens not 4-byte      */
     GQA_ERR_SCALE = 5,       /* scale is not finite                                     */
@@ -158,8 +159,9 @@ int gqa_decode_validate(const gqa_decode_args *args);
 typedef struct gqa_decode_plan {
     int32_t num_chunks;      /* wavefronts launched (h_kv per token range)         */
     int32_t min_chunk;       /* smallest token range in key rows                   */
-    int32_t split_blocks;    /* workgroups of the partial kernel (4 wavefronts)    */
-    int32_t merge_blocks;    /* workgroups of the merge kernel (batch * h_kv)      */
+    int32_t split_blocks;    /* workgroups of the sweep kernel (4 wavefronts each) */
+    int32_t merge_blocks;    /* workgroups of the merge kernel                     */
+    int32_t merge_threads;   /* threads per merge workgroup (256 or 1024)          */
     size_t workspace_bytes;  /* partial-triple scratch the call needs              */
 } gqa_decode_plan;
 

@@ -127,11 +127,14 @@ def test_plan_automatic_and_explicit(lib):
     assert st == B.GQA_OK
     assert plan.num_chunks == 256 * 4                       # one wavefront per SIMD
     assert plan.split_blocks == 256                         # 4-wave workgroups
-    assert plan.merge_blocks == 4 * 8
+    assert plan.merge_blocks == 4 * 8                       # batch * h_kv (G = 4 heads per block)
+    assert plan.merge_threads == 256                        # 128 ranges / batch 4 = 32 pieces
     assert plan.min_chunk > 0
     st, plan = B.gqa_decode_make_plan(_args(num_chunks=7, min_chunk=1024), 256, 8)
     assert st == B.GQA_OK
     assert (plan.num_chunks, plan.min_chunk, plan.split_blocks) == (8, 1024, 2)   # at least h_kv
+    st, plan = B.gqa_decode_make_plan(_args(batch=1, h_kv=1, h_q=8), 256, 8)
+    assert (st, plan.merge_threads) == (B.GQA_OK, 1024)     # one sequence cut into 1024 ranges
     st, plan = B.gqa_decode_make_plan(_args(num_chunks=7, h_kv=1, h_q=8), 256, 8)
     assert (st, plan.num_chunks, plan.split_blocks) == (B.GQA_OK, 7, 2)
     st, plan = B.gqa_decode_make_plan(_args(h_kv=6, h_q=48), 256, 12)
@@ -164,4 +167,4 @@ def test_error_message_is_cleared_on_success(lib):
 def test_struct_mirrors_match_header_sizes(lib):
     # gqa_decode_args: 5 pointers, 6 int32 + float, 2 more int32, pointer, size_t, pointer
     assert ctypes.sizeof(B.GqaArgs) == 5 * 8 + 4 * 4 + 4 + 4 * 4 + 4 + 8 + 8 + 8 + 2 * 8
-    assert ctypes.sizeof(B.GqaPlan) == 4 * 4 + 8
+    assert ctypes.sizeof(B.GqaPlan) == 5 * 4 + 4 + 8
