@@ -252,7 +252,7 @@ def main():
     }
     # Achievable read bandwidth on this machine: the plain read probe over the
     # same K and V bytes, timed the same way.
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")     # GQA_PROBE_SINK_WORDS words
     reps = 10
     for i in range(2):
         gqa.gqa_probe_read(d.k, d.k.numel() * d.k.element_size(), sink, stream)

@@ -259,8 +259,11 @@ def gqa_probe_copy(src, dst, nbytes: int, stream=None) -> int:
     return st
 
 
+GQA_PROBE_SINK_WORDS = 256
+
+
 def gqa_probe_read(src, nbytes: int, sink, stream=None) -> int:
-    """Plain device read of nbytes folded into *sink (measurement reference)."""
+    """Plain device read of nbytes folded into GQA_PROBE_SINK_WORDS uint32 words at sink."""
     st = lib().gqa_probe_read(_ptr(src), int(nbytes), _ptr(sink), _stream(stream))
     if st != GQA_OK:
         raise GqaError(st, "gqa_probe_read failed")

@@ -172,7 +172,7 @@ struct Bf16Step {
 #pragma unroll
         for (int i = 0; i < 8; ++i) load_words<VW>(B.v[i], rv, lo.v[i]);
     }
-    __device__ __forceinline__ static void compute(const Buf &B, const uint4 (&qop)[NKP], int nvalid,
+    __device__ __forceinline__ static void compute(const Buf &B, const uint4 (&qop)[NKP], int lo, int hi,
                                                    int kg, float sl2, float &m_run, float &l_run,
                                                    f32x4_t (&acc)[VEC]) {
         float sv[8];
@@ -186,7 +186,10 @@ struct Bf16Step {
                                                             0, 0, 0);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                sv[4 * b + q] = (8 * kg + 4 * b + q < nvalid) ? s[q] * sl2 : -INFINITY;
+            {
+                const int key = 8 * kg + 4 * b + q;
+                sv[4 * b + q] = (key >= lo && key < hi) ? s[q] * sl2 : -INFINITY;
+            }
         }
         softmax_step<8, VEC>(sv, m_run, l_run, acc);
         // P = hi + lo, both bf16, packed two keys per word (key 2w in the low half).
@@ -256,7 +259,7 @@ struct F32Step {
 #pragma unroll
         for (int r = 0; r < 4; ++r) load_words<VW>(B.v[r], rv, lo.v[r]);
     }
-    __device__ __forceinline__ static void compute(const Buf &B, const uint4 (&qop)[NKP], int nvalid,
+    __device__ __forceinline__ static void compute(const Buf &B, const uint4 (&qop)[NKP], int lo, int hi,
                                                    int kg, float sl2, float &m_run, float &l_run,
                                                    f32x4_t (&acc)[VEC]) {
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -269,7 +272,10 @@ struct F32Step {
         }
         float sv[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sv[q] = (4 * kg + q < nvalid) ? s[q] * sl2 : -INFINITY;
+        for (int q = 0; q < 4; ++q) {
+            const int key = 4 * kg + q;
+            sv[q] = (key >= lo && key < hi) ? s[q] * sl2 : -INFINITY;
+        }
         softmax_step<4, VEC>(sv, m_run, l_run, acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -335,21 +341,26 @@ __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int 
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    const int nkeys = t1 - t0;
-    const int nstep = (nkeys + S::kKeys - 1) / S::kKeys;
-    const int64_t row0 = (off + t0) * P.h_kv + j;
+    // Steps cover key rows aligned to kKeys in the packed K/V (absolute row index),
+    // so a step never straddles a kKeys-row boundary of the cache: the first step
+    // of a piece starts at the aligned row at or below it (its leading rows, which
+    // belong to the previous sequence and are in bounds, are masked), and the
+    // buffer resources end at the piece's last row, so rows past it read as zero.
+    const int64_t first = off + t0;                              // absolute key row
+    const int64_t abase = first - (first % S::kKeys);
+    const int lead = static_cast<int>(first - abase);            // masked rows of step 0
+    const int span = lead + (t1 - t0);                           // keys from abase to the end
+    const int nstep = (span + S::kKeys - 1) / S::kKeys;
+    const int64_t row0 = abase * P.h_kv + j;
     const uint8_t *kbase = P.k + row0 * S::ROWB;
     const uint8_t *vbase = P.v + row0 * S::ROWB;
     const float sl2 = P.scale_log2;
     const typename S::Lanes lo(rowstride);
 
-    // Step st covers keys [kKeys*st, kKeys*st + kKeys) of the piece; its buffer
-    // resources span exactly its valid rows, so rows past the piece read as zero
-    // (and their scores are masked to -inf).
     auto load_step = [&](typename S::Buf &B, int st) {
-        const int nvalid = min(S::kKeys, nkeys - st * S::kKeys);
+        const int hi = min(S::kKeys, span - st * S::kKeys);
         const int64_t boff = static_cast<int64_t>(st) * S::kKeys * rowstride;
-        const uint32_t bytes = static_cast<uint32_t>(nvalid * rowstride);
+        const uint32_t bytes = static_cast<uint32_t>(hi * rowstride);
         S::load(B, buffer_rsrc(kbase + boff, bytes), buffer_rsrc(vbase + boff, bytes), lo);
     };
 
@@ -366,7 +377,8 @@ __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int 
         for (int u = 0; u < kDepth; ++u) {
             load_step(buf[(u + kDepth - 1) % kDepth], min(st + kDepth - 1, nstep - 1));
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
-            S::compute(buf[u], qop, min(S::kKeys, nkeys - st * S::kKeys), kg, sl2, m_run, l_run, acc);
+            S::compute(buf[u], qop, st == 0 ? lead : 0, min(S::kKeys, span - st * S::kKeys), kg, sl2,
+                       m_run, l_run, acc);
             if (++st == nstep) goto swept;
         }
     }

@@ -6,13 +6,16 @@
  *   gqa_probe_copy  copies `bytes` bytes src -> dst; a kernel of known traffic,
  *                   used to scale hardware byte counters (FETCH_SIZE, WRITE_SIZE)
  *                   to bytes.
- *   gqa_probe_read  reads `bytes` bytes and folds them (XOR of all 32-bit words)
- *                   into *sink with an atomic XOR, so the loads cannot be elided;
- *                   its rate is the achievable HBM read bandwidth, the practical
- *                   ceiling of the bandwidth-bound decode sweep.
+ *   gqa_probe_read  reads `bytes` bytes and folds them (XOR of 32-bit words) into
+ *                   the GQA_PROBE_SINK_WORDS words at `sink` with atomic XORs, so the
+ *                   loads cannot be elided (the XOR of all sink words is the XOR of
+ *                   all words read, if the sink started zeroed); its rate is the
+ *                   achievable HBM read bandwidth, the practical ceiling of the
+ *                   bandwidth-bound decode sweep.
  *
  * Pointers are device memory of the current HIP device, owned by the caller.
- * src, dst and bytes must be multiples of 16 (sink: 4-byte aligned).  Work is
+ * src, dst and bytes must be multiples of 16 (sink: 4-byte aligned, GQA_PROBE_SINK_WORDS
+ * uint32 words).  Work is
  * enqueued on `stream` (hipStream_t, NULL = null stream) without synchronising.
  * Returns 0, 1 (NULL pointer), 4 (misaligned) or 7 (HIP error), the same codes
  * as gqa_status in gqa_decode.h.
@@ -22,6 +25,8 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+#define GQA_PROBE_SINK_WORDS 256
 
 #ifdef __cplusplus
 extern "C" {

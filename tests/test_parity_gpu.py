@@ -258,10 +258,10 @@ def test_probe_copy_and_read_are_exact():
     n = (37 << 20) + 48
     src = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
     dst = torch.zeros_like(src)
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")     # GQA_PROBE_SINK_WORDS
     B.gqa_probe_copy(src, dst, n)
     B.gqa_probe_read(src, n, sink)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
     want = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
-    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(want)
+    assert int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))) == int(want)
