@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(PKG, "libgqa_decode.so")
 
 GQA_DTYPE_BF16 = 0
 GQA_DTYPE_F32 = 1
+GQA_DTYPE_F16 = 2
 
 GQA_OK = 0
 GQA_ERR_NULL = 1
@@ -31,7 +32,7 @@ GQA_ERR_HIP = 7
 GQA_ERR_ARG = 8
 
 # Every function include/gqa_decode.h and include/gqa_probe.h declare.
-EXPORTS = ("gqa_decode", "gqa_decode_f32", "gqa_decode_ex", "gqa_decode_validate",
+EXPORTS = ("gqa_decode", "gqa_decode_f32", "gqa_decode_f16", "gqa_decode_ex", "gqa_decode_validate",
            "gqa_decode_make_plan", "gqa_decode_workspace_bytes", "gqa_status_str",
            "gqa_last_error_message", "gqa_release", "gqa_probe_copy", "gqa_probe_read")
 
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode.restype = ctypes.c_int
     L.gqa_decode_f32.argtypes = sig
     L.gqa_decode_f32.restype = ctypes.c_int
+    L.gqa_decode_f16.argtypes = sig
+    L.gqa_decode_f16.restype = ctypes.c_int
     L.gqa_decode_ex.argtypes = [ctypes.POINTER(GqaArgs)]
     L.gqa_decode_ex.restype = ctypes.c_int
     L.gqa_decode_validate.argtypes = [ctypes.POINTER(GqaArgs)]
@@ -135,7 +138,9 @@ def _dtype_code(t) -> int:
         return GQA_DTYPE_BF16
     if t.dtype == torch.float32:
         return GQA_DTYPE_F32
-    raise TypeError("q/k/v/o must be bfloat16 or float32 tensors, got %s" % t.dtype)
+    if t.dtype == torch.float16:
+        return GQA_DTYPE_F16
+    raise TypeError("q/k/v/o must be bfloat16, float16 or float32 tensors, got %s" % t.dtype)
 
 
 def _stream(stream) -> Optional[int]:
@@ -163,6 +168,15 @@ def gqa_decode_f32(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_head
                    scale: float, stream=None) -> int:
     """fp32 in / fp32 out."""
     st = lib().gqa_decode_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens), batch, h_q, h_kv,
+                              d_head, float(scale), _stream(stream))
+    _check(st)
+    return st
+
+
+def gqa_decode_f16(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_head: int,
+                   scale: float, stream=None) -> int:
+    """fp16 in / fp16 out."""
+    st = lib().gqa_decode_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens), batch, h_q, h_kv,
                               d_head, float(scale), _stream(stream))
     _check(st)
     return st

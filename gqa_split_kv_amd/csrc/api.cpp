@@ -27,9 +27,9 @@ std::map<int, int> g_num_cus;                                   // device -> com
 std::map<std::pair<int, int>, int> g_waves_per_cu;               // (device, variant) -> waves
 std::map<std::pair<int, uintptr_t>, OwnedWorkspace> g_workspaces; // (device, stream)
 
-int variant_id(int in_bf16, int out_bf16, int D) { return (in_bf16 << 2) | (out_bf16 << 1) | (D == 128); }
+int variant_id(int in_dtype, int out_dtype, int D) { return (in_dtype << 3) | (out_dtype << 1) | (D == 128); }
 
-int device_shape(int dev, int in_bf16, int out_bf16, int D, int *num_cus, int *waves_per_cu) {
+int device_shape(int dev, int in_dtype, int out_dtype, int D, int *num_cus, int *waves_per_cu) {
     std::lock_guard<std::mutex> lock(g_mu);
     auto it = g_num_cus.find(dev);
     if (it == g_num_cus.end()) {
@@ -41,11 +41,11 @@ int device_shape(int dev, int in_bf16, int out_bf16, int D, int *num_cus, int *w
         it = g_num_cus.emplace(dev, n).first;
     }
     *num_cus = it->second;
-    const auto key = std::make_pair(dev, variant_id(in_bf16, out_bf16, D));
+    const auto key = std::make_pair(dev, variant_id(in_dtype, out_dtype, D));
     auto wt = g_waves_per_cu.find(key);
     if (wt == g_waves_per_cu.end()) {
         int blocks = 0;
-        hipError_t e = gqa::sweep_occupancy(in_bf16, out_bf16, D, &blocks);
+        hipError_t e = gqa::sweep_occupancy(in_dtype, out_dtype, D, &blocks);
         if (e != hipSuccess || blocks <= 0)
             return gqa::fail(GQA_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
         wt = g_waves_per_cu.emplace(key, blocks * gqa::kWavesPerBlock).first;
@@ -84,13 +84,11 @@ int decode_ex(const gqa_decode_args *a) {
     gqa::clear_error();
     int st = gqa::validate(a);
     if (st != GQA_OK) return st;
-    const int in_bf16 = a->in_dtype == GQA_DTYPE_BF16;
-    const int out_bf16 = a->out_dtype == GQA_DTYPE_BF16;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
     int num_cus = 0, waves_per_cu = 0;
-    st = device_shape(dev, in_bf16, out_bf16, a->d_head, &num_cus, &waves_per_cu);
+    st = device_shape(dev, a->in_dtype, a->out_dtype, a->d_head, &num_cus, &waves_per_cu);
     if (st != GQA_OK) return st;
     gqa_decode_plan plan;
     st = gqa::make_plan(a, num_cus, waves_per_cu, &plan);
@@ -125,11 +123,11 @@ int decode_ex(const gqa_decode_args *a) {
     }
     if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess)
         return gqa::fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
-    e = gqa::launch_sweep(P, in_bf16, out_bf16, a->d_head, plan.split_blocks, stream);
+    e = gqa::launch_sweep(P, a->in_dtype, a->out_dtype, a->d_head, plan.split_blocks, stream);
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "sweep kernel launch failed: %s", hipGetErrorString(e));
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess)
         return gqa::fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
-    e = gqa::launch_merge(P, out_bf16, a->d_head, plan.merge_blocks, plan.merge_threads, stream);
+    e = gqa::launch_merge(P, a->out_dtype, a->d_head, plan.merge_blocks, plan.merge_threads, stream);
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
     return GQA_OK;
 }
@@ -181,6 +179,14 @@ int gqa_decode_f32(const void *q, const void *k, const void *v, void *o, const i
     return gqa_decode_ex(&a);
 }
 
+int gqa_decode_f16(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
+                   int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale,
+                   void *stream) {
+    const gqa_decode_args a =
+        make_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, stream, GQA_DTYPE_F16);
+    return gqa_decode_ex(&a);
+}
+
 int gqa_decode_validate(const gqa_decode_args *args) {
     try {
         gqa::clear_error();
@@ -212,8 +218,7 @@ int gqa_decode_workspace_bytes(const gqa_decode_args *args, size_t *bytes) {
             hipError_t e = hipGetDevice(&dev);
             if (e != hipSuccess)
                 return gqa::fail(GQA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
-            st = device_shape(dev, args->in_dtype == GQA_DTYPE_BF16, args->out_dtype == GQA_DTYPE_BF16,
-                              args->d_head, &num_cus, &waves_per_cu);
+            st = device_shape(dev, args->in_dtype, args->out_dtype, args->d_head, &num_cus, &waves_per_cu);
             if (st != GQA_OK) return st;
         }
         gqa_decode_plan plan;

@@ -13,6 +13,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -119,6 +121,17 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return u >> 16;
 }
 
+// Two outputs rounded to nearest even, packed (the first in the low half):
+// bf16 (kHalf = false) or IEEE fp16 (kHalf = true).
+template <bool kHalf>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if constexpr (kHalf) {
+        const f32x2_t v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+    } else {
+        return bf16_rne(a) | (bf16_rne(b) << 16);
+    }
+}
 
 }  // namespace dev
 }  // namespace gqa

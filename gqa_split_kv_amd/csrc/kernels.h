@@ -23,16 +23,17 @@ struct DecodeParams {
 };
 
 // Enqueues the partial kernel and the merge kernel on `stream`.
-// Enqueues the sweep (partial) kernel: `blocks` workgroups of kThreads.
-hipError_t launch_sweep(const DecodeParams &P, int in_bf16, int out_bf16, int D, int blocks,
+// Enqueues the sweep (partial) kernel: `blocks` workgroups of kThreads.  Dtypes
+// are GQA_DTYPE_* codes.
+hipError_t launch_sweep(const DecodeParams &P, int in_dtype, int out_dtype, int D, int blocks,
                         hipStream_t stream);
 
 // Resident workgroups of the sweep kernel per compute unit.
-hipError_t sweep_occupancy(int in_bf16, int out_bf16, int D, int *blocks_per_cu);
+hipError_t sweep_occupancy(int in_dtype, int out_dtype, int D, int *blocks_per_cu);
 
 // Enqueues the merge kernel: `blocks` = batch * h_kv * G workgroups of `threads`
 // (kMergeThreadsNarrow or kMergeThreadsWide).
-hipError_t launch_merge(const DecodeParams &P, int out_bf16, int D, int blocks, int threads,
+hipError_t launch_merge(const DecodeParams &P, int out_dtype, int D, int blocks, int threads,
                         hipStream_t stream);
 
 }  // namespace gqa

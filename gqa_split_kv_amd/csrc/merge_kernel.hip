@@ -31,13 +31,16 @@ namespace {
 
 using namespace dev;
 
-template <bool kBf16Out>
+constexpr int kF32 = 1;
+constexpr int kF16 = 2;
+
+// Stores four consecutive outputs of one head, rounded to the output type.
+template <int kOut>
 __device__ __forceinline__ void store_quad(uint8_t *row, int eq, float4 x) {
-    if constexpr (kBf16Out)
-        reinterpret_cast<uint2 *>(row)[eq] =
-            make_uint2(bf16_rne(x.x) | (bf16_rne(x.y) << 16), bf16_rne(x.z) | (bf16_rne(x.w) << 16));
-    else
+    if constexpr (kOut == kF32)
         reinterpret_cast<float4 *>(row)[eq] = x;
+    else
+        reinterpret_cast<uint2 *>(row)[eq] = make_uint2(pack2<kOut == kF16>(x.x, x.y), pack2<kOut == kF16>(x.z, x.w));
 }
 
 // Folds a batch of pieces into a running (M, L, acc) with the merge rule: the new
@@ -60,7 +63,7 @@ __device__ __forceinline__ void fold(Running &r, float m, float l, float4 o) {
 }
 
 // Workgroup layout: kHeads query heads x PL piece lanes x QD element quads.
-template <bool kBf16Out, int D, int kThreadsM, int kHeads>
+template <int kOut, int D, int kThreadsM, int kHeads>
 __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
     constexpr int QD = D / 4;                        // element quads per head
     constexpr int PL = kThreadsM / (QD * kHeads);    // piece lanes
@@ -81,9 +84,9 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
     const int g = g0 + hh;
     const bool active = g < G;
     const int len = uniform32(seq_len_at(P.seq_lens, b));
-    uint8_t *orow = P.o + (static_cast<int64_t>(b) * P.h_q + j * G + g) * D * (kBf16Out ? 2 : 4);
+    uint8_t *orow = P.o + (static_cast<int64_t>(b) * P.h_q + j * G + g) * D * (kOut == kF32 ? 4 : 2);
     if (len == 0) {
-        if (pl == 0 && active) store_quad<kBf16Out>(orow, eq, make_float4(0.f, 0.f, 0.f, 0.f));
+        if (pl == 0 && active) store_quad<kOut>(orow, eq, make_float4(0.f, 0.f, 0.f, 0.f));
         return;
     }
     const int64_t total = total_len(P.seq_lens, P.batch);
@@ -139,33 +142,35 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
     }
     if (active) {
         const float inv = 1.0f / r.L;
-        store_quad<kBf16Out>(orow, eq, make_float4(r.acc.x * inv, r.acc.y * inv, r.acc.z * inv, r.acc.w * inv));
+        store_quad<kOut>(orow, eq, make_float4(r.acc.x * inv, r.acc.y * inv, r.acc.z * inv, r.acc.w * inv));
     }
+}
+
+template <int kOut>
+hipError_t launch_out(const DecodeParams &P, int D, int blocks, int threads, hipStream_t stream) {
+    // Narrow: 256 threads covering 256/(D/4) heads with one piece lane each
+    // (few pieces per sequence).  Wide: 1024 threads, one head, 1024/(D/4) piece lanes.
+    if (threads == kMergeThreadsWide) {
+        if (D == 128)
+            hipLaunchKernelGGL((merge_kernel<kOut, 128, kMergeThreadsWide, 1>), dim3(blocks), dim3(kMergeThreadsWide), 0, stream, P);
+        else
+            hipLaunchKernelGGL((merge_kernel<kOut, 64, kMergeThreadsWide, 1>), dim3(blocks), dim3(kMergeThreadsWide), 0, stream, P);
+    } else {
+        if (D == 128)
+            hipLaunchKernelGGL((merge_kernel<kOut, 128, kMergeThreadsNarrow, 8>), dim3(blocks), dim3(kMergeThreadsNarrow), 0, stream, P);
+        else
+            hipLaunchKernelGGL((merge_kernel<kOut, 64, kMergeThreadsNarrow, 16>), dim3(blocks), dim3(kMergeThreadsNarrow), 0, stream, P);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_merge(const DecodeParams &P, int out_bf16, int D, int blocks, int threads,
+hipError_t launch_merge(const DecodeParams &P, int out_dtype, int D, int blocks, int threads,
                         hipStream_t stream) {
-    // Narrow: 256 threads covering 256/(D/4) heads with one piece lane each
-    // (few pieces per sequence).  Wide: 1024 threads, one head, 1024/(D/4) piece lanes.
-#define GQA_MERGE(O, DD, T, H) \
-    hipLaunchKernelGGL((merge_kernel<O, DD, T, H>), dim3(blocks), dim3(T), 0, stream, P)
-    if (threads == kMergeThreadsWide) {
-        if (out_bf16) {
-            if (D == 128) GQA_MERGE(true, 128, kMergeThreadsWide, 1); else GQA_MERGE(true, 64, kMergeThreadsWide, 1);
-        } else {
-            if (D == 128) GQA_MERGE(false, 128, kMergeThreadsWide, 1); else GQA_MERGE(false, 64, kMergeThreadsWide, 1);
-        }
-    } else {
-        if (out_bf16) {
-            if (D == 128) GQA_MERGE(true, 128, kMergeThreadsNarrow, 8); else GQA_MERGE(true, 64, kMergeThreadsNarrow, 16);
-        } else {
-            if (D == 128) GQA_MERGE(false, 128, kMergeThreadsNarrow, 8); else GQA_MERGE(false, 64, kMergeThreadsNarrow, 16);
-        }
-    }
-#undef GQA_MERGE
-    return hipGetLastError();
+    if (out_dtype == kF32) return launch_out<kF32>(P, D, blocks, threads, stream);
+    if (out_dtype == kF16) return launch_out<kF16>(P, D, blocks, threads, stream);
+    return launch_out<0>(P, D, blocks, threads, stream);
 }
 
 }  // namespace gqa

@@ -66,8 +66,10 @@ static int check_basic(const gqa_decode_args *a) {
     if (a->d_head != 64 && a->d_head != 128)
         return fail(GQA_ERR_UNSUPPORTED, "d_head %d not supported (64 or 128)", a->d_head);
     const bool pair_ok = (a->in_dtype == GQA_DTYPE_BF16 && a->out_dtype == GQA_DTYPE_BF16) ||
+                         (a->in_dtype == GQA_DTYPE_BF16 && a->out_dtype == GQA_DTYPE_F32) ||
                          (a->in_dtype == GQA_DTYPE_F32 && a->out_dtype == GQA_DTYPE_F32) ||
-                         (a->in_dtype == GQA_DTYPE_BF16 && a->out_dtype == GQA_DTYPE_F32);
+                         (a->in_dtype == GQA_DTYPE_F16 && a->out_dtype == GQA_DTYPE_F16) ||
+                         (a->in_dtype == GQA_DTYPE_F16 && a->out_dtype == GQA_DTYPE_F32);
     if (!pair_ok)
         return fail(GQA_ERR_UNSUPPORTED, "dtype pair (in %d, out %d) not supported", a->in_dtype,
                     a->out_dtype);

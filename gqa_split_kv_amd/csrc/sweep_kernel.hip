@@ -99,7 +99,12 @@ __device__ __forceinline__ void load_words(uint32_t (&dst)[NW], __amdgpu_buffer_
 // step's (m, l, O) into the state): the scores of head lane%16 are reduced
 // across the four lane groups, the state is rescaled by 2^(m_old - m_new) and
 // p = 2^(s - m_new) is returned in place of s.
-template <int N, int VEC>
+//
+// kOffset shifts the exponent of p (not of the running max): p = 2^(s - m_new +
+// kOffset), so l and O of the triple carry a constant factor 2^kOffset, which
+// cancels in O / l and in the merge (every piece of a sequence carries it).
+// fp16 P uses 15 so that small weights stay inside fp16's exponent range.
+template <int N, int VEC, int kOffset>
 __device__ __forceinline__ void softmax_step(float (&sv)[N], float &m_run, float &l_run,
                                              f32x4_t (&acc)[VEC]) {
     float mx = sv[0];
@@ -112,7 +117,7 @@ __device__ __forceinline__ void softmax_step(float (&sv)[N], float &m_run, float
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
+        sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new + static_cast<float>(kOffset));
         sum += sv[i];
     }
     l_run = l_run * alpha + sum;
@@ -121,23 +126,32 @@ __device__ __forceinline__ void softmax_step(float (&sv)[N], float &m_run, float
     m_run = m_new;
 }
 
-// ------------------------------------------------------------------ bf16 steps
+// ------------------------------------------------------------------ bf16 / fp16 steps
 //
-// One step = 32 keys.  Q K^T: two v_mfma_f32_16x16x32_bf16 groups (16 keys each)
-// with K rows as the A operand (M = keys) and Q^T as B (N = query heads); lane l
-// of QK block b loads key row 8*(m/4) + 4b + m%4 (m = l%16), so that after the
-// product lane l holds the scores of keys 8*kg + i (kg = l/16, i = 0..7) of its
-// head -- exactly the eight keys it contributes to the P V product below.
+// One step = 32 keys.  Q K^T: two v_mfma_f32_16x16x32_{bf16,f16} groups (16 keys
+// each) with K rows as the A operand (M = keys) and Q^T as B (N = query heads);
+// lane l of QK block b loads key row 8*(m/4) + 4b + m%4 (m = l%16), so that after
+// the product lane l holds the scores of keys 8*kg + i (kg = l/16, i = 0..7) of
+// its head -- exactly the eight keys it contributes to the P V product below.
 //
-// P V: O^T[d][g] += V^T[d][key] P^T[key][g] as v_mfma_f32_16x16x32_bf16 with
-// the 32 keys as the contraction.  Lane l loads 16 bytes (8 d) of key rows
-// 8*kg + i, i = 0..7 (each load instruction reads four whole rows), and repacks
-// them in registers so its A operand for column c holds d = VEC*(l%16) + c of its
-// eight keys.  P is split into a bf16 high part (round to nearest) and a bf16
+// P V: O^T[d][g] += V^T[d][key] P^T[key][g] as the same MFMA with the 32 keys as
+// the contraction.  Lane l loads 16 bytes (8 d) of key rows 8*kg + i, i = 0..7
+// (each load instruction reads four whole rows), and repacks them in registers
+// so its A operand for column c holds d = VEC*(l%16) + c of its eight keys.  P is
+// split into a high part (round to nearest in the input's 16-bit format) and a
 // low part (the rounded remainder) and the product is issued twice, so P keeps
-// ~16 significant bits; V, Q and K are exact in bf16.
-template <int D>
-struct Bf16Step {
+// ~16 (bf16) or ~22 (fp16) significant bits; V, Q and K are exact.
+template <int D, bool kHalf>
+struct Packed16Step {
+    // 16x16x32 product of eight 16-bit values per lane, in the input's format.
+    __device__ __forceinline__ static f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+        if constexpr (kHalf)
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                          __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                           __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
     static constexpr int kKeys = 32;
     static constexpr int ES = 2;
     static constexpr int ROWB = D * ES;
@@ -180,10 +194,7 @@ struct Bf16Step {
         for (int b = 0; b < 2; ++b) {
             f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int p = 0; p < NKP; ++p)
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, B.k[b][p]),
-                                                            __builtin_bit_cast(bf16x8_t, qop[p]), s,
-                                                            0, 0, 0);
+            for (int p = 0; p < NKP; ++p) s = mfma16(B.k[b][p], qop[p], s);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
             {
@@ -191,20 +202,26 @@ struct Bf16Step {
                 sv[4 * b + q] = (key >= lo && key < hi) ? s[q] * sl2 : -INFINITY;
             }
         }
-        softmax_step<8, VEC>(sv, m_run, l_run, acc);
-        // P = hi + lo, both bf16, packed two keys per word (key 2w in the low half).
+        softmax_step<8, VEC, kHalf ? 15 : 0>(sv, m_run, l_run, acc);
+        // P = hi + lo in the 16-bit format, packed two keys per word (key 2w low).
         uint32_t phi[4], plo[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const f32x2_t pw = {sv[2 * w], sv[2 * w + 1]};
-            const bf16x2_t h = __builtin_convertvector(pw, bf16x2_t);
-            const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-            const f32x2_t r = {pw[0] - __uint_as_float(hb << 16), pw[1] - __uint_as_float(hb & 0xffff0000u)};
-            phi[w] = hb;
-            plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+            if constexpr (kHalf) {
+                const f16x2_t h = __builtin_convertvector(pw, f16x2_t);
+                const f32x2_t hf = __builtin_convertvector(h, f32x2_t);
+                phi[w] = __builtin_bit_cast(uint32_t, h);
+                plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw - hf, f16x2_t));
+            } else {
+                const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw, bf16x2_t));
+                const f32x2_t r = {pw[0] - __uint_as_float(hb << 16), pw[1] - __uint_as_float(hb & 0xffff0000u)};
+                phi[w] = hb;
+                plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+            }
         }
-        const bf16x8_t bhi = __builtin_bit_cast(bf16x8_t, make_uint4(phi[0], phi[1], phi[2], phi[3]));
-        const bf16x8_t blo = __builtin_bit_cast(bf16x8_t, make_uint4(plo[0], plo[1], plo[2], plo[3]));
+        const uint4 bhi = make_uint4(phi[0], phi[1], phi[2], phi[3]);
+        const uint4 blo = make_uint4(plo[0], plo[1], plo[2], plo[3]);
 #pragma unroll
         for (int c = 0; c < VEC; ++c) {
             // A operand of column c: element i = V[key 8kg + i][d = VEC*m + c].
@@ -215,9 +232,9 @@ struct Bf16Step {
                 const uint32_t y = B.v[2 * w + 1][c >> 1];
                 a[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
             }
-            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(a[0], a[1], a[2], a[3]));
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bhi, acc[c], 0, 0, 0);
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, blo, acc[c], 0, 0, 0);
+            const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
+            acc[c] = mfma16(av, bhi, acc[c]);
+            acc[c] = mfma16(av, blo, acc[c]);
         }
     }
 };
@@ -276,7 +293,7 @@ struct F32Step {
             const int key = 4 * kg + q;
             sv[q] = (key >= lo && key < hi) ? s[q] * sl2 : -INFINITY;
         }
-        softmax_step<4, VEC>(sv, m_run, l_run, acc);
+        softmax_step<4, VEC, 0>(sv, m_run, l_run, acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -285,36 +302,35 @@ struct F32Step {
     }
 };
 
-template <bool kBf16In, int D>
-using Step = typename std::conditional<kBf16In, Bf16Step<D>, F32Step<D>>::type;
+// Element types, numbered as the GQA_DTYPE_* codes of the C ABI.
+constexpr int kBf16 = 0;
+constexpr int kF32 = 1;
+constexpr int kF16 = 2;
 
-template <bool kBf16Out>
-__device__ __forceinline__ void store_row(uint8_t *dst, const float *x, int n);
+template <int kIn, int D>
+using Step = typename std::conditional<kIn == kF32, F32Step<D>, Packed16Step<D, kIn == kF16>>::type;
 
-// Stores n (multiple of 8) consecutive values.
-template <>
-__device__ __forceinline__ void store_row<true>(uint8_t *dst, const float *x, int n) {
-    for (int i = 0; i < n; i += 8) {
-        uint4 w;
-        w.x = bf16_rne(x[i + 0]) | (bf16_rne(x[i + 1]) << 16);
-        w.y = bf16_rne(x[i + 2]) | (bf16_rne(x[i + 3]) << 16);
-        w.z = bf16_rne(x[i + 4]) | (bf16_rne(x[i + 5]) << 16);
-        w.w = bf16_rne(x[i + 6]) | (bf16_rne(x[i + 7]) << 16);
-        *reinterpret_cast<uint4 *>(dst + 2 * i) = w;
+// Stores n (a multiple of 8) consecutive outputs, rounded to the output type.
+template <int kOut>
+__device__ __forceinline__ void store_row(uint8_t *dst, const float *x, int n) {
+    if constexpr (kOut == kF32) {
+        for (int i = 0; i < n; i += 4)
+            *reinterpret_cast<float4 *>(dst + 4 * i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+    } else {
+        for (int i = 0; i < n; i += 8) {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = pack2<kOut == kF16>(x[i + 2 * k], x[i + 2 * k + 1]);
+            *reinterpret_cast<uint4 *>(dst + 2 * i) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
     }
 }
 
-template <>
-__device__ __forceinline__ void store_row<false>(uint8_t *dst, const float *x, int n) {
-    for (int i = 0; i < n; i += 4)
-        *reinterpret_cast<float4 *>(dst + 4 * i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
-}
-
 // One piece: keys [t0, t1) of (sequence b, kv head j); off = keys before b.
-template <bool kBf16In, bool kBf16Out, int D, int kDepth>
+template <int kIn, int kOut, int D, int kDepth>
 __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int j, int64_t off,
                                               int t0, int t1, int len, int w) {
-    using S = Step<kBf16In, D>;
+    using S = Step<kIn, D>;
     constexpr int VEC = S::VEC;
     const int lane = lane_id();
     const int g = lane & 15;
@@ -398,8 +414,8 @@ swept:
             for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[c][q] * inv;
         if (g < G) {
             const int64_t orow = static_cast<int64_t>(b) * P.h_q + j * G + g;
-            uint8_t *dst = P.o + (orow * D + 4 * VEC * kg) * (kBf16Out ? 2 : 4);
-            store_row<kBf16Out>(dst, out, 4 * VEC);
+            uint8_t *dst = P.o + (orow * D + 4 * VEC * kg) * (kOut == kF32 ? 4 : 2);
+            store_row<kOut>(dst, out, 4 * VEC);
         }
     } else {
         // Slot 0: a piece of a sequence that began before this range; slot 1: the
@@ -411,13 +427,13 @@ swept:
             for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[c][q];
         if (g < G) {
             const int64_t srow = (static_cast<int64_t>(w) * 2 + slot) * G + g;
-            store_row<false>(reinterpret_cast<uint8_t *>(P.ws_o + srow * D + 4 * VEC * kg), out, 4 * VEC);
+            store_row<kF32>(reinterpret_cast<uint8_t *>(P.ws_o + srow * D + 4 * VEC * kg), out, 4 * VEC);
             if (kg == 0) P.ws_ml[srow] = make_float2(m_run, l_tot);
         }
     }
 }
 
-template <bool kBf16In, bool kBf16Out, int D, int kDepth>
+template <int kIn, int kOut, int D, int kDepth>
 __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
     const int w = uniform32(static_cast<int>(blockIdx.x) * kWavesPerBlock +
                             static_cast<int>(threadIdx.x) / kWave);
@@ -439,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
         const int t0 = uniform32(static_cast<int>(pos - off));
         const int64_t lim = end - off;
         const int t1 = uniform32(static_cast<int>(lim < len ? lim : len));
-        process_piece<kBf16In, kBf16Out, D, kDepth>(P, b, j, off, t0, t1, len, w);
+        process_piece<kIn, kOut, D, kDepth>(P, b, j, off, t0, t1, len, w);
         pos = off + t1;
         if (pos >= end) break;
         off += len;   // next non-empty sequence (one exists: pos < total)
@@ -450,30 +466,42 @@ __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
     }
 }
 
-}  // namespace
-
-hipError_t launch_sweep(const DecodeParams &P, int in_bf16, int out_bf16, int D, int blocks,
-                        hipStream_t stream) {
-#define GQA_LAUNCH(I, O, DD)                                                                        \
-    hipLaunchKernelGGL((split_kernel<I, O, DD, kSweepDepth>), dim3(blocks), dim3(kThreads), 0, stream, P)
-    if (in_bf16 && out_bf16) {
-        if (D == 128) GQA_LAUNCH(true, true, 128); else GQA_LAUNCH(true, true, 64);
-    } else if (in_bf16) {
-        if (D == 128) GQA_LAUNCH(true, false, 128); else GQA_LAUNCH(true, false, 64);
-    } else {
-        if (D == 128) GQA_LAUNCH(false, false, 128); else GQA_LAUNCH(false, false, 64);
-    }
-#undef GQA_LAUNCH
+template <int kIn, int kOut>
+hipError_t launch_io(const DecodeParams &P, int D, int blocks, hipStream_t stream) {
+    if (D == 128)
+        hipLaunchKernelGGL((split_kernel<kIn, kOut, 128, kSweepDepth>), dim3(blocks), dim3(kThreads), 0, stream, P);
+    else
+        hipLaunchKernelGGL((split_kernel<kIn, kOut, 64, kSweepDepth>), dim3(blocks), dim3(kThreads), 0, stream, P);
     return hipGetLastError();
 }
 
-hipError_t sweep_occupancy(int in_bf16, int out_bf16, int D, int *blocks_per_cu) {
-#define GQA_OCC(I, O, DD) \
-    hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, split_kernel<I, O, DD, kSweepDepth>, kThreads, 0)
-    if (in_bf16 && out_bf16) return D == 128 ? GQA_OCC(true, true, 128) : GQA_OCC(true, true, 64);
-    if (in_bf16) return D == 128 ? GQA_OCC(true, false, 128) : GQA_OCC(true, false, 64);
-    return D == 128 ? GQA_OCC(false, false, 128) : GQA_OCC(false, false, 64);
-#undef GQA_OCC
+template <int kIn, int kOut>
+hipError_t occupancy_io(int D, int *blocks_per_cu) {
+    return D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                          blocks_per_cu, split_kernel<kIn, kOut, 128, kSweepDepth>, kThreads, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                          blocks_per_cu, split_kernel<kIn, kOut, 64, kSweepDepth>, kThreads, 0);
+}
+
+}  // namespace
+
+// (in, out) pairs the validation admits: (bf16, bf16), (bf16, f32), (f32, f32),
+// (f16, f16), (f16, f32).
+hipError_t launch_sweep(const DecodeParams &P, int in_dtype, int out_dtype, int D, int blocks,
+                        hipStream_t stream) {
+    if (in_dtype == kBf16) return out_dtype == kBf16 ? launch_io<kBf16, kBf16>(P, D, blocks, stream)
+                                                     : launch_io<kBf16, kF32>(P, D, blocks, stream);
+    if (in_dtype == kF16) return out_dtype == kF16 ? launch_io<kF16, kF16>(P, D, blocks, stream)
+                                                   : launch_io<kF16, kF32>(P, D, blocks, stream);
+    return launch_io<kF32, kF32>(P, D, blocks, stream);
+}
+
+hipError_t sweep_occupancy(int in_dtype, int out_dtype, int D, int *blocks_per_cu) {
+    if (in_dtype == kBf16) return out_dtype == kBf16 ? occupancy_io<kBf16, kBf16>(D, blocks_per_cu)
+                                                     : occupancy_io<kBf16, kF32>(D, blocks_per_cu);
+    if (in_dtype == kF16) return out_dtype == kF16 ? occupancy_io<kF16, kF16>(D, blocks_per_cu)
+                                                   : occupancy_io<kF16, kF32>(D, blocks_per_cu);
+    return occupancy_io<kF32, kF32>(D, blocks_per_cu);
 }
 
 }  // namespace gqa

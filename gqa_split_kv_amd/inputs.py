@@ -9,9 +9,9 @@ Layouts (row-major, contiguous):
   k, v      [sum(seq_lens), h_kv, d]   sequences packed back to back
   seq_lens  int32[batch]
 
-Element values are i.i.d. N(0, 1) drawn in float32 and rounded to bf16
-(round-to-nearest-even) for the bf16 workloads; the fp32 workload keeps the
-float32 draws.  The long-context stress workload scales a random 0.1% of the
+Element values are i.i.d. N(0, 1) drawn in float32 and rounded to bf16 or
+IEEE fp16 (round-to-nearest-even) for the 16-bit workloads; the fp32 workload
+keeps the float32 draws.  The long-context stress workload scales a random 0.1% of the
 key rows of every sequence (all kv heads of that row) by 8, which makes the
 softmax peaked.
 
@@ -39,7 +39,7 @@ import numpy as np
 class Workload:
     cfg: int
     name: str
-    dtype: str               # "bf16" or "f32" (inputs; the accumulator is always fp32)
+    dtype: str               # "bf16", "f16" or "f32" (inputs; the accumulator is always fp32)
     batch: int
     h_q: int
     h_kv: int
@@ -120,7 +120,7 @@ def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
 
 @dataclass
 class HostCase:
-    q: np.ndarray            # uint16 bf16 bits or float32, [batch, h_q, d]
+    q: np.ndarray            # uint16 bf16 bits, float16 or float32, [batch, h_q, d]
     k: np.ndarray            # [sum(seq_lens), h_kv, d]
     v: np.ndarray
     seq_lens: np.ndarray     # int32[batch]
@@ -157,6 +157,8 @@ def host_case(batch: int, h_q: int, h_kv: int, d: int, seq_lens: Sequence[int], 
         scale = 1.0 / float(np.sqrt(d))
     if dtype == "bf16":
         q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    elif dtype == "f16":
+        q, k, v = q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)   # nearest even
     elif dtype != "f32":
         raise ValueError(dtype)
     return HostCase(q, k, v, sl, float(scale), dtype, peaks)
@@ -203,7 +205,7 @@ def device_case(batch: int, h_q: int, h_kv: int, d: int, seq_lens: Sequence[int]
     import torch
     sl = np.asarray(seq_lens, dtype=np.int32).reshape(batch)
     rows = int(np.clip(sl, 0, None).sum())
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
     base_seed = int(np.random.SeedSequence(seed).generate_state(1)[0])
     q = _torch_normal((batch, h_q, d), base_seed + 0, device, tdt)
     k = _torch_normal((rows, h_kv, d), base_seed + 1, device, tdt)
@@ -236,7 +238,7 @@ def to_host_bits(t) -> np.ndarray:
     c = t.detach().contiguous().cpu()
     if c.dtype == torch.bfloat16:
         return c.view(torch.int16).numpy().view(np.uint16)
-    if c.dtype == torch.float32:
+    if c.dtype in (torch.float32, torch.float16):
         return c.numpy()
     raise TypeError(c.dtype)
 
@@ -246,6 +248,6 @@ def from_host_bits(a: np.ndarray, device: str = "cuda"):
     import torch
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
-    if a.dtype == np.float32:
+    if a.dtype in (np.float32, np.float16):
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
     raise TypeError(a.dtype)

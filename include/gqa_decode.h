@@ -36,7 +36,7 @@
  *             so a call needs no host synchronisation)
  *
  * Supported: d_head in {64, 128}; G = h_q / h_kv in 1..16; (in, out) dtypes
- * (bf16, bf16), (f32, f32) and (bf16, f32).  q, k, v, o must be 16-byte aligned,
+ * (bf16, bf16), (bf16, f32), (f16, f16), (f16, f32) and (f32, f32).  q, k, v, o must be 16-byte aligned,
  * seq_lens 4-byte aligned.
  *
  * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
@@ -60,6 +60,7 @@ extern "C" {
 /* Element types. */
 #define GQA_DTYPE_BF16 0
 #define GQA_DTYPE_F32 1
+#define GQA_DTYPE_F16 2 /* IEEE binary16 */
 
 /* Status codes. */
 typedef enum gqa_status {
@@ -87,6 +88,12 @@ int gqa_decode(const void *q, const void *k, const void *v, void *o, const int32
 
 /* gqa_decode_f32 -- the same operation with fp32 q/k/v in and fp32 o out. */
 int gqa_decode_f32(const void *q, const void *k, const void *v, void *o,
+                   const int32_t *seq_lens, int32_t batch, int32_t h_q, int32_t h_kv,
+                   int32_t d_head, float scale, void *stream);
+
+/* gqa_decode_f16 -- the same operation with IEEE fp16 q/k/v in and fp16 o out (the
+ * page's element type); fp32 accumulation, o rounded to nearest even. */
+int gqa_decode_f16(const void *q, const void *k, const void *v, void *o,
                    const int32_t *seq_lens, int32_t batch, int32_t h_q, int32_t h_kv,
                    int32_t d_head, float scale, void *stream);
 
@@ -125,8 +132,8 @@ typedef struct gqa_decode_args {
     int32_t h_kv;
     int32_t d_head;
     float scale;
-    int32_t in_dtype;  /* GQA_DTYPE_BF16 or GQA_DTYPE_F32 */
-    int32_t out_dtype; /* GQA_DTYPE_BF16 or GQA_DTYPE_F32 */
+    int32_t in_dtype;  /* GQA_DTYPE_BF16, GQA_DTYPE_F16 or GQA_DTYPE_F32 */
+    int32_t out_dtype; /* the input's type, or GQA_DTYPE_F32 */
     int32_t num_chunks;
     int32_t min_chunk;
     void *workspace;

@@ -19,7 +19,8 @@ Source: kernbench2 page "_gqa_attention_decode_long.py": the "Tile 0" block
 block.  Readings where that page is silent are listed in oracle.c's header.
 
 Inputs are numpy arrays: bf16 tensors travel as their raw bits in uint16
-arrays (dtype code 0), fp32 tensors as float32 arrays (dtype code 1).
+arrays (dtype code 0), fp32 tensors as float32 arrays (dtype code 1), IEEE fp16
+tensors as float16 arrays (dtype code 2).
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ from . import build as _build
 
 BF16 = 0
 F32 = 1
+F16 = 2
 
 _lib = None
 
@@ -53,6 +55,8 @@ def _load():
     lib.oracle_partial_f64.argtypes = [P, P, P, P, i32, i32, i32, i32, ctypes.c_double, i32, i32,
                                        i32, i32, i32, P, P, P]
     lib.oracle_partial_f64.restype = ctypes.c_int
+    lib.oracle_widen_f64.argtypes = [P, ctypes.c_int64, i32, P]
+    lib.oracle_widen_f64.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -69,7 +73,17 @@ def _dtype_code(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.float32:
         return F32
-    raise TypeError("oracle inputs are uint16 (bf16 bits) or float32, got %s" % a.dtype)
+    if a.dtype == np.float16:
+        return F16
+    raise TypeError("oracle inputs are uint16 (bf16 bits), float16 or float32, got %s" % a.dtype)
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    """The exact widening to float64 the oracle applies to its inputs."""
+    a = np.ascontiguousarray(a)
+    out = np.empty(a.shape, dtype=np.float64)
+    _load().oracle_widen_f64(_ptr(a), a.size, _dtype_code(a), _ptr(out))
+    return out
 
 
 def _ptr(a: np.ndarray):

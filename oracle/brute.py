@@ -5,7 +5,7 @@ It computes the same plain definition as oracle.c (softmax of scale * q.k_t over
 the keys of a sequence, applied to its V rows; query head h reads kv head
 h // G), but in Python's decimal arithmetic with 50 significant digits and a
 correctly rounded exp, so that it pins the fp64 oracle to within its own
-rounding.  Every input is converted exactly (bf16 bits -> float -> Decimal).
+rounding.  Every input is converted exactly (bf16 bits, fp16 or fp32 -> float -> Decimal).
 
 Source: kernbench2 page "_gqa_attention_decode_long.py", "Tile 0" block over all
 keys and the final normalise-and-store block.
@@ -20,7 +20,7 @@ import numpy as np
 def _exact(a: np.ndarray):
     if a.dtype == np.uint16:
         f = (a.astype(np.uint32) << 16).view(np.float32)
-    elif a.dtype == np.float32:
+    elif a.dtype in (np.float32, np.float16):
         f = a
     else:
         raise TypeError(a.dtype)

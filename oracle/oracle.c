@@ -27,7 +27,8 @@
  *   - K and V are packed [sum(seq_lens), h_kv, d] (the page has no batch axis).
  *
  * Every input element is widened exactly to double (bf16 is read as its raw
- * 16 bits and shifted into a float; float widens exactly).  Sums run in index
+ * 16 bits and shifted into a float; IEEE fp16 is decoded from its bits; float
+ * widens exactly).  Sums run in index
  * order.  OpenMP spreads (sequence, kv head) pairs over the host cores; that
  * changes nothing in the arithmetic of any single output.
  */
@@ -41,13 +42,36 @@
 
 #define ORACLE_BF16 0
 #define ORACLE_F32 1
+#define ORACLE_F16 2
+
+/* IEEE binary16 bits -> double, exactly: (1024 + m) * 2^(e - 25) for a normal
+ * number, m * 2^-24 for a subnormal, infinities and NaN kept. */
+static double half_bits_to_double(uint16_t h) {
+    const int sign = h >> 15;
+    const int e = (h >> 10) & 0x1f;
+    const int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m | 0x400), e - 25);
+    return sign ? -v : v;
+}
 
 static double widen(const void *base, int64_t idx, int dtype) {
     if (dtype == ORACLE_F32) return (double)((const float *)base)[idx];
+    if (dtype == ORACLE_F16) return half_bits_to_double(((const uint16_t *)base)[idx]);
     uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* The widening the oracle applies to its inputs, exposed for testing. */
+void oracle_widen_f64(const void *src, int64_t n, int32_t dtype, double *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = widen(src, i, dtype);
 }
 
 static int32_t clamp_len(int32_t n) { return n > 0 ? n : 0; }

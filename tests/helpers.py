@@ -1,8 +1,9 @@
 """Shared helpers of the GPU tests: run the HIP path through the C ABI, run the
 oracle on the same inputs, and compare them to the tolerance stated for the
-method (bf16 inputs, fp32 accumulation: max |err| <= 2e-3 and relative L2 <=
-1e-3 on the fp32 result; a bf16 result is held to the nearest-even bf16
-rounding of the oracle, within one bf16 ulp and relative L2 <= 1e-3).
+method (16-bit inputs, fp32 accumulation: max |err| <= 2e-3 and relative L2 <=
+1e-3 on the fp32 result; a bf16 or fp16 result is held to the nearest-even
+rounding of the oracle in its format: within one ulp of it or 1e-5, and
+relative L2 <= 1e-3).
 """
 from __future__ import annotations
 
@@ -94,9 +95,28 @@ def oracle_of(case) -> np.ndarray:
     return oracle.gqa_decode_f64(case.q, case.k, case.v, case.seq_lens, case.scale)
 
 
+def check_f16(got: np.ndarray, ref: np.ndarray, what: str = ""):
+    """fp16 result: each element within one fp16 ulp of the nearest-even fp16
+    rounding of the oracle, or within 1e-5 of it; rel-L2 <= 1e-3 against it."""
+    want = ref.astype(np.float16)              # one rounding, nearest even
+    steps = np.abs(bf16_ordinal(got.view(np.uint16)) - bf16_ordinal(want.view(np.uint16)))
+    g = got.astype(np.float64)
+    wf = want.astype(np.float64)
+    assert np.isfinite(g).all(), what + ": non-finite output"
+    ok = (steps <= 1) | (np.abs(g - wf) <= BF16_ABS_SLACK)
+    r = rel_l2(g, wf)
+    bad = int((~ok).sum())
+    assert bad == 0 and r <= REL_L2, "%s: %d elements beyond 1 ulp and %.0e; rel-L2 %.3g" % (
+        what, bad, BF16_ABS_SLACK, r)
+    big = np.abs(wf) >= 1e-3
+    return int(steps[big].max()) if big.any() else 0, r, rel_l2(g, ref)
+
+
 def compare(out_t, ref: np.ndarray, what: str = ""):
     import torch
     h = out_host(out_t)
     if out_t.dtype == torch.bfloat16:
         return check_bf16(h, ref, what)
+    if out_t.dtype == torch.float16:
+        return check_f16(h, ref, what)
     return check_f32(h, ref, what)

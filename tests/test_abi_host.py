@@ -57,6 +57,8 @@ def test_valid_arguments_pass(lib):
     assert _validate() == B.GQA_OK
     assert _validate(in_dtype=B.GQA_DTYPE_F32, out_dtype=B.GQA_DTYPE_F32, d_head=64) == B.GQA_OK
     assert _validate(out_dtype=B.GQA_DTYPE_F32) == B.GQA_OK
+    assert _validate(in_dtype=B.GQA_DTYPE_F16, out_dtype=B.GQA_DTYPE_F16) == B.GQA_OK
+    assert _validate(in_dtype=B.GQA_DTYPE_F16, out_dtype=B.GQA_DTYPE_F32) == B.GQA_OK
     for G, h_kv in [(1, 8), (2, 4), (4, 8), (8, 8), (16, 1), (3, 2), (5, 1)]:
         assert _validate(h_q=G * h_kv, h_kv=h_kv) == B.GQA_OK
 
@@ -80,6 +82,9 @@ def test_shape_errors(lib, kw):
 @pytest.mark.parametrize("kw", [dict(d_head=96), dict(d_head=256), dict(d_head=0),
                                 dict(h_q=32 * 8, h_kv=8), dict(h_q=17, h_kv=1),
                                 dict(in_dtype=B.GQA_DTYPE_F32, out_dtype=B.GQA_DTYPE_BF16),
+                                dict(in_dtype=B.GQA_DTYPE_F32, out_dtype=B.GQA_DTYPE_F16),
+                                dict(in_dtype=B.GQA_DTYPE_F16, out_dtype=B.GQA_DTYPE_BF16),
+                                dict(in_dtype=B.GQA_DTYPE_BF16, out_dtype=B.GQA_DTYPE_F16),
                                 dict(in_dtype=7), dict(out_dtype=3), dict(h_q=70000, h_kv=70000)])
 def test_unsupported(lib, kw):
     assert _validate(**kw) == B.GQA_ERR_UNSUPPORTED

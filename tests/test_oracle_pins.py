@@ -37,6 +37,21 @@ def _f64(a):
     return bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
 
 
+def test_input_widening_is_exact_for_every_16_bit_pattern():
+    # Library routines fix the values: numpy's IEEE half conversion, and bf16 as
+    # the upper half of a float32.
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    h = bits.view(np.float16)
+    w = oracle.widen(h)
+    ref = h.astype(np.float64)
+    assert ((w == ref) | (np.isnan(w) & np.isnan(ref))).all()
+    wb = oracle.widen(bits)
+    refb = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert ((wb == refb) | (np.isnan(wb) & np.isnan(refb))).all()
+    x = np.random.default_rng(0).standard_normal(1000).astype(np.float32)
+    assert np.array_equal(oracle.widen(x), x.astype(np.float64))
+
+
 def _rel(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
@@ -47,7 +62,7 @@ def _rel(a, b):
 # ---------------------------------------------------------------- brute force
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("G,h_kv", [(1, 2), (2, 1), (4, 1), (2, 2)])
 @pytest.mark.parametrize("seq_lens", [[0], [1], [2, 5], [16, 0, 3]])
 def test_oracle_matches_decimal_brute_force(dtype, G, h_kv, seq_lens):
@@ -99,9 +114,10 @@ def _sdpa_reference(c, G):
     return np.stack(out)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("G,h_kv,d", [(1, 4, 16), (8, 1, 64), (4, 2, 32), (16, 1, 32), (8, 8, 128)])
-def test_gqa_equals_mha_with_repeated_kv_heads(G, h_kv, d):
-    c = host_case(3, G * h_kv, h_kv, d, [37, 1, 130], "bf16", seed=100 + G, scale=d ** -0.5)
+def test_gqa_equals_mha_with_repeated_kv_heads(G, h_kv, d, dtype):
+    c = host_case(3, G * h_kv, h_kv, d, [37, 1, 130], dtype, seed=100 + G, scale=d ** -0.5)
     got = oracle.gqa_decode_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
     ref = _sdpa_reference(c, G)
     assert np.abs(got - ref).max() <= 1e-12

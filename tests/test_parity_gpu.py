@@ -100,14 +100,15 @@ def test_long_context_peaked_workload_full_size():
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("G,h_kv", [(1, 4), (2, 2), (3, 1), (4, 2), (8, 1), (8, 2), (16, 1), (5, 3)])
-@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
+@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"),
+                                       ("f16", "f16"), ("f16", "f32")])
 def test_heads_dims_dtypes(d, G, h_kv, dtype, out):
     import torch
     lens = [37, 0, 300, 16, 1]
     c = host_case(len(lens), G * h_kv, h_kv, d, lens, dtype, seed=G * 100 + h_kv * 10 + d)
     ref = oracle_of(c)
     q, k, v, sl = upload(c)
-    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    odt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out]
     for nc, mc in [(0, 0), (5, 1), (64, 16)]:
         o = run_hip(q, k, v, sl, c.scale, out_dtype=odt, num_chunks=nc, min_chunk=mc)
         compare(o, ref, "G=%d h_kv=%d d=%d %s->%s nc=%d mc=%d" % (G, h_kv, d, dtype, out, nc, mc))
@@ -227,6 +228,42 @@ def test_c_names_and_f32_entry_point():
     B.gqa_decode(q, k, v, ob, sl, 2, 8, 2, 64, cb.scale)
     torch.cuda.synchronize()
     compare(ob, refb, "gqa_decode")
+
+
+def test_f16_entry_point_and_70b_shape():
+    """fp16 (the pages' element type) through gqa_decode_f16 and gqa_decode_ex, on the
+    70B-shaped head layout with ragged lengths, peaked keys included."""
+    import torch
+    lens = [4000, 1, 17, 9001, 1024, 33]
+    c = host_case(len(lens), 64, 8, 128, lens, "f16", seed=97, peaked_frac=0.001, peak_factor=8.0)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    o = torch.full((len(lens), 64, 128), float("nan"), dtype=torch.float16, device="cuda")
+    B.gqa_decode_f16(q, k, v, o, sl, len(lens), 64, 8, 128, c.scale)
+    torch.cuda.synchronize()
+    compare(o, ref, "gqa_decode_f16")
+    for nc, mc in [(0, 0), (64, 1), (8, 16)]:
+        o32 = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=mc)
+        e, r = compare(o32, ref, "f16 -> f32 nc=%d" % nc)
+        assert e < 1e-4 and r < 1e-4, (e, r)
+
+
+def test_f16_small_weights_keep_their_mass():
+    """A long sequence whose weights are mostly far below fp16's range relative to
+    the maximum: the sum of the small weights must not be lost."""
+    import torch
+    S = 20000
+    c = host_case(1, 8, 1, 128, [S], "f16", seed=98, scale=1.0)
+    qf = np.zeros_like(c.q)
+    qf[0, :, 0] = 3.0                                   # scores = 3 * k[:, 0]
+    k = c.k.copy()
+    k[:, 0, 0] = np.float16(0.0)
+    k[7, 0, 0] = np.float16(6.0)                        # one key leads by 18 (weight ratio e^-18)
+    ref = oracle_of(type(c)(qf, k, c.v, c.seq_lens, 1.0, "f16"))
+    q_, k_, v_, sl = upload(type(c)(qf, k, c.v, c.seq_lens, 1.0, "f16"))
+    o32 = run_hip(q_, k_, v_, sl, 1.0, out_dtype=torch.float32)
+    e, r = compare(o32, ref, "f16 small weights")
+    assert e < 1e-4, e
 
 
 def test_runs_on_the_given_stream_and_is_deterministic():
