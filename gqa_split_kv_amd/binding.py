@@ -49,6 +49,7 @@ class GqaArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("sweep_events", ctypes.c_void_p * 2),
+        ("t_q", ctypes.c_int32),
     ]
 
 
@@ -184,7 +185,7 @@ def gqa_decode_f16(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_head
 
 def make_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, in_dtype, out_dtype,
               num_chunks=0, min_chunk=0, workspace=None, workspace_bytes=0, stream=0,
-              sweep_events=None) -> GqaArgs:
+              sweep_events=None, t_q=0) -> GqaArgs:
     a = GqaArgs()
     a.q, a.k, a.v, a.o, a.seq_lens = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens)
     a.batch, a.h_q, a.h_kv, a.d_head = int(batch), int(h_q), int(h_kv), int(d_head)
@@ -197,6 +198,7 @@ def make_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, in_dtype, o
     if sweep_events is not None:
         a.sweep_events[0] = int(sweep_events[0])
         a.sweep_events[1] = int(sweep_events[1])
+    a.t_q = int(t_q)
     return a
 
 
@@ -242,25 +244,28 @@ def gqa_release() -> None:
 
 def decode(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype=None,
            num_chunks: int = 0, min_chunk: int = 0, workspace=None, stream=None):
-    """o = GQA decode of q [batch, h_q, d] against packed k, v [sum(seq_lens), h_kv, d].
+    """o = GQA decode of q [batch, h_q, d] (or [batch, t_q, h_q, d] for t_q query
+    tokens per sequence) against packed k, v [sum(seq_lens), h_kv, d].
 
     seq_lens is an int32 device tensor.  out_dtype defaults to q's dtype; pass
-    torch.float32 with bf16 inputs for the fp32 result.  Returns `out`.
+    torch.float32 with 16-bit inputs for the fp32 result.  Returns `out`.
     """
     import torch
-    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
-        raise ValueError("q must be [batch, h_q, d]; k, v [sum(seq_lens), h_kv, d]")
-    batch, h_q, d = q.shape
+    if q.dim() not in (3, 4) or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [batch, h_q, d] or [batch, t_q, h_q, d]; k, v [sum(seq_lens), h_kv, d]")
+    t_q = q.shape[1] if q.dim() == 4 else 0
+    batch, h_q, d = q.shape[0], q.shape[-2], q.shape[-1]
     h_kv = k.shape[1]
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
     if out is None:
-        out = torch.empty((batch, h_q, d), dtype=out_dtype or q.dtype, device=q.device)
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     ws_bytes = 0
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()
     args = make_args(q, k, v, out, seq_lens, batch, h_q, h_kv, d, scale, _dtype_code(q),
-                     _dtype_code(out), num_chunks, min_chunk, workspace, ws_bytes, _stream(stream))
+                     _dtype_code(out), num_chunks, min_chunk, workspace, ws_bytes, _stream(stream),
+                     t_q=t_q)
     gqa_decode_ex(args)
     return out
 

@@ -21,7 +21,7 @@ constexpr int kThreads = 64 * kWavesPerBlock;
 constexpr int kMergeThreadsNarrow = 256;
 constexpr int kMergeThreadsWide = 1024;
 constexpr int kWideMergePieces = 32;   // expected pieces per sequence above which the merge is wide
-constexpr int kMaxG = 16;           // query heads per kv head held by one 16-wide MFMA tile
+constexpr int kMaxG = 16;           // rows (query heads x query tokens) per kv head in one 16-wide MFMA tile
 constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxHeadsKv = 1 << 16;   // keeps 16 key rows of lane offsets within 32 bits
 constexpr int kMaxMinChunk = 1 << 30;
@@ -43,13 +43,13 @@ void clear_error();
 int validate(const gqa_decode_args *a);
 
 // Workspace layout for `num_chunks` wavefronts: two partial-triple slots per
-// wavefront, each G rows of (O[D] fp32) plus (m, l) fp32.
+// wavefront, each R = G * t_q rows of (O[D] fp32) plus (m, l) fp32.
 struct WorkspaceLayout {
     size_t o_offset;    // float  [num_chunks][2][G][D]
     size_t ml_offset;   // float2 [num_chunks][2][G]
     size_t bytes;
 };
-WorkspaceLayout workspace_layout(int64_t num_chunks, int G, int D);
+WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D);
 
 int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decode_plan *plan);
 

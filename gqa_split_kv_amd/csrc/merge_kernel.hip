@@ -1,7 +1,8 @@
 // merge_kernel.hip -- log-sum-exp merge of the partial triples a sequence left in
 // the workspace when its keys were cut across several sweep ranges.
 //
-// For query head g of (sequence b, kv head j) with pieces s = ca .. cb (range s
+// For row (query token t, query head g) of (sequence b, kv head j) with pieces
+// s = ca .. cb (range s
 // was swept by wavefront s*h_kv + j; the first piece sits in slot 1 of its
 // wavefront, the rest in slot 0):
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s O_s 2^(m_s - M) / L
@@ -11,8 +12,9 @@
 // normalise and store.  m is in log2 units (the sweep folds log2 e into the
 // scale), so the weights are exp2.
 //
-// Layout: a workgroup covers (sequence, kv head) and a group of query heads.
-// Thread (pl, h, eq) owns four consecutive elements d = 4eq .. 4eq+3 of head h
+// Layout: a workgroup covers (sequence, kv head) and a group of rows (query
+// token, query head).  Thread (pl, h, eq) owns four consecutive elements
+// d = 4eq .. 4eq+3 of row h
 // and the pieces s = ca + pl, ca + pl + PL, ...; it loads eight pieces at a time
 // and folds them into a running (M, L, acc) with the merge rule; the piece lanes
 // are then folded through LDS in ascending order, so the result is
@@ -52,8 +54,10 @@ struct Running {
 
 __device__ __forceinline__ void fold(Running &r, float m, float l, float4 o) {
     const float Mn = fmaxf(r.M, m);
-    const float a = __builtin_amdgcn_exp2f(r.M - Mn);   // 0 when r is empty
-    const float f = __builtin_amdgcn_exp2f(m - Mn);     // 0 for an empty side
+    // Both sides empty (-inf): exponentiate against 0 so the identity stays NaN-free.
+    const float Mr = Mn == -INFINITY ? 0.f : Mn;
+    const float a = __builtin_amdgcn_exp2f(r.M - Mr);   // 0 when r is empty
+    const float f = __builtin_amdgcn_exp2f(m - Mr);     // 0 for an empty side
     r.L = r.L * a + l * f;
     r.acc.x = r.acc.x * a + o.x * f;
     r.acc.y = r.acc.y * a + o.y * f;
@@ -62,29 +66,34 @@ __device__ __forceinline__ void fold(Running &r, float m, float l, float4 o) {
     r.M = Mn;
 }
 
-// Workgroup layout: kHeads query heads x PL piece lanes x QD element quads.
-template <int kOut, int D, int kThreadsM, int kHeads>
+// Workgroup layout: kRows rows x PL piece lanes x QD element quads; a row is one
+// (query token, query head) of the kv head, row = t * G + g.
+template <int kOut, int D, int kThreadsM, int kRows>
 __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
-    constexpr int QD = D / 4;                        // element quads per head
-    constexpr int PL = kThreadsM / (QD * kHeads);    // piece lanes
+    constexpr int QD = D / 4;                        // element quads per row
+    constexpr int PL = kThreadsM / (QD * kRows);     // piece lanes
     constexpr int kBatch = 8;                        // pieces in flight per thread
-    static_assert(PL >= 1 && PL * QD * kHeads == kThreadsM, "layout");
-    __shared__ Running s_run[PL > 1 ? PL : 1][kHeads][QD];
+    static_assert(PL >= 1 && PL * QD * kRows == kThreadsM, "layout");
+    __shared__ Running s_run[PL > 1 ? PL : 1][kRows][QD];
 
     const int G = P.G;
-    const int groups = (G + kHeads - 1) / kHeads;
+    const int R = P.R;
+    const int groups = (R + kRows - 1) / kRows;
     const int unit = static_cast<int>(blockIdx.x) / groups;
-    const int g0 = (static_cast<int>(blockIdx.x) - unit * groups) * kHeads;
+    const int r0 = (static_cast<int>(blockIdx.x) - unit * groups) * kRows;
     const int b = unit / P.h_kv;
     const int j = unit - b * P.h_kv;
-    const int t = static_cast<int>(threadIdx.x);
-    const int eq = t % QD;
-    const int hh = (t / QD) % kHeads;
-    const int pl = t / (QD * kHeads);
-    const int g = g0 + hh;
-    const bool active = g < G;
+    const int tid = static_cast<int>(threadIdx.x);
+    const int eq = tid % QD;
+    const int hh = (tid / QD) % kRows;
+    const int pl = tid / (QD * kRows);
+    const int g = r0 + hh;                           // row within the kv head
+    const bool active = g < R;
+    const int tq = (active ? g : R - 1) / G;
+    const int gh = (active ? g : R - 1) - tq * G;
     const int len = uniform32(seq_len_at(P.seq_lens, b));
-    uint8_t *orow = P.o + (static_cast<int64_t>(b) * P.h_q + j * G + g) * D * (kOut == kF32 ? 4 : 2);
+    uint8_t *orow = P.o + ((static_cast<int64_t>(b) * P.t_q + tq) * P.h_q + j * G + gh) * D *
+                              (kOut == kF32 ? 4 : 2);
     if (len == 0) {
         if (pl == 0 && active) store_quad<kOut>(orow, eq, make_float4(0.f, 0.f, 0.f, 0.f));
         return;
@@ -105,7 +114,7 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
             for (int i = 0; i < kBatch; ++i) {
                 const int64_t s = s0 + static_cast<int64_t>(i) * PL;
                 if (s <= cb) {
-                    const int64_t row = ((s * P.h_kv + j) * 2 + (s == ca ? 1 : 0)) * G + g;
+                    const int64_t row = ((s * P.h_kv + j) * 2 + (s == ca ? 1 : 0)) * R + g;
                     ml[i] = P.ws_ml[row];
                     ov[i] = reinterpret_cast<const float4 *>(P.ws_o + row * D)[eq];
                 } else {
@@ -116,11 +125,14 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
             float mb = ml[0].x;
 #pragma unroll
             for (int i = 1; i < kBatch; ++i) mb = fmaxf(mb, ml[i].x);
-            // One rescale per batch: fold the batch at its own maximum, then into r.
+            // One rescale per batch: fold the batch at its own maximum, then into r
+            // (an all-empty batch, e.g. a query token that sees none of these keys,
+            // is exponentiated against 0 and stays the identity).
+            const float mbr = mb == -INFINITY ? 0.f : mb;
             Running bt = {mb, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
 #pragma unroll
             for (int i = 0; i < kBatch; ++i) {
-                const float f = __builtin_amdgcn_exp2f(ml[i].x - mb);   // 0 for the padding
+                const float f = __builtin_amdgcn_exp2f(ml[i].x - mbr);   // 0 for the padding
                 bt.L += f * ml[i].y;
                 bt.acc.x += f * ov[i].x;
                 bt.acc.y += f * ov[i].y;
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
         }
     }
     if (active) {
-        const float inv = 1.0f / r.L;
+        const float inv = r.L > 0.f ? 1.0f / r.L : 0.f;   // a query token with no key gives 0
         store_quad<kOut>(orow, eq, make_float4(r.acc.x * inv, r.acc.y * inv, r.acc.z * inv, r.acc.w * inv));
     }
 }

@@ -38,13 +38,18 @@ static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-WorkspaceLayout workspace_layout(int64_t num_chunks, int G, int D) {
+WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D) {
     WorkspaceLayout L;
-    const size_t slots = static_cast<size_t>(num_chunks) * 2 * static_cast<size_t>(G);
+    const size_t slots = static_cast<size_t>(num_chunks) * 2 * static_cast<size_t>(rows);
     L.o_offset = 0;
     L.ml_offset = round_up(slots * static_cast<size_t>(D) * sizeof(float), 256);
     L.bytes = round_up(L.ml_offset + slots * 2 * sizeof(float), 256);
     return L;
+}
+
+// Rows of the MFMA N axis per kv head: G query heads x t_q query tokens.
+static int rows_per_kv_head(const gqa_decode_args *a) {
+    return (a->h_q / a->h_kv) * (a->t_q > 0 ? a->t_q : 1);
 }
 
 static int check_basic(const gqa_decode_args *a) {
@@ -63,6 +68,12 @@ static int check_basic(const gqa_decode_args *a) {
     const int G = a->h_q / a->h_kv;
     if (G > kMaxG)
         return fail(GQA_ERR_UNSUPPORTED, "G = h_q/h_kv = %d exceeds %d", G, kMaxG);
+    if (a->t_q < 0) return fail(GQA_ERR_SHAPE, "t_q %d is negative", a->t_q);
+    const int tq = a->t_q > 0 ? a->t_q : 1;
+    if (static_cast<int64_t>(G) * tq > kMaxG)
+        return fail(GQA_ERR_UNSUPPORTED, "G * t_q = %d * %d exceeds %d rows", G, tq, kMaxG);
+    if (static_cast<int64_t>(a->batch) * tq * a->h_q > 0x7fffffff)
+        return fail(GQA_ERR_SHAPE, "batch * t_q * h_q exceeds 2^31-1");
     if (a->d_head != 64 && a->d_head != 128)
         return fail(GQA_ERR_UNSUPPORTED, "d_head %d not supported (64 or 128)", a->d_head);
     const bool pair_ok = (a->in_dtype == GQA_DTYPE_BF16 && a->out_dtype == GQA_DTYPE_BF16) ||
@@ -99,7 +110,7 @@ int validate(const gqa_decode_args *a) {
     if (a->num_chunks > 0) {
         int64_t chunks = static_cast<int64_t>(a->num_chunks) / a->h_kv * a->h_kv;
         if (chunks < a->h_kv) chunks = a->h_kv;
-        const WorkspaceLayout L = workspace_layout(chunks, a->h_q / a->h_kv, a->d_head);
+        const WorkspaceLayout L = workspace_layout(chunks, rows_per_kv_head(a), a->d_head);
         st = check_workspace(a, L.bytes);
         if (st != GQA_OK) return st;
     }
@@ -122,7 +133,7 @@ int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decod
     chunks = chunks / a->h_kv * a->h_kv;
     if (chunks < a->h_kv) chunks = a->h_kv;
     if (chunks > kMaxChunks) return fail(GQA_ERR_ARG, "h_kv %d needs more than %d wavefronts", a->h_kv, kMaxChunks);
-    const WorkspaceLayout L = workspace_layout(chunks, a->h_q / a->h_kv, a->d_head);
+    const WorkspaceLayout L = workspace_layout(chunks, rows_per_kv_head(a), a->d_head);
     st = check_workspace(a, L.bytes);
     if (st != GQA_OK) return st;
     plan->num_chunks = static_cast<int32_t>(chunks);
@@ -130,11 +141,11 @@ int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decod
     plan->split_blocks = static_cast<int32_t>((chunks + kWavesPerBlock - 1) / kWavesPerBlock);
     // Expected pieces per sequence: token ranges per sequence on average.
     const int64_t ranges = chunks / a->h_kv;
-    const int G = a->h_q / a->h_kv;
+    const int R = rows_per_kv_head(a);
     const bool wide = ranges / a->batch > kWideMergePieces;
     plan->merge_threads = wide ? kMergeThreadsWide : kMergeThreadsNarrow;
-    const int heads_per_block = wide ? 1 : kMergeThreadsNarrow / (a->d_head / 4);
-    plan->merge_blocks = a->batch * a->h_kv * ((G + heads_per_block - 1) / heads_per_block);
+    const int rows_per_block = wide ? 1 : kMergeThreadsNarrow / (a->d_head / 4);
+    plan->merge_blocks = a->batch * a->h_kv * ((R + rows_per_block - 1) / rows_per_block);
     plan->workspace_bytes = L.bytes;
     return GQA_OK;
 }

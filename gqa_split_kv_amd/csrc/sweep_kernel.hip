@@ -113,11 +113,14 @@ __device__ __forceinline__ void softmax_step(float (&sv)[N], float &m_run, float
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first step
+    // A row that has seen no key yet (all masked) keeps the identity (-inf, 0, 0):
+    // exponentiate against 0 instead of -inf so that nothing becomes NaN.
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);   // 0 while the state is empty
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new + static_cast<float>(kOffset));
+        sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref + static_cast<float>(kOffset));
         sum += sv[i];
     }
     l_run = l_run * alpha + sum;
@@ -333,21 +336,25 @@ __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int 
     using S = Step<kIn, D>;
     constexpr int VEC = S::VEC;
     const int lane = lane_id();
-    const int g = lane & 15;
+    const int r = lane & 15;        // MFMA N row: query token t and head g of this kv head
     const int kg = lane >> 4;
     const int G = P.G;
+    const int R = P.R;              // rows in use: G * t_q
+    const bool row_ok = r < R;
+    const int t = (row_ok ? r : R - 1) / G;
+    const int g = (row_ok ? r : R - 1) - t * G;
+    const int64_t qo_row = (static_cast<int64_t>(b) * P.t_q + t) * P.h_q + j * G + g;   // q and o row
     const int rowstride = P.h_kv * S::ROWB;
 
-    // Q operand: query head j*G + g, bytes [64p + 16kg, +16) of its row (zero for g >= G):
+    // Q operand: query row (t, g), bytes [64p + 16kg, +16) of it (zero for unused rows):
     // the same d permutation as the K rows, so the contraction covers every d once.
     uint4 qop[S::NKP];
     {
-        const int gq = g < G ? g : G - 1;
-        const uint8_t *qrow = P.q + (static_cast<int64_t>(b) * P.h_q + j * G + gq) * S::ROWB + 16 * kg;
+        const uint8_t *qrow = P.q + qo_row * S::ROWB + 16 * kg;
 #pragma unroll
         for (int p = 0; p < S::NKP; ++p) {
             qop[p] = *reinterpret_cast<const uint4 *>(qrow + 64 * p);
-            if (g >= G) qop[p] = make_uint4(0, 0, 0, 0);
+            if (!row_ok) qop[p] = make_uint4(0, 0, 0, 0);
         }
     }
 
@@ -372,6 +379,10 @@ __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int 
     const uint8_t *vbase = P.v + row0 * S::ROWB;
     const float sl2 = P.scale_log2;
     const typename S::Lanes lo(rowstride);
+    // Causal limit of query token t among the t_q new tokens: it sees the keys at
+    // sequence positions below len - t_q + t + 1.  In step coordinates (key i of
+    // step st sits at position abase - off + kKeys*st + i) the bound is cap - kKeys*st.
+    const int cap = len - P.t_q + t + 1 - static_cast<int>(abase - off);
 
     auto load_step = [&](typename S::Buf &B, int st) {
         const int hi = min(S::kKeys, span - st * S::kKeys);
@@ -393,8 +404,9 @@ __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int 
         for (int u = 0; u < kDepth; ++u) {
             load_step(buf[(u + kDepth - 1) % kDepth], min(st + kDepth - 1, nstep - 1));
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
-            S::compute(buf[u], qop, st == 0 ? lead : 0, min(S::kKeys, span - st * S::kKeys), kg, sl2,
-                       m_run, l_run, acc);
+            S::compute(buf[u], qop, st == 0 ? lead : 0,
+                       min(min(S::kKeys, span - st * S::kKeys), cap - st * S::kKeys), kg, sl2, m_run,
+                       l_run, acc);
             if (++st == nstep) goto swept;
         }
     }
@@ -403,18 +415,18 @@ swept:
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
 
-    // The lane's outputs: O[g][d] for d in [4*VEC*kg, 4*VEC*kg + 4*VEC), index q*VEC + c.
+    // The lane's outputs: O[row][d] for d in [4*VEC*kg, 4*VEC*kg + 4*VEC), index q*VEC + c.
     float out[4 * VEC];
     if (t0 == 0 && t1 == len) {
-        // The whole sequence was in this range: normalise and store.
-        const float inv = 1.0f / l_tot;
+        // The whole sequence was in this range: normalise and store (a query token
+        // that sees no key gives 0).
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[c][q] * inv;
-        if (g < G) {
-            const int64_t orow = static_cast<int64_t>(b) * P.h_q + j * G + g;
-            uint8_t *dst = P.o + (orow * D + 4 * VEC * kg) * (kOut == kF32 ? 4 : 2);
+        if (row_ok) {
+            uint8_t *dst = P.o + (qo_row * D + 4 * VEC * kg) * (kOut == kF32 ? 4 : 2);
             store_row<kOut>(dst, out, 4 * VEC);
         }
     } else {
@@ -425,8 +437,8 @@ swept:
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[c][q];
-        if (g < G) {
-            const int64_t srow = (static_cast<int64_t>(w) * 2 + slot) * G + g;
+        if (row_ok) {
+            const int64_t srow = (static_cast<int64_t>(w) * 2 + slot) * R + r;
             store_row<kF32>(reinterpret_cast<uint8_t *>(P.ws_o + srow * D + 4 * VEC * kg), out, 4 * VEC);
             if (kg == 0) P.ws_ml[srow] = make_float2(m_run, l_tot);
         }

@@ -5,7 +5,7 @@ This module only draws and lays out input data; it holds none of the method's
 arithmetic and imports neither the HIP binding nor the oracle.
 
 Layouts (row-major, contiguous):
-  q, o      [batch, h_q, d]
+  q, o      [batch, h_q, d], or [batch, t_q, h_q, d] with t_q query tokens per sequence
   k, v      [sum(seq_lens), h_kv, d]   sequences packed back to back
   seq_lens  int32[batch]
 
@@ -120,7 +120,7 @@ def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
 
 @dataclass
 class HostCase:
-    q: np.ndarray            # uint16 bf16 bits, float16 or float32, [batch, h_q, d]
+    q: np.ndarray            # uint16 bf16 bits, float16 or float32, [batch, (t_q,) h_q, d]
     k: np.ndarray            # [sum(seq_lens), h_kv, d]
     v: np.ndarray
     seq_lens: np.ndarray     # int32[batch]
@@ -136,11 +136,13 @@ def _normal(seed: int, idx: int, n: int) -> np.ndarray:
 
 def host_case(batch: int, h_q: int, h_kv: int, d: int, seq_lens: Sequence[int], dtype: str = "bf16",
               seed: int = 0, scale: Optional[float] = None, peaked_frac: float = 0.0,
-              peak_factor: float = 8.0) -> HostCase:
-    """Draw q, k, v for the given shape on the host."""
+              peak_factor: float = 8.0, t_q: int = 0) -> HostCase:
+    """Draw q, k, v for the given shape on the host; t_q > 0 gives q t_q query
+    tokens per sequence ([batch, t_q, h_q, d])."""
     sl = np.asarray(seq_lens, dtype=np.int32).reshape(batch)
     rows = int(np.clip(sl, 0, None).sum())
-    q = _normal(seed, 0, batch * h_q * d).reshape(batch, h_q, d)
+    qshape = (batch, t_q, h_q, d) if t_q > 0 else (batch, h_q, d)
+    q = _normal(seed, 0, int(np.prod(qshape))).reshape(qshape)
     k = _normal(seed, 1, rows * h_kv * d).reshape(rows, h_kv, d)
     v = _normal(seed, 2, rows * h_kv * d).reshape(rows, h_kv, d)
     peaks: List[np.ndarray] = []
@@ -200,14 +202,15 @@ def _torch_normal(shape, seed: int, device, out_dtype, chunk_rows: int = 1 << 18
 
 def device_case(batch: int, h_q: int, h_kv: int, d: int, seq_lens: Sequence[int], dtype: str = "bf16",
                 seed: int = 0, scale: Optional[float] = None, peaked_frac: float = 0.0,
-                peak_factor: float = 8.0, device: str = "cuda") -> DeviceCase:
+                peak_factor: float = 8.0, device: str = "cuda", t_q: int = 0) -> DeviceCase:
     """Draw q, k, v directly on the device (for multi-GiB workloads)."""
     import torch
     sl = np.asarray(seq_lens, dtype=np.int32).reshape(batch)
     rows = int(np.clip(sl, 0, None).sum())
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
     base_seed = int(np.random.SeedSequence(seed).generate_state(1)[0])
-    q = _torch_normal((batch, h_q, d), base_seed + 0, device, tdt)
+    qshape = (batch, t_q, h_q, d) if t_q > 0 else (batch, h_q, d)
+    q = _torch_normal(qshape, base_seed + 0, device, tdt)
     k = _torch_normal((rows, h_kv, d), base_seed + 1, device, tdt)
     v = _torch_normal((rows, h_kv, d), base_seed + 2, device, tdt)
     if peaked_frac > 0.0:

@@ -67,8 +67,9 @@ typedef enum gqa_status {
     GQA_OK = 0,
     GQA_ERR_NULL = 1,        /* a required pointer is NULL                              */
     GQA_ERR_SHAPE = 2,       /* batch, h_q or h_kv <= 0, h_q not a multiple of h_kv,    *
-                              * or batch * h_q above 2^31-1                             */
-    GQA_ERR_UNSUPPORTED = 3, /* d_head not 64/128, G > 16, or dtype pair not supported  */
+                              * t_q < 0, or batch * t_q * h_q above 2^31-1              */
+    GQA_ERR_UNSUPPORTED = 3, /* d_head not 64/128, G * t_q > 16, or dtype pair          *
+                              * not supported                                           */
     GQA_ERR_ALIGN = 4,       /* q/k/v/o not 16-byte aligned or seq_lens not 4-byte      */
     GQA_ERR_SCALE = 5,       /* scale is not finite                                     */
     GQA_ERR_WORKSPACE = 6,   /* caller workspace too small or not 256-byte aligned      */
@@ -120,6 +121,7 @@ int gqa_decode_f16(const void *q, const void *k, const void *v, void *o,
  *             demand and freed by gqa_release(); callers that capture HIP graphs
  *             must pass their own.
  * sweep_events  See the field's comment; leave NULL outside profiling.
+ * t_q         See the field's comment; 0 for the single-token decode.
  */
 typedef struct gqa_decode_args {
     const void *q;
@@ -144,6 +146,12 @@ typedef struct gqa_decode_args {
      * (sweep) kernel and the second just after it, so its duration can be read
      * with hipEventElapsedTime without a profiler.  NULL = not recorded. */
     void *sweep_events[2];
+    /* Query tokens per sequence (multi-token decode, e.g. verifying draft tokens);
+     * 0 or 1 = one.  With t_q > 1, q and o are [batch, t_q, h_q, d_head], the last
+     * t_q key rows of every sequence belong to the new tokens, and query token t
+     * attends to the keys at positions 0 .. seq_len - t_q + t (causal among the new
+     * tokens; a token that sees no key gives 0).  G * t_q must not exceed 16. */
+    int32_t t_q;
 } gqa_decode_args;
 
 /* gqa_decode_ex -- the operation with every field of `args` (see above). */

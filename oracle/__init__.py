@@ -49,6 +49,9 @@ def _load():
     i32 = ctypes.c_int32
     lib.oracle_gqa_decode_f64.argtypes = [P, P, P, P, i32, i32, i32, i32, ctypes.c_double, i32, P]
     lib.oracle_gqa_decode_f64.restype = ctypes.c_int
+    lib.oracle_gqa_decode_tq_f64.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_double,
+                                             i32, P]
+    lib.oracle_gqa_decode_tq_f64.restype = ctypes.c_int
     lib.oracle_softmax_weights_f64.argtypes = [P, P, P, i32, i32, i32, i32, ctypes.c_double, i32,
                                                i32, i32, P]
     lib.oracle_softmax_weights_f64.restype = ctypes.c_int
@@ -91,6 +94,7 @@ def _ptr(a: np.ndarray):
 
 
 def _prep(q, k, v, seq_lens):
+    """Single-query inputs: q [batch, h_q, d]."""
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
     v = np.ascontiguousarray(v) if v is not None else None
@@ -113,7 +117,21 @@ def _prep(q, k, v, seq_lens):
 
 
 def gqa_decode_f64(q, k, v, seq_lens, scale: float) -> np.ndarray:
-    """o[b, h, :] = softmax(scale * q[b,h] K_j^T) V_j, j = h // (h_q // h_kv); float64."""
+    """o[b, h, :] = softmax(scale * q[b,h] K_j^T) V_j, j = h // (h_q // h_kv); float64.
+
+    With q of shape [batch, t_q, h_q, d] (t_q query tokens per sequence, the last
+    t_q key rows being theirs) query token t sees keys 0 .. S - t_q + t and the
+    result is [batch, t_q, h_q, d]."""
+    q = np.ascontiguousarray(q)
+    if q.ndim == 4:
+        batch, t_q, h_q, d = q.shape
+        _, k, v, sl, code, _, _, h_kv, _ = _prep(q.reshape(batch, t_q * h_q, d), k, v, seq_lens)
+        out = np.empty((batch, t_q, h_q, d), dtype=np.float64)
+        rc = _load().oracle_gqa_decode_tq_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(sl), batch, t_q, h_q,
+                                              h_kv, d, float(scale), code, _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_gqa_decode_tq_f64 failed (%d)" % rc)
+        return out
     q, k, v, sl, code, batch, h_q, h_kv, d = _prep(q, k, v, seq_lens)
     out = np.empty((batch, h_q, d), dtype=np.float64)
     rc = _load().oracle_gqa_decode_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(sl), batch, h_q, h_kv, d,

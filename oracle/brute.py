@@ -29,7 +29,11 @@ def _exact(a: np.ndarray):
 
 def brute_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, scale: float,
                  digits: int = 50):
-    """Returns a nested list [batch][h_q][d] of Decimal outputs."""
+    """Returns a nested list [batch][h_q][d] of Decimal outputs; for q of shape
+    [batch, t_q, h_q, d], [batch][t_q][h_q][d] with query token t seeing keys
+    0 .. S - t_q + t."""
+    if q.ndim == 4:
+        return _brute_tq(q, k, v, seq_lens, scale, digits)
     batch, h_q, d = q.shape
     h_kv = k.shape[1]
     G = h_q // h_kv
@@ -63,4 +67,21 @@ def brute_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, scale: f
                 ob.append(o)
             out.append(ob)
             base += S
+    return out
+
+
+def _brute_tq(q, k, v, seq_lens, scale, digits):
+    batch, t_q, h_q, d = q.shape
+    out = []
+    base = 0
+    for b in range(batch):
+        S = max(int(seq_lens[b]), 0)
+        ob = []
+        for t in range(t_q):
+            St = min(S, max(0, S - t_q + t + 1))
+            # query token t alone against the first St keys of its sequence
+            r = brute_decode(q[b:b + 1, t], k[base:base + St], v[base:base + St], [St], scale, digits)
+            ob.append(r[0])
+        out.append(ob)
+        base += S
     return out

@@ -91,13 +91,11 @@ static int64_t seq_base(const int32_t *seq_lens, int32_t b) {
     return base;
 }
 
-/* s_t for one (b, h) over keys [t0, t1) into s[0 .. t1-t0). */
-static void scores(const void *q, const void *k, int32_t h_q, int32_t h_kv, int32_t d,
-                   double scale, int dtype, int32_t b, int32_t h, int64_t base, int32_t t0,
-                   int32_t t1, double *s) {
-    const int32_t G = h_q / h_kv;
-    const int32_t j = h / G;
-    const int64_t qrow = ((int64_t)b * h_q + h) * d;
+/* s_t for query row qrow (element offset into q) against kv head j over keys
+ * [t0, t1) of the sequence starting at row `base`, into s[0 .. t1-t0). */
+static void scores_row(const void *q, const void *k, int64_t qrow, int32_t j, int32_t h_kv,
+                       int32_t d, double scale, int dtype, int64_t base, int32_t t0, int32_t t1,
+                       double *s) {
     for (int32_t t = t0; t < t1; ++t) {
         const int64_t krow = ((base + t) * h_kv + j) * (int64_t)d;
         double dot = 0.0;
@@ -106,13 +104,25 @@ static void scores(const void *q, const void *k, int32_t h_q, int32_t h_kv, int3
     }
 }
 
+/* s_t for one (b, h) of a single-query decode (q is [batch, h_q, d]). */
+static void scores(const void *q, const void *k, int32_t h_q, int32_t h_kv, int32_t d,
+                   double scale, int dtype, int32_t b, int32_t h, int64_t base, int32_t t0,
+                   int32_t t1, double *s) {
+    const int32_t G = h_q / h_kv;
+    scores_row(q, k, ((int64_t)b * h_q + h) * d, h / G, h_kv, d, scale, dtype, base, t0, t1, s);
+}
+
 /*
- * Full decode: out is double[batch, h_q, d].  Returns 0, or -1 on bad shape.
+ * Full decode with t_q query tokens per sequence: q and out are
+ * [batch, t_q, h_q, d]; the last t_q key rows of a sequence of S keys belong to
+ * the new tokens, and query token t sees keys 0 .. S - t_q + t (causal among the
+ * new tokens): S_t = min(S, max(0, S - t_q + t + 1)) keys.  S_t = 0 gives 0.
+ * t_q = 1 is the single-token decode of the page.  Returns 0, or -1 on bad shape.
  */
-int oracle_gqa_decode_f64(const void *q, const void *k, const void *v, const int32_t *seq_lens,
-                          int32_t batch, int32_t h_q, int32_t h_kv, int32_t d, double scale,
-                          int32_t dtype, double *out) {
-    if (batch < 0 || h_q <= 0 || h_kv <= 0 || d <= 0 || h_q % h_kv != 0) return -1;
+int oracle_gqa_decode_tq_f64(const void *q, const void *k, const void *v, const int32_t *seq_lens,
+                             int32_t batch, int32_t t_q, int32_t h_q, int32_t h_kv, int32_t d,
+                             double scale, int32_t dtype, double *out) {
+    if (batch < 0 || t_q <= 0 || h_q <= 0 || h_kv <= 0 || d <= 0 || h_q % h_kv != 0) return -1;
     const int32_t G = h_q / h_kv;
     int64_t *bases = (int64_t *)malloc(sizeof(int64_t) * (size_t)(batch > 0 ? batch : 1));
     int32_t max_len = 0;
@@ -133,28 +143,34 @@ int oracle_gqa_decode_f64(const void *q, const void *k, const void *v, const int
             const int32_t b = (int32_t)(u / h_kv);
             const int32_t j = (int32_t)(u % h_kv);
             const int32_t S = clamp_len(seq_lens[b]);
-            for (int32_t g = 0; g < G; ++g) {
-                const int32_t h = j * G + g;
-                double *o = out + ((int64_t)b * h_q + h) * d;
-                if (S == 0) {
-                    for (int32_t i = 0; i < d; ++i) o[i] = 0.0;
-                    continue;
+            for (int32_t t = 0; t < t_q; ++t) {
+                int32_t St = S - t_q + t + 1;
+                if (St < 0) St = 0;
+                if (St > S) St = S;
+                for (int32_t g = 0; g < G; ++g) {
+                    const int32_t h = j * G + g;
+                    const int64_t row = ((int64_t)b * t_q + t) * h_q + h;
+                    double *o = out + row * d;
+                    if (St == 0) {
+                        for (int32_t i = 0; i < d; ++i) o[i] = 0.0;
+                        continue;
+                    }
+                    /* pass 1: scores and their maximum */
+                    scores_row(q, k, row * d, j, h_kv, d, scale, dtype, bases[b], 0, St, s);
+                    double m = -INFINITY;
+                    for (int32_t x = 0; x < St; ++x)
+                        if (s[x] > m) m = s[x];
+                    /* pass 2: weights, their sum, and the weighted sum of V rows */
+                    double l = 0.0;
+                    for (int32_t i = 0; i < d; ++i) acc[i] = 0.0;
+                    for (int32_t x = 0; x < St; ++x) {
+                        const double w = exp(s[x] - m);
+                        l += w;
+                        const int64_t vrow = ((bases[b] + x) * h_kv + j) * (int64_t)d;
+                        for (int32_t i = 0; i < d; ++i) acc[i] += w * widen(v, vrow + i, dtype);
+                    }
+                    for (int32_t i = 0; i < d; ++i) o[i] = acc[i] / l;
                 }
-                /* pass 1: scores and their maximum */
-                scores(q, k, h_q, h_kv, d, scale, dtype, b, h, bases[b], 0, S, s);
-                double m = -INFINITY;
-                for (int32_t t = 0; t < S; ++t)
-                    if (s[t] > m) m = s[t];
-                /* pass 2: weights, their sum, and the weighted sum of V rows */
-                double l = 0.0;
-                for (int32_t i = 0; i < d; ++i) acc[i] = 0.0;
-                for (int32_t t = 0; t < S; ++t) {
-                    const double w = exp(s[t] - m);
-                    l += w;
-                    const int64_t vrow = ((bases[b] + t) * h_kv + j) * (int64_t)d;
-                    for (int32_t i = 0; i < d; ++i) acc[i] += w * widen(v, vrow + i, dtype);
-                }
-                for (int32_t i = 0; i < d; ++i) o[i] = acc[i] / l;
             }
         }
         free(s);
@@ -162,6 +178,13 @@ int oracle_gqa_decode_f64(const void *q, const void *k, const void *v, const int
     }
     free(bases);
     return failed ? -2 : 0;
+}
+
+/* Single-token decode: out is double[batch, h_q, d]. */
+int oracle_gqa_decode_f64(const void *q, const void *k, const void *v, const int32_t *seq_lens,
+                          int32_t batch, int32_t h_q, int32_t h_kv, int32_t d, double scale,
+                          int32_t dtype, double *out) {
+    return oracle_gqa_decode_tq_f64(q, k, v, seq_lens, batch, 1, h_q, h_kv, d, scale, dtype, out);
 }
 
 /*

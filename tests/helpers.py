@@ -64,8 +64,7 @@ def run_hip(q, k, v, seq_lens, scale, out_dtype=None, num_chunks=0, min_chunk=0,
             workspace=None, stream=None):
     """Device tensors in; the decode output tensor (synchronised) out."""
     import torch
-    batch, h_q, d = q.shape
-    out = torch.empty((batch, h_q, d), dtype=out_dtype or q.dtype, device=q.device)
+    out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if poison:
         out.fill_(float("nan"))
     B.decode(q, k, v, seq_lens, scale=scale, out=out, num_chunks=num_chunks, min_chunk=min_chunk,

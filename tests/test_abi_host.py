@@ -90,6 +90,17 @@ def test_unsupported(lib, kw):
     assert _validate(**kw) == B.GQA_ERR_UNSUPPORTED
 
 
+def test_multi_token_limits(lib):
+    assert _validate(t_q=2, h_q=64, h_kv=8) == B.GQA_OK          # G 8 x 2 tokens = 16 rows
+    assert _validate(t_q=3, h_q=64, h_kv=8) == B.GQA_ERR_UNSUPPORTED
+    assert _validate(t_q=16, h_q=8, h_kv=8) == B.GQA_OK
+    assert _validate(t_q=-1) == B.GQA_ERR_SHAPE
+    st, p1 = B.gqa_decode_make_plan(_args(num_chunks=64), 256, 4)
+    st2, p4 = B.gqa_decode_make_plan(_args(num_chunks=64, t_q=4), 256, 4)
+    assert st == st2 == B.GQA_OK
+    assert p4.workspace_bytes >= 4 * p1.workspace_bytes - 256
+
+
 @pytest.mark.parametrize("field", ["q", "k", "v", "o"])
 def test_alignment_16_bytes(lib, field):
     assert _validate(**{field: 0x10008}) == B.GQA_ERR_ALIGN
@@ -171,5 +182,5 @@ def test_error_message_is_cleared_on_success(lib):
 
 def test_struct_mirrors_match_header_sizes(lib):
     # gqa_decode_args: 5 pointers, 6 int32 + float, 2 more int32, pointer, size_t, pointer
-    assert ctypes.sizeof(B.GqaArgs) == 5 * 8 + 4 * 4 + 4 + 4 * 4 + 4 + 8 + 8 + 8 + 2 * 8
+    assert ctypes.sizeof(B.GqaArgs) == 5 * 8 + 4 * 4 + 4 + 4 * 4 + 4 + 8 + 8 + 8 + 2 * 8 + 8
     assert ctypes.sizeof(B.GqaPlan) == 5 * 4 + 4 + 8

@@ -15,6 +15,11 @@ then the final normalise-and-store block).  These tests hold it to:
     its (m, l, O) triple and merged with the page's `_merge_running` rule in the
     page's two merge orders (1-D chain and centre-root mesh), gives the direct
     result.
+Multi-token decode (t_q query tokens per sequence, the last t_q key rows being
+theirs; token t sees keys 0 .. S - t_q + t) is pinned the same way: brute force
+per token, torch's float64 SDPA with the matching boolean mask, t_q = 1 equal to
+the single-token call, and the last token equal to a single-token decode over
+all S keys.
 A final test plants plausible mistakes in copies of the definition and checks
 that the pins used here catch every one of them.
 """
@@ -121,6 +126,83 @@ def test_gqa_equals_mha_with_repeated_kv_heads(G, h_kv, d, dtype):
     got = oracle.gqa_decode_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
     ref = _sdpa_reference(c, G)
     assert np.abs(got - ref).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- multi-token decode
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("t_q", [2, 3])
+@pytest.mark.parametrize("seq_lens", [[0], [1], [2, 5], [3, 0, 9]])
+def test_multi_token_oracle_matches_decimal_brute_force(dtype, t_q, seq_lens):
+    c = host_case(len(seq_lens), 4, 2, 8, seq_lens, dtype, seed=70 + t_q, scale=0.41, t_q=t_q)
+    got = oracle.gqa_decode_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    ref = np.array(brute_decode(c.q, c.k, c.v, c.seq_lens, c.scale), dtype=np.float64)
+    assert got.shape == ref.shape == c.q.shape
+    assert np.abs(got - ref).max() <= 1e-13 * max(1.0, np.abs(ref).max())
+
+
+def _sdpa_masked_reference(c, G):
+    """torch float64 SDPA, kv heads repeated G times, boolean mask keeping key s
+    for query token t iff s <= S - t_q + t.  Tokens whose mask is empty (S < t_q)
+    are set to NaN here: SDPA's value for an all-masked row differs between torch
+    versions, and the definition's value for them (0) is checked separately."""
+    import torch
+    batch, t_q, h_q, d = c.q.shape
+    q = torch.from_numpy(_f64(c.q))
+    k = torch.from_numpy(_f64(c.k))
+    v = torch.from_numpy(_f64(c.v))
+    out = np.full((batch, t_q, h_q, d), np.nan)
+    base = 0
+    for b, S in enumerate(c.seq_lens):
+        S = int(S)
+        if S > 0:
+            kb = k[base:base + S].permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+            vb = v[base:base + S].permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+            qb = q[b].permute(1, 0, 2).contiguous()                            # [h_q, t_q, d]
+            t = torch.arange(t_q).unsqueeze(1)
+            s = torch.arange(S).unsqueeze(0)
+            mask = s <= S - t_q + t                                            # [t_q, S]
+            o = torch.nn.functional.scaled_dot_product_attention(
+                qb.unsqueeze(0), kb.unsqueeze(0), vb.unsqueeze(0), attn_mask=mask, scale=c.scale)
+            out[b] = o[0].permute(1, 0, 2).numpy()
+            for tt in range(t_q):
+                if S - t_q + tt < 0:
+                    out[b, tt] = np.nan
+        base += S
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("G,h_kv,d,t_q", [(8, 1, 64, 2), (4, 2, 32, 4), (1, 4, 16, 16), (2, 8, 128, 8)])
+def test_multi_token_equals_masked_sdpa(G, h_kv, d, t_q, dtype):
+    c = host_case(3, G * h_kv, h_kv, d, [37, 3, 130], dtype, seed=200 + t_q, scale=d ** -0.5,
+                  t_q=t_q)
+    got = oracle.gqa_decode_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    ref = _sdpa_masked_reference(c, G)
+    seen = ~np.isnan(ref)
+    assert np.abs(got[seen] - ref[seen]).max() <= 1e-12
+    # a token that sees no key (S < t_q) gives 0
+    assert (got[~seen] == 0).all()
+    assert (~seen).any() == (t_q > 3)
+
+
+def test_multi_token_with_one_token_is_the_single_token_decode():
+    c = host_case(3, 8, 2, 32, [17, 0, 64], "bf16", seed=5, t_q=1)
+    one = oracle.gqa_decode_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    flat = oracle.gqa_decode_f64(c.q[:, 0], c.k, c.v, c.seq_lens, c.scale)
+    assert one.shape == (3, 1, 8, 32)
+    assert np.array_equal(one[:, 0], flat)
+
+
+def test_last_token_sees_every_key_and_earlier_tokens_see_a_prefix():
+    c = host_case(2, 8, 2, 32, [40, 7], "f32", seed=6, t_q=4)
+    got = oracle.gqa_decode_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    last = oracle.gqa_decode_f64(np.ascontiguousarray(c.q[:, 3]), c.k, c.v, c.seq_lens, c.scale)
+    assert np.array_equal(got[:, 3], last)
+    # token 1 of sequence 0 equals a single-token decode over its first 40 - 4 + 2 keys
+    sub = oracle.gqa_decode_f64(np.ascontiguousarray(c.q[:1, 1]), c.k[:38], c.v[:38], [38], c.scale)
+    assert np.array_equal(got[0, 1], sub[0])
 
 
 # ---------------------------------------------------------------- closed forms
@@ -333,6 +415,49 @@ def test_pins_catch_planted_mistakes():
     for mut in ("head_modulo", "reshape_k", "no_scale", "sign", "drop_last_key",
                 "normalise_by_count"):
         assert not _pins(lambda *a, m=mut: _definition(*a, mutate=m)), mut
+
+
+def _definition_tq(q, k, v, seq_lens, scale, mutate=None):
+    """Multi-token definition built on _definition, with planted mistakes (test only)."""
+    batch, t_q = q.shape[:2]
+    out = np.zeros(q.shape)
+    base = 0
+    for b in range(batch):
+        S = int(seq_lens[b])
+        for t in range(t_q):
+            if mutate == "mask_off_by_one":
+                St = max(0, min(S, S - t_q + t))
+            elif mutate == "mask_reversed":
+                St = max(0, min(S, S - t)) if S >= t_q else max(0, min(S, S - t_q + t + 1))
+            elif mutate == "no_mask":
+                St = S
+            else:
+                St = max(0, min(S, S - t_q + t + 1))
+            qt = q[b:b + 1, t]
+            if mutate == "token_swap":
+                qt = q[b:b + 1, t_q - 1 - t]
+            out[b, t] = _definition(qt, k[base:base + St], v[base:base + St], [St], scale)[0]
+        base += S
+    return out
+
+
+def _pins_tq(fn):
+    c = host_case(2, 4, 2, 8, [6, 2], "f32", seed=41, scale=0.6, t_q=3)
+    ok = np.abs(fn(c.q, c.k, c.v, c.seq_lens, c.scale)
+                - np.array(brute_decode(c.q, c.k, c.v, c.seq_lens, c.scale), float)).max() < 1e-12
+    c2 = host_case(3, 8, 2, 16, [37, 3, 130], "bf16", seed=42, scale=0.25, t_q=4)
+    ref = _sdpa_masked_reference(c2, 4)
+    got = fn(c2.q, c2.k, c2.v, c2.seq_lens, c2.scale)
+    seen = ~np.isnan(ref)
+    ok &= np.abs(got[seen] - ref[seen]).max() < 1e-12 and (got[~seen] == 0).all()
+    return bool(ok)
+
+
+def test_multi_token_pins_catch_planted_mistakes():
+    assert _pins_tq(_definition_tq)
+    assert _pins_tq(lambda *a: oracle.gqa_decode_f64(*a))
+    for mut in ("mask_off_by_one", "mask_reversed", "no_mask", "token_swap"):
+        assert not _pins_tq(lambda *a, m=mut: _definition_tq(*a, mutate=m)), mut
 
 
 def test_bf16_rounding_helper_is_round_to_nearest_even():

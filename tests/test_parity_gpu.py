@@ -143,6 +143,69 @@ def test_forced_chunking_ragged_batch(nc, mc):
     compare(o16, ref, "bf16 nc=%d mc=%d" % (nc, mc))
 
 
+# ------------------------------------------------------------------ multi-token decode
+
+
+@pytest.mark.parametrize("G,h_kv,t_q", [(8, 1, 2), (4, 2, 4), (1, 4, 16), (2, 8, 8), (3, 1, 5),
+                                        (16, 1, 1), (5, 2, 3)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"),
+                                       ("f16", "f16")])
+def test_multi_token_heads_dims_dtypes(G, h_kv, t_q, d, dtype, out):
+    import torch
+    lens = [37, 0, 300, 2, 1, 16, 129]
+    c = host_case(len(lens), G * h_kv, h_kv, d, lens, dtype, seed=G * 31 + t_q * 7 + d, t_q=t_q)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    odt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out]
+    for nc, mc in [(0, 0), (5, 1), (64, 16), (1000, 1)]:
+        _say("t_q", t_q, "G", G, "h_kv", h_kv, "d", d, dtype, "->", out, "nc", nc, "mc", mc)
+        o = run_hip(q, k, v, sl, c.scale, out_dtype=odt, num_chunks=nc, min_chunk=mc)
+        assert o.shape == (len(lens), t_q, G * h_kv, d)
+        compare(o, ref, "t_q=%d G=%d h_kv=%d d=%d %s->%s nc=%d mc=%d" % (t_q, G, h_kv, d, dtype, out,
+                                                                         nc, mc))
+
+
+@pytest.mark.parametrize("nc,mc", [(0, 0), (1, 1), (3, 7), (64, 1), (4096, 1), (7, 1024)])
+def test_multi_token_ragged_70b_heads(nc, mc):
+    import torch
+    lens = [513, 1, 2000, 0, 77, 1024, 3, 3333]
+    c = host_case(len(lens), 64, 8, 128, lens, "bf16", seed=56, t_q=2)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    _say("t_q 2 ragged, nc", nc, "mc", mc)
+    o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=mc)
+    compare(o, ref, "t_q=2 nc=%d mc=%d" % (nc, mc))
+    o16 = run_hip(q, k, v, sl, c.scale, num_chunks=nc, min_chunk=mc)
+    compare(o16, ref, "t_q=2 bf16 nc=%d mc=%d" % (nc, mc))
+
+
+def test_multi_token_short_sequences_give_zero_for_unseen_tokens():
+    import torch
+    lens = [0, 1, 2, 3, 4, 5]
+    t_q = 4
+    c = host_case(len(lens), 8, 2, 128, lens, "bf16", seed=9, t_q=t_q)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    for nc, mc in [(0, 0), (2, 1), (12, 1)]:
+        o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=mc)
+        compare(o, ref, "short t_q=4 nc=%d" % nc)
+        for b, L in enumerate(lens):
+            for t in range(t_q):
+                if L - t_q + t < 0:
+                    assert (o[b, t] == 0).all().item(), (b, t)
+
+
+def test_multi_token_one_token_matches_single_token_call():
+    import torch
+    lens = [700, 33, 0, 4096]
+    c = host_case(len(lens), 32, 8, 128, lens, "bf16", seed=11, t_q=1)
+    q, k, v, sl = upload(c)
+    o4 = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32)
+    o3 = run_hip(q[:, 0].contiguous(), k, v, sl, c.scale, out_dtype=torch.float32)
+    assert torch.equal(o4[:, 0], o3)
+
+
 def test_peaked_keys_exercise_running_max():
     import torch
     lens = [4096, 8192]
