@@ -144,9 +144,10 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="workload number 1..5 (default 4)")
     ap.add_argument("--num-chunks", type=int, default=0)
     ap.add_argument("--min-chunk", type=int, default=0)
-    ap.add_argument("--rotate", type=int, default=1,
+    ap.add_argument("--rotate", type=int, default=0,
                     help="independent copies of q/k/v cycled through (defeats the 256 MiB "
-                         "last-level cache on small workloads)")
+                         "last-level cache on small workloads); 0 = enough copies for 1 GiB "
+                         "of K+V, at most 64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -168,6 +169,9 @@ def main():
     torch.cuda.set_device(0)
     hip = Hip()
     log("generating workload %d (%s)" % (w.cfg, w.name))
+    kv_bytes = w.kv_bytes()
+    if args.rotate <= 0:
+        args.rotate = 1 if kv_bytes >= (1 << 30) else min(64, -(-(1 << 30) // max(kv_bytes, 1)))
     sets = [device_workload(w) if r == 0 else None for r in range(args.rotate)]
     d = sets[0]
     for r in range(1, args.rotate):
@@ -185,23 +189,29 @@ def main():
     ev_steps = [(hip.event(), hip.event()) for _ in range(args.steps)]
     ev_all = (hip.event(), hip.event())
 
-    def step(i, events=None):
+    def step_args(i, events=None):
         s = sets[i % args.rotate]
-        a = gqa.make_args(s.q, s.k, s.v, out, s.seq_lens, w.batch, w.h_q, w.h_kv, w.d, s.scale,
-                          dt_code, dt_code, args.num_chunks, args.min_chunk, ws, ws_bytes, stream,
-                          sweep_events=events)
-        gqa.gqa_decode_ex(a)
+        return gqa.make_args(s.q, s.k, s.v, out, s.seq_lens, w.batch, w.h_q, w.h_kv, w.d, s.scale,
+                             dt_code, dt_code, args.num_chunks, args.min_chunk, ws, ws_bytes, stream,
+                             sweep_events=events)
 
+    # Argument blocks are built before the timed region, so the loop issues only
+    # the library calls (at a few microseconds per step the Python that fills a
+    # block would otherwise be what is measured).
+    warm_args = [step_args(i) for i in range(args.rotate)]
+    timed_args = [step_args(i, ev_steps[i]) for i in range(args.steps)]
     log("warmup %d steps" % args.warmup)
     for i in range(args.warmup):
-        step(i)
+        gqa.gqa_decode_ex(warm_args[i % args.rotate])
     torch.cuda.synchronize()
     log("timing %d steps" % args.steps)
+    decode_ex = gqa.gqa_decode_ex
     t0 = time.perf_counter()
     hip.record(ev_all[0], stream)
-    for i in range(args.steps):
-        step(i, ev_steps[i])
+    for a in timed_args:
+        decode_ex(a)
     hip.record(ev_all[1], stream)
+    submit = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     hip.sync(ev_all[1])
@@ -222,6 +232,7 @@ def main():
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_peak_hbm": round(100.0 * value / HBM_PEAK_GBS, 2),
         "wall_s_timed_region": round(wall, 4),
+        "host_us_per_call": round(submit / args.steps * 1e6, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -58,7 +58,8 @@ class GqaPlan(ctypes.Structure):
     _fields_ = [
         ("num_chunks", ctypes.c_int32), ("min_chunk", ctypes.c_int32),
         ("split_blocks", ctypes.c_int32), ("merge_blocks", ctypes.c_int32),
-        ("merge_threads", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+        ("merge_threads", ctypes.c_int32), ("merge_slices", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
     ]
 
 

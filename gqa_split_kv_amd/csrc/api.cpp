@@ -129,7 +129,8 @@ int decode_ex(const gqa_decode_args *a) {
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "sweep kernel launch failed: %s", hipGetErrorString(e));
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess)
         return gqa::fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
-    e = gqa::launch_merge(P, a->out_dtype, a->d_head, plan.merge_blocks, plan.merge_threads, stream);
+    e = gqa::launch_merge(P, a->out_dtype, a->d_head, plan.merge_blocks, plan.merge_threads,
+                          plan.merge_slices, stream);
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
     return GQA_OK;
 }

@@ -16,11 +16,17 @@ namespace gqa {
 // Wavefronts per workgroup of the sweep kernel.
 constexpr int kWavesPerBlock = GQA_SWEEP_WAVES;
 constexpr int kThreads = 64 * kWavesPerBlock;
-// Merge kernel workgroup sizes: narrow (8 piece lanes at d_head 128) when a
-// sequence is expected to be cut into few pieces, wide (32 lanes) when into many.
+// Merge kernel layouts.  Narrow: 256 threads over whole rows with one piece lane
+// (8 rows at d_head 128), for sequences cut into few pieces.  Wide: 1024 threads,
+// one row, 1024 / (d_head / 4) piece lanes, for sequences cut into many.  Split:
+// 1024 threads, one row, a slice of kMergeSliceQuads * 4 elements of d, 128 piece
+// lanes, when the wide layout would launch fewer than kSplitMergeBelowBlocks
+// workgroups (a few long sequences: most of the GPU would sit idle).
 constexpr int kMergeThreadsNarrow = 256;
 constexpr int kMergeThreadsWide = 1024;
+constexpr int kMergeSliceQuads = 8;
 constexpr int kWideMergePieces = 32;   // expected pieces per sequence above which the merge is wide
+constexpr int kSplitMergeBelowBlocks = 256;
 constexpr int kMaxG = 16;           // rows (query heads x query tokens) per kv head in one 16-wide MFMA tile
 constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxHeadsKv = 1 << 16;   // keeps 16 key rows of lane offsets within 32 bits

@@ -33,9 +33,10 @@ hipError_t launch_sweep(const DecodeParams &P, int in_dtype, int out_dtype, int 
 // Resident workgroups of the sweep kernel per compute unit.
 hipError_t sweep_occupancy(int in_dtype, int out_dtype, int D, int *blocks_per_cu);
 
-// Enqueues the merge kernel: `blocks` = batch * h_kv * G workgroups of `threads`
-// (kMergeThreadsNarrow or kMergeThreadsWide).
-hipError_t launch_merge(const DecodeParams &P, int out_dtype, int D, int blocks, int threads,
+// Enqueues the merge kernel: `blocks` workgroups of `threads` (kMergeThreadsNarrow
+// or kMergeThreadsWide), each row's d cut into `slices` slices (1, or d / 32 for
+// the split layout), as the plan sets them.
+hipError_t launch_merge(const DecodeParams &P, int out_dtype, int D, int blocks, int threads, int slices,
                         hipStream_t stream);
 
 }  // namespace gqa

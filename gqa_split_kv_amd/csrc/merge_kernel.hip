@@ -12,16 +12,18 @@
 // normalise and store.  m is in log2 units (the sweep folds log2 e into the
 // scale), so the weights are exp2.
 //
-// Layout: a workgroup covers (sequence, kv head) and a group of rows (query
-// token, query head).  Thread (pl, h, eq) owns four consecutive elements
-// d = 4eq .. 4eq+3 of row h
-// and the pieces s = ca + pl, ca + pl + PL, ...; it loads eight pieces at a time
-// and folds them into a running (M, L, acc) with the merge rule; the piece lanes
-// are then folded through LDS in ascending order, so the result is
-// deterministic.  The narrow layout (one piece lane, up to 8 heads per
-// workgroup at d 128) serves sequences cut into few pieces; the wide one (one
-// head, 32 piece lanes at d 128) serves a long sequence cut into many.  Also
-// writes zeros for an empty sequence.
+// Layout: a workgroup covers (sequence, kv head), a group of rows (query token,
+// query head) and a slice of d.  Thread (pl, h, eq) owns four consecutive
+// elements d = 4eq .. 4eq+3 of row h and the pieces s = ca + pl, ca + pl + PL,
+// ...; it loads eight pieces at a time and folds them into a running (M, L, acc)
+// with the merge rule; the piece lanes are then folded in a fixed tree (lanes of
+// a wavefront by shuffles, then the wavefronts through LDS in ascending order),
+// so the result is deterministic.  Three layouts: narrow (one piece lane, up to
+// 8 rows of all of d per workgroup at d 128) for sequences cut into few pieces;
+// wide (one row, all of d, 32 piece lanes at d 128) for long sequences cut into
+// many; split (one row, 32 elements of d, 128 piece lanes) for a few units cut
+// into very many pieces, where the wide layout would leave most of the GPU idle.
+// Also writes zeros for an empty sequence.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -66,27 +68,44 @@ __device__ __forceinline__ void fold(Running &r, float m, float l, float4 o) {
     r.M = Mn;
 }
 
-// Workgroup layout: kRows rows x PL piece lanes x QD element quads; a row is one
+__device__ __forceinline__ Running shfl_xor_running(const Running &r, int mask) {
+    Running o;
+    o.M = __shfl_xor(r.M, mask);
+    o.L = __shfl_xor(r.L, mask);
+    o.acc.x = __shfl_xor(r.acc.x, mask);
+    o.acc.y = __shfl_xor(r.acc.y, mask);
+    o.acc.z = __shfl_xor(r.acc.z, mask);
+    o.acc.w = __shfl_xor(r.acc.w, mask);
+    return o;
+}
+
+// Workgroup layout: kRows rows x PL piece lanes x kQuads element quads (one d
+// slice of 4 kQuads elements; D / (4 kQuads) slices per row); a row is one
 // (query token, query head) of the kv head, row = t * G + g.
-template <int kOut, int D, int kThreadsM, int kRows>
+template <int kOut, int D, int kThreadsM, int kRows, int kQuads>
 __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
-    constexpr int QD = D / 4;                        // element quads per row
-    constexpr int PL = kThreadsM / (QD * kRows);     // piece lanes
+    constexpr int TP = kQuads * kRows;               // threads per piece lane
+    constexpr int PL = kThreadsM / TP;               // piece lanes
+    constexpr int kSlices = D / (4 * kQuads);
     constexpr int kBatch = 8;                        // pieces in flight per thread
-    static_assert(PL >= 1 && PL * QD * kRows == kThreadsM, "layout");
-    __shared__ Running s_run[PL > 1 ? PL : 1][kRows][QD];
+    constexpr int kWaves = kThreadsM / kWave;
+    static_assert(PL >= 1 && PL * TP == kThreadsM && kSlices * 4 * kQuads == D, "layout");
+    static_assert(PL == 1 || TP <= kWave, "piece lanes are folded within and across wavefronts");
+    __shared__ Running s_run[PL > 1 ? kWaves : 1][PL > 1 ? TP : 1];
 
     const int G = P.G;
     const int R = P.R;
     const int groups = (R + kRows - 1) / kRows;
-    const int unit = static_cast<int>(blockIdx.x) / groups;
-    const int r0 = (static_cast<int>(blockIdx.x) - unit * groups) * kRows;
+    const int blk = static_cast<int>(blockIdx.x) / kSlices;
+    const int slice = static_cast<int>(blockIdx.x) - blk * kSlices;
+    const int unit = blk / groups;
+    const int r0 = (blk - unit * groups) * kRows;
     const int b = unit / P.h_kv;
     const int j = unit - b * P.h_kv;
     const int tid = static_cast<int>(threadIdx.x);
-    const int eq = tid % QD;
-    const int hh = (tid / QD) % kRows;
-    const int pl = tid / (QD * kRows);
+    const int eq = slice * kQuads + tid % kQuads;    // element quad within the row
+    const int hh = (tid / kQuads) % kRows;
+    const int pl = tid / TP;
     const int g = r0 + hh;                           // row within the kv head
     const bool active = g < R;
     const int tq = (active ? g : R - 1) / G;
@@ -143,12 +162,20 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
         }
     }
     if constexpr (PL > 1) {
-        s_run[pl][hh][eq] = r;
-        __syncthreads();
-        if (pl != 0) return;
+        // Piece lanes of one wavefront sit TP lanes apart: fold them pairwise.
 #pragma unroll
-        for (int i = 1; i < PL; ++i) {
-            const Running x = s_run[i][hh][eq];
+        for (int mask = TP; mask < kWave; mask <<= 1) {
+            const Running x = shfl_xor_running(r, mask);
+            fold(r, x.M, x.L, x.acc);
+        }
+        const int wv = tid / kWave;
+        const int ln = tid % kWave;
+        if (ln < TP) s_run[wv][ln] = r;
+        __syncthreads();
+        if (wv != 0 || ln >= TP) return;
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) {
+            const Running x = s_run[i][ln];
             fold(r, x.M, x.L, x.acc);
         }
     }
@@ -158,31 +185,36 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
     }
 }
 
+template <int kOut, int D>
+void launch_d(const DecodeParams &P, int blocks, int threads, int slices, hipStream_t stream) {
+    constexpr int QD = D / 4;
+    if (slices > 1)          // split: one row, kMergeSliceQuads quads, 1024 threads
+        hipLaunchKernelGGL((merge_kernel<kOut, D, kMergeThreadsWide, 1, kMergeSliceQuads>), dim3(blocks),
+                           dim3(kMergeThreadsWide), 0, stream, P);
+    else if (threads == kMergeThreadsWide)   // wide: one row, all of d
+        hipLaunchKernelGGL((merge_kernel<kOut, D, kMergeThreadsWide, 1, QD>), dim3(blocks),
+                           dim3(kMergeThreadsWide), 0, stream, P);
+    else                     // narrow: kMergeThreadsNarrow / QD rows, one piece lane
+        hipLaunchKernelGGL((merge_kernel<kOut, D, kMergeThreadsNarrow, kMergeThreadsNarrow / QD, QD>),
+                           dim3(blocks), dim3(kMergeThreadsNarrow), 0, stream, P);
+}
+
 template <int kOut>
-hipError_t launch_out(const DecodeParams &P, int D, int blocks, int threads, hipStream_t stream) {
-    // Narrow: 256 threads covering 256/(D/4) heads with one piece lane each
-    // (few pieces per sequence).  Wide: 1024 threads, one head, 1024/(D/4) piece lanes.
-    if (threads == kMergeThreadsWide) {
-        if (D == 128)
-            hipLaunchKernelGGL((merge_kernel<kOut, 128, kMergeThreadsWide, 1>), dim3(blocks), dim3(kMergeThreadsWide), 0, stream, P);
-        else
-            hipLaunchKernelGGL((merge_kernel<kOut, 64, kMergeThreadsWide, 1>), dim3(blocks), dim3(kMergeThreadsWide), 0, stream, P);
-    } else {
-        if (D == 128)
-            hipLaunchKernelGGL((merge_kernel<kOut, 128, kMergeThreadsNarrow, 8>), dim3(blocks), dim3(kMergeThreadsNarrow), 0, stream, P);
-        else
-            hipLaunchKernelGGL((merge_kernel<kOut, 64, kMergeThreadsNarrow, 16>), dim3(blocks), dim3(kMergeThreadsNarrow), 0, stream, P);
-    }
+hipError_t launch_out(const DecodeParams &P, int D, int blocks, int threads, int slices, hipStream_t stream) {
+    if (D == 128)
+        launch_d<kOut, 128>(P, blocks, threads, slices, stream);
+    else
+        launch_d<kOut, 64>(P, blocks, threads, slices, stream);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_merge(const DecodeParams &P, int out_dtype, int D, int blocks, int threads,
+hipError_t launch_merge(const DecodeParams &P, int out_dtype, int D, int blocks, int threads, int slices,
                         hipStream_t stream) {
-    if (out_dtype == kF32) return launch_out<kF32>(P, D, blocks, threads, stream);
-    if (out_dtype == kF16) return launch_out<kF16>(P, D, blocks, threads, stream);
-    return launch_out<0>(P, D, blocks, threads, stream);
+    if (out_dtype == kF32) return launch_out<kF32>(P, D, blocks, threads, slices, stream);
+    if (out_dtype == kF16) return launch_out<kF16>(P, D, blocks, threads, slices, stream);
+    return launch_out<0>(P, D, blocks, threads, slices, stream);
 }
 
 }  // namespace gqa

@@ -143,9 +143,11 @@ int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decod
     const int64_t ranges = chunks / a->h_kv;
     const int R = rows_per_kv_head(a);
     const bool wide = ranges / a->batch > kWideMergePieces;
+    const bool split = wide && static_cast<int64_t>(a->batch) * a->h_kv * R < kSplitMergeBelowBlocks;
     plan->merge_threads = wide ? kMergeThreadsWide : kMergeThreadsNarrow;
+    plan->merge_slices = split ? a->d_head / (4 * kMergeSliceQuads) : 1;
     const int rows_per_block = wide ? 1 : kMergeThreadsNarrow / (a->d_head / 4);
-    plan->merge_blocks = a->batch * a->h_kv * ((R + rows_per_block - 1) / rows_per_block);
+    plan->merge_blocks = a->batch * a->h_kv * ((R + rows_per_block - 1) / rows_per_block) * plan->merge_slices;
     plan->workspace_bytes = L.bytes;
     return GQA_OK;
 }

@@ -177,6 +177,7 @@ typedef struct gqa_decode_plan {
     int32_t split_blocks;    /* workgroups of the sweep kernel (4 wavefronts each) */
     int32_t merge_blocks;    /* workgroups of the merge kernel                     */
     int32_t merge_threads;   /* threads per merge workgroup (256 or 1024)          */
+    int32_t merge_slices;    /* d slices per output row in the merge (1 or d / 32) */
     size_t workspace_bytes;  /* partial-triple scratch the call needs              */
 } gqa_decode_plan;
 

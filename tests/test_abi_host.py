@@ -149,8 +149,13 @@ def test_plan_automatic_and_explicit(lib):
     st, plan = B.gqa_decode_make_plan(_args(num_chunks=7, min_chunk=1024), 256, 8)
     assert st == B.GQA_OK
     assert (plan.num_chunks, plan.min_chunk, plan.split_blocks) == (8, 1024, 2)   # at least h_kv
+    assert plan.merge_slices == 1
     st, plan = B.gqa_decode_make_plan(_args(batch=1, h_kv=1, h_q=8), 256, 8)
     assert (st, plan.merge_threads) == (B.GQA_OK, 1024)     # one sequence cut into 1024 ranges
+    # ... and only 8 rows: each row's d is split over 4 workgroups
+    assert (plan.merge_slices, plan.merge_blocks) == (4, 8 * 4)
+    st, plan = B.gqa_decode_make_plan(_args(batch=64, h_kv=1, h_q=8, num_chunks=64 * 64), 256, 8)
+    assert (plan.merge_threads, plan.merge_slices, plan.merge_blocks) == (1024, 1, 64 * 8)
     st, plan = B.gqa_decode_make_plan(_args(num_chunks=7, h_kv=1, h_q=8), 256, 8)
     assert (st, plan.num_chunks, plan.split_blocks) == (B.GQA_OK, 7, 2)
     st, plan = B.gqa_decode_make_plan(_args(h_kv=6, h_q=48), 256, 12)
@@ -183,4 +188,4 @@ def test_error_message_is_cleared_on_success(lib):
 def test_struct_mirrors_match_header_sizes(lib):
     # gqa_decode_args: 5 pointers, 6 int32 + float, 2 more int32, pointer, size_t, pointer
     assert ctypes.sizeof(B.GqaArgs) == 5 * 8 + 4 * 4 + 4 + 4 * 4 + 4 + 8 + 8 + 8 + 2 * 8 + 8
-    assert ctypes.sizeof(B.GqaPlan) == 5 * 4 + 4 + 8
+    assert ctypes.sizeof(B.GqaPlan) == 6 * 4 + 8
