@@ -1,4 +1,4 @@
-"""ctypes binding of libgqa_decode.so (include/gqa_decode.h).
+"""ctypes binding of libgqa_decode.so (include/gqa_decode.h, include/gqa_prefill.h).
 
 Argument marshalling only: tensors become device pointers, the current torch
 stream becomes the hipStream_t, and every step of the decode runs in the HIP
@@ -6,7 +6,8 @@ kernels behind the C ABI.  There is no fallback: if the library is missing or
 was not built, calls raise.
 
 Functions with the C names take raw pointers or tensors exactly as the C ABI
-does; `decode` is the convenience wrapper that allocates the output tensor.
+does; `decode` and `prefill` are the convenience wrappers that allocate the
+output tensor.
 """
 from __future__ import annotations
 
@@ -31,10 +32,11 @@ GQA_ERR_WORKSPACE = 6
 GQA_ERR_HIP = 7
 GQA_ERR_ARG = 8
 
-# Every function include/gqa_decode.h and include/gqa_probe.h declare.
+# Every function include/gqa_decode.h, include/gqa_prefill.h and include/gqa_probe.h declare.
 EXPORTS = ("gqa_decode", "gqa_decode_f32", "gqa_decode_f16", "gqa_decode_ex", "gqa_decode_validate",
            "gqa_decode_make_plan", "gqa_decode_workspace_bytes", "gqa_status_str",
-           "gqa_last_error_message", "gqa_release", "gqa_probe_copy", "gqa_probe_read")
+           "gqa_last_error_message", "gqa_release", "gqa_prefill", "gqa_prefill_f16", "gqa_prefill_ex",
+           "gqa_prefill_validate", "gqa_probe_copy", "gqa_probe_read")
 
 
 class GqaArgs(ctypes.Structure):
@@ -72,6 +74,18 @@ class GqaError(RuntimeError):
 _lib = None
 
 
+class GqaPrefillArgs(ctypes.Structure):
+    """Mirror of gqa_prefill_args."""
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+        ("d_head", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32), ("stream", ctypes.c_void_p),
+    ]
+
+
 def lib() -> ctypes.CDLL:
     """The loaded library; raises if it was not built (no fallback path exists)."""
     global _lib
@@ -104,6 +118,14 @@ def lib() -> ctypes.CDLL:
     L.gqa_last_error_message.restype = ctypes.c_char_p
     L.gqa_release.argtypes = []
     L.gqa_release.restype = None
+    L.gqa_prefill.argtypes = sig
+    L.gqa_prefill.restype = ctypes.c_int
+    L.gqa_prefill_f16.argtypes = sig
+    L.gqa_prefill_f16.restype = ctypes.c_int
+    L.gqa_prefill_ex.argtypes = [ctypes.POINTER(GqaPrefillArgs)]
+    L.gqa_prefill_ex.restype = ctypes.c_int
+    L.gqa_prefill_validate.argtypes = [ctypes.POINTER(GqaPrefillArgs)]
+    L.gqa_prefill_validate.restype = ctypes.c_int
     L.gqa_probe_copy.argtypes = [P, P, ctypes.c_size_t, P]
     L.gqa_probe_copy.restype = ctypes.c_int
     L.gqa_probe_read.argtypes = [P, ctypes.c_size_t, P, P]
@@ -268,6 +290,68 @@ def decode(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype
                      _dtype_code(out), num_chunks, min_chunk, workspace, ws_bytes, _stream(stream),
                      t_q=t_q)
     gqa_decode_ex(args)
+    return out
+
+
+def gqa_prefill(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_head: int, scale: float,
+                stream=None) -> int:
+    """Causal prefill, bf16 in / bf16 out.  Raises GqaError on a non-zero status."""
+    st = lib().gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens), batch, h_q, h_kv,
+                           d_head, float(scale), _stream(stream))
+    _check(st)
+    return st
+
+
+def gqa_prefill_f16(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_head: int,
+                    scale: float, stream=None) -> int:
+    """Causal prefill, fp16 in / fp16 out."""
+    st = lib().gqa_prefill_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens), batch, h_q, h_kv,
+                               d_head, float(scale), _stream(stream))
+    _check(st)
+    return st
+
+
+def make_prefill_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, in_dtype, out_dtype,
+                      num_blocks=0, stream=0) -> GqaPrefillArgs:
+    a = GqaPrefillArgs()
+    a.q, a.k, a.v, a.o, a.seq_lens = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens)
+    a.batch, a.h_q, a.h_kv, a.d_head = int(batch), int(h_q), int(h_kv), int(d_head)
+    a.scale = float(scale)
+    a.in_dtype, a.out_dtype = int(in_dtype), int(out_dtype)
+    a.num_blocks = int(num_blocks)
+    a.stream = stream
+    return a
+
+
+def gqa_prefill_ex(args: GqaPrefillArgs) -> int:
+    st = lib().gqa_prefill_ex(ctypes.byref(args))
+    _check(st)
+    return st
+
+
+def gqa_prefill_validate(args: GqaPrefillArgs) -> int:
+    """Host-side checks only; returns the status (does not raise)."""
+    return int(lib().gqa_prefill_validate(ctypes.byref(args)))
+
+
+def prefill(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype=None,
+            num_blocks: int = 0, stream=None):
+    """o = causal GQA prefill of q [sum(seq_lens), h_q, d] against k, v
+    [sum(seq_lens), h_kv, d] (each token sees its sequence's keys up to itself).
+    seq_lens is an int32 device tensor.  Returns `out`."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [sum(seq_lens), h_q, d]; k, v [sum(seq_lens), h_kv, d]")
+    h_q, d = q.shape[1], q.shape[2]
+    h_kv = k.shape[1]
+    batch = int(seq_lens.numel())
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    args = make_prefill_args(q, k, v, out, seq_lens, batch, h_q, h_kv, d, scale, _dtype_code(q),
+                             _dtype_code(out), num_blocks, _stream(stream))
+    gqa_prefill_ex(args)
     return out
 
 

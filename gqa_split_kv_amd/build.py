@@ -44,6 +44,12 @@ def build(verbose: bool = False) -> str:
         _run([HIPCC, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *NO_PACKED_FP32, *DEVICE_FLAGS,
               "-c", src, "-o", obj], verbose)
         objs.append(obj)
+    # Prefill kernel: its accumulators live in AGPRs (no VGPR-form MFMA).
+    src = os.path.join(CSRC, "prefill_kernel.hip")
+    obj = os.path.join(BUILD, "prefill_kernel.o")
+    _run([HIPCC, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *NO_PACKED_FP32, "-c", src, "-o", obj],
+         verbose)
+    objs.append(obj)
     # Measurement probes (plain copy / read kernels).
     src = os.path.join(CSRC, "probe_kernels.hip")
     obj = os.path.join(BUILD, "probe_kernels.o")

@@ -1,6 +1,6 @@
 // api.cpp -- the extern "C" entry points of libgqa_decode.so (declared in
-// include/gqa_decode.h): validation, planning, the library-owned workspace
-// cache, and the launch.  No C++ exception leaves this file.
+// include/gqa_decode.h and include/gqa_prefill.h): validation, planning, the
+// library-owned workspace cache, and the launches.  No C++ exception leaves this file.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -135,6 +135,70 @@ int decode_ex(const gqa_decode_args *a) {
     return GQA_OK;
 }
 
+// Resident prefill workgroups per compute unit, cached per (device, variant).
+std::map<std::pair<int, int>, int> g_prefill_blocks_per_cu;
+
+int prefill_ex(const gqa_prefill_args *a) {
+    gqa::clear_error();
+    int st = gqa::validate_prefill(a);
+    if (st != GQA_OK) return st;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    int blocks = a->num_blocks;
+    if (blocks == 0) {
+        int num_cus = 0, waves = 0;
+        st = device_shape(dev, GQA_DTYPE_BF16, GQA_DTYPE_BF16, a->d_head, &num_cus, &waves);
+        if (st != GQA_OK) return st;
+        std::lock_guard<std::mutex> lock(g_mu);
+        const auto key = std::make_pair(dev, variant_id(a->in_dtype, a->out_dtype, a->d_head));
+        auto it = g_prefill_blocks_per_cu.find(key);
+        if (it == g_prefill_blocks_per_cu.end()) {
+            int per_cu = 0;
+            e = gqa::prefill_occupancy(a->in_dtype, a->out_dtype, a->d_head, &per_cu);
+            if (e != hipSuccess || per_cu <= 0)
+                return gqa::fail(GQA_ERR_HIP, "prefill occupancy query failed: %s", hipGetErrorString(e));
+            it = g_prefill_blocks_per_cu.emplace(key, per_cu).first;
+        }
+        blocks = num_cus * it->second;
+    }
+    gqa::PrefillParams P;
+    P.q = static_cast<const uint8_t *>(a->q);
+    P.k = static_cast<const uint8_t *>(a->k);
+    P.v = static_cast<const uint8_t *>(a->v);
+    P.o = static_cast<uint8_t *>(a->o);
+    P.seq_lens = a->seq_lens;
+    P.batch = a->batch;
+    P.h_q = a->h_q;
+    P.h_kv = a->h_kv;
+    P.G = a->h_q / a->h_kv;
+    P.scale_log2 = static_cast<float>(static_cast<double>(a->scale) * 1.4426950408889634074);
+    e = gqa::launch_prefill(P, a->in_dtype, a->out_dtype, a->d_head, blocks,
+                            reinterpret_cast<hipStream_t>(a->stream));
+    if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "prefill kernel launch failed: %s", hipGetErrorString(e));
+    return GQA_OK;
+}
+
+gqa_prefill_args make_prefill_args(const void *q, const void *k, const void *v, void *o,
+                                   const int32_t *seq_lens, int32_t batch, int32_t h_q, int32_t h_kv,
+                                   int32_t d_head, float scale, void *stream, int dtype) {
+    gqa_prefill_args a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.seq_lens = seq_lens;
+    a.batch = batch;
+    a.h_q = h_q;
+    a.h_kv = h_kv;
+    a.d_head = d_head;
+    a.scale = scale;
+    a.in_dtype = dtype;
+    a.out_dtype = dtype;
+    a.stream = stream;
+    return a;
+}
+
 gqa_decode_args make_args(const void *q, const void *k, const void *v, void *o,
                           const int32_t *seq_lens, int32_t batch, int32_t h_q, int32_t h_kv,
                           int32_t d_head, float scale, void *stream, int dtype) {
@@ -188,6 +252,37 @@ int gqa_decode_f16(const void *q, const void *k, const void *v, void *o, const i
     const gqa_decode_args a =
         make_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, stream, GQA_DTYPE_F16);
     return gqa_decode_ex(&a);
+}
+
+int gqa_prefill_ex(const gqa_prefill_args *args) {
+    try {
+        return prefill_ex(args);
+    } catch (...) {
+        return gqa::fail(GQA_ERR_HIP, "internal error");
+    }
+}
+
+int gqa_prefill(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens, int32_t batch,
+                int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream) {
+    const gqa_prefill_args a =
+        make_prefill_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, stream, GQA_DTYPE_BF16);
+    return gqa_prefill_ex(&a);
+}
+
+int gqa_prefill_f16(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
+                    int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream) {
+    const gqa_prefill_args a =
+        make_prefill_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, stream, GQA_DTYPE_F16);
+    return gqa_prefill_ex(&a);
+}
+
+int gqa_prefill_validate(const gqa_prefill_args *args) {
+    try {
+        gqa::clear_error();
+        return gqa::validate_prefill(args);
+    } catch (...) {
+        return gqa::fail(GQA_ERR_HIP, "internal error");
+    }
 }
 
 int gqa_decode_validate(const gqa_decode_args *args) {

@@ -1,6 +1,7 @@
-// device_common.h -- device helpers shared by the sweep and merge kernels:
-// wavefront scans over seq_lens, the stream-K range arithmetic both kernels
-// must agree on, and bf16 rounding.  Internal to the library.
+// device_common.h -- device helpers shared by the decode (sweep, merge) and
+// prefill kernels: wavefront scans over seq_lens, the stream-K range arithmetic
+// the sweep and merge kernels must agree on, buffer loads, and 16-bit rounding.
+// Internal to the library.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -113,6 +114,22 @@ __device__ void locate(const int32_t *seq_lens, int batch, int h_kv, int64_t pos
 __device__ __forceinline__ int64_t chunk_keys(int64_t total, int num_chunks, int min_chunk) {
     const int64_t c = (total + num_chunks - 1) / num_chunks;
     return c > min_chunk ? c : static_cast<int64_t>(min_chunk);
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, stride 0): loads at offsets
+// at or beyond `bytes` return zero without touching memory.  Both inputs must be
+// wave-uniform; readfirstlane makes that visible so the resource sits in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    const int64_t a = uniform64(reinterpret_cast<int64_t>(base));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(a), 0,
+                                             uniform32(static_cast<int>(bytes)), 0x00020000);
+}
+
+// 16-byte buffer load with the given cache-policy bits.
+template <int kCpol>
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpol);
+    return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {

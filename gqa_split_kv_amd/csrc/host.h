@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "gqa_decode.h"
+#include "gqa_prefill.h"
 
 namespace gqa {
 
@@ -27,8 +28,12 @@ constexpr int kMergeThreadsWide = 1024;
 constexpr int kMergeSliceQuads = 8;
 constexpr int kWideMergePieces = 32;   // expected pieces per sequence above which the merge is wide
 constexpr int kSplitMergeBelowBlocks = 256;
+// Prefill kernel: 4-wavefront workgroups owning 256 rows (256 / G tokens x G heads).
+constexpr int kPrefillThreads = 256;
+constexpr int kPrefillRows = 256;
 constexpr int kMaxG = 16;           // rows (query heads x query tokens) per kv head in one 16-wide MFMA tile
 constexpr int kMaxChunks = 1 << 24;
+constexpr int kMaxPrefillBlocks = 1 << 20;
 constexpr int kMaxHeadsKv = 1 << 16;   // keeps 16 key rows of lane offsets within 32 bits
 constexpr int kMaxMinChunk = 1 << 30;
 constexpr int kAutoMinChunk = 32;   // default smallest token range
@@ -47,6 +52,9 @@ void clear_error();
 // Argument checks in a fixed order (null, shape, support, alignment, scale,
 // tuning ranges, and the caller workspace when num_chunks is explicit).
 int validate(const gqa_decode_args *a);
+
+// Host checks of a prefill call (status, message via fail()).
+int validate_prefill(const gqa_prefill_args *a);
 
 // Workspace layout for `num_chunks` wavefronts: two partial-triple slots per
 // wavefront, each R = G * t_q rows of (O[D] fp32) plus (m, l) fp32.

@@ -1,5 +1,5 @@
-// kernels.h -- parameters and launchers of the gfx950 decode kernels
-// (sweep_kernel.hip, merge_kernel.hip).  Internal to the library.
+// kernels.h -- parameters and launchers of the gfx950 kernels (sweep_kernel.hip,
+// merge_kernel.hip, prefill_kernel.hip).  Internal to the library.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,5 +38,23 @@ hipError_t sweep_occupancy(int in_dtype, int out_dtype, int D, int *blocks_per_c
 // the split layout), as the plan sets them.
 hipError_t launch_merge(const DecodeParams &P, int out_dtype, int D, int blocks, int threads, int slices,
                         hipStream_t stream);
+
+// Causal prefill: every token of every sequence attends to keys 0 .. itself.
+struct PrefillParams {
+    const uint8_t *q;          // [sum(seq_lens), h_q, D] in_dtype
+    const uint8_t *k;          // [sum(seq_lens), h_kv, D] in_dtype
+    const uint8_t *v;
+    uint8_t *o;                // [sum(seq_lens), h_q, D] out_dtype
+    const int32_t *seq_lens;   // [batch]
+    int32_t batch, h_q, h_kv, G;
+    float scale_log2;          // scale * log2(e)
+};
+
+// Enqueues the prefill kernel: `blocks` workgroups of kPrefillThreads.
+hipError_t launch_prefill(const PrefillParams &P, int in_dtype, int out_dtype, int D, int blocks,
+                          hipStream_t stream);
+
+// Resident workgroups of the prefill kernel per compute unit.
+hipError_t prefill_occupancy(int in_dtype, int out_dtype, int D, int *blocks_per_cu);
 
 }  // namespace gqa

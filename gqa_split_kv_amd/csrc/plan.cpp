@@ -117,6 +117,37 @@ int validate(const gqa_decode_args *a) {
     return GQA_OK;
 }
 
+int validate_prefill(const gqa_prefill_args *a) {
+    if (!a) return fail(GQA_ERR_NULL, "args is NULL");
+    if (!a->q || !a->k || !a->v || !a->o || !a->seq_lens)
+        return fail(GQA_ERR_NULL, "q, k, v, o and seq_lens must be non-NULL");
+    if (a->batch <= 0 || a->h_q <= 0 || a->h_kv <= 0)
+        return fail(GQA_ERR_SHAPE, "batch (%d), h_q (%d) and h_kv (%d) must be positive", a->batch,
+                    a->h_q, a->h_kv);
+    if (a->h_q % a->h_kv != 0)
+        return fail(GQA_ERR_SHAPE, "h_q (%d) is not a multiple of h_kv (%d)", a->h_q, a->h_kv);
+    if (a->h_kv > kMaxHeadsKv)
+        return fail(GQA_ERR_UNSUPPORTED, "h_kv %d exceeds %d", a->h_kv, kMaxHeadsKv);
+    const int G = a->h_q / a->h_kv;
+    if (G > kMaxG) return fail(GQA_ERR_UNSUPPORTED, "G = h_q/h_kv = %d exceeds %d", G, kMaxG);
+    if (a->d_head != 64 && a->d_head != 128)
+        return fail(GQA_ERR_UNSUPPORTED, "d_head %d not supported (64 or 128)", a->d_head);
+    const bool pair_ok = (a->in_dtype == GQA_DTYPE_BF16 && a->out_dtype == GQA_DTYPE_BF16) ||
+                         (a->in_dtype == GQA_DTYPE_BF16 && a->out_dtype == GQA_DTYPE_F32) ||
+                         (a->in_dtype == GQA_DTYPE_F16 && a->out_dtype == GQA_DTYPE_F16) ||
+                         (a->in_dtype == GQA_DTYPE_F16 && a->out_dtype == GQA_DTYPE_F32);
+    if (!pair_ok)
+        return fail(GQA_ERR_UNSUPPORTED, "prefill dtype pair (in %d, out %d) not supported", a->in_dtype,
+                    a->out_dtype);
+    if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->o, 16))
+        return fail(GQA_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+    if (!aligned(a->seq_lens, 4)) return fail(GQA_ERR_ALIGN, "seq_lens must be 4-byte aligned");
+    if (!std::isfinite(a->scale)) return fail(GQA_ERR_SCALE, "scale is not finite");
+    if (a->num_blocks < 0 || a->num_blocks > kMaxPrefillBlocks)
+        return fail(GQA_ERR_ARG, "num_blocks %d out of range [0, %d]", a->num_blocks, kMaxPrefillBlocks);
+    return GQA_OK;
+}
+
 int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decode_plan *plan) {
     int st = check_basic(a);
     if (st != GQA_OK) return st;

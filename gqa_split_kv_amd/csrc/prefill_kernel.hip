@@ -1,0 +1,421 @@
+// prefill_kernel.hip -- gfx950 (CDNA4) causal GQA prefill.
+//
+// Every token t of a sequence attends to the keys at positions 0 .. t of that
+// sequence: o = softmax(scale * q_t K[0..t]^T) V[0..t] for each query head, the
+// head reading kv head h / G.  This is the multi-token decode definition with
+// the query tokens being the whole sequence (the long-context prefill panel of
+// the kernbench2 page "_gqa_attention_decode_long.py", commit description:
+// T_q = S_kv, d_head 128, one KV group, the query axis split across workers
+// with disjoint output rows, so no cross-worker reduction is needed).
+//
+// Mapping to one MI355X:
+//   * A workgroup (4 wavefronts) owns one tile of 256 rows = 256 / G tokens x G
+//     query heads of one (sequence, kv head), and sweeps the keys 0 .. its last
+//     token in steps of 32 with the page's online-softmax fold; the rows are
+//     disjoint, so every tile normalises and stores its own outputs.
+//   * The 32-key K and V tiles go HBM/L2 -> registers -> LDS (double buffered,
+//     one barrier per step, the next tile's loads in flight during the current
+//     step) and are shared by all 256 rows, so the K/V bytes per output row
+//     fall with the tile height.
+//   * Each wavefront owns 64 rows as four 16-row N tiles of
+//     v_mfma_f32_16x16x32_{bf16,f16}: S^T = K Q^T with the keys on the M axis
+//     (the K rows are read from LDS in the key order that leaves lane l holding
+//     keys 8*(l/16) .. +7 of its row), then O^T += V^T P^T with P split into a
+//     high and a low 16-bit part (two products; about 16 significant bits of P
+//     for bf16, 22 for fp16).  The V^T operand is rebuilt from LDS rows once per
+//     step and reused by the four N tiles.
+//   * The running maximum is allowed to lag the true one by up to 8 (log2
+//     units): the accumulators are rescaled only when some row of an N tile
+//     exceeds its reference by more, which removes almost every rescale of the
+//     128 accumulators per lane.  Weights are then at most 2^8 (times 2^7 for
+//     fp16, to keep small weights inside its exponent range), and the common
+//     factor cancels in O / l.
+//   * Tiles are handed out in a fixed snake order over a persistent grid: the
+//     tiles of a (sequence, kv head) are enumerated last token first (longest
+//     first), and workgroup w takes tiles w, 2g-1-w, 2g+w, ... (g = grid size),
+//     which evens out the causal triangle's work.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace gqa {
+namespace {
+
+using namespace dev;
+
+constexpr int kBf16 = 0;
+constexpr int kF32 = 1;
+constexpr int kF16 = 2;
+
+constexpr int kWavesP = kPrefillThreads / kWave;   // 4
+constexpr int kNT = 4;                             // 16-row N tiles per wavefront
+constexpr int kRowsPerWave = 16 * kNT;             // 64
+constexpr int kStepKeys = 32;                      // keys per LDS stage
+constexpr float kLagLog2 = 8.f;                    // allowed lag of the running maximum
+static_assert(kWavesP * kRowsPerWave == kPrefillRows, "tile rows");
+
+template <bool kHalf>
+__device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+    if constexpr (kHalf)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Tiles of `len` tokens with `tt` tokens per tile.
+__device__ __forceinline__ int64_t tiles_of(int64_t len, int tt) { return (len + tt - 1) / tt; }
+
+// Work items (tiles x kv heads) of the whole batch; the same value in every lane.
+__device__ int64_t count_items(const int32_t *seq_lens, int batch, int tt, int h_kv) {
+    const int lane = lane_id();
+    int64_t acc = 0;
+    for (int base = 0; base < batch; base += kWave) {
+        const int i = base + lane;
+        const int64_t n = (i < batch) ? tiles_of(seq_len_at(seq_lens, i), tt) : 0;
+        acc += shfl64(inclusive_scan64(n), kWave - 1);
+    }
+    return uniform64(acc * h_kv);
+}
+
+// The sequence b holding work item `it`, with off = tokens before b, len = its
+// length and local = the item's index among b's items.
+__device__ void locate_item(const int32_t *seq_lens, int batch, int tt, int h_kv, int64_t it, int &b,
+                            int64_t &off, int &len, int64_t &local) {
+    const int lane = lane_id();
+    int64_t run_items = 0, run_len = 0;
+    for (int base = 0; base < batch; base += kWave) {
+        const int i = base + lane;
+        const int64_t li = (i < batch) ? seq_len_at(seq_lens, i) : 0;
+        const int64_t ni = tiles_of(li, tt) * h_kv;
+        const int64_t inc_n = inclusive_scan64(ni);
+        const int64_t inc_l = inclusive_scan64(li);
+        const bool hit = (i < batch) && (run_items + inc_n > it);
+        const unsigned long long mask = __ballot(hit);
+        if (mask) {
+            const int src = __ffsll(static_cast<long long>(mask)) - 1;
+            b = base + src;
+            len = uniform32(static_cast<int>(shfl64(li, src)));
+            off = uniform64(run_len + shfl64(inc_l, src) - len);
+            local = uniform64(it - (run_items + shfl64(inc_n, src) - shfl64(ni, src)));
+            return;
+        }
+        run_items += shfl64(inc_n, kWave - 1);
+        run_len += shfl64(inc_l, kWave - 1);
+    }
+    b = batch;
+    off = run_len;
+    len = 0;
+    local = 0;
+}
+
+template <int kOut>
+__device__ __forceinline__ void store_out(uint8_t *dst, const float *x, int n) {
+    if constexpr (kOut == kF32) {
+        for (int i = 0; i < n; i += 4)
+            *reinterpret_cast<float4 *>(dst + 4 * i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+    } else {
+        for (int i = 0; i < n; i += 8) {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = pack2<kOut == kF16>(x[i + 2 * k], x[i + 2 * k + 1]);
+            *reinterpret_cast<uint4 *>(dst + 2 * i) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
+
+template <int kIn, int kOut, int D>
+struct PrefillTile {
+    static constexpr bool kHalf = kIn == kF16;
+    static constexpr int ROWB = D * 2;              // bytes of one key row of one kv head
+    static constexpr int LROW = ROWB + 16;          // LDS row pitch (16-byte skew between rows)
+    static constexpr int NKP = ROWB / 64;           // 16-byte K pieces per lane per 16-key block
+    static constexpr int VEC = D / 16;              // d elements per lane per V row
+    static constexpr int VW = VEC / 2;              // 32-bit words per lane per V row
+    static constexpr int CH = ROWB / 16;            // 16-byte chunks per key row
+    static constexpr int kPer = kStepKeys * CH / kPrefillThreads;   // chunks per thread (K and V each)
+    static constexpr int kOff = kHalf ? 7 : 0;      // exponent offset of P
+    static constexpr int kTileBytes = kStepKeys * LROW;
+    static_assert(kPer * kPrefillThreads == kStepKeys * CH, "tile load split");
+
+    // One step: S^T = K Q^T for the four N tiles, masked online softmax with the
+    // lagging maximum, then O^T += V^T P^T.
+    __device__ __forceinline__ static void step(const uint8_t *Kt, const uint8_t *Vt, int k0,
+                                                const uint4 (&qop)[kNT][NKP], const int (&cap)[kNT],
+                                                float sl2, float (&m_ref)[kNT], float (&l_run)[kNT],
+                                                f32x4_t (&acc)[kNT][VEC]) {
+        const int lane = lane_id();
+        const int m = lane & 15;
+        const int kg = lane >> 4;
+        uint4 kop[2][NKP];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int p = 0; p < NKP; ++p)
+                kop[b][p] = *reinterpret_cast<const uint4 *>(Kt + (8 * (m >> 2) + 4 * b + (m & 3)) * LROW +
+                                                             64 * p + 16 * kg);
+        uint4 bhi[kNT], blo[kNT];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            float sv[8];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < NKP; ++p) s = mfma16<kHalf>(kop[b][p], qop[nt][p], s);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int key = k0 + 8 * kg + 4 * b + q;
+                    sv[4 * b + q] = key < cap[nt] ? s[q] * sl2 : -INFINITY;
+                }
+            }
+            float mx = sv[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // Move the reference only when a row's maximum passes it by more than the
+            // allowed lag (wave-uniform branch; rows that did not ask follow along).
+            if (__ballot(mx > m_ref[nt] + kLagLog2)) {
+                const float m_new = fmaxf(m_ref[nt], mx);
+                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref[nt] - m_new);
+                l_run[nt] *= alpha;
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) acc[nt][c] *= alpha;
+                m_ref[nt] = m_new;
+            }
+            // A row that has seen no key yet keeps the reference -inf: exponentiate
+            // against 0 so its masked scores give weight 0, not NaN.
+            const float mu = m_ref[nt] == -INFINITY ? 0.f : m_ref[nt];
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sv[i] = __builtin_amdgcn_exp2f(sv[i] - mu + static_cast<float>(kOff));
+                sum += sv[i];
+            }
+            l_run[nt] += sum;
+            uint32_t phi[4], plo[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const f32x2_t pw = {sv[2 * w], sv[2 * w + 1]};
+                if constexpr (kHalf) {
+                    const f16x2_t h = __builtin_convertvector(pw, f16x2_t);
+                    const f32x2_t hf = __builtin_convertvector(h, f32x2_t);
+                    phi[w] = __builtin_bit_cast(uint32_t, h);
+                    plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw - hf, f16x2_t));
+                } else {
+                    const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw, bf16x2_t));
+                    const f32x2_t r = {pw[0] - __uint_as_float(hb << 16), pw[1] - __uint_as_float(hb & 0xffff0000u)};
+                    phi[w] = hb;
+                    plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+                }
+            }
+            bhi[nt] = make_uint4(phi[0], phi[1], phi[2], phi[3]);
+            blo[nt] = make_uint4(plo[0], plo[1], plo[2], plo[3]);
+        }
+        // V rows 8kg + i, elements [VEC*m, VEC*m + VEC).
+        uint32_t vr[8][VW];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint8_t *src = Vt + (8 * kg + i) * LROW + m * VEC * 2;
+            if constexpr (VW == 4) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(src);
+                vr[i][0] = x.x;
+                vr[i][1] = x.y;
+                vr[i][2] = x.z;
+                vr[i][3] = x.w;
+            } else {
+                const uint2 x = *reinterpret_cast<const uint2 *>(src);
+                vr[i][0] = x.x;
+                vr[i][1] = x.y;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+            // A operand of column c: element i = V[key 8kg + i][d = VEC*m + c].
+            uint32_t a[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x = vr[2 * w][c >> 1];
+                const uint32_t y = vr[2 * w + 1][c >> 1];
+                a[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+            }
+            const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                acc[nt][c] = mfma16<kHalf>(av, bhi[nt], acc[nt][c]);
+                acc[nt][c] = mfma16<kHalf>(av, blo[nt], acc[nt][c]);
+            }
+        }
+    }
+
+    // Tile `tile` of (sequence b at token offset off, length len; kv head j).
+    __device__ __forceinline__ static void run(const PrefillParams &P, uint8_t (*lds)[2][kTileBytes], int64_t off,
+                                               int len, int j, int tile) {
+        const int tid = static_cast<int>(threadIdx.x);
+        const int wave = tid / kWave;
+        const int lane = lane_id();
+        const int m = lane & 15;
+        const int kg = lane >> 4;
+        const int G = P.G;
+        const int tt = kPrefillRows / G;                 // tokens per tile
+        const int tstart = tile * tt;
+        const int tcount = min(tt, len - tstart);         // > 0
+        const int rowstride = P.h_kv * ROWB;
+
+        // The lane's rows: row = 64 wave + 16 nt + m -> (token, head) = (row / G, row % G).
+        int cap[kNT];
+        uint4 qop[kNT][NKP];
+        int64_t orow[kNT];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            const int row = wave * kRowsPerWave + 16 * nt + m;
+            const int tok = row / G;
+            const int gh = row - tok * G;
+            const bool active = tok < tcount;
+            cap[nt] = active ? tstart + tok + 1 : 0;   // keys visible: positions < cap
+            orow[nt] = ((off + tstart + (active ? tok : 0)) * P.h_q + j * G + gh);
+            const uint8_t *qrow = P.q + orow[nt] * ROWB + 16 * kg;
+#pragma unroll
+            for (int p = 0; p < NKP; ++p) {
+                qop[nt][p] = *reinterpret_cast<const uint4 *>(qrow + 64 * p);
+                if (!active) qop[nt][p] = make_uint4(0, 0, 0, 0);
+            }
+        }
+        const int wtok_lo = (wave * kRowsPerWave) / G;
+        const int wtok_hi = min((wave * kRowsPerWave + kRowsPerWave - 1) / G, tcount - 1);
+        const int wkeys = wtok_lo < tcount ? tstart + wtok_hi + 1 : 0;   // keys this wavefront needs
+        const int nkeys = tstart + tcount;                                 // keys the tile needs
+        const int nsteps = (nkeys + kStepKeys - 1) / kStepKeys;
+        const uint8_t *kbase = P.k + (off * P.h_kv + j) * ROWB;
+        const uint8_t *vbase = P.v + (off * P.h_kv + j) * ROWB;
+
+        uint32_t goff[kPer], loff[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = tid + i * kPrefillThreads;
+            const int r = c / CH;
+            const int col = c - r * CH;
+            goff[i] = static_cast<uint32_t>(r * rowstride + col * 16);
+            loff[i] = static_cast<uint32_t>(r * LROW + col * 16);
+        }
+        uint4 rk[kPer], rv[kPer];
+        auto fetch = [&](int st) {
+            const int k0 = st * kStepKeys;
+            const uint32_t bytes = static_cast<uint32_t>(min(kStepKeys, len - k0) * rowstride);
+            const int64_t boff = static_cast<int64_t>(k0) * rowstride;
+            const auto rsk = make_rsrc(kbase + boff, bytes);
+            const auto rsv = make_rsrc(vbase + boff, bytes);
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                rk[i] = buffer_load16<0>(rsk, goff[i]);
+                rv[i] = buffer_load16<0>(rsv, goff[i]);
+            }
+        };
+        auto stash = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                *reinterpret_cast<uint4 *>(lds[buf][0] + loff[i]) = rk[i];
+                *reinterpret_cast<uint4 *>(lds[buf][1] + loff[i]) = rv[i];
+            }
+        };
+
+        float m_ref[kNT], l_run[kNT];
+        f32x4_t acc[kNT][VEC];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            m_ref[nt] = -INFINITY;
+            l_run[nt] = 0.f;
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) acc[nt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        const float sl2 = P.scale_log2;
+        fetch(0);
+        stash(0);
+        __syncthreads();
+        for (int st = 0; st < nsteps; ++st) {
+            const bool more = st + 1 < nsteps;
+            if (more) fetch(st + 1);
+            if (st * kStepKeys < wkeys)
+                step(lds[st & 1][0], lds[st & 1][1], st * kStepKeys, qop, cap, sl2, m_ref, l_run, acc);
+            if (more) stash((st + 1) & 1);
+            __syncthreads();
+        }
+
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 16);
+            l_tot += __shfl_xor(l_tot, 32);
+            const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+            float out[4 * VEC];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[nt][c][q] * inv;
+            if (cap[nt] > 0)
+                store_out<kOut>(P.o + (orow[nt] * D + 4 * VEC * kg) * (kOut == kF32 ? 4 : 2), out, 4 * VEC);
+        }
+    }
+};
+
+template <int kIn, int kOut, int D>
+__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams P) {
+    using T = PrefillTile<kIn, kOut, D>;
+    __shared__ __align__(16) uint8_t lds[2][2][T::kTileBytes];
+    const int tt = kPrefillRows / P.G;
+    const int64_t items = count_items(P.seq_lens, P.batch, tt, P.h_kv);
+    const int64_t g = gridDim.x;
+    const int64_t w = blockIdx.x;
+    for (int64_t r = 0; r * g < items; ++r) {
+        const int64_t it = r * g + ((r & 1) ? g - 1 - w : w);   // snake order
+        if (it >= items) continue;
+        int b, len;
+        int64_t off, local;
+        locate_item(P.seq_lens, P.batch, tt, P.h_kv, it, b, off, len, local);
+        const int ntile = static_cast<int>(tiles_of(len, tt));
+        const int j = static_cast<int>(local / ntile);
+        const int tile = ntile - 1 - static_cast<int>(local - static_cast<int64_t>(j) * ntile);   // longest first
+        T::run(P, lds, off, len, j, tile);
+    }
+}
+
+template <int kIn, int kOut>
+hipError_t launch_pio(const PrefillParams &P, int D, int blocks, hipStream_t stream) {
+    if (D == 128)
+        hipLaunchKernelGGL((prefill_kernel<kIn, kOut, 128>), dim3(blocks), dim3(kPrefillThreads), 0, stream, P);
+    else
+        hipLaunchKernelGGL((prefill_kernel<kIn, kOut, 64>), dim3(blocks), dim3(kPrefillThreads), 0, stream, P);
+    return hipGetLastError();
+}
+
+template <int kIn, int kOut>
+hipError_t occupancy_pio(int D, int *blocks_per_cu) {
+    return D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, prefill_kernel<kIn, kOut, 128>,
+                                                                   kPrefillThreads, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, prefill_kernel<kIn, kOut, 64>,
+                                                                   kPrefillThreads, 0);
+}
+
+}  // namespace
+
+// (in, out) pairs the prefill validation admits: (bf16, bf16), (bf16, f32),
+// (f16, f16), (f16, f32).
+hipError_t launch_prefill(const PrefillParams &P, int in_dtype, int out_dtype, int D, int blocks,
+                          hipStream_t stream) {
+    if (in_dtype == kBf16) return out_dtype == kBf16 ? launch_pio<kBf16, kBf16>(P, D, blocks, stream)
+                                                     : launch_pio<kBf16, kF32>(P, D, blocks, stream);
+    return out_dtype == kF16 ? launch_pio<kF16, kF16>(P, D, blocks, stream)
+                             : launch_pio<kF16, kF32>(P, D, blocks, stream);
+}
+
+hipError_t prefill_occupancy(int in_dtype, int out_dtype, int D, int *blocks_per_cu) {
+    if (in_dtype == kBf16) return out_dtype == kBf16 ? occupancy_pio<kBf16, kBf16>(D, blocks_per_cu)
+                                                     : occupancy_pio<kBf16, kF32>(D, blocks_per_cu);
+    return out_dtype == kF16 ? occupancy_pio<kF16, kF16>(D, blocks_per_cu)
+                             : occupancy_pio<kF16, kF32>(D, blocks_per_cu);
+}
+
+}  // namespace gqa

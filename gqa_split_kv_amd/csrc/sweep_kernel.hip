@@ -1,4 +1,4 @@
-// decode_kernels.hip -- gfx950 (CDNA4) kernels of split-KV GQA decode.
+// sweep_kernel.hip -- gfx950 (CDNA4) key-sweep kernel of split-KV GQA decode.
 //
 // Method (kernbench2 page "_gqa_attention_decode_long.py"): the keys of every
 // (sequence, kv head) are swept in tiles; each tile gives a partial online-softmax

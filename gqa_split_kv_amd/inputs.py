@@ -166,6 +166,28 @@ def host_case(batch: int, h_q: int, h_kv: int, d: int, seq_lens: Sequence[int], 
     return HostCase(q, k, v, sl, float(scale), dtype, peaks)
 
 
+def host_prefill_case(batch: int, h_q: int, h_kv: int, d: int, seq_lens: Sequence[int], dtype: str = "bf16",
+                      seed: int = 0, scale: Optional[float] = None, peaked_frac: float = 0.0,
+                      peak_factor: float = 8.0) -> HostCase:
+    """Prefill inputs: q [sum(seq_lens), h_q, d] (every token a query), k and v as
+    host_case draws them (same streams and peaked rows)."""
+    c = host_case(batch, h_q, h_kv, d, seq_lens, dtype, seed=seed, scale=scale, peaked_frac=peaked_frac,
+                  peak_factor=peak_factor)
+    rows = int(np.clip(c.seq_lens, 0, None).sum())
+    qf = _normal(seed, 0, rows * h_q * d).reshape(rows, h_q, d)
+    if dtype == "bf16":
+        qf = f32_to_bf16_bits(qf)
+    elif dtype == "f16":
+        qf = qf.astype(np.float16)
+    c.q = qf
+    return c
+
+
+# Causal prefill of one KV group over a 32K-token sequence (the long-context
+# prefill panel: T_q = S_kv = 32768, h_q 8, h_kv 1, d_head 128, bf16).
+PREFILL_32K = Workload(6, "prefill_single_kv_group_hq8_hkv1_d128_S32768", "bf16", 1, 8, 1, 128, 32768)
+
+
 def host_workload(w: Workload) -> HostCase:
     return host_case(w.batch, w.h_q, w.h_kv, w.d, w.seq_lens(), w.dtype, seed=w.seed,
                      scale=w.scale, peaked_frac=w.peaked_frac, peak_factor=w.peak_factor)

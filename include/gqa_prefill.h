@@ -1,0 +1,92 @@
+/*
+ * gqa_prefill.h -- C ABI of the causal grouped-query-attention prefill in
+ * libgqa_decode.so (MI355X, gfx950).
+ *
+ * The operation (kernbench2 page "_gqa_attention_decode_long.py", commit
+ * description: the long-context prefill panel with T_q = S_kv, d_head 128 and one
+ * KV group, the query axis split across workers with disjoint output rows): the
+ * decode operation of gqa_decode.h with every token of a sequence as a query.
+ * For every sequence b < batch, token t < S = seq_lens[b] (negative counts as 0),
+ * query head h < h_q, with G = h_q / h_kv, kv head j = h / G and
+ * base = seq_lens[0] + ... + seq_lens[b-1]:
+ *
+ *   s_u              = scale * sum_i q[base+t, h, i] * k[base+u, j, i]     u <= t
+ *   o[base+t, h, :]  = sum_{u <= t} softmax(s)_u * v[base+u, j, :]
+ *
+ * i.e. causal attention of each sequence over its own keys (the queries are the
+ * sequence's own tokens, key u visible to token t iff u <= t).  The page says
+ * nothing of the mask; this is the multi-token decode rule of gqa_decode.h with
+ * t_q = S.  fp32 accumulation; a 16-bit output is the nearest-even rounding of the
+ * fp32 result.
+ *
+ * Tensor layouts (row-major, contiguous, device memory of the current HIP device,
+ * owned by the caller; the library never frees or keeps them):
+ *   q, o      [sum(seq_lens), h_q, d_head]    in_dtype / out_dtype, sequences packed
+ *   k, v      [sum(seq_lens), h_kv, d_head]   in_dtype, packed the same way
+ *   seq_lens  int32[batch], device memory, read only by the kernel
+ *
+ * Supported: d_head in {64, 128}; G in 1..16; (in, out) dtypes (bf16, bf16),
+ * (bf16, f32), (f16, f16), (f16, f32).  q, k, v, o 16-byte aligned, seq_lens
+ * 4-byte aligned.  No workspace: every output row is written by exactly one
+ * workgroup, so nothing is allocated and the call is capturable in a HIP graph.
+ *
+ * Asynchrony and errors as in gqa_decode.h: work is enqueued on `stream`, host
+ * errors return a gqa_status before anything is enqueued (o untouched), and
+ * gqa_last_error_message() describes the last error of the calling thread.
+ */
+#ifndef GQA_PREFILL_H
+#define GQA_PREFILL_H
+
+#include "gqa_decode.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Full argument block.  Zero-initialise it, then set the fields.
+ *
+ * num_blocks  Workgroups of the persistent grid (each takes tiles of 256 / G
+ *             tokens x G heads in a fixed order); 0 = one per resident slot
+ *             (compute units x resident workgroups per compute unit).  Range
+ *             0..2^20.  The result does not depend on it.
+ */
+typedef struct gqa_prefill_args {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    const int32_t *seq_lens;
+    int32_t batch;
+    int32_t h_q;
+    int32_t h_kv;
+    int32_t d_head;
+    float scale;
+    int32_t in_dtype;   /* GQA_DTYPE_BF16 or GQA_DTYPE_F16                  */
+    int32_t out_dtype;  /* in_dtype or GQA_DTYPE_F32                        */
+    int32_t num_blocks;
+    void *stream;       /* hipStream_t; NULL = the null stream              */
+} gqa_prefill_args;
+
+/* gqa_prefill -- bf16 q/k/v in, bf16 o out.  Returns a gqa_status. */
+int gqa_prefill(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
+                int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream);
+
+/* gqa_prefill_f16 -- IEEE fp16 q/k/v in, fp16 o out. */
+int gqa_prefill_f16(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
+                    int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream);
+
+/* gqa_prefill_ex -- any supported dtype pair and grid size. */
+int gqa_prefill_ex(const gqa_prefill_args *args);
+
+/* Host-side checks only (no device access); returns the status gqa_prefill_ex
+ * would return before enqueueing anything: GQA_ERR_NULL, GQA_ERR_SHAPE (batch,
+ * h_q or h_kv <= 0, h_q not a multiple of h_kv), GQA_ERR_UNSUPPORTED (d_head, G,
+ * h_kv above 65536 or the dtype pair), GQA_ERR_ALIGN, GQA_ERR_SCALE, GQA_ERR_ARG
+ * (num_blocks out of range). */
+int gqa_prefill_validate(const gqa_prefill_args *args);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_PREFILL_H */

@@ -8,6 +8,9 @@ it.  The two share no code.
 
 Contents
   gqa_decode_f64     direct softmax(scale * q K^T) V per query head (oracle.c)
+  gqa_prefill_f64    causal prefill: every token of a sequence as a query over
+                     its own prefix (the multi-token rule with t_q = S)
+  gqa_prefill_rows_f64  chosen rows of gqa_prefill_f64, one token at a time
   softmax_weights    the normalised weights of one (sequence, head)
   partial_f64        the (m, l, O) triple of one (sequence, head) over a key range
   merge              (merge.py) the log-sum-exp merge of two triples, and the
@@ -138,6 +141,44 @@ def gqa_decode_f64(q, k, v, seq_lens, scale: float) -> np.ndarray:
                                        float(scale), code, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_gqa_decode_f64 failed (%d)" % rc)
+    return out
+
+
+def gqa_prefill_f64(q, k, v, seq_lens, scale: float) -> np.ndarray:
+    """Causal prefill, float64: q, k, v packed [sum(S), heads, d]; row base_b + t,
+    head h = softmax over keys 0 .. t of sequence b (the multi-token decode of
+    gqa_decode_f64 with t_q = S_b: the query tokens are the sequence itself).
+    Source: kernbench2 page "_gqa_attention_decode_long.py", commit description
+    (prefill panel, T_q = S_kv); the causal rule is this package's reading."""
+    q = np.ascontiguousarray(q)
+    sl = np.clip(np.asarray(seq_lens, dtype=np.int64), 0, None)
+    if q.ndim != 3 or q.shape[0] != int(sl.sum()):
+        raise ValueError("q must be [sum(seq_lens), h_q, d]")
+    out = np.zeros(q.shape, dtype=np.float64)
+    base = 0
+    for S in sl:
+        S = int(S)
+        if S:
+            qb = np.ascontiguousarray(q[base:base + S])[None]
+            out[base:base + S] = gqa_decode_f64(qb, k[base:base + S], v[base:base + S], [S], scale)[0]
+        base += S
+    return out
+
+
+def gqa_prefill_rows_f64(q, k, v, seq_lens, scale: float, tokens) -> np.ndarray:
+    """Rows `tokens` (indices into the packed token axis) of gqa_prefill_f64, each
+    computed as a single-token decode of that token over its sequence's keys
+    0 .. itself; float64 [len(tokens), h_q, d]."""
+    sl = np.clip(np.asarray(seq_lens, dtype=np.int64), 0, None)
+    ends = np.cumsum(sl)
+    out = np.empty((len(tokens),) + tuple(q.shape[1:]), dtype=np.float64)
+    for n, r in enumerate(tokens):
+        r = int(r)
+        b = int(np.searchsorted(ends, r, side="right"))
+        base = int(ends[b] - sl[b])
+        t = r - base
+        qr = np.ascontiguousarray(q[r:r + 1])
+        out[n] = gqa_decode_f64(qr, k[base:base + t + 1], v[base:base + t + 1], [t + 1], scale)[0]
     return out
 
 

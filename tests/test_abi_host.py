@@ -189,3 +189,46 @@ def test_struct_mirrors_match_header_sizes(lib):
     # gqa_decode_args: 5 pointers, 6 int32 + float, 2 more int32, pointer, size_t, pointer
     assert ctypes.sizeof(B.GqaArgs) == 5 * 8 + 4 * 4 + 4 + 4 * 4 + 4 + 8 + 8 + 8 + 2 * 8 + 8
     assert ctypes.sizeof(B.GqaPlan) == 6 * 4 + 8
+
+
+# ------------------------------------------------------------------ prefill
+
+
+def _pargs(**kw):
+    base = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, seq_lens=0x50000, batch=1, h_q=8,
+                h_kv=1, d_head=128, scale=0.088, in_dtype=B.GQA_DTYPE_BF16,
+                out_dtype=B.GQA_DTYPE_BF16)
+    base.update(kw)
+    return B.make_prefill_args(**base)
+
+
+def _pvalidate(**kw):
+    return B.gqa_prefill_validate(_pargs(**kw))
+
+
+def test_prefill_validation(lib):
+    assert _pvalidate() == B.GQA_OK
+    assert _pvalidate(out_dtype=B.GQA_DTYPE_F32) == B.GQA_OK
+    assert _pvalidate(in_dtype=B.GQA_DTYPE_F16, out_dtype=B.GQA_DTYPE_F16, d_head=64) == B.GQA_OK
+    assert _pvalidate(in_dtype=B.GQA_DTYPE_F16, out_dtype=B.GQA_DTYPE_F32) == B.GQA_OK
+    assert _pvalidate(in_dtype=B.GQA_DTYPE_F32, out_dtype=B.GQA_DTYPE_F32) == B.GQA_ERR_UNSUPPORTED
+    assert _pvalidate(in_dtype=B.GQA_DTYPE_BF16, out_dtype=B.GQA_DTYPE_F16) == B.GQA_ERR_UNSUPPORTED
+    assert _pvalidate(q=0) == B.GQA_ERR_NULL
+    assert _pvalidate(seq_lens=0) == B.GQA_ERR_NULL
+    assert B.lib().gqa_prefill_validate(None) == B.GQA_ERR_NULL
+    assert _pvalidate(batch=0) == B.GQA_ERR_SHAPE
+    assert _pvalidate(h_q=12, h_kv=8) == B.GQA_ERR_SHAPE
+    assert _pvalidate(h_q=32, h_kv=1) == B.GQA_ERR_UNSUPPORTED      # G = 32
+    assert _pvalidate(h_q=70000, h_kv=70000) == B.GQA_ERR_UNSUPPORTED
+    assert _pvalidate(d_head=96) == B.GQA_ERR_UNSUPPORTED
+    assert _pvalidate(o=0x40008) == B.GQA_ERR_ALIGN
+    assert _pvalidate(seq_lens=0x50002) == B.GQA_ERR_ALIGN
+    assert _pvalidate(scale=float("inf")) == B.GQA_ERR_SCALE
+    assert _pvalidate(num_blocks=-1) == B.GQA_ERR_ARG
+    assert _pvalidate(num_blocks=(1 << 20) + 1) == B.GQA_ERR_ARG
+    assert _pvalidate(num_blocks=(1 << 20) + 1) == B.GQA_ERR_ARG and "num_blocks" in B.last_error_message()
+    assert _pvalidate(num_blocks=1 << 20) == B.GQA_OK
+
+
+def test_prefill_args_struct_size(lib):
+    assert ctypes.sizeof(B.GqaPrefillArgs) == 5 * 8 + 4 * 4 + 4 + 3 * 4 + 8

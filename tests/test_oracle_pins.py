@@ -20,6 +20,10 @@ theirs; token t sees keys 0 .. S - t_q + t) is pinned the same way: brute force
 per token, torch's float64 SDPA with the matching boolean mask, t_q = 1 equal to
 the single-token call, and the last token equal to a single-token decode over
 all S keys.
+Causal prefill (every token of a sequence a query over its own prefix) is
+pinned to brute force per sequence, to torch's float64 SDPA with is_causal, and
+to closed forms (the first token returns its own V row; the last token is the
+single-token decode over the whole sequence).
 A final test plants plausible mistakes in copies of the definition and checks
 that the pins used here catch every one of them.
 """
@@ -33,7 +37,7 @@ import pytest
 import oracle
 from oracle import merge as M
 from oracle.brute import brute_decode
-from gqa_split_kv_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits, host_case
+from gqa_split_kv_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits, host_case, host_prefill_case
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -203,6 +207,83 @@ def test_last_token_sees_every_key_and_earlier_tokens_see_a_prefix():
     # token 1 of sequence 0 equals a single-token decode over its first 40 - 4 + 2 keys
     sub = oracle.gqa_decode_f64(np.ascontiguousarray(c.q[:1, 1]), c.k[:38], c.v[:38], [38], c.scale)
     assert np.array_equal(got[0, 1], sub[0])
+
+
+# ---------------------------------------------------------------- causal prefill
+
+
+def _brute_prefill(c):
+    out = []
+    base = 0
+    for S in c.seq_lens:
+        S = int(S)
+        if S:
+            r = brute_decode(np.ascontiguousarray(c.q[base:base + S])[None], c.k[base:base + S],
+                             c.v[base:base + S], [S], c.scale)
+            out.append(np.array(r, dtype=np.float64)[0])
+        base += S
+    return np.concatenate(out) if out else np.zeros(c.q.shape)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("seq_lens", [[1], [3], [2, 0, 4]])
+def test_prefill_oracle_matches_decimal_brute_force(dtype, seq_lens):
+    c = host_prefill_case(len(seq_lens), 4, 2, 8, seq_lens, dtype, seed=80, scale=0.45)
+    got = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    ref = _brute_prefill(c)
+    assert got.shape == ref.shape == c.q.shape
+    assert np.abs(got - ref).max() <= 1e-13 * max(1.0, np.abs(ref).max())
+
+
+def _sdpa_causal_reference(c, G):
+    """torch float64 SDPA per sequence with is_causal=True (query t sees keys <= t),
+    kv heads repeated G times."""
+    import torch
+    q = torch.from_numpy(_f64(c.q))
+    k = torch.from_numpy(_f64(c.k))
+    v = torch.from_numpy(_f64(c.v))
+    out = np.zeros(c.q.shape)
+    base = 0
+    for S in c.seq_lens:
+        S = int(S)
+        if S:
+            qb = q[base:base + S].permute(1, 0, 2).contiguous()
+            kb = k[base:base + S].permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+            vb = v[base:base + S].permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+            o = torch.nn.functional.scaled_dot_product_attention(qb[None], kb[None], vb[None],
+                                                                 is_causal=True, scale=c.scale)
+            out[base:base + S] = o[0].permute(1, 0, 2).numpy()
+        base += S
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("G,h_kv,d", [(8, 1, 64), (4, 2, 32), (1, 4, 16), (16, 1, 32), (3, 2, 16)])
+def test_prefill_equals_causal_sdpa(G, h_kv, d, dtype):
+    c = host_prefill_case(3, G * h_kv, h_kv, d, [37, 1, 90], dtype, seed=300 + G, scale=d ** -0.5)
+    got = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    assert np.abs(got - _sdpa_causal_reference(c, G)).max() <= 1e-12
+
+
+def test_prefill_rows_equal_full_prefill():
+    c = host_prefill_case(3, 8, 2, 32, [40, 1, 70], "bf16", seed=81)
+    full = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    rows = [0, 39, 40, 41, 110, 75, 1]
+    part = oracle.gqa_prefill_rows_f64(c.q, c.k, c.v, c.seq_lens, c.scale, rows)
+    assert np.abs(part - full[rows]).max() <= 1e-15
+
+
+def test_prefill_first_and_last_tokens():
+    c = host_prefill_case(2, 8, 2, 32, [25, 9], "f32", seed=82)
+    got = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    v = _f64(c.v)
+    for base in (0, 25):
+        # the first token sees only its own key: its V row, per kv group
+        for h in range(8):
+            assert np.array_equal(got[base, h], v[base, h // 4])
+    # the last token sees the whole sequence: the single-token decode
+    last = oracle.gqa_decode_f64(np.ascontiguousarray(c.q[[24, 33]]), c.k, c.v, c.seq_lens, c.scale)
+    assert np.abs(got[[24, 33]] - last).max() <= 1e-15
 
 
 # ---------------------------------------------------------------- closed forms
@@ -451,6 +532,35 @@ def _pins_tq(fn):
     seen = ~np.isnan(ref)
     ok &= np.abs(got[seen] - ref[seen]).max() < 1e-12 and (got[~seen] == 0).all()
     return bool(ok)
+
+
+def _definition_prefill(q, k, v, seq_lens, scale, mutate=None):
+    """Causal prefill from _definition_tq (t_q = S per sequence), with planted mistakes."""
+    out = np.zeros(q.shape)
+    base = 0
+    for S in seq_lens:
+        S = int(S)
+        if S:
+            qb = q[base:base + S][None]
+            out[base:base + S] = _definition_tq(qb, k[base:base + S], v[base:base + S], [S], scale,
+                                                mutate=mutate)[0]
+        base += S
+    return out
+
+
+def _pins_prefill(fn):
+    c = host_prefill_case(2, 4, 2, 8, [5, 3], "f32", seed=51, scale=0.6)
+    ok = np.abs(fn(c.q, c.k, c.v, c.seq_lens, c.scale) - _brute_prefill(c)).max() < 1e-12
+    c2 = host_prefill_case(3, 8, 2, 16, [37, 1, 60], "bf16", seed=52, scale=0.25)
+    ok &= np.abs(fn(c2.q, c2.k, c2.v, c2.seq_lens, c2.scale) - _sdpa_causal_reference(c2, 4)).max() < 1e-12
+    return bool(ok)
+
+
+def test_prefill_pins_catch_planted_mistakes():
+    assert _pins_prefill(_definition_prefill)
+    assert _pins_prefill(lambda *a: oracle.gqa_prefill_f64(*a))
+    for mut in ("mask_off_by_one", "mask_reversed", "no_mask", "token_swap"):
+        assert not _pins_prefill(lambda *a, m=mut: _definition_prefill(*a, mutate=m)), mut
 
 
 def test_multi_token_pins_catch_planted_mistakes():

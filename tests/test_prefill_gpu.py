@@ -1,0 +1,153 @@
+"""Parity of the causal prefill (gqa_prefill_ex through the C ABI) with the fp64
+CPU oracle, on an MI355X.
+
+Every token of a sequence is a query over its sequence's keys up to itself.  The
+HIP result is compared with oracle.gqa_prefill_f64 (or, at the 32K-token size,
+with oracle.gqa_prefill_rows_f64 on sampled tokens) under the same rules as the
+decode tests: fp32 results max |err| <= 2e-3 and relative L2 <= 1e-3; 16-bit
+results within one ulp of the nearest-even rounding of the oracle (or 1e-5).
+Outputs are NaN-poisoned before each call so an unwritten element fails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gqa_split_kv_amd import binding as B
+from gqa_split_kv_amd.inputs import PREFILL_32K, host_prefill_case
+
+from helpers import compare, upload
+
+pytestmark = pytest.mark.gpu
+
+_TORCH_DT = {"bf16": "bfloat16", "f16": "float16", "f32": "float32"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "these tests need an MI355X GPU"
+    B.lib()
+    yield
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _run(q, k, v, sl, scale, out_dtype=None, num_blocks=0):
+    import torch
+    out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    out.fill_(float("nan"))
+    B.prefill(q, k, v, sl, scale=scale, out=out, num_blocks=num_blocks)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("G,h_kv", [(8, 1), (4, 2), (1, 2), (16, 1), (3, 2), (2, 1)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("f16", "f16"), ("f16", "f32")])
+def test_prefill_heads_dims_dtypes(G, h_kv, d, dtype, out):
+    import torch
+    lens = [300, 1, 0, 77, 33]
+    c = host_prefill_case(len(lens), G * h_kv, h_kv, d, lens, dtype, seed=G * 13 + h_kv + d)
+    ref = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    q, k, v, sl = upload(c)
+    odt = getattr(torch, _TORCH_DT[out])
+    for nb in (0, 1, 5):
+        _say("prefill G", G, "h_kv", h_kv, "d", d, dtype, "->", out, "num_blocks", nb)
+        o = _run(q, k, v, sl, c.scale, odt, nb)
+        compare(o, ref, "prefill G=%d h_kv=%d d=%d %s->%s nb=%d" % (G, h_kv, d, dtype, out, nb))
+
+
+def test_prefill_longer_ragged_batch_and_grid_independence():
+    import torch
+    lens = [1500, 2, 700, 0, 1025]
+    c = host_prefill_case(len(lens), 16, 2, 128, lens, "bf16", seed=21)
+    ref = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    q, k, v, sl = upload(c)
+    outs = []
+    for nb in (0, 3, 64, 4096):
+        _say("prefill ragged, num_blocks", nb)
+        o = _run(q, k, v, sl, c.scale, torch.float32, nb)
+        compare(o, ref, "ragged nb=%d" % nb)
+        outs.append(o)
+    # every row is computed by one workgroup in a fixed order: the grid size does
+    # not change a single bit
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_prefill_peaked_keys():
+    import torch
+    lens = [2048, 600]
+    c = host_prefill_case(2, 8, 1, 128, lens, "bf16", seed=23, peaked_frac=0.01, peak_factor=8.0)
+    ref = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    q, k, v, sl = upload(c)
+    o = _run(q, k, v, sl, c.scale, torch.float32)
+    compare(o, ref, "peaked")
+
+
+def test_prefill_empty_and_single_token_sequences():
+    import torch
+    lens = [0, 1, 0, 1, 2]
+    c = host_prefill_case(len(lens), 8, 2, 64, lens, "bf16", seed=24)
+    ref = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    q, k, v, sl = upload(c)
+    o = _run(q, k, v, sl, c.scale, torch.float32)
+    compare(o, ref, "tiny")
+
+
+def test_prefill_32k_single_kv_group_sampled_rows():
+    """The long-context prefill panel at full size: 32768 tokens, h_q 8, h_kv 1,
+    d 128, bf16; sampled tokens (tile edges, both ends, random) against the oracle
+    one token at a time, plus finiteness of every output."""
+    import torch
+    w = PREFILL_32K
+    c = host_prefill_case(w.batch, w.h_q, w.h_kv, w.d, w.seq_lens(), w.dtype, seed=w.seed)
+    q, k, v, sl = upload(c)
+    _say("prefill 32K: bf16 and fp32 outputs")
+    o16 = _run(q, k, v, sl, c.scale)
+    o32 = _run(q, k, v, sl, c.scale, torch.float32)
+    assert torch.isfinite(o32).all().item() and torch.isfinite(o16.float()).all().item()
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, 1, 31, 32, 33, 1023, 1024, 4095, 16383, 16384, 32735, 32736, 32766, 32767] +
+                      list(rng.integers(0, 32768, size=18))))
+    _say("oracle on", len(rows), "sampled tokens")
+    ref = oracle.gqa_prefill_rows_f64(c.q, c.k, c.v, c.seq_lens, c.scale, rows)
+    idx = torch.tensor(rows, device=o32.device)
+    compare(o32.index_select(0, idx), ref, "32K fp32 rows")
+    compare(o16.index_select(0, idx), ref, "32K bf16 rows")
+
+
+def test_prefill_invalid_arguments_leave_output_untouched():
+    import torch
+    c = host_prefill_case(2, 8, 2, 64, [5, 7], "bf16", seed=25)
+    q, k, v, sl = upload(c)
+    out = torch.full(q.shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    a = B.make_prefill_args(q, k, v, out, sl, 2, 8, 2, 64, c.scale, B.GQA_DTYPE_F32, B.GQA_DTYPE_F32)
+    assert B.gqa_prefill_validate(a) == B.GQA_ERR_UNSUPPORTED
+    with pytest.raises(B.GqaError):
+        B.gqa_prefill_ex(a)
+    a = B.make_prefill_args(q, k, v, out, sl, 2, 8, 2, 96, c.scale, B.GQA_DTYPE_BF16, B.GQA_DTYPE_BF16)
+    with pytest.raises(B.GqaError):
+        B.gqa_prefill_ex(a)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all().item()
+
+
+def test_prefill_c_names():
+    import torch
+    c = host_prefill_case(2, 8, 2, 128, [100, 40], "bf16", seed=26)
+    ref = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    q, k, v, sl = upload(c)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.gqa_prefill(q, k, v, out, sl, 2, 8, 2, 128, c.scale)
+    torch.cuda.synchronize()
+    compare(out, ref, "gqa_prefill")
+    c16 = host_prefill_case(2, 8, 2, 128, [100, 40], "f16", seed=26)
+    ref16 = oracle.gqa_prefill_f64(c16.q, c16.k, c16.v, c16.seq_lens, c16.scale)
+    q, k, v, sl = upload(c16)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float16, device="cuda")
+    B.gqa_prefill_f16(q, k, v, out, sl, 2, 8, 2, 128, c16.scale)
+    torch.cuda.synchronize()
+    compare(out, ref16, "gqa_prefill_f16")
