@@ -28,9 +28,16 @@ constexpr int kMergeThreadsWide = 1024;
 constexpr int kMergeSliceQuads = 8;
 constexpr int kWideMergePieces = 32;   // expected pieces per sequence above which the merge is wide
 constexpr int kSplitMergeBelowBlocks = 256;
-// Prefill kernel: 4-wavefront workgroups owning 256 rows (256 / G tokens x G heads).
-constexpr int kPrefillThreads = 256;
-constexpr int kPrefillRows = 256;
+// Prefill kernel: workgroups of GQA_PREFILL_THREADS threads owning GQA_PREFILL_ROWS
+// rows (GQA_PREFILL_ROWS / G tokens x G heads), 32 rows per wavefront.
+#ifndef GQA_PREFILL_THREADS
+#define GQA_PREFILL_THREADS 512
+#endif
+#ifndef GQA_PREFILL_ROWS
+#define GQA_PREFILL_ROWS 256
+#endif
+constexpr int kPrefillThreads = GQA_PREFILL_THREADS;
+constexpr int kPrefillRows = GQA_PREFILL_ROWS;
 constexpr int kMaxG = 16;           // rows (query heads x query tokens) per kv head in one 16-wide MFMA tile
 constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxPrefillBlocks = 1 << 20;

@@ -49,9 +49,9 @@ constexpr int kBf16 = 0;
 constexpr int kF32 = 1;
 constexpr int kF16 = 2;
 
-constexpr int kWavesP = kPrefillThreads / kWave;   // 4
-constexpr int kNT = 4;                             // 16-row N tiles per wavefront
-constexpr int kRowsPerWave = 16 * kNT;             // 64
+constexpr int kWavesP = kPrefillThreads / kWave;   // 8
+constexpr int kNT = kPrefillRows / kWavesP / 16;   // 16-row N tiles per wavefront (2)
+constexpr int kRowsPerWave = 16 * kNT;             // 32
 constexpr int kStepKeys = 32;                      // keys per LDS stage
 constexpr float kLagLog2 = 8.f;                    // allowed lag of the running maximum
 static_assert(kWavesP * kRowsPerWave == kPrefillRows, "tile rows");
@@ -131,19 +131,30 @@ template <int kIn, int kOut, int D>
 struct PrefillTile {
     static constexpr bool kHalf = kIn == kF16;
     static constexpr int ROWB = D * 2;              // bytes of one key row of one kv head
-    static constexpr int LROW = ROWB + 16;          // LDS row pitch (16-byte skew between rows)
+    static constexpr int LROW = ROWB;               // LDS row pitch (chunks swizzled, see swz)
     static constexpr int NKP = ROWB / 64;           // 16-byte K pieces per lane per 16-key block
     static constexpr int VEC = D / 16;              // d elements per lane per V row
     static constexpr int VW = VEC / 2;              // 32-bit words per lane per V row
     static constexpr int CH = ROWB / 16;            // 16-byte chunks per key row
-    static constexpr int kPer = kStepKeys * CH / kPrefillThreads;   // chunks per thread (K and V each)
+    static constexpr int kChunks = kStepKeys * CH;  // 16-byte chunks of a K (or V) tile
+    static constexpr int kPer = (kChunks + kPrefillThreads - 1) / kPrefillThreads;   // per thread
     static constexpr int kOff = kHalf ? 7 : 0;      // exponent offset of P
     static constexpr int kTileBytes = kStepKeys * LROW;
-    static_assert(kPer * kPrefillThreads == kStepKeys * CH, "tile load split");
 
-    // One step: S^T = K Q^T for the four N tiles, masked online softmax with the
-    // lagging maximum, then O^T += V^T P^T.
+    // LDS layout of a K or V tile: key row r at r * LROW, its 16-byte chunk c at
+    // chunk position c ^ swz(r).  The K operand reads hit rows {0-3, 8-11, 16-19,
+    // 24-27} (+4 for the second block) in one instruction, the V reads 8 chunks of
+    // one row; the swizzle spreads both over distinct banks.
+    __device__ __forceinline__ static int swz(int r) { return ((r & 3) | ((r >> 1) & 12)) & (CH - 1); }
+
+    // One step: S^T = K Q^T for the N tiles, online softmax with the lagging
+    // maximum, then O^T += V^T P^T.  kDiag: some key of the step lies beyond some
+    // row's causal limit, so scores are masked (chosen per wavefront and step;
+    // off the diagonal no row needs it).  sl2 > 0 (a negative scale is folded
+    // into Q).
+    template <bool kDiag>
     __device__ __forceinline__ static void step(const uint8_t *Kt, const uint8_t *Vt, int k0,
+                                                const uint32_t (&koff)[2][NKP], const uint32_t (&voff)[8],
                                                 const uint4 (&qop)[kNT][NKP], const int (&cap)[kNT],
                                                 float sl2, float (&m_ref)[kNT], float (&l_run)[kNT],
                                                 f32x4_t (&acc)[kNT][VEC]) {
@@ -154,29 +165,32 @@ struct PrefillTile {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int p = 0; p < NKP; ++p)
-                kop[b][p] = *reinterpret_cast<const uint4 *>(Kt + (8 * (m >> 2) + 4 * b + (m & 3)) * LROW +
-                                                             64 * p + 16 * kg);
+            for (int p = 0; p < NKP; ++p) kop[b][p] = *reinterpret_cast<const uint4 *>(Kt + koff[b][p]);
         uint4 bhi[kNT], blo[kNT];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
-            float sv[8];
+            float sv[8];   // raw scores q.k of keys k0 + 8kg + i
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p = 0; p < NKP; ++p) s = mfma16<kHalf>(kop[b][p], qop[nt][p], s);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int key = k0 + 8 * kg + 4 * b + q;
-                    sv[4 * b + q] = key < cap[nt] ? s[q] * sl2 : -INFINITY;
-                }
+                for (int q = 0; q < 4; ++q) sv[4 * b + q] = s[q];
             }
-            float mx = sv[0];
+            const int lim = cap[nt] - (k0 + 8 * kg);   // keys i < lim are visible
+            float mx;
+            if constexpr (kDiag) {
+                mx = -INFINITY;
 #pragma unroll
-            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+                for (int i = 0; i < 8; ++i) mx = i < lim ? fmaxf(mx, sv[i]) : mx;
+            } else {
+                mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                           fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = mx == -INFINITY ? -INFINITY : mx * sl2;   // scaled, log2 units
             // Move the reference only when a row's maximum passes it by more than the
             // allowed lag (wave-uniform branch; rows that did not ask follow along).
             if (__ballot(mx > m_ref[nt] + kLagLog2)) {
@@ -187,16 +201,15 @@ struct PrefillTile {
                 for (int c = 0; c < VEC; ++c) acc[nt][c] *= alpha;
                 m_ref[nt] = m_new;
             }
-            // A row that has seen no key yet keeps the reference -inf: exponentiate
-            // against 0 so its masked scores give weight 0, not NaN.
-            const float mu = m_ref[nt] == -INFINITY ? 0.f : m_ref[nt];
-            float sum = 0.f;
+            // p = 2^(s*sl2 - m_ref + kOff); a row with no visible key yet keeps the
+            // reference -inf and takes 0 in its place (its weights are masked to 0).
+            const float nmu = static_cast<float>(kOff) - (m_ref[nt] == -INFINITY ? 0.f : m_ref[nt]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                sv[i] = __builtin_amdgcn_exp2f(sv[i] - mu + static_cast<float>(kOff));
-                sum += sv[i];
+                sv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], sl2, nmu));
+                if constexpr (kDiag) sv[i] = i < lim ? sv[i] : 0.f;
             }
-            l_run[nt] += sum;
+            l_run[nt] += ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
             uint32_t phi[4], plo[4];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -220,7 +233,7 @@ struct PrefillTile {
         uint32_t vr[8][VW];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint8_t *src = Vt + (8 * kg + i) * LROW + m * VEC * 2;
+            const uint8_t *src = Vt + voff[i];
             if constexpr (VW == 4) {
                 const uint4 x = *reinterpret_cast<const uint4 *>(src);
                 vr[i][0] = x.x;
@@ -256,7 +269,7 @@ struct PrefillTile {
     __device__ __forceinline__ static void run(const PrefillParams &P, uint8_t (*lds)[2][kTileBytes], int64_t off,
                                                int len, int j, int tile) {
         const int tid = static_cast<int>(threadIdx.x);
-        const int wave = tid / kWave;
+        const int wave = uniform32(tid / kWave);
         const int lane = lane_id();
         const int m = lane & 15;
         const int kg = lane >> 4;
@@ -265,6 +278,9 @@ struct PrefillTile {
         const int tstart = tile * tt;
         const int tcount = min(tt, len - tstart);         // > 0
         const int rowstride = P.h_kv * ROWB;
+
+        const uint32_t qflip = P.scale_log2 < 0.f ? 0x80008000u : 0u;
+        const float sl2 = fabsf(P.scale_log2);
 
         // The lane's rows: row = 64 wave + 16 nt + m -> (token, head) = (row / G, row % G).
         int cap[kNT];
@@ -281,8 +297,13 @@ struct PrefillTile {
             const uint8_t *qrow = P.q + orow[nt] * ROWB + 16 * kg;
 #pragma unroll
             for (int p = 0; p < NKP; ++p) {
-                qop[nt][p] = *reinterpret_cast<const uint4 *>(qrow + 64 * p);
-                if (!active) qop[nt][p] = make_uint4(0, 0, 0, 0);
+                uint4 x = *reinterpret_cast<const uint4 *>(qrow + 64 * p);
+                // A negative scale: negate q (exact) so the kernel scales by |scale|.
+                x.x ^= qflip;
+                x.y ^= qflip;
+                x.z ^= qflip;
+                x.w ^= qflip;
+                qop[nt][p] = active ? x : make_uint4(0, 0, 0, 0);
             }
         }
         const int wtok_lo = (wave * kRowsPerWave) / G;
@@ -293,14 +314,34 @@ struct PrefillTile {
         const uint8_t *kbase = P.k + (off * P.h_kv + j) * ROWB;
         const uint8_t *vbase = P.v + (off * P.h_kv + j) * ROWB;
 
+        // Chunk c of a tile: key row c / CH, bytes 16 (c % CH).  With fewer chunks
+        // than threads (d_head 64) the extra threads load nothing.
         uint32_t goff[kPer], loff[kPer];
+        bool cok[kPer];
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int c = tid + i * kPrefillThreads;
-            const int r = c / CH;
-            const int col = c - r * CH;
+            cok[i] = c < kChunks;
+            const int r = (cok[i] ? c : 0) / CH;
+            const int col = (cok[i] ? c : 0) - r * CH;
             goff[i] = static_cast<uint32_t>(r * rowstride + col * 16);
-            loff[i] = static_cast<uint32_t>(r * LROW + col * 16);
+            loff[i] = static_cast<uint32_t>(r * LROW + (col ^ swz(r)) * 16);
+        }
+        // Per-lane LDS offsets of the step's operands (fixed for the whole tile):
+        // K operand of block b, piece p: row 8(m/4) + 4b + m%4, chunk 4p + kg;
+        // V: row 8kg + i, elements [VEC m, VEC m + VEC) (chunk VEC m / 8).
+        uint32_t koff[2][NKP], voff[8];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int r = 8 * (m >> 2) + 4 * b + (m & 3);
+#pragma unroll
+            for (int p = 0; p < NKP; ++p) koff[b][p] = static_cast<uint32_t>(r * LROW + ((4 * p + kg) ^ swz(r)) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * kg + i;
+            const int byte = m * VEC * 2;   // 16 (d 128) or 8 (d 64) bytes per lane
+            voff[i] = static_cast<uint32_t>(r * LROW + (((byte >> 4) ^ swz(r)) << 4) + (byte & 15));
         }
         uint4 rk[kPer], rv[kPer];
         auto fetch = [&](int st) {
@@ -318,8 +359,10 @@ struct PrefillTile {
         auto stash = [&](int buf) {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
-                *reinterpret_cast<uint4 *>(lds[buf][0] + loff[i]) = rk[i];
-                *reinterpret_cast<uint4 *>(lds[buf][1] + loff[i]) = rv[i];
+                if (cok[i]) {
+                    *reinterpret_cast<uint4 *>(lds[buf][0] + loff[i]) = rk[i];
+                    *reinterpret_cast<uint4 *>(lds[buf][1] + loff[i]) = rv[i];
+                }
             }
         };
 
@@ -332,15 +375,29 @@ struct PrefillTile {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) acc[nt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        const float sl2 = P.scale_log2;
         fetch(0);
         stash(0);
         __syncthreads();
-        for (int st = 0; st < nsteps; ++st) {
+        // Steps whose keys every row of the tile sees (below the tile's first
+        // token) run unmasked; the rest -- the tile's diagonal band -- masked, each
+        // wavefront skipping the steps beyond its own last token.  Two loops, so
+        // the unmasked one carries no masking code at all.
+        const int nfull = min(nsteps, (tstart + 1) / kStepKeys);
+        int st = 0;
+        for (; st < nfull; ++st) {
             const bool more = st + 1 < nsteps;
             if (more) fetch(st + 1);
-            if (st * kStepKeys < wkeys)
-                step(lds[st & 1][0], lds[st & 1][1], st * kStepKeys, qop, cap, sl2, m_ref, l_run, acc);
+            step<false>(lds[st & 1][0], lds[st & 1][1], st * kStepKeys, koff, voff, qop, cap, sl2, m_ref, l_run,
+                        acc);
+            if (more) stash((st + 1) & 1);
+            __syncthreads();
+        }
+        for (; st < nsteps; ++st) {
+            const bool more = st + 1 < nsteps;
+            if (more) fetch(st + 1);
+            const int k0 = st * kStepKeys;
+            if (k0 < wkeys)
+                step<true>(lds[st & 1][0], lds[st & 1][1], k0, koff, voff, qop, cap, sl2, m_ref, l_run, acc);
             if (more) stash((st + 1) & 1);
             __syncthreads();
         }
