@@ -83,6 +83,7 @@ class GqaPrefillArgs(ctypes.Structure):
         ("d_head", ctypes.c_int32), ("scale", ctypes.c_float),
         ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("num_blocks", ctypes.c_int32), ("stream", ctypes.c_void_p),
+        ("split_pv", ctypes.c_int32),
     ]
 
 
@@ -312,7 +313,7 @@ def gqa_prefill_f16(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_hea
 
 
 def make_prefill_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, in_dtype, out_dtype,
-                      num_blocks=0, stream=0) -> GqaPrefillArgs:
+                      num_blocks=0, stream=0, split_pv=0) -> GqaPrefillArgs:
     a = GqaPrefillArgs()
     a.q, a.k, a.v, a.o, a.seq_lens = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens)
     a.batch, a.h_q, a.h_kv, a.d_head = int(batch), int(h_q), int(h_kv), int(d_head)
@@ -320,6 +321,7 @@ def make_prefill_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, in_
     a.in_dtype, a.out_dtype = int(in_dtype), int(out_dtype)
     a.num_blocks = int(num_blocks)
     a.stream = stream
+    a.split_pv = int(split_pv)
     return a
 
 
@@ -335,7 +337,7 @@ def gqa_prefill_validate(args: GqaPrefillArgs) -> int:
 
 
 def prefill(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype=None,
-            num_blocks: int = 0, stream=None):
+            num_blocks: int = 0, stream=None, split_pv: int = 0):
     """o = causal GQA prefill of q [sum(seq_lens), h_q, d] against k, v
     [sum(seq_lens), h_kv, d] (each token sees its sequence's keys up to itself).
     seq_lens is an int32 device tensor.  Returns `out`."""
@@ -350,7 +352,7 @@ def prefill(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtyp
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     args = make_prefill_args(q, k, v, out, seq_lens, batch, h_q, h_kv, d, scale, _dtype_code(q),
-                             _dtype_code(out), num_blocks, _stream(stream))
+                             _dtype_code(out), num_blocks, _stream(stream), split_pv)
     gqa_prefill_ex(args)
     return out
 

@@ -173,6 +173,7 @@ int prefill_ex(const gqa_prefill_args *a) {
     P.h_kv = a->h_kv;
     P.G = a->h_q / a->h_kv;
     P.scale_log2 = static_cast<float>(static_cast<double>(a->scale) * 1.4426950408889634074);
+    P.split_pv = a->split_pv;
     e = gqa::launch_prefill(P, a->in_dtype, a->out_dtype, a->d_head, blocks,
                             reinterpret_cast<hipStream_t>(a->stream));
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "prefill kernel launch failed: %s", hipGetErrorString(e));

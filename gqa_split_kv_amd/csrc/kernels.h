@@ -48,6 +48,7 @@ struct PrefillParams {
     const int32_t *seq_lens;   // [batch]
     int32_t batch, h_q, h_kv, G;
     float scale_log2;          // scale * log2(e)
+    int32_t split_pv;          // 1: split P V products everywhere
 };
 
 // Enqueues the prefill kernel: `blocks` workgroups of kPrefillThreads.

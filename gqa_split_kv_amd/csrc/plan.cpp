@@ -145,6 +145,7 @@ int validate_prefill(const gqa_prefill_args *a) {
     if (!std::isfinite(a->scale)) return fail(GQA_ERR_SCALE, "scale is not finite");
     if (a->num_blocks < 0 || a->num_blocks > kMaxPrefillBlocks)
         return fail(GQA_ERR_ARG, "num_blocks %d out of range [0, %d]", a->num_blocks, kMaxPrefillBlocks);
+    if (a->split_pv != 0 && a->split_pv != 1) return fail(GQA_ERR_ARG, "split_pv %d is not 0 or 1", a->split_pv);
     return GQA_OK;
 }
 

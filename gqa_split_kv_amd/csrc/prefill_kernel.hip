@@ -17,19 +17,26 @@
 //     one barrier per step, the next tile's loads in flight during the current
 //     step) and are shared by all 256 rows, so the K/V bytes per output row
 //     fall with the tile height.
-//   * Each wavefront owns 64 rows as four 16-row N tiles of
+//   * Each wavefront owns 32 rows as two 16-row N tiles of
 //     v_mfma_f32_16x16x32_{bf16,f16}: S^T = K Q^T with the keys on the M axis
 //     (the K rows are read from LDS in the key order that leaves lane l holding
-//     keys 8*(l/16) .. +7 of its row), then O^T += V^T P^T with P split into a
-//     high and a low 16-bit part (two products; about 16 significant bits of P
-//     for bf16, 22 for fp16).  The V^T operand is rebuilt from LDS rows once per
-//     step and reused by the four N tiles.
+//     keys 8*(l/16) .. +7 of its row), then O^T += V^T P^T and l += 1^T P^T (the
+//     row sums come out of the matrix core, from the same rounded P).  The V^T
+//     operand is rebuilt from LDS rows once per step and reused by both N tiles.
+//     Two wavefronts share a SIMD (at most 256 VGPRs each, no AGPR traffic).
+//   * P V precision: by default P is rounded to fp16 and V read as fp16 (bf16 V
+//     is converted while the tile is staged: exact for magnitudes in fp16's
+//     normal range), one product per step.  A bf16 tile whose largest |v| is not
+//     in [2^-10, 2^16) sends the rest of the tile's sweep to the split product
+//     (P as a high and a low part in the input format, V as given, two
+//     products), which the diagonal band always uses and which the caller can
+//     ask for everywhere.
 //   * The running maximum is allowed to lag the true one by up to 8 (log2
 //     units): the accumulators are rescaled only when some row of an N tile
 //     exceeds its reference by more, which removes almost every rescale of the
-//     128 accumulators per lane.  Weights are then at most 2^8 (times 2^7 for
-//     fp16, to keep small weights inside its exponent range), and the common
-//     factor cancels in O / l.
+//     accumulators.  Weights are then at most 2^(8+7) (the 2^7 keeps small
+//     weights inside fp16's exponent range), and the common factor cancels in
+//     O / l.
 //   * Tiles are handed out in a fixed snake order over a persistent grid: the
 //     tiles of a (sequence, kv head) are enumerated last token first (longest
 //     first), and workgroup w takes tiles w, 2g-1-w, 2g+w, ... (g = grid size),
@@ -138,8 +145,14 @@ struct PrefillTile {
     static constexpr int CH = ROWB / 16;            // 16-byte chunks per key row
     static constexpr int kChunks = kStepKeys * CH;  // 16-byte chunks of a K (or V) tile
     static constexpr int kPer = (kChunks + kPrefillThreads - 1) / kPrefillThreads;   // per thread
-    static constexpr int kOff = kHalf ? 7 : 0;      // exponent offset of P
+    static constexpr int kOff = 7;                  // exponent offset of P: p <= 2^(8 + 7)
     static constexpr int kTileBytes = kStepKeys * LROW;
+    // LDS regions of a stage: K, V in fp16 (the fast P V operand) and, for bf16
+    // input, V as given (the exact fallback's operand).
+    static constexpr int kRegions = kHalf ? 2 : 3;
+    static constexpr int kK = 0, kV16 = 1, kVraw = kHalf ? 1 : 2;
+    static constexpr uint32_t kOnesF16 = 0x3c003c00u;
+    static constexpr uint32_t kOnesIn = kHalf ? 0x3c003c00u : 0x3f803f80u;
 
     // LDS layout of a K or V tile: key row r at r * LROW, its 16-byte chunk c at
     // chunk position c ^ swz(r).  The K operand reads hit rows {0-3, 8-11, 16-19,
@@ -147,46 +160,66 @@ struct PrefillTile {
     // one row; the swizzle spreads both over distinct banks.
     __device__ __forceinline__ static int swz(int r) { return ((r & 3) | ((r >> 1) & 12)) & (CH - 1); }
 
+    // bf16 -> fp16 of two packed values (exact inside fp16's range: bf16's 8-bit
+    // significand fits in fp16's 11).
+    __device__ __forceinline__ static uint32_t bf16x2_to_f16x2(uint32_t w) {
+        const f32x2_t f = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+    }
+    // Range tests on the magnitude bits t of two packed bf16 (t = w & 0x7fff7fff):
+    // a half >= x carries into its bit 15 when 0x8000 - x is added.
+    //   >= 2^16 (0x4780): the value would overflow fp16;
+    //   >= 2^-10 (0x3a80): the tile's largest value keeps ~14 significant bits in
+    //   fp16 even where smaller values fall into fp16's subnormals.
+    __device__ __forceinline__ static uint32_t at_least_2p16(uint32_t t) { return (t + 0x38803880u) & 0x80008000u; }
+    __device__ __forceinline__ static uint32_t at_least_2m10(uint32_t t) { return (t + 0x45804580u) & 0x80008000u; }
+
     // One step: S^T = K Q^T for the N tiles, online softmax with the lagging
-    // maximum, then O^T += V^T P^T.  kDiag: some key of the step lies beyond some
-    // row's causal limit, so scores are masked (chosen per wavefront and step;
-    // off the diagonal no row needs it).  sl2 > 0 (a negative scale is folded
-    // into Q).
-    template <bool kDiag>
+    // maximum, then O^T += V^T P^T and l += 1^T P^T (the row sums from the same
+    // rounded P as the product).
+    //   kDiag   some key of the step lies beyond some row's causal limit: mask
+    //           (chosen per wavefront and step; off the diagonal no row needs it).
+    //   kSplit  P in the input's 16-bit format as a high and a low part (two
+    //           products, V as given); otherwise P in fp16 (one product) against
+    //           V converted to fp16.
+    // sl2 > 0 (a negative scale is folded into Q).
+    template <bool kDiag, bool kSplit>
     __device__ __forceinline__ static void step(const uint8_t *Kt, const uint8_t *Vt, int k0,
                                                 const uint32_t (&koff)[2][NKP], const uint32_t (&voff)[8],
                                                 const uint4 (&qop)[kNT][NKP], const int (&cap)[kNT],
-                                                float sl2, float (&m_ref)[kNT], float (&l_run)[kNT],
+                                                float sl2, float (&m_ref)[kNT], f32x4_t (&accl)[kNT],
                                                 f32x4_t (&acc)[kNT][VEC]) {
+        constexpr bool kPvHalf = kSplit ? kHalf : true;   // element type of the P V product
         const int lane = lane_id();
-        const int m = lane & 15;
         const int kg = lane >> 4;
         uint4 kop[2][NKP];
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int p = 0; p < NKP; ++p) kop[b][p] = *reinterpret_cast<const uint4 *>(Kt + koff[b][p]);
-        uint4 bhi[kNT], blo[kNT];
+        float sv[kNT][8];   // raw scores q.k of keys k0 + 8kg + i
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            float sv[8];   // raw scores q.k of keys k0 + 8kg + i
+        for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p = 0; p < NKP; ++p) s = mfma16<kHalf>(kop[b][p], qop[nt][p], s);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) sv[4 * b + q] = s[q];
+                for (int q = 0; q < 4; ++q) sv[nt][4 * b + q] = s[q];
             }
+        uint4 bhi[kNT], blo[kNT];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
             const int lim = cap[nt] - (k0 + 8 * kg);   // keys i < lim are visible
             float mx;
             if constexpr (kDiag) {
                 mx = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) mx = i < lim ? fmaxf(mx, sv[i]) : mx;
+                for (int i = 0; i < 8; ++i) mx = i < lim ? fmaxf(mx, sv[nt][i]) : mx;
             } else {
-                mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                           fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+                mx = fmaxf(fmaxf(fmaxf(sv[nt][0], sv[nt][1]), fmaxf(sv[nt][2], sv[nt][3])),
+                           fmaxf(fmaxf(sv[nt][4], sv[nt][5]), fmaxf(sv[nt][6], sv[nt][7])));
             }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -196,7 +229,7 @@ struct PrefillTile {
             if (__ballot(mx > m_ref[nt] + kLagLog2)) {
                 const float m_new = fmaxf(m_ref[nt], mx);
                 const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref[nt] - m_new);
-                l_run[nt] *= alpha;
+                accl[nt] *= alpha;
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) acc[nt][c] *= alpha;
                 m_ref[nt] = m_new;
@@ -204,21 +237,23 @@ struct PrefillTile {
             // p = 2^(s*sl2 - m_ref + kOff); a row with no visible key yet keeps the
             // reference -inf and takes 0 in its place (its weights are masked to 0).
             const float nmu = static_cast<float>(kOff) - (m_ref[nt] == -INFINITY ? 0.f : m_ref[nt]);
+            float pv[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                sv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], sl2, nmu));
-                if constexpr (kDiag) sv[i] = i < lim ? sv[i] : 0.f;
+                pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][i], sl2, nmu));
+                if constexpr (kDiag) pv[i] = i < lim ? pv[i] : 0.f;
             }
-            l_run[nt] += ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
             uint32_t phi[4], plo[4];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const f32x2_t pw = {sv[2 * w], sv[2 * w + 1]};
-                if constexpr (kHalf) {
+                const f32x2_t pw = {pv[2 * w], pv[2 * w + 1]};
+                if constexpr (kPvHalf) {
                     const f16x2_t h = __builtin_convertvector(pw, f16x2_t);
-                    const f32x2_t hf = __builtin_convertvector(h, f32x2_t);
                     phi[w] = __builtin_bit_cast(uint32_t, h);
-                    plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw - hf, f16x2_t));
+                    if constexpr (kSplit) {
+                        const f32x2_t hf = __builtin_convertvector(h, f32x2_t);
+                        plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw - hf, f16x2_t));
+                    }
                 } else {
                     const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw, bf16x2_t));
                     const f32x2_t r = {pw[0] - __uint_as_float(hb << 16), pw[1] - __uint_as_float(hb & 0xffff0000u)};
@@ -227,7 +262,7 @@ struct PrefillTile {
                 }
             }
             bhi[nt] = make_uint4(phi[0], phi[1], phi[2], phi[3]);
-            blo[nt] = make_uint4(plo[0], plo[1], plo[2], plo[3]);
+            if constexpr (kSplit) blo[nt] = make_uint4(plo[0], plo[1], plo[2], plo[3]);
         }
         // V rows 8kg + i, elements [VEC*m, VEC*m + VEC).
         uint32_t vr[8][VW];
@@ -259,15 +294,22 @@ struct PrefillTile {
             const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
-                acc[nt][c] = mfma16<kHalf>(av, bhi[nt], acc[nt][c]);
-                acc[nt][c] = mfma16<kHalf>(av, blo[nt], acc[nt][c]);
+                acc[nt][c] = mfma16<kPvHalf>(av, bhi[nt], acc[nt][c]);
+                if constexpr (kSplit) acc[nt][c] = mfma16<kPvHalf>(av, blo[nt], acc[nt][c]);
             }
+        }
+        const uint32_t one = kPvHalf ? kOnesF16 : kOnesIn;
+        const uint4 ones = make_uint4(one, one, one, one);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            accl[nt] = mfma16<kPvHalf>(ones, bhi[nt], accl[nt]);
+            if constexpr (kSplit) accl[nt] = mfma16<kPvHalf>(ones, blo[nt], accl[nt]);
         }
     }
 
     // Tile `tile` of (sequence b at token offset off, length len; kv head j).
-    __device__ __forceinline__ static void run(const PrefillParams &P, uint8_t (*lds)[2][kTileBytes], int64_t off,
-                                               int len, int j, int tile) {
+    __device__ __forceinline__ static void run(const PrefillParams &P, uint8_t (*lds)[kRegions][kTileBytes],
+                                               int *flags, int64_t off, int len, int j, int tile) {
         const int tid = static_cast<int>(threadIdx.x);
         const int wave = uniform32(tid / kWave);
         const int lane = lane_id();
@@ -280,9 +322,10 @@ struct PrefillTile {
         const int rowstride = P.h_kv * ROWB;
 
         const uint32_t qflip = P.scale_log2 < 0.f ? 0x80008000u : 0u;
-        const float sl2 = fabsf(P.scale_log2);
+        // |scale| * log2 e, kept above 0 so that masked (-inf) scores stay -inf.
+        const float sl2 = fmaxf(fabsf(P.scale_log2), 1.17549435e-38f);
 
-        // The lane's rows: row = 64 wave + 16 nt + m -> (token, head) = (row / G, row % G).
+        // The lane's rows: row = 32 wave + 16 nt + m -> (token, head) = (row / G, row % G).
         int cap[kNT];
         uint4 qop[kNT][NKP];
         int64_t orow[kNT];
@@ -356,56 +399,101 @@ struct PrefillTile {
                 rv[i] = buffer_load16<0>(rsv, goff[i]);
             }
         };
-        auto stash = [&](int buf) {
+        // Stage tile st into buffer st & 1.  bf16 input: V is stored as given and
+        // converted to fp16, and the tile's range is recorded in flag slot st % 3:
+        // word 0 set if some |v| >= 2^16, word 1 set if some |v| >= 2^-10.  The fp16
+        // product is used only for tiles with word 0 clear and word 1 set; from the
+        // first other tile on, this tile's remaining steps take the exact path.
+        auto stash = [&](int st) {
+            uint8_t(*B)[kTileBytes] = lds[st & 1];
+            uint32_t big = 0, normal = 0;
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 if (cok[i]) {
-                    *reinterpret_cast<uint4 *>(lds[buf][0] + loff[i]) = rk[i];
-                    *reinterpret_cast<uint4 *>(lds[buf][1] + loff[i]) = rv[i];
+                    *reinterpret_cast<uint4 *>(B[kK] + loff[i]) = rk[i];
+                    *reinterpret_cast<uint4 *>(B[kVraw] + loff[i]) = rv[i];
+                    if constexpr (!kHalf) {
+                        const uint4 x = rv[i];
+                        const uint32_t t[4] = {x.x & 0x7fff7fffu, x.y & 0x7fff7fffu, x.z & 0x7fff7fffu,
+                                               x.w & 0x7fff7fffu};
+                        big |= at_least_2p16(t[0]) | at_least_2p16(t[1]) | at_least_2p16(t[2]) | at_least_2p16(t[3]);
+                        normal |= at_least_2m10(t[0]) | at_least_2m10(t[1]) | at_least_2m10(t[2]) |
+                                  at_least_2m10(t[3]);
+                        *reinterpret_cast<uint4 *>(B[kV16] + loff[i]) =
+                            make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
+                                       bf16x2_to_f16x2(x.w));
+                    }
                 }
             }
+            if constexpr (!kHalf) {
+                if (big) flags[2 * (st % 3)] = 1;
+                if (normal) flags[2 * (st % 3) + 1] = 1;
+            }
+        };
+        // Slot st % 3 is written while tile st is staged (step st - 1), read in step
+        // st and cleared in step st + 1 -- each separated from the next use by a
+        // barrier.
+        auto tile_fast = [&](int st) -> bool {
+            if constexpr (kHalf) return true;
+            else return uniform32(flags[2 * (st % 3)]) == 0 && uniform32(flags[2 * (st % 3) + 1]) != 0;
+        };
+        auto clear_flag = [&](int st) {
+            if constexpr (!kHalf)
+                if (tid == 0) {
+                    flags[2 * ((st + 2) % 3)] = 0;
+                    flags[2 * ((st + 2) % 3) + 1] = 0;
+                }
         };
 
-        float m_ref[kNT], l_run[kNT];
+        float m_ref[kNT];
+        f32x4_t accl[kNT];
         f32x4_t acc[kNT][VEC];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
             m_ref[nt] = -INFINITY;
-            l_run[nt] = 0.f;
+            accl[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < VEC; ++c) acc[nt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if constexpr (!kHalf) {
+            if (tid < 4) flags[tid] = 0;   // slots of tiles 0 and 1
+            __syncthreads();
         }
         fetch(0);
         stash(0);
         __syncthreads();
         // Steps whose keys every row of the tile sees (below the tile's first
-        // token) run unmasked; the rest -- the tile's diagonal band -- masked, each
-        // wavefront skipping the steps beyond its own last token.  Two loops, so
-        // the unmasked one carries no masking code at all.
+        // token) run unmasked with fp16 P V; the rest -- the tile's diagonal band,
+        // and everything from a tile whose V range does not suit fp16 on -- masked
+        // with the exact split product, each wavefront skipping the steps beyond its
+        // own last token.  Two loops, so the fast one carries no masking or fallback
+        // code at all.
         const int nfull = min(nsteps, (tstart + 1) / kStepKeys);
         int st = 0;
         for (; st < nfull; ++st) {
+            if (P.split_pv || !tile_fast(st)) break;   // the same for the whole workgroup
             const bool more = st + 1 < nsteps;
             if (more) fetch(st + 1);
-            step<false>(lds[st & 1][0], lds[st & 1][1], st * kStepKeys, koff, voff, qop, cap, sl2, m_ref, l_run,
-                        acc);
-            if (more) stash((st + 1) & 1);
+            clear_flag(st);
+            step<false, false>(lds[st & 1][kK], lds[st & 1][kV16], st * kStepKeys, koff, voff, qop, cap, sl2, m_ref,
+                               accl, acc);
+            if (more) stash(st + 1);
             __syncthreads();
         }
         for (; st < nsteps; ++st) {
             const bool more = st + 1 < nsteps;
             if (more) fetch(st + 1);
+            clear_flag(st);
             const int k0 = st * kStepKeys;
             if (k0 < wkeys)
-                step<true>(lds[st & 1][0], lds[st & 1][1], k0, koff, voff, qop, cap, sl2, m_ref, l_run, acc);
-            if (more) stash((st + 1) & 1);
+                step<true, true>(lds[st & 1][kK], lds[st & 1][kVraw], k0, koff, voff, qop, cap, sl2, m_ref, accl, acc);
+            if (more) stash(st + 1);
             __syncthreads();
         }
 
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
-            float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 16);
-            l_tot += __shfl_xor(l_tot, 32);
+            const float l_tot = accl[nt][0];   // every element of the ones product is the row sum
             const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
             float out[4 * VEC];
 #pragma unroll
@@ -421,7 +509,8 @@ struct PrefillTile {
 template <int kIn, int kOut, int D>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams P) {
     using T = PrefillTile<kIn, kOut, D>;
-    __shared__ __align__(16) uint8_t lds[2][2][T::kTileBytes];
+    __shared__ __align__(16) uint8_t lds[2][T::kRegions][T::kTileBytes];
+    __shared__ int flags[6];
     const int tt = kPrefillRows / P.G;
     const int64_t items = count_items(P.seq_lens, P.batch, tt, P.h_kv);
     const int64_t g = gridDim.x;
@@ -435,7 +524,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         const int ntile = static_cast<int>(tiles_of(len, tt));
         const int j = static_cast<int>(local / ntile);
         const int tile = ntile - 1 - static_cast<int>(local - static_cast<int64_t>(j) * ntile);   // longest first
-        T::run(P, lds, off, len, j, tile);
+        T::run(P, lds, flags, off, len, j, tile);
     }
 }
 

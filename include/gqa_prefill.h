@@ -49,6 +49,15 @@ extern "C" {
  *             tokens x G heads in a fixed order); 0 = one per resident slot
  *             (compute units x resident workgroups per compute unit).  Range
  *             0..2^20.  The result does not depend on it.
+ * split_pv    Precision of the P V product.  0 (default): P is rounded to fp16
+ *             (11 significant bits, times a common power of two that cancels) and
+ *             V taken in fp16, one matrix-core product; for bf16 input a 32-key
+ *             tile of V whose largest magnitude is not in [2^-10, 2^16) switches
+ *             the rest of that tile's sweep to the split product, so the fp16
+ *             rounding of V never loses range or precision.  Typical error
+ *             against the exact result: relative L2 ~1e-4.  1: P split into a
+ *             high and a low 16-bit part everywhere (about 16 significant bits,
+ *             two products, ~1.5x the matrix-core work); error ~1e-6.
  */
 typedef struct gqa_prefill_args {
     const void *q;
@@ -65,6 +74,7 @@ typedef struct gqa_prefill_args {
     int32_t out_dtype;  /* in_dtype or GQA_DTYPE_F32                        */
     int32_t num_blocks;
     void *stream;       /* hipStream_t; NULL = the null stream              */
+    int32_t split_pv;   /* 0 or 1, see above                                */
 } gqa_prefill_args;
 
 /* gqa_prefill -- bf16 q/k/v in, bf16 o out.  Returns a gqa_status. */
@@ -82,7 +92,7 @@ int gqa_prefill_ex(const gqa_prefill_args *args);
  * would return before enqueueing anything: GQA_ERR_NULL, GQA_ERR_SHAPE (batch,
  * h_q or h_kv <= 0, h_q not a multiple of h_kv), GQA_ERR_UNSUPPORTED (d_head, G,
  * h_kv above 65536 or the dtype pair), GQA_ERR_ALIGN, GQA_ERR_SCALE, GQA_ERR_ARG
- * (num_blocks out of range). */
+ * (num_blocks out of range, split_pv not 0 or 1). */
 int gqa_prefill_validate(const gqa_prefill_args *args);
 
 #ifdef __cplusplus

@@ -228,7 +228,9 @@ def test_prefill_validation(lib):
     assert _pvalidate(num_blocks=(1 << 20) + 1) == B.GQA_ERR_ARG
     assert _pvalidate(num_blocks=(1 << 20) + 1) == B.GQA_ERR_ARG and "num_blocks" in B.last_error_message()
     assert _pvalidate(num_blocks=1 << 20) == B.GQA_OK
+    assert _pvalidate(split_pv=1) == B.GQA_OK
+    assert _pvalidate(split_pv=2) == B.GQA_ERR_ARG and "split_pv" in B.last_error_message()
 
 
 def test_prefill_args_struct_size(lib):
-    assert ctypes.sizeof(B.GqaPrefillArgs) == 5 * 8 + 4 * 4 + 4 + 3 * 4 + 8
+    assert ctypes.sizeof(B.GqaPrefillArgs) == 5 * 8 + 4 * 4 + 4 + 3 * 4 + 8 + 8
