@@ -59,7 +59,10 @@ constexpr int kF16 = 2;
 constexpr int kWavesP = kPrefillThreads / kWave;   // 8
 constexpr int kNT = kPrefillRows / kWavesP / 16;   // 16-row N tiles per wavefront (2)
 constexpr int kRowsPerWave = 16 * kNT;             // 32
-constexpr int kStepKeys = 32;                      // keys per LDS stage
+#ifndef GQA_PREFILL_STEP_KEYS
+#define GQA_PREFILL_STEP_KEYS 64
+#endif
+constexpr int kStepKeys = GQA_PREFILL_STEP_KEYS;   // keys per LDS stage (a multiple of 32)
 constexpr float kLagLog2 = 8.f;                    // allowed lag of the running maximum
 static_assert(kWavesP * kRowsPerWave == kPrefillRows, "tile rows");
 
@@ -190,37 +193,44 @@ struct PrefillTile {
                                                 float sl2, float (&m_ref)[kNT], f32x4_t (&accl)[kNT],
                                                 f32x4_t (&acc)[kNT][VEC]) {
         constexpr bool kPvHalf = kSplit ? kHalf : true;   // element type of the P V product
+        constexpr int kH = kStepKeys / 32;                 // 32-key halves of the step
         const int lane = lane_id();
         const int kg = lane >> 4;
-        uint4 kop[2][NKP];
+        // S^T = K Q^T, half by half: lane holds keys k0 + 32h + 8kg + i of its rows.
+        float sv[kNT][kH][8];
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int h = 0; h < kH; ++h) {
+            uint4 kop[2][NKP];
 #pragma unroll
-            for (int p = 0; p < NKP; ++p) kop[b][p] = *reinterpret_cast<const uint4 *>(Kt + koff[b][p]);
-        float sv[kNT][8];   // raw scores q.k of keys k0 + 8kg + i
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
+                for (int p = 0; p < NKP; ++p)
+                    kop[b][p] = *reinterpret_cast<const uint4 *>(Kt + h * 32 * LROW + koff[b][p]);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-                for (int p = 0; p < NKP; ++p) s = mfma16<kHalf>(kop[b][p], qop[nt][p], s);
+                for (int b = 0; b < 2; ++b) {
+                    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int q = 0; q < 4; ++q) sv[nt][4 * b + q] = s[q];
-            }
-        uint4 bhi[kNT], blo[kNT];
+                    for (int p = 0; p < NKP; ++p) s = mfma16<kHalf>(kop[b][p], qop[nt][p], s);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) sv[nt][h][4 * b + q] = s[q];
+                }
+        }
+        uint4 bhi[kNT][kH], blo[kNT][kH];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
-            const int lim = cap[nt] - (k0 + 8 * kg);   // keys i < lim are visible
-            float mx;
-            if constexpr (kDiag) {
-                mx = -INFINITY;
+            const int lim = cap[nt] - (k0 + 8 * kg);   // key 32h + i is visible iff 32h + i < lim
+            float mx = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) mx = i < lim ? fmaxf(mx, sv[nt][i]) : mx;
-            } else {
-                mx = fmaxf(fmaxf(fmaxf(sv[nt][0], sv[nt][1]), fmaxf(sv[nt][2], sv[nt][3])),
-                           fmaxf(fmaxf(sv[nt][4], sv[nt][5]), fmaxf(sv[nt][6], sv[nt][7])));
-            }
+            for (int h = 0; h < kH; ++h)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if constexpr (kDiag)
+                        mx = 32 * h + i < lim ? fmaxf(mx, sv[nt][h][i]) : mx;
+                    else
+                        mx = fmaxf(mx, sv[nt][h][i]);
+                }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             mx = mx == -INFINITY ? -INFINITY : mx * sl2;   // scaled, log2 units
@@ -237,74 +247,82 @@ struct PrefillTile {
             // p = 2^(s*sl2 - m_ref + kOff); a row with no visible key yet keeps the
             // reference -inf and takes 0 in its place (its weights are masked to 0).
             const float nmu = static_cast<float>(kOff) - (m_ref[nt] == -INFINITY ? 0.f : m_ref[nt]);
-            float pv[8];
+#pragma unroll
+            for (int h = 0; h < kH; ++h) {
+                float pv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][h][i], sl2, nmu));
+                    if constexpr (kDiag) pv[i] = 32 * h + i < lim ? pv[i] : 0.f;
+                }
+                uint32_t phi[4], plo[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const f32x2_t pw = {pv[2 * w], pv[2 * w + 1]};
+                    if constexpr (kPvHalf) {
+                        const f16x2_t hv = __builtin_convertvector(pw, f16x2_t);
+                        phi[w] = __builtin_bit_cast(uint32_t, hv);
+                        if constexpr (kSplit) {
+                            const f32x2_t hf = __builtin_convertvector(hv, f32x2_t);
+                            plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw - hf, f16x2_t));
+                        }
+                    } else {
+                        const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw, bf16x2_t));
+                        const f32x2_t r = {pw[0] - __uint_as_float(hb << 16), pw[1] - __uint_as_float(hb & 0xffff0000u)};
+                        phi[w] = hb;
+                        plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+                    }
+                }
+                bhi[nt][h] = make_uint4(phi[0], phi[1], phi[2], phi[3]);
+                if constexpr (kSplit) blo[nt][h] = make_uint4(plo[0], plo[1], plo[2], plo[3]);
+            }
+        }
+        // O^T += V^T P^T per half: V rows 32h + 8kg + i, elements [VEC*m, VEC*m + VEC).
+#pragma unroll
+        for (int h = 0; h < kH; ++h) {
+            uint32_t vr[8][VW];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][i], sl2, nmu));
-                if constexpr (kDiag) pv[i] = i < lim ? pv[i] : 0.f;
-            }
-            uint32_t phi[4], plo[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const f32x2_t pw = {pv[2 * w], pv[2 * w + 1]};
-                if constexpr (kPvHalf) {
-                    const f16x2_t h = __builtin_convertvector(pw, f16x2_t);
-                    phi[w] = __builtin_bit_cast(uint32_t, h);
-                    if constexpr (kSplit) {
-                        const f32x2_t hf = __builtin_convertvector(h, f32x2_t);
-                        plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw - hf, f16x2_t));
-                    }
+                const uint8_t *src = Vt + h * 32 * LROW + voff[i];
+                if constexpr (VW == 4) {
+                    const uint4 x = *reinterpret_cast<const uint4 *>(src);
+                    vr[i][0] = x.x;
+                    vr[i][1] = x.y;
+                    vr[i][2] = x.z;
+                    vr[i][3] = x.w;
                 } else {
-                    const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw, bf16x2_t));
-                    const f32x2_t r = {pw[0] - __uint_as_float(hb << 16), pw[1] - __uint_as_float(hb & 0xffff0000u)};
-                    phi[w] = hb;
-                    plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+                    const uint2 x = *reinterpret_cast<const uint2 *>(src);
+                    vr[i][0] = x.x;
+                    vr[i][1] = x.y;
                 }
             }
-            bhi[nt] = make_uint4(phi[0], phi[1], phi[2], phi[3]);
-            if constexpr (kSplit) blo[nt] = make_uint4(plo[0], plo[1], plo[2], plo[3]);
-        }
-        // V rows 8kg + i, elements [VEC*m, VEC*m + VEC).
-        uint32_t vr[8][VW];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint8_t *src = Vt + voff[i];
-            if constexpr (VW == 4) {
-                const uint4 x = *reinterpret_cast<const uint4 *>(src);
-                vr[i][0] = x.x;
-                vr[i][1] = x.y;
-                vr[i][2] = x.z;
-                vr[i][3] = x.w;
-            } else {
-                const uint2 x = *reinterpret_cast<const uint2 *>(src);
-                vr[i][0] = x.x;
-                vr[i][1] = x.y;
-            }
-        }
+            for (int c = 0; c < VEC; ++c) {
+                // A operand of column c: element i = V[key 8kg + i][d = VEC*m + c].
+                // One byte permute per word: the low (even c) or high (odd c) halves
+                // of two rows' words, row 2w in the low half.
+                uint32_t a[4];
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) {
-            // A operand of column c: element i = V[key 8kg + i][d = VEC*m + c].
-            uint32_t a[4];
+                for (int w = 0; w < 4; ++w)
+                    a[w] = __builtin_amdgcn_perm(vr[2 * w + 1][c >> 1], vr[2 * w][c >> 1],
+                                                 (c & 1) ? 0x07060302u : 0x05040100u);
+                const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t x = vr[2 * w][c >> 1];
-                const uint32_t y = vr[2 * w + 1][c >> 1];
-                a[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-            }
-            const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                acc[nt][c] = mfma16<kPvHalf>(av, bhi[nt], acc[nt][c]);
-                if constexpr (kSplit) acc[nt][c] = mfma16<kPvHalf>(av, blo[nt], acc[nt][c]);
+                for (int nt = 0; nt < kNT; ++nt) {
+                    acc[nt][c] = mfma16<kPvHalf>(av, bhi[nt][h], acc[nt][c]);
+                    if constexpr (kSplit) acc[nt][c] = mfma16<kPvHalf>(av, blo[nt][h], acc[nt][c]);
+                }
             }
         }
         const uint32_t one = kPvHalf ? kOnesF16 : kOnesIn;
         const uint4 ones = make_uint4(one, one, one, one);
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            accl[nt] = mfma16<kPvHalf>(ones, bhi[nt], accl[nt]);
-            if constexpr (kSplit) accl[nt] = mfma16<kPvHalf>(ones, blo[nt], accl[nt]);
-        }
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+            for (int h = 0; h < kH; ++h) {
+                accl[nt] = mfma16<kPvHalf>(ones, bhi[nt][h], accl[nt]);
+                if constexpr (kSplit) accl[nt] = mfma16<kPvHalf>(ones, blo[nt][h], accl[nt]);
+            }
     }
 
     // Tile `tile` of (sequence b at token offset off, length len; kv head j).
