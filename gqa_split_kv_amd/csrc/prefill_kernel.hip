@@ -122,19 +122,13 @@ __device__ void locate_item(const int32_t *seq_lens, int batch, int tt, int h_kv
     local = 0;
 }
 
+// Stores 4 consecutive outputs, rounded to the output type.
 template <int kOut>
-__device__ __forceinline__ void store_out(uint8_t *dst, const float *x, int n) {
-    if constexpr (kOut == kF32) {
-        for (int i = 0; i < n; i += 4)
-            *reinterpret_cast<float4 *>(dst + 4 * i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
-    } else {
-        for (int i = 0; i < n; i += 8) {
-            uint32_t w[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) w[k] = pack2<kOut == kF16>(x[i + 2 * k], x[i + 2 * k + 1]);
-            *reinterpret_cast<uint4 *>(dst + 2 * i) = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-    }
+__device__ __forceinline__ void store4(uint8_t *dst, const float (&x)[4]) {
+    if constexpr (kOut == kF32)
+        *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+    else
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<kOut == kF16>(x[0], x[1]), pack2<kOut == kF16>(x[2], x[3]));
 }
 
 template <int kIn, int kOut, int D>
@@ -144,7 +138,6 @@ struct PrefillTile {
     static constexpr int LROW = ROWB;               // LDS row pitch (chunks swizzled, see swz)
     static constexpr int NKP = ROWB / 64;           // 16-byte K pieces per lane per 16-key block
     static constexpr int VEC = D / 16;              // d elements per lane per V row
-    static constexpr int VW = VEC / 2;              // 32-bit words per lane per V row
     static constexpr int CH = ROWB / 16;            // 16-byte chunks per key row
     static constexpr int kChunks = kStepKeys * CH;  // 16-byte chunks of a K (or V) tile
     static constexpr int kPer = (kChunks + kPrefillThreads - 1) / kPrefillThreads;   // per thread
@@ -158,10 +151,25 @@ struct PrefillTile {
     static constexpr uint32_t kOnesIn = kHalf ? 0x3c003c00u : 0x3f803f80u;
 
     // LDS layout of a K or V tile: key row r at r * LROW, its 16-byte chunk c at
-    // chunk position c ^ swz(r).  The K operand reads hit rows {0-3, 8-11, 16-19,
-    // 24-27} (+4 for the second block) in one instruction, the V reads 8 chunks of
-    // one row; the swizzle spreads both over distinct banks.
+    // chunk position c ^ swz(r) (K) or c ^ swzv(r) (V).  One K operand read hits
+    // rows {0-3, 8-11, 16-19, 24-27} (+4 for the second block) at one chunk; one
+    // transposed V read (see v_operand) hits 4 consecutive rows at 2 chunks.  The
+    // swizzles spread both over distinct banks.
     __device__ __forceinline__ static int swz(int r) { return ((r & 3) | ((r >> 1) & 12)) & (CH - 1); }
+    __device__ __forceinline__ static int swzv(int r) { return (2 * (r & 3)) & (CH - 1); }
+
+    // ds_read_b64_tr_b16: within each group of 16 lanes, lane l receives element
+    // l % 4 of the 8-byte blocks addressed by lanes 4e + (l % 16) / 4, e = 0..3
+    // (its elements e).  With lane 4e + q of group kg addressing V[key 8kg + 4t +
+    // e][d = 16c + 4q .. +3], lane (m, kg) receives V[8kg + 4t + e][16c + m]: two
+    // reads (t = 0, 1) give it the eight keys 8kg .. 8kg + 7 at d = 16c + m, the A
+    // operand of V^T P^T for the d block c, with no register shuffling.
+    __device__ __forceinline__ static uint2 lds_read_tr16(const uint8_t *p) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s *)(const_cast<uint8_t *>(p)));
+        return __builtin_bit_cast(uint2, r);
+    }
 
     // bf16 -> fp16 of two packed values (exact inside fp16's range: bf16's 8-bit
     // significand fits in fp16's 11).
@@ -188,7 +196,7 @@ struct PrefillTile {
     // sl2 > 0 (a negative scale is folded into Q).
     template <bool kDiag, bool kSplit>
     __device__ __forceinline__ static void step(const uint8_t *Kt, const uint8_t *Vt, int k0,
-                                                const uint32_t (&koff)[2][NKP], const uint32_t (&voff)[8],
+                                                const uint32_t (&koff)[2][NKP], const uint32_t (&voff)[4],
                                                 const uint4 (&qop)[kNT][NKP], const int (&cap)[kNT],
                                                 float sl2, float (&m_ref)[kNT], f32x4_t (&accl)[kNT],
                                                 f32x4_t (&acc)[kNT][VEC]) {
@@ -277,36 +285,16 @@ struct PrefillTile {
                 if constexpr (kSplit) blo[nt][h] = make_uint4(plo[0], plo[1], plo[2], plo[3]);
             }
         }
-        // O^T += V^T P^T per half: V rows 32h + 8kg + i, elements [VEC*m, VEC*m + VEC).
+        // O^T += V^T P^T per half and d block c (d = 16c + M): the A operand is
+        // read transposed from LDS (keys 32h + 8kg + i, d = 16c + m).
 #pragma unroll
         for (int h = 0; h < kH; ++h) {
-            uint32_t vr[8][VW];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint8_t *src = Vt + h * 32 * LROW + voff[i];
-                if constexpr (VW == 4) {
-                    const uint4 x = *reinterpret_cast<const uint4 *>(src);
-                    vr[i][0] = x.x;
-                    vr[i][1] = x.y;
-                    vr[i][2] = x.z;
-                    vr[i][3] = x.w;
-                } else {
-                    const uint2 x = *reinterpret_cast<const uint2 *>(src);
-                    vr[i][0] = x.x;
-                    vr[i][1] = x.y;
-                }
-            }
 #pragma unroll
             for (int c = 0; c < VEC; ++c) {
-                // A operand of column c: element i = V[key 8kg + i][d = VEC*m + c].
-                // One byte permute per word: the low (even c) or high (odd c) halves
-                // of two rows' words, row 2w in the low half.
-                uint32_t a[4];
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    a[w] = __builtin_amdgcn_perm(vr[2 * w + 1][c >> 1], vr[2 * w][c >> 1],
-                                                 (c & 1) ? 0x07060302u : 0x05040100u);
-                const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
+                const uint8_t *base = Vt + h * 32 * LROW + (c >> 2) * 128 + voff[c & 3];
+                const uint2 lo = lds_read_tr16(base);
+                const uint2 hi = lds_read_tr16(base + 4 * LROW);
+                const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) {
                     acc[nt][c] = mfma16<kPvHalf>(av, bhi[nt][h], acc[nt][c]);
@@ -377,7 +365,7 @@ struct PrefillTile {
 
         // Chunk c of a tile: key row c / CH, bytes 16 (c % CH).  With fewer chunks
         // than threads (d_head 64) the extra threads load nothing.
-        uint32_t goff[kPer], loff[kPer];
+        uint32_t goff[kPer], loffk[kPer], loffv[kPer];
         bool cok[kPer];
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -386,23 +374,27 @@ struct PrefillTile {
             const int r = (cok[i] ? c : 0) / CH;
             const int col = (cok[i] ? c : 0) - r * CH;
             goff[i] = static_cast<uint32_t>(r * rowstride + col * 16);
-            loff[i] = static_cast<uint32_t>(r * LROW + (col ^ swz(r)) * 16);
+            loffk[i] = static_cast<uint32_t>(r * LROW + (col ^ swz(r)) * 16);
+            loffv[i] = static_cast<uint32_t>(r * LROW + (col ^ swzv(r)) * 16);
         }
         // Per-lane LDS offsets of the step's operands (fixed for the whole tile):
-        // K operand of block b, piece p: row 8(m/4) + 4b + m%4, chunk 4p + kg;
-        // V: row 8kg + i, elements [VEC m, VEC m + VEC) (chunk VEC m / 8).
-        uint32_t koff[2][NKP], voff[8];
+        // K operand of block b, piece p: row 8(m/4) + 4b + m%4, chunk 4p + kg.
+        // V (transposed read, t = 0, d block c = 4 ch + cl): lane 4e + q of group kg
+        // addresses row 8kg + e (+ 4t), d = 16c + 4q, i.e. chunk 2c + q/2, bytes
+        // 8 (q % 2); with the swizzle (2c + q/2) ^ 2e = 8ch + 2(cl ^ e) + q/2.
+        uint32_t koff[2][NKP], voff[4];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int r = 8 * (m >> 2) + 4 * b + (m & 3);
 #pragma unroll
             for (int p = 0; p < NKP; ++p) koff[b][p] = static_cast<uint32_t>(r * LROW + ((4 * p + kg) ^ swz(r)) * 16);
         }
+        {
+            const int e = m >> 2;
+            const int q = m & 3;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 8 * kg + i;
-            const int byte = m * VEC * 2;   // 16 (d 128) or 8 (d 64) bytes per lane
-            voff[i] = static_cast<uint32_t>(r * LROW + (((byte >> 4) ^ swz(r)) << 4) + (byte & 15));
+            for (int cl = 0; cl < 4; ++cl)
+                voff[cl] = static_cast<uint32_t>((8 * kg + e) * LROW + 32 * (cl ^ e) + 16 * (q >> 1) + 8 * (q & 1));
         }
         uint4 rk[kPer], rv[kPer];
         auto fetch = [&](int st) {
@@ -428,8 +420,8 @@ struct PrefillTile {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 if (cok[i]) {
-                    *reinterpret_cast<uint4 *>(B[kK] + loff[i]) = rk[i];
-                    *reinterpret_cast<uint4 *>(B[kVraw] + loff[i]) = rv[i];
+                    *reinterpret_cast<uint4 *>(B[kK] + loffk[i]) = rk[i];
+                    *reinterpret_cast<uint4 *>(B[kVraw] + loffv[i]) = rv[i];
                     if constexpr (!kHalf) {
                         const uint4 x = rv[i];
                         const uint32_t t[4] = {x.x & 0x7fff7fffu, x.y & 0x7fff7fffu, x.z & 0x7fff7fffu,
@@ -437,7 +429,7 @@ struct PrefillTile {
                         big |= at_least_2p16(t[0]) | at_least_2p16(t[1]) | at_least_2p16(t[2]) | at_least_2p16(t[3]);
                         normal |= at_least_2m10(t[0]) | at_least_2m10(t[1]) | at_least_2m10(t[2]) |
                                   at_least_2m10(t[3]);
-                        *reinterpret_cast<uint4 *>(B[kV16] + loff[i]) =
+                        *reinterpret_cast<uint4 *>(B[kV16] + loffv[i]) =
                             make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
                                        bf16x2_to_f16x2(x.w));
                     }
@@ -513,13 +505,15 @@ struct PrefillTile {
         for (int nt = 0; nt < kNT; ++nt) {
             const float l_tot = accl[nt][0];   // every element of the ones product is the row sum
             const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-            float out[4 * VEC];
+            // acc[nt][c][q] is O[row][d = 16c + 4kg + q].
+            if (cap[nt] > 0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[nt][c][q] * inv;
-            if (cap[nt] > 0)
-                store_out<kOut>(P.o + (orow[nt] * D + 4 * VEC * kg) * (kOut == kF32 ? 4 : 2), out, 4 * VEC);
+                for (int c = 0; c < VEC; ++c) {
+                    const float x[4] = {acc[nt][c][0] * inv, acc[nt][c][1] * inv, acc[nt][c][2] * inv,
+                                        acc[nt][c][3] * inv};
+                    store4<kOut>(P.o + (orow[nt] * D + 16 * c + 4 * kg) * (kOut == kF32 ? 4 : 2), x);
+                }
+            }
         }
     }
 };
