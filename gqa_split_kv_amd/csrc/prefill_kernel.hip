@@ -225,43 +225,62 @@ struct PrefillTile {
                     for (int q = 0; q < 4; ++q) sv[nt][h][4 * b + q] = s[q];
                 }
         }
-        uint4 bhi[kNT][kH], blo[kNT][kH];
+        // Row maxima of the step and the (rare) move of the references, for both N
+        // tiles before any exponential, so that everything after it -- P for
+        // each half, the P V products, the row sums -- is one branch-free stretch
+        // the scheduler can interleave (the exponentials of half 1 with the
+        // products of half 0).
+        int lim[kNT];
+        float mxs[kNT];
+        bool move = false;
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
-            const int lim = cap[nt] - (k0 + 8 * kg);   // key 32h + i is visible iff 32h + i < lim
+            lim[nt] = cap[nt] - (k0 + 8 * kg);   // key 32h + i is visible iff 32h + i < lim
             float mx = -INFINITY;
 #pragma unroll
             for (int h = 0; h < kH; ++h)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     if constexpr (kDiag)
-                        mx = 32 * h + i < lim ? fmaxf(mx, sv[nt][h][i]) : mx;
+                        mx = 32 * h + i < lim[nt] ? fmaxf(mx, sv[nt][h][i]) : mx;
                     else
                         mx = fmaxf(mx, sv[nt][h][i]);
                 }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            mx = mx == -INFINITY ? -INFINITY : mx * sl2;   // scaled, log2 units
-            // Move the reference only when a row's maximum passes it by more than the
-            // allowed lag (wave-uniform branch; rows that did not ask follow along).
-            if (__ballot(mx > m_ref[nt] + kLagLog2)) {
-                const float m_new = fmaxf(m_ref[nt], mx);
+            mxs[nt] = mx == -INFINITY ? -INFINITY : mx * sl2;   // scaled, log2 units
+            move |= mxs[nt] > m_ref[nt] + kLagLog2;
+        }
+        // Move the references only when some row's maximum passes its reference by
+        // more than the allowed lag (wave-uniform branch; rows that did not ask
+        // follow along, with alpha = 1 where nothing changes).
+        if (__ballot(move)) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                const float m_new = fmaxf(m_ref[nt], mxs[nt]);
                 const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref[nt] - m_new);
                 accl[nt] *= alpha;
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) acc[nt][c] *= alpha;
                 m_ref[nt] = m_new;
             }
-            // p = 2^(s*sl2 - m_ref + kOff); a row with no visible key yet keeps the
-            // reference -inf and takes 0 in its place (its weights are masked to 0).
-            const float nmu = static_cast<float>(kOff) - (m_ref[nt] == -INFINITY ? 0.f : m_ref[nt]);
+        }
+        // p = 2^(s*sl2 - m_ref + kOff); a row with no visible key yet keeps the
+        // reference -inf and takes 0 in its place (its weights are masked to 0).
+        float nmu[kNT];
 #pragma unroll
-            for (int h = 0; h < kH; ++h) {
+        for (int nt = 0; nt < kNT; ++nt)
+            nmu[nt] = static_cast<float>(kOff) - (m_ref[nt] == -INFINITY ? 0.f : m_ref[nt]);
+        uint4 bhi[kNT][kH], blo[kNT][kH];
+#pragma unroll
+        for (int h = 0; h < kH; ++h) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
                 float pv[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][h][i], sl2, nmu));
-                    if constexpr (kDiag) pv[i] = 32 * h + i < lim ? pv[i] : 0.f;
+                    pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][h][i], sl2, nmu[nt]));
+                    if constexpr (kDiag) pv[i] = 32 * h + i < lim[nt] ? pv[i] : 0.f;
                 }
                 uint32_t phi[4], plo[4];
 #pragma unroll
@@ -284,11 +303,8 @@ struct PrefillTile {
                 bhi[nt][h] = make_uint4(phi[0], phi[1], phi[2], phi[3]);
                 if constexpr (kSplit) blo[nt][h] = make_uint4(plo[0], plo[1], plo[2], plo[3]);
             }
-        }
-        // O^T += V^T P^T per half and d block c (d = 16c + M): the A operand is
-        // read transposed from LDS (keys 32h + 8kg + i, d = 16c + m).
-#pragma unroll
-        for (int h = 0; h < kH; ++h) {
+            // O^T += V^T P^T for this half, d block c (d = 16c + M): the A operand is
+            // read transposed from LDS (keys 32h + 8kg + i, d = 16c + m).
 #pragma unroll
             for (int c = 0; c < VEC; ++c) {
                 const uint8_t *base = Vt + h * 32 * LROW + (c >> 2) * 128 + voff[c & 3];
@@ -480,24 +496,24 @@ struct PrefillTile {
         // code at all.
         const int nfull = min(nsteps, (tstart + 1) / kStepKeys);
         int st = 0;
+        // The last step fetches its own tile again and stages it into the idle
+        // buffer (nobody reads it), which keeps the loop bodies free of branches.
         for (; st < nfull; ++st) {
             if (P.split_pv || !tile_fast(st)) break;   // the same for the whole workgroup
-            const bool more = st + 1 < nsteps;
-            if (more) fetch(st + 1);
+            fetch(min(st + 1, nsteps - 1));
             clear_flag(st);
             step<false, false>(lds[st & 1][kK], lds[st & 1][kV16], st * kStepKeys, koff, voff, qop, cap, sl2, m_ref,
                                accl, acc);
-            if (more) stash(st + 1);
+            stash(st + 1);
             __syncthreads();
         }
         for (; st < nsteps; ++st) {
-            const bool more = st + 1 < nsteps;
-            if (more) fetch(st + 1);
+            fetch(min(st + 1, nsteps - 1));
             clear_flag(st);
             const int k0 = st * kStepKeys;
             if (k0 < wkeys)
                 step<true, true>(lds[st & 1][kK], lds[st & 1][kVraw], k0, koff, voff, qop, cap, sl2, m_ref, accl, acc);
-            if (more) stash(st + 1);
+            stash(st + 1);
             __syncthreads();
         }
 
