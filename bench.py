@@ -18,6 +18,10 @@ Prints one JSON line:
                  traffic = HBM bytes per launch from the committed rocprofv3
                  counter summary if it was taken on the current kernel source
   cpu_baseline   the fp64 CPU oracle on the same inputs, on the host cores
+  prefill        the causal prefill row at its own workload (one KV group, 32768
+                 tokens, h_q 8, d_head 128, bf16): ms per call and TFLOP/s of
+                 the algorithmic causal work against the bf16 matrix-core peak,
+                 in both P V precision modes, with the oracle's rate on a sample
 """
 from __future__ import annotations
 
@@ -34,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16 matrix-core peak of one MI355X
 METRIC = "µs/decode step + K/V HBM GB/s (% of peak), GQA h_q=64 h_kv=8 d=128 @32K"
 # Sources that define the sweep kernel's code (its counter data is tied to them).
 KERNEL_SRCS = [os.path.join(ROOT, "gqa_split_kv_amd", "csrc", f)
@@ -136,6 +141,63 @@ def cpu_baseline(d, w, budget_s: float):
     }
 
 
+def prefill_flops(seq_lens, h_q: int, d: int) -> float:
+    """Algorithmic causal-prefill work: token t of a sequence meets t + 1 keys, each
+    costing 2d flops for q.k and 2d for the weighted V sum, per query head."""
+    return float(sum(4.0 * d * h_q * S * (S + 1) / 2 for S in seq_lens))
+
+
+def prefill_row(hip, stream, steps: int, with_oracle: bool):
+    """Times gqa_prefill_ex on the 32K-token single-KV-group workload."""
+    import torch
+    import gqa_split_kv_amd as gqa
+    from gqa_split_kv_amd.inputs import PREFILL_32K, device_prefill_case
+    w = PREFILL_32K
+    log("prefill: generating %s" % w.name)
+    c = device_prefill_case(w.batch, w.h_q, w.h_kv, w.d, w.seq_lens(), w.dtype, seed=w.seed)
+    out = torch.empty_like(c.q)
+    flops = prefill_flops(c.seq_lens_host, w.h_q, w.d)
+    row = {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv, "d_head": w.d,
+           "seq_len": int(c.seq_lens_host[0]), "dtype": "bf16", "causal": True,
+           "algorithmic_flops_per_call": flops}
+    for split in (0, 1):
+        a = gqa.make_prefill_args(c.q, c.k, c.v, out, c.seq_lens, w.batch, w.h_q, w.h_kv, w.d, c.scale,
+                                  gqa.GQA_DTYPE_BF16, gqa.GQA_DTYPE_BF16, 0, stream, split)
+        for _ in range(2):
+            gqa.gqa_prefill_ex(a)
+        torch.cuda.synchronize()
+        ev = (hip.event(), hip.event())
+        hip.record(ev[0], stream)
+        for _ in range(steps):
+            gqa.gqa_prefill_ex(a)
+        hip.record(ev[1], stream)
+        hip.sync(ev[1])
+        ms = hip.ms(*ev) / steps
+        tf = flops / (ms / 1e3) / 1e12
+        key = "split_pv" if split else "default"
+        row[key] = {"ms_per_call": round(ms, 4), "tflops": round(tf, 1)}
+        if not split:
+            row["ms_per_call"] = round(ms, 4)
+            row["roofline"] = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tf, 1),
+                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "kernel_us": round(ms * 1e3, 1)}
+    if with_oracle:
+        import numpy as np
+        import oracle
+        from gqa_split_kv_amd.inputs import to_host_bits
+        qh, kh, vh = to_host_bits(c.q), to_host_bits(c.k), to_host_bits(c.v)
+        S = int(c.seq_lens_host[0])
+        toks = list(range(S - 8, S))            # the 8 longest rows
+        t = time.perf_counter()
+        oracle.gqa_prefill_rows_f64(qh, kh, vh, c.seq_lens_host, c.scale, toks)
+        dt = time.perf_counter() - t
+        sample_flops = sum(4.0 * w.d * w.h_q * (tk + 1) for tk in toks)
+        row["cpu_baseline"] = {"value": round(sample_flops / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": oracle.num_threads(), "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": "the last 8 of 32768 tokens (all 8 heads), fp64, one token at a time"}
+    return row
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +212,8 @@ def main():
                          "of K+V, at most 64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--prefill-steps", type=int, default=10,
+                    help="timed calls of the causal prefill row (0 skips it)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (profiler calibration)")
     args = ap.parse_args()
@@ -286,6 +350,8 @@ def main():
         result["copy_probe_bytes"] = n
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, w, args.cpu_budget)
+    if args.prefill_steps > 0:
+        result["prefill"] = prefill_row(hip, stream, args.prefill_steps, not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
 
 

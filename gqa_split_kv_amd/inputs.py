@@ -251,6 +251,23 @@ def device_case(batch: int, h_q: int, h_kv: int, d: int, seq_lens: Sequence[int]
     return DeviceCase(q, k, v, sl_dev, sl, float(scale), dtype)
 
 
+def device_prefill_case(batch: int, h_q: int, h_kv: int, d: int, seq_lens: Sequence[int], dtype: str = "bf16",
+                        seed: int = 0, scale: Optional[float] = None, device: str = "cuda") -> DeviceCase:
+    """Prefill inputs drawn on the device: q [sum(seq_lens), h_q, d], k and v
+    [sum(seq_lens), h_kv, d]."""
+    import torch
+    sl = np.asarray(seq_lens, dtype=np.int32).reshape(batch)
+    rows = int(np.clip(sl, 0, None).sum())
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    base_seed = int(np.random.SeedSequence(seed).generate_state(1)[0])
+    q = _torch_normal((rows, h_q, d), base_seed + 0, device, tdt)
+    k = _torch_normal((rows, h_kv, d), base_seed + 1, device, tdt)
+    v = _torch_normal((rows, h_kv, d), base_seed + 2, device, tdt)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    return DeviceCase(q, k, v, torch.from_numpy(sl.copy()).to(device), sl, float(scale), dtype)
+
+
 def device_workload(w: Workload, device: str = "cuda") -> DeviceCase:
     return device_case(w.batch, w.h_q, w.h_kv, w.d, w.seq_lens(), w.dtype, seed=w.seed,
                        scale=w.scale, peaked_frac=w.peaked_frac, peak_factor=w.peak_factor,
