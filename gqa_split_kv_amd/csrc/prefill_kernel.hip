@@ -143,10 +143,10 @@ struct PrefillTile {
     static constexpr int kPer = (kChunks + kPrefillThreads - 1) / kPrefillThreads;   // per thread
     static constexpr int kOff = 7;                  // exponent offset of P: p <= 2^(8 + 7)
     static constexpr int kTileBytes = kStepKeys * LROW;
-    // LDS regions of a stage: K, V in fp16 (the fast P V operand) and, for bf16
-    // input, V as given (the exact fallback's operand).
-    static constexpr int kRegions = kHalf ? 2 : 3;
-    static constexpr int kK = 0, kV16 = 1, kVraw = kHalf ? 1 : 2;
+    // LDS regions of a stage: K and V.  The fast loop stages V in fp16 (for bf16
+    // input converted on the way), the masked / split loop V as given.
+    static constexpr int kRegions = 2;
+    static constexpr int kK = 0, kV = 1;
     static constexpr uint32_t kOnesF16 = 0x3c003c00u;
     static constexpr uint32_t kOnesIn = kHalf ? 0x3c003c00u : 0x3f803f80u;
 
@@ -177,13 +177,16 @@ struct PrefillTile {
         const f32x2_t f = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
     }
-    // Range tests on the magnitude bits t of two packed bf16 (t = w & 0x7fff7fff):
-    // a half >= x carries into its bit 15 when 0x8000 - x is added.
-    //   >= 2^16 (0x4780): the value would overflow fp16;
+    // Range of a tile's V for the fp16 product, on bf16 magnitude bits (which
+    // order like the magnitudes): the thread keeps the largest magnitude of its
+    // chunks (packed 16-bit maximum, two operations per word) and tests it once:
+    //   >= 2^16 (0x4780): a value would overflow fp16;
     //   >= 2^-10 (0x3a80): the tile's largest value keeps ~14 significant bits in
     //   fp16 even where smaller values fall into fp16's subnormals.
-    __device__ __forceinline__ static uint32_t at_least_2p16(uint32_t t) { return (t + 0x38803880u) & 0x80008000u; }
-    __device__ __forceinline__ static uint32_t at_least_2m10(uint32_t t) { return (t + 0x45804580u) & 0x80008000u; }
+    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+    __device__ __forceinline__ static u16x2_t mag_max(u16x2_t m, uint32_t w) {
+        return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w & 0x7fff7fffu));
+    }
 
     // One step: S^T = K Q^T for the N tiles, online softmax with the lagging
     // maximum, then O^T += V^T P^T and l += 1^T P^T (the row sums from the same
@@ -425,35 +428,45 @@ struct PrefillTile {
                 rv[i] = buffer_load16<0>(rsv, goff[i]);
             }
         };
-        // Stage tile st into buffer st & 1.  bf16 input: V is stored as given and
-        // converted to fp16, and the tile's range is recorded in flag slot st % 3:
-        // word 0 set if some |v| >= 2^16, word 1 set if some |v| >= 2^-10.  The fp16
-        // product is used only for tiles with word 0 clear and word 1 set; from the
-        // first other tile on, this tile's remaining steps take the exact path.
-        auto stash = [&](int st) {
+        // Stage tile st into buffer st & 1 for the fast loop: K, and V in fp16 (bf16
+        // input is converted on the way and the tile's range is recorded in flag
+        // slot st % 3: word 0 set if some |v| >= 2^16, word 1 set if some |v| >=
+        // 2^-10; the fp16 product is used only for tiles with word 0 clear and word
+        // 1 set).
+        auto stash_fast = [&](int st) {
             uint8_t(*B)[kTileBytes] = lds[st & 1];
-            uint32_t big = 0, normal = 0;
+            u16x2_t mag = {0, 0};
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 if (cok[i]) {
                     *reinterpret_cast<uint4 *>(B[kK] + loffk[i]) = rk[i];
-                    *reinterpret_cast<uint4 *>(B[kVraw] + loffv[i]) = rv[i];
-                    if constexpr (!kHalf) {
-                        const uint4 x = rv[i];
-                        const uint32_t t[4] = {x.x & 0x7fff7fffu, x.y & 0x7fff7fffu, x.z & 0x7fff7fffu,
-                                               x.w & 0x7fff7fffu};
-                        big |= at_least_2p16(t[0]) | at_least_2p16(t[1]) | at_least_2p16(t[2]) | at_least_2p16(t[3]);
-                        normal |= at_least_2m10(t[0]) | at_least_2m10(t[1]) | at_least_2m10(t[2]) |
-                                  at_least_2m10(t[3]);
-                        *reinterpret_cast<uint4 *>(B[kV16] + loffv[i]) =
+                    const uint4 x = rv[i];
+                    if constexpr (kHalf) {
+                        *reinterpret_cast<uint4 *>(B[kV] + loffv[i]) = x;
+                    } else {
+                        mag = mag_max(mag_max(mag_max(mag_max(mag, x.x), x.y), x.z), x.w);
+                        *reinterpret_cast<uint4 *>(B[kV] + loffv[i]) =
                             make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
                                        bf16x2_to_f16x2(x.w));
                     }
                 }
             }
             if constexpr (!kHalf) {
-                if (big) flags[2 * (st % 3)] = 1;
-                if (normal) flags[2 * (st % 3) + 1] = 1;
+                const unsigned m = mag.x > mag.y ? mag.x : mag.y;
+                if (m >= 0x4780u) flags[2 * (st % 3)] = 1;
+                if (m >= 0x3a80u) flags[2 * (st % 3) + 1] = 1;
+            }
+        };
+        // Stage tile st as given (the masked / split loop), or only its V (`v_only`:
+        // re-staging, over its fp16 copy, the tile the fast loop stopped at).
+        auto stash_raw = [&](int st, bool v_only) {
+            uint8_t(*B)[kTileBytes] = lds[st & 1];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                if (cok[i]) {
+                    if (!v_only) *reinterpret_cast<uint4 *>(B[kK] + loffk[i]) = rk[i];
+                    *reinterpret_cast<uint4 *>(B[kV] + loffv[i]) = rv[i];
+                }
             }
         };
         // Slot st % 3 is written while tile st is staged (step st - 1), read in step
@@ -486,7 +499,7 @@ struct PrefillTile {
             __syncthreads();
         }
         fetch(0);
-        stash(0);
+        stash_fast(0);
         __syncthreads();
         // Steps whose keys every row of the tile sees (below the tile's first
         // token) run unmasked with fp16 P V; the rest -- the tile's diagonal band,
@@ -496,24 +509,28 @@ struct PrefillTile {
         // code at all.
         const int nfull = min(nsteps, (tstart + 1) / kStepKeys);
         int st = 0;
-        // The last step fetches its own tile again and stages it into the idle
-        // buffer (nobody reads it), which keeps the loop bodies free of branches.
         for (; st < nfull; ++st) {
             if (P.split_pv || !tile_fast(st)) break;   // the same for the whole workgroup
             fetch(min(st + 1, nsteps - 1));
             clear_flag(st);
-            step<false, false>(lds[st & 1][kK], lds[st & 1][kV16], st * kStepKeys, koff, voff, qop, cap, sl2, m_ref,
+            step<false, false>(lds[st & 1][kK], lds[st & 1][kV], st * kStepKeys, koff, voff, qop, cap, sl2, m_ref,
                                accl, acc);
-            stash(st + 1);
+            stash_fast(st + 1);
+            __syncthreads();
+        }
+        // Tile st was staged for the fast loop; its chunks are still in the staging
+        // registers (the last fetch was of tile st), so for bf16 input its V is put
+        // back as given before the masked / split loop reads it.
+        if constexpr (!kHalf) {
+            stash_raw(st, true);
             __syncthreads();
         }
         for (; st < nsteps; ++st) {
             fetch(min(st + 1, nsteps - 1));
-            clear_flag(st);
             const int k0 = st * kStepKeys;
             if (k0 < wkeys)
-                step<true, true>(lds[st & 1][kK], lds[st & 1][kVraw], k0, koff, voff, qop, cap, sl2, m_ref, accl, acc);
-            stash(st + 1);
+                step<true, true>(lds[st & 1][kK], lds[st & 1][kV], k0, koff, voff, qop, cap, sl2, m_ref, accl, acc);
+            stash_raw(st + 1, false);
             __syncthreads();
         }
 

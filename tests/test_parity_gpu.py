@@ -180,6 +180,31 @@ def test_multi_token_ragged_70b_heads(nc, mc):
     compare(o16, ref, "t_q=2 bf16 nc=%d mc=%d" % (nc, mc))
 
 
+def test_multi_token_70b_shaped_ragged_full_size_sampled():
+    """Two query tokens per sequence on the 70B-shaped ragged workload at full size
+    (64 sequences of 1K-32K keys, G 8 x t_q 2 = 16 rows), automatic plan as the
+    benchmark runs the decode; the oracle checks 6 sampled sequences whole."""
+    import torch
+    import oracle
+    from gqa_split_kv_amd.inputs import device_case
+    w = WORKLOADS[4]
+    sl_host = w.seq_lens()
+    _say("generating the 70B-shaped ragged workload with t_q = 2")
+    d = device_case(w.batch, w.h_q, w.h_kv, w.d, sl_host, w.dtype, seed=w.seed + 50, t_q=2)
+    out32 = run_hip(d.q, d.k, d.v, d.seq_lens, d.scale, out_dtype=torch.float32)
+    out16 = run_hip(d.q, d.k, d.v, d.seq_lens, d.scale)
+    offs = np.concatenate([[0], np.cumsum(sl_host)])
+    for b in (0, 1, 17, 31, 48, 63):
+        S = int(sl_host[b])
+        _say("oracle on sequence", b, "of", S, "keys")
+        kb = to_host_bits(d.k[offs[b]:offs[b] + S])
+        vb = to_host_bits(d.v[offs[b]:offs[b] + S])
+        qb = to_host_bits(d.q[b:b + 1])
+        ref = oracle.gqa_decode_f64(qb, kb, vb, [S], d.scale)
+        compare(out32[b:b + 1], ref, "t_q=2 seq %d fp32" % b)
+        compare(out16[b:b + 1], ref, "t_q=2 seq %d bf16" % b)
+
+
 def test_multi_token_short_sequences_give_zero_for_unseen_tokens():
     import torch
     lens = [0, 1, 2, 3, 4, 5]
