@@ -62,7 +62,12 @@ constexpr int kRowsPerWave = 16 * kNT;             // 32
 #ifndef GQA_PREFILL_STEP_KEYS
 #define GQA_PREFILL_STEP_KEYS 64
 #endif
-constexpr int kStepKeys = GQA_PREFILL_STEP_KEYS;   // keys per LDS stage (a multiple of 32)
+constexpr int kStepKeys = GQA_PREFILL_STEP_KEYS;   // keys per compute step (a multiple of 32)
+#ifndef GQA_PREFILL_STAGE_STEPS
+#define GQA_PREFILL_STAGE_STEPS 2
+#endif
+constexpr int kStageSteps = GQA_PREFILL_STAGE_STEPS;   // compute steps per LDS stage (per barrier)
+constexpr int kStageKeys = kStepKeys * kStageSteps;
 constexpr float kLagLog2 = 8.f;                    // allowed lag of the running maximum
 static_assert(kWavesP * kRowsPerWave == kPrefillRows, "tile rows");
 
@@ -139,10 +144,10 @@ struct PrefillTile {
     static constexpr int NKP = ROWB / 64;           // 16-byte K pieces per lane per 16-key block
     static constexpr int VEC = D / 16;              // d elements per lane per V row
     static constexpr int CH = ROWB / 16;            // 16-byte chunks per key row
-    static constexpr int kChunks = kStepKeys * CH;  // 16-byte chunks of a K (or V) tile
+    static constexpr int kChunks = kStepKeys * CH;  // 16-byte chunks of one step's K (or V) rows
     static constexpr int kPer = (kChunks + kPrefillThreads - 1) / kPrefillThreads;   // per thread
     static constexpr int kOff = 7;                  // exponent offset of P: p <= 2^(8 + 7)
-    static constexpr int kTileBytes = kStepKeys * LROW;
+    static constexpr int kTileBytes = kStageKeys * LROW;
     // LDS regions of a stage: K and V.  The fast loop stages V in fp16 (for bf16
     // input converted on the way), the masked / split loop V as given.
     static constexpr int kRegions = 2;
@@ -378,7 +383,7 @@ struct PrefillTile {
         const int wtok_hi = min((wave * kRowsPerWave + kRowsPerWave - 1) / G, tcount - 1);
         const int wkeys = wtok_lo < tcount ? tstart + wtok_hi + 1 : 0;   // keys this wavefront needs
         const int nkeys = tstart + tcount;                                 // keys the tile needs
-        const int nsteps = (nkeys + kStepKeys - 1) / kStepKeys;
+        const int nstages = (nkeys + kStageKeys - 1) / kStageKeys;
         const uint8_t *kbase = P.k + (off * P.h_kv + j) * ROWB;
         const uint8_t *vbase = P.v + (off * P.h_kv + j) * ROWB;
 
@@ -415,10 +420,11 @@ struct PrefillTile {
             for (int cl = 0; cl < 4; ++cl)
                 voff[cl] = static_cast<uint32_t>((8 * kg + e) * LROW + 32 * (cl ^ e) + 16 * (q >> 1) + 8 * (q & 1));
         }
+        // Staging moves one step's rows (part `pt` of stage `sg`) at a time.
         uint4 rk[kPer], rv[kPer];
-        auto fetch = [&](int st) {
-            const int k0 = st * kStepKeys;
-            const uint32_t bytes = static_cast<uint32_t>(min(kStepKeys, len - k0) * rowstride);
+        auto fetch = [&](int sg, int pt) {
+            const int k0 = sg * kStageKeys + pt * kStepKeys;
+            const uint32_t bytes = k0 < len ? static_cast<uint32_t>(min(kStepKeys, len - k0) * rowstride) : 0u;
             const int64_t boff = static_cast<int64_t>(k0) * rowstride;
             const auto rsk = make_rsrc(kbase + boff, bytes);
             const auto rsv = make_rsrc(vbase + boff, bytes);
@@ -433,19 +439,20 @@ struct PrefillTile {
         // slot st % 3: word 0 set if some |v| >= 2^16, word 1 set if some |v| >=
         // 2^-10; the fp16 product is used only for tiles with word 0 clear and word
         // 1 set).
-        auto stash_fast = [&](int st) {
+        auto stash_fast = [&](int st, int pt) {
             uint8_t(*B)[kTileBytes] = lds[st & 1];
+            const uint32_t po = static_cast<uint32_t>(pt * kStepKeys * LROW);
             u16x2_t mag = {0, 0};
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 if (cok[i]) {
-                    *reinterpret_cast<uint4 *>(B[kK] + loffk[i]) = rk[i];
+                    *reinterpret_cast<uint4 *>(B[kK] + po + loffk[i]) = rk[i];
                     const uint4 x = rv[i];
                     if constexpr (kHalf) {
-                        *reinterpret_cast<uint4 *>(B[kV] + loffv[i]) = x;
+                        *reinterpret_cast<uint4 *>(B[kV] + po + loffv[i]) = x;
                     } else {
                         mag = mag_max(mag_max(mag_max(mag_max(mag, x.x), x.y), x.z), x.w);
-                        *reinterpret_cast<uint4 *>(B[kV] + loffv[i]) =
+                        *reinterpret_cast<uint4 *>(B[kV] + po + loffv[i]) =
                             make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
                                        bf16x2_to_f16x2(x.w));
                     }
@@ -459,13 +466,14 @@ struct PrefillTile {
         };
         // Stage tile st as given (the masked / split loop), or only its V (`v_only`:
         // re-staging, over its fp16 copy, the tile the fast loop stopped at).
-        auto stash_raw = [&](int st, bool v_only) {
+        auto stash_raw = [&](int st, int pt, bool v_only) {
             uint8_t(*B)[kTileBytes] = lds[st & 1];
+            const uint32_t po = static_cast<uint32_t>(pt * kStepKeys * LROW);
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 if (cok[i]) {
-                    if (!v_only) *reinterpret_cast<uint4 *>(B[kK] + loffk[i]) = rk[i];
-                    *reinterpret_cast<uint4 *>(B[kV] + loffv[i]) = rv[i];
+                    if (!v_only) *reinterpret_cast<uint4 *>(B[kK] + po + loffk[i]) = rk[i];
+                    *reinterpret_cast<uint4 *>(B[kV] + po + loffv[i]) = rv[i];
                 }
             }
         };
@@ -498,8 +506,11 @@ struct PrefillTile {
             if (tid < 4) flags[tid] = 0;   // slots of tiles 0 and 1
             __syncthreads();
         }
-        fetch(0);
-        stash_fast(0);
+#pragma unroll
+        for (int pt = 0; pt < kStageSteps; ++pt) {
+            fetch(0, pt);
+            stash_fast(0, pt);
+        }
         __syncthreads();
         // Steps whose keys every row of the tile sees (below the tile's first
         // token) run unmasked with fp16 P V; the rest -- the tile's diagonal band,
@@ -507,30 +518,45 @@ struct PrefillTile {
         // with the exact split product, each wavefront skipping the steps beyond its
         // own last token.  Two loops, so the fast one carries no masking or fallback
         // code at all.
-        const int nfull = min(nsteps, (tstart + 1) / kStepKeys);
+        // One barrier per stage of kStageSteps steps, so the two wavefronts of a
+        // SIMD can drift apart within a stage.  Each step's part of the next stage
+        // is fetched before the step and staged after it (into the other buffer).
+        const int nfull = min(nstages, (tstart + 1) / kStageKeys);
         int st = 0;
         for (; st < nfull; ++st) {
             if (P.split_pv || !tile_fast(st)) break;   // the same for the whole workgroup
-            fetch(min(st + 1, nsteps - 1));
             clear_flag(st);
-            step<false, false>(lds[st & 1][kK], lds[st & 1][kV], st * kStepKeys, koff, voff, qop, cap, sl2, m_ref,
-                               accl, acc);
-            stash_fast(st + 1);
+            const int nx = min(st + 1, nstages - 1);
+#pragma unroll
+            for (int pt = 0; pt < kStageSteps; ++pt) {
+                fetch(nx, pt);
+                step<false, false>(lds[st & 1][kK] + pt * kStepKeys * LROW, lds[st & 1][kV] + pt * kStepKeys * LROW,
+                                   st * kStageKeys + pt * kStepKeys, koff, voff, qop, cap, sl2, m_ref, accl, acc);
+                stash_fast(st + 1, pt);
+            }
             __syncthreads();
         }
-        // Tile st was staged for the fast loop; its chunks are still in the staging
-        // registers (the last fetch was of tile st), so for bf16 input its V is put
-        // back as given before the masked / split loop reads it.
+        // Stage st was staged for the fast loop; for bf16 input its V is put back as
+        // given (fetched again) before the masked / split loop reads it.
         if constexpr (!kHalf) {
-            stash_raw(st, true);
+#pragma unroll
+            for (int pt = 0; pt < kStageSteps; ++pt) {
+                fetch(st, pt);
+                stash_raw(st, pt, true);
+            }
             __syncthreads();
         }
-        for (; st < nsteps; ++st) {
-            fetch(min(st + 1, nsteps - 1));
-            const int k0 = st * kStepKeys;
-            if (k0 < wkeys)
-                step<true, true>(lds[st & 1][kK], lds[st & 1][kV], k0, koff, voff, qop, cap, sl2, m_ref, accl, acc);
-            stash_raw(st + 1, false);
+        for (; st < nstages; ++st) {
+            const int nx = min(st + 1, nstages - 1);
+#pragma unroll
+            for (int pt = 0; pt < kStageSteps; ++pt) {
+                fetch(nx, pt);
+                const int k0 = st * kStageKeys + pt * kStepKeys;
+                if (k0 < wkeys)
+                    step<true, true>(lds[st & 1][kK] + pt * kStepKeys * LROW, lds[st & 1][kV] + pt * kStepKeys * LROW,
+                                     k0, koff, voff, qop, cap, sl2, m_ref, accl, acc);
+                stash_raw(st + 1, pt, false);
+            }
             __syncthreads();
         }
 
