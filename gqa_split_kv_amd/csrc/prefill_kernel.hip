@@ -9,28 +9,30 @@
 // with disjoint output rows, so no cross-worker reduction is needed).
 //
 // Mapping to one MI355X:
-//   * A workgroup (4 wavefronts) owns one tile of 256 rows = 256 / G tokens x G
+//   * A workgroup (8 wavefronts) owns one tile of 256 rows = 256 / G tokens x G
 //     query heads of one (sequence, kv head), and sweeps the keys 0 .. its last
-//     token in steps of 32 with the page's online-softmax fold; the rows are
-//     disjoint, so every tile normalises and stores its own outputs.
-//   * The 32-key K and V tiles go HBM/L2 -> registers -> LDS (double buffered,
-//     one barrier per step, the next tile's loads in flight during the current
-//     step) and are shared by all 256 rows, so the K/V bytes per output row
-//     fall with the tile height.
+//     token with the page's online-softmax fold; the rows are disjoint, so every
+//     tile normalises and stores its own outputs.
+//   * K and V go HBM/L2 -> registers -> LDS in 128-key stages (double buffered,
+//     one barrier per stage) that all 256 rows share, so the K/V bytes per output
+//     row fall with the tile height.  A stage is computed as two 64-key steps;
+//     each step's part of the next stage is loaded before the step and written to
+//     the other buffer after it.  LDS rows are XOR-swizzled in 16-byte chunks
+//     (one pattern for K, one for V) so the operand reads hit distinct banks.
 //   * Each wavefront owns 32 rows as two 16-row N tiles of
 //     v_mfma_f32_16x16x32_{bf16,f16}: S^T = K Q^T with the keys on the M axis
 //     (the K rows are read from LDS in the key order that leaves lane l holding
 //     keys 8*(l/16) .. +7 of its row), then O^T += V^T P^T and l += 1^T P^T (the
 //     row sums come out of the matrix core, from the same rounded P).  The V^T
-//     operand is rebuilt from LDS rows once per step and reused by both N tiles.
-//     Two wavefronts share a SIMD (at most 256 VGPRs each, no AGPR traffic).
+//     operand comes straight out of LDS through transpose reads.  Two wavefronts
+//     share a SIMD (at most 256 VGPRs each, no AGPR traffic).
 //   * P V precision: by default P is rounded to fp16 and V read as fp16 (bf16 V
-//     is converted while the tile is staged: exact for magnitudes in fp16's
-//     normal range), one product per step.  A bf16 tile whose largest |v| is not
-//     in [2^-10, 2^16) sends the rest of the tile's sweep to the split product
-//     (P as a high and a low part in the input format, V as given, two
-//     products), which the diagonal band always uses and which the caller can
-//     ask for everywhere.
+//     is converted while it is staged: exact for magnitudes in fp16's normal
+//     range), one product per step.  A bf16 stage whose largest |v| is not in
+//     [2^-10, 2^16) sends the rest of the tile's sweep to the split product (P as
+//     a high and a low part in the input format, V as given, two products),
+//     which the diagonal band always uses and which the caller can ask for
+//     everywhere.
 //   * The running maximum is allowed to lag the true one by up to 8 (log2
 //     units): the accumulators are rescaled only when some row of an N tile
 //     exceeds its reference by more, which removes almost every rescale of the

@@ -51,8 +51,8 @@ extern "C" {
  *             0..2^20.  The result does not depend on it.
  * split_pv    Precision of the P V product.  0 (default): P is rounded to fp16
  *             (11 significant bits, times a common power of two that cancels) and
- *             V taken in fp16, one matrix-core product; for bf16 input a 64-key
- *             tile of V whose largest magnitude is not in [2^-10, 2^16) switches
+ *             V taken in fp16, one matrix-core product; for bf16 input a 128-key
+ *             block of V whose largest magnitude is not in [2^-10, 2^16) switches
  *             the rest of that tile's sweep to the split product, so the fp16
  *             rounding of V never loses range or precision.  Typical error
  *             against the exact result: relative L2 ~1e-4.  1: P split into a
