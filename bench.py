@@ -18,6 +18,8 @@ Prints one JSON line:
                  traffic = HBM bytes per launch from the committed rocprofv3
                  counter summary if it was taken on the current kernel source
   cpu_baseline   the fp64 CPU oracle on the same inputs, on the host cores
+  decode_variants  the same batch with fp16 q/k/v and with two query tokens per
+                 sequence (t_q = 2): step time, GB/s and the sweep kernel's roofline
   prefill        the causal prefill row at its own workload (one KV group, 32768
                  tokens, h_q 8, d_head 128, bf16): ms per call and TFLOP/s of
                  the algorithmic causal work against the bf16 matrix-core peak,
@@ -141,6 +143,62 @@ def cpu_baseline(d, w, budget_s: float):
     }
 
 
+def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
+    """The decode path's other input forms on the same batch and K/V bytes:
+    fp16 q/k/v (gqa_decode_f16's kernels, fp16 out) and two query tokens per
+    sequence (bf16, t_q = 2: every sequence's last two tokens, causal between
+    them; G * t_q = 16 rows per kv head).  Each is timed like the headline step,
+    with the sweep kernel's own HIP events."""
+    import torch
+    import gqa_split_kv_amd as gqa
+    from gqa_split_kv_amd.inputs import device_queries
+    rows = {}
+    forms = [
+        ("f16", lambda: (d.q.to(torch.float16), d.k.to(torch.float16), d.v.to(torch.float16)),
+         gqa.GQA_DTYPE_F16, 0),
+        ("bf16_t_q2", lambda: (device_queries(w.batch, 2, w.h_q, w.d, "bf16", seed=w.seed + 7), d.k, d.v),
+         gqa.GQA_DTYPE_BF16, 2),
+    ]
+    for name, make, code, t_q in forms:
+        log("decode variant %s" % name)
+        q, k, v = make()
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+        probe = gqa.make_args(q, k, v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale, code, code,
+                              stream=stream, t_q=t_q)
+        ws_bytes = gqa.gqa_decode_workspace_bytes(probe)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        ev_steps = [(hip.event(), hip.event()) for _ in range(steps)]
+        timed = [gqa.make_args(q, k, v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale, code, code,
+                               0, 0, ws, ws_bytes, stream, sweep_events=e, t_q=t_q) for e in ev_steps]
+        warm = gqa.make_args(q, k, v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale, code, code,
+                             0, 0, ws, ws_bytes, stream, t_q=t_q)
+        for _ in range(3):
+            gqa.gqa_decode_ex(warm)
+        torch.cuda.synchronize()
+        ev = (hip.event(), hip.event())
+        hip.record(ev[0], stream)
+        for a in timed:
+            gqa.gqa_decode_ex(a)
+        hip.record(ev[1], stream)
+        hip.sync(ev[1])
+        ms = hip.ms(*ev) / steps
+        sweep_ms = sum(hip.ms(a, b) for a, b in ev_steps) / steps
+        achieved = kv_bytes / (sweep_ms / 1e3) / 1e9
+        rows[name] = {"t_q": max(t_q, 1), "dtype": "f16" if code == gqa.GQA_DTYPE_F16 else "bf16",
+                      "us_per_step": round(ms * 1e3, 2),
+                      "gb_s": round(kv_bytes / (ms / 1e3) / 1e9, 2),
+                      "roofline": {"kernel": "split_kernel (key sweep)", "bound": "hbm",
+                                   "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(achieved / HBM_PEAK_GBS, 4),
+                                   "kernel_us": round(sweep_ms * 1e3, 2)}}
+        for e in ev_steps + [ev]:
+            hip.destroy(e[0])
+            hip.destroy(e[1])
+        del q, k, v, out, ws, timed, warm
+        torch.cuda.empty_cache()
+    return rows
+
+
 def prefill_flops(seq_lens, h_q: int, d: int) -> float:
     """Algorithmic causal-prefill work: token t of a sequence meets t + 1 keys, each
     costing 2d flops for q.k and 2d for the weighted V sum, per query head."""
@@ -214,6 +272,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--prefill-steps", type=int, default=10,
                     help="timed calls of the causal prefill row (0 skips it)")
+    ap.add_argument("--variant-steps", type=int, default=20,
+                    help="timed steps of each other decode form (fp16, t_q = 2) on the same batch; 0 skips")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (profiler calibration)")
     args = ap.parse_args()
@@ -350,6 +410,8 @@ def main():
         result["copy_probe_bytes"] = n
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, w, args.cpu_budget)
+    if args.variant_steps > 0:
+        result["decode_variants"] = decode_variants(hip, stream, w, d, kv_bytes, args.variant_steps)
     if args.prefill_steps > 0:
         result["prefill"] = prefill_row(hip, stream, args.prefill_steps, not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)

@@ -251,6 +251,15 @@ def device_case(batch: int, h_q: int, h_kv: int, d: int, seq_lens: Sequence[int]
     return DeviceCase(q, k, v, sl_dev, sl, float(scale), dtype)
 
 
+def device_queries(batch: int, t_q: int, h_q: int, d: int, dtype: str = "bf16", seed: int = 0,
+                   device: str = "cuda"):
+    """A seeded N(0,1) query block [batch, t_q, h_q, d] drawn on the device."""
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    base_seed = int(np.random.SeedSequence(seed).generate_state(1)[0])
+    return _torch_normal((batch, t_q, h_q, d), base_seed, device, tdt)
+
+
 def device_prefill_case(batch: int, h_q: int, h_kv: int, d: int, seq_lens: Sequence[int], dtype: str = "bf16",
                         seed: int = 0, scale: Optional[float] = None, device: str = "cuda") -> DeviceCase:
     """Prefill inputs drawn on the device: q [sum(seq_lens), h_q, d], k and v
