@@ -220,7 +220,8 @@ def prefill_row(hip, stream, steps: int, with_oracle: bool):
            "algorithmic_flops_per_call": flops}
     for split in (0, 1):
         a = gqa.make_prefill_args(c.q, c.k, c.v, out, c.seq_lens, w.batch, w.h_q, w.h_kv, w.d, c.scale,
-                                  gqa.GQA_DTYPE_BF16, gqa.GQA_DTYPE_BF16, 0, stream, split)
+                                  gqa.GQA_DTYPE_BF16, gqa.GQA_DTYPE_BF16, 0, stream, split,
+                                  total_tokens=c.q.shape[0])
         for _ in range(2):
             gqa.gqa_prefill_ex(a)
         torch.cuda.synchronize()

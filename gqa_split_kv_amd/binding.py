@@ -36,7 +36,7 @@ GQA_ERR_ARG = 8
 EXPORTS = ("gqa_decode", "gqa_decode_f32", "gqa_decode_f16", "gqa_decode_ex", "gqa_decode_validate",
            "gqa_decode_make_plan", "gqa_decode_workspace_bytes", "gqa_status_str",
            "gqa_last_error_message", "gqa_release", "gqa_prefill", "gqa_prefill_f16", "gqa_prefill_ex",
-           "gqa_prefill_validate", "gqa_probe_copy", "gqa_probe_read")
+           "gqa_prefill_validate", "gqa_prefill_workspace_bytes", "gqa_probe_copy", "gqa_probe_read")
 
 
 class GqaArgs(ctypes.Structure):
@@ -84,6 +84,8 @@ class GqaPrefillArgs(ctypes.Structure):
         ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("num_blocks", ctypes.c_int32), ("stream", ctypes.c_void_p),
         ("split_pv", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int64),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -119,7 +121,7 @@ def lib() -> ctypes.CDLL:
     L.gqa_last_error_message.restype = ctypes.c_char_p
     L.gqa_release.argtypes = []
     L.gqa_release.restype = None
-    L.gqa_prefill.argtypes = sig
+    L.gqa_prefill.argtypes = [P, P, P, P, P, i32, ctypes.c_int64, i32, i32, i32, ctypes.c_float, P]
     L.gqa_prefill.restype = ctypes.c_int
     L.gqa_prefill_f16.argtypes = sig
     L.gqa_prefill_f16.restype = ctypes.c_int
@@ -127,6 +129,8 @@ def lib() -> ctypes.CDLL:
     L.gqa_prefill_ex.restype = ctypes.c_int
     L.gqa_prefill_validate.argtypes = [ctypes.POINTER(GqaPrefillArgs)]
     L.gqa_prefill_validate.restype = ctypes.c_int
+    L.gqa_prefill_workspace_bytes.argtypes = [ctypes.POINTER(GqaPrefillArgs), ctypes.POINTER(ctypes.c_size_t)]
+    L.gqa_prefill_workspace_bytes.restype = ctypes.c_int
     L.gqa_probe_copy.argtypes = [P, P, ctypes.c_size_t, P]
     L.gqa_probe_copy.restype = ctypes.c_int
     L.gqa_probe_read.argtypes = [P, ctypes.c_size_t, P, P]
@@ -294,11 +298,11 @@ def decode(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype
     return out
 
 
-def gqa_prefill(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_head: int, scale: float,
-                stream=None) -> int:
+def gqa_prefill(q, k, v, o, seq_lens, batch: int, total_tokens: int, h_q: int, h_kv: int, d_head: int,
+                scale: float, stream=None) -> int:
     """Causal prefill, bf16 in / bf16 out.  Raises GqaError on a non-zero status."""
-    st = lib().gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens), batch, h_q, h_kv,
-                           d_head, float(scale), _stream(stream))
+    st = lib().gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens), batch, int(total_tokens), h_q,
+                           h_kv, d_head, float(scale), _stream(stream))
     _check(st)
     return st
 
@@ -313,7 +317,8 @@ def gqa_prefill_f16(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_hea
 
 
 def make_prefill_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, in_dtype, out_dtype,
-                      num_blocks=0, stream=0, split_pv=0) -> GqaPrefillArgs:
+                      num_blocks=0, stream=0, split_pv=0, total_tokens=0, workspace=None,
+                      workspace_bytes=0) -> GqaPrefillArgs:
     a = GqaPrefillArgs()
     a.q, a.k, a.v, a.o, a.seq_lens = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens)
     a.batch, a.h_q, a.h_kv, a.d_head = int(batch), int(h_q), int(h_kv), int(d_head)
@@ -322,6 +327,9 @@ def make_prefill_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, in_
     a.num_blocks = int(num_blocks)
     a.stream = stream
     a.split_pv = int(split_pv)
+    a.total_tokens = int(total_tokens)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = int(workspace_bytes)
     return a
 
 
@@ -336,11 +344,19 @@ def gqa_prefill_validate(args: GqaPrefillArgs) -> int:
     return int(lib().gqa_prefill_validate(ctypes.byref(args)))
 
 
+def gqa_prefill_workspace_bytes(args: GqaPrefillArgs) -> int:
+    """Workspace bytes the prefill call needs (0 where it uses none)."""
+    n = ctypes.c_size_t()
+    _check(lib().gqa_prefill_workspace_bytes(ctypes.byref(args), ctypes.byref(n)))
+    return int(n.value)
+
+
 def prefill(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype=None,
-            num_blocks: int = 0, stream=None, split_pv: int = 0):
+            num_blocks: int = 0, stream=None, split_pv: int = 0, workspace=None, total_tokens=None):
     """o = causal GQA prefill of q [sum(seq_lens), h_q, d] against k, v
     [sum(seq_lens), h_kv, d] (each token sees its sequence's keys up to itself).
-    seq_lens is an int32 device tensor.  Returns `out`."""
+    seq_lens is an int32 device tensor; total_tokens defaults to q's row count;
+    workspace (a device byte tensor) defaults to the library's own.  Returns `out`."""
     import torch
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q must be [sum(seq_lens), h_q, d]; k, v [sum(seq_lens), h_kv, d]")
@@ -351,8 +367,12 @@ def prefill(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtyp
         scale = 1.0 / float(d) ** 0.5
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if total_tokens is None:
+        total_tokens = q.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = make_prefill_args(q, k, v, out, seq_lens, batch, h_q, h_kv, d, scale, _dtype_code(q),
-                             _dtype_code(out), num_blocks, _stream(stream), split_pv)
+                             _dtype_code(out), num_blocks, _stream(stream), split_pv, total_tokens, workspace,
+                             ws_bytes)
     gqa_prefill_ex(args)
     return out
 

@@ -174,16 +174,40 @@ int prefill_ex(const gqa_prefill_args *a) {
     P.G = a->h_q / a->h_kv;
     P.scale_log2 = static_cast<float>(static_cast<double>(a->scale) * 1.4426950408889634074);
     P.split_pv = a->split_pv;
-    e = gqa::launch_prefill(P, a->in_dtype, a->out_dtype, a->d_head, blocks,
-                            reinterpret_cast<hipStream_t>(a->stream));
+    hipStream_t stream = reinterpret_cast<hipStream_t>(a->stream);
+    const gqa::PrefillWorkspace W = gqa::prefill_workspace(a);
+    P.v16 = a->in_dtype == GQA_DTYPE_F16 ? P.v : nullptr;
+    P.vflags = nullptr;
+    P.nblk = 0;
+    if (W.bytes > 0) {
+        void *ws = a->workspace;
+        if (!ws) {
+            st = owned_workspace(dev, stream, W.bytes, &ws);
+            if (st != GQA_OK) return st;
+        }
+        gqa::VconvParams V;
+        V.v = P.v;
+        V.v16 = static_cast<uint8_t *>(ws);
+        V.flags = static_cast<uint8_t *>(ws) + W.flags_offset;
+        V.total = a->total_tokens;
+        V.nblk = W.nblk;
+        V.h_kv = a->h_kv;
+        e = gqa::launch_vconv(V, a->d_head, a->h_kv, stream);
+        if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "V conversion kernel launch failed: %s", hipGetErrorString(e));
+        P.v16 = V.v16;
+        P.vflags = V.flags;
+        P.nblk = W.nblk;
+    }
+    e = gqa::launch_prefill(P, a->in_dtype, a->out_dtype, a->d_head, blocks, stream);
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "prefill kernel launch failed: %s", hipGetErrorString(e));
     return GQA_OK;
 }
 
 gqa_prefill_args make_prefill_args(const void *q, const void *k, const void *v, void *o,
-                                   const int32_t *seq_lens, int32_t batch, int32_t h_q, int32_t h_kv,
-                                   int32_t d_head, float scale, void *stream, int dtype) {
+                                   const int32_t *seq_lens, int32_t batch, int64_t total_tokens, int32_t h_q,
+                                   int32_t h_kv, int32_t d_head, float scale, void *stream, int dtype) {
     gqa_prefill_args a = {};
+    a.total_tokens = total_tokens;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -264,16 +288,16 @@ int gqa_prefill_ex(const gqa_prefill_args *args) {
 }
 
 int gqa_prefill(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens, int32_t batch,
-                int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream) {
-    const gqa_prefill_args a =
-        make_prefill_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, stream, GQA_DTYPE_BF16);
+                int64_t total_tokens, int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream) {
+    const gqa_prefill_args a = make_prefill_args(q, k, v, o, seq_lens, batch, total_tokens, h_q, h_kv, d_head,
+                                                 scale, stream, GQA_DTYPE_BF16);
     return gqa_prefill_ex(&a);
 }
 
 int gqa_prefill_f16(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
                     int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream) {
     const gqa_prefill_args a =
-        make_prefill_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, stream, GQA_DTYPE_F16);
+        make_prefill_args(q, k, v, o, seq_lens, batch, 0, h_q, h_kv, d_head, scale, stream, GQA_DTYPE_F16);
     return gqa_prefill_ex(&a);
 }
 
@@ -281,6 +305,19 @@ int gqa_prefill_validate(const gqa_prefill_args *args) {
     try {
         gqa::clear_error();
         return gqa::validate_prefill(args);
+    } catch (...) {
+        return gqa::fail(GQA_ERR_HIP, "internal error");
+    }
+}
+
+int gqa_prefill_workspace_bytes(const gqa_prefill_args *args, size_t *bytes) {
+    try {
+        gqa::clear_error();
+        if (!bytes) return gqa::fail(GQA_ERR_NULL, "bytes is NULL");
+        int st = gqa::validate_prefill(args, false);
+        if (st != GQA_OK) return st;
+        *bytes = gqa::prefill_workspace(args).bytes;
+        return GQA_OK;
     } catch (...) {
         return gqa::fail(GQA_ERR_HIP, "internal error");
     }

@@ -22,6 +22,18 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
 
+// Maximum of x over the four lanes l mod 16 + 16 r (r = 0..3) that share l's
+// position within a 16-lane row, with the two row-swap permutes of gfx950:
+// permlane16_swap with both operands x returns rows (0, 0, 2, 2) in one half of
+// its result and (1, 1, 3, 3) in the other, permlane32_swap rows (0, 1, 0, 1)
+// and (2, 3, 2, 3).  No LDS traffic.
+__device__ __forceinline__ float max_over_rows(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ int64_t shfl64(int64_t x, int src) {
     const int lo = __shfl(static_cast<int>(static_cast<uint32_t>(x)), src);
     const int hi = __shfl(static_cast<int>(x >> 32), src);

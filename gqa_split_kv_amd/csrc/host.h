@@ -38,6 +38,10 @@ constexpr int kSplitMergeBelowBlocks = 256;
 #endif
 constexpr int kPrefillThreads = GQA_PREFILL_THREADS;
 constexpr int kPrefillRows = GQA_PREFILL_ROWS;
+// Tokens per range-checked block of the prefill's fp16 copy of bf16 V, and the
+// workgroup size of the kernel that makes the copy.
+constexpr int kPrefillVBlock = 128;
+constexpr int kVconvThreads = 256;
 constexpr int kMaxG = 16;           // rows (query heads x query tokens) per kv head in one 16-wide MFMA tile
 constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxPrefillBlocks = 1 << 20;
@@ -60,8 +64,20 @@ void clear_error();
 // tuning ranges, and the caller workspace when num_chunks is explicit).
 int validate(const gqa_decode_args *a);
 
-// Host checks of a prefill call (status, message via fail()).
-int validate_prefill(const gqa_prefill_args *a);
+// Host checks of a prefill call (status, message via fail()); the caller
+// workspace is checked too unless `check_workspace` is false.
+int validate_prefill(const gqa_prefill_args *a, bool check_workspace = true);
+
+// Prefill workspace: the fp16 copy of V [total_tokens, h_kv, D] at 0, the block
+// flags [h_kv][nblk] (bytes) at flags_offset.  bytes = 0 (and nblk = 0) when the
+// call makes no copy (fp16 input, split_pv = 1, or total_tokens = 0).
+struct PrefillWorkspace {
+    size_t flags_offset;
+    size_t bytes;
+    int64_t nblk;
+};
+PrefillWorkspace prefill_workspace(const gqa_prefill_args *a);
+constexpr int64_t kMaxPrefillRowsHeads = int64_t(1) << 37;   // total_tokens * h_kv limit
 
 // Workspace layout for `num_chunks` wavefronts: two partial-triple slots per
 // wavefront, each R = G * t_q rows of (O[D] fp32) plus (m, l) fp32.

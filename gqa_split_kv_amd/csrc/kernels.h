@@ -49,7 +49,23 @@ struct PrefillParams {
     int32_t batch, h_q, h_kv, G;
     float scale_log2;          // scale * log2(e)
     int32_t split_pv;          // 1: split P V products everywhere
+    const uint8_t *v16;        // V in fp16 (the copy for bf16 input, v itself for fp16), or null
+    const uint8_t *vflags;     // [h_kv][nblk] 1 = 128-token block of V not fit for fp16 (bf16 input)
+    int64_t nblk;              // blocks in the copy (0: none)
 };
+
+// fp16 copy of bf16 V for the prefill's fast loop (vconv_kernel).
+struct VconvParams {
+    const uint8_t *v;          // [total, h_kv, D] bf16
+    uint8_t *v16;              // [total, h_kv, D] fp16
+    uint8_t *flags;            // [h_kv][nblk]
+    int64_t total;             // token rows
+    int64_t nblk;              // ceil(total / kPrefillVBlock)
+    int32_t h_kv;
+};
+
+// Enqueues vconv_kernel over nblk x h_kv workgroups.
+hipError_t launch_vconv(const VconvParams &p, int D, int h_kv, hipStream_t stream);
 
 // Enqueues the prefill kernel: `blocks` workgroups of kPrefillThreads.
 hipError_t launch_prefill(const PrefillParams &P, int in_dtype, int out_dtype, int D, int blocks,

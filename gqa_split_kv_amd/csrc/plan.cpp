@@ -117,7 +117,18 @@ int validate(const gqa_decode_args *a) {
     return GQA_OK;
 }
 
-int validate_prefill(const gqa_prefill_args *a) {
+PrefillWorkspace prefill_workspace(const gqa_prefill_args *a) {
+    PrefillWorkspace W = {0, 0, 0};
+    if (a->in_dtype != GQA_DTYPE_BF16 || a->split_pv != 0 || a->total_tokens <= 0) return W;
+    W.nblk = (a->total_tokens + kPrefillVBlock - 1) / kPrefillVBlock;
+    const size_t copy = static_cast<size_t>(a->total_tokens) * static_cast<size_t>(a->h_kv) *
+                        static_cast<size_t>(a->d_head) * 2;
+    W.flags_offset = round_up(copy, 256);
+    W.bytes = round_up(W.flags_offset + static_cast<size_t>(W.nblk) * static_cast<size_t>(a->h_kv), 256);
+    return W;
+}
+
+int validate_prefill(const gqa_prefill_args *a, bool check_workspace) {
     if (!a) return fail(GQA_ERR_NULL, "args is NULL");
     if (!a->q || !a->k || !a->v || !a->o || !a->seq_lens)
         return fail(GQA_ERR_NULL, "q, k, v, o and seq_lens must be non-NULL");
@@ -146,6 +157,18 @@ int validate_prefill(const gqa_prefill_args *a) {
     if (a->num_blocks < 0 || a->num_blocks > kMaxPrefillBlocks)
         return fail(GQA_ERR_ARG, "num_blocks %d out of range [0, %d]", a->num_blocks, kMaxPrefillBlocks);
     if (a->split_pv != 0 && a->split_pv != 1) return fail(GQA_ERR_ARG, "split_pv %d is not 0 or 1", a->split_pv);
+    if (a->total_tokens < 0 || (a->total_tokens > 0 && a->total_tokens > kMaxPrefillRowsHeads / a->h_kv))
+        return fail(GQA_ERR_ARG, "total_tokens %lld out of range [0, 2^37 / h_kv]",
+                    static_cast<long long>(a->total_tokens));
+    if (check_workspace && a->workspace) {
+        const PrefillWorkspace W = prefill_workspace(a);
+        if (W.bytes > 0) {
+            if (!aligned(a->workspace, 256)) return fail(GQA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+            if (a->workspace_bytes < W.bytes)
+                return fail(GQA_ERR_WORKSPACE, "workspace holds %zu bytes, the call needs %zu", a->workspace_bytes,
+                            W.bytes);
+        }
+    }
     return GQA_OK;
 }
 

@@ -13,12 +13,15 @@
 //     query heads of one (sequence, kv head), and sweeps the keys 0 .. its last
 //     token with the page's online-softmax fold; the rows are disjoint, so every
 //     tile normalises and stores its own outputs.
-//   * K and V go HBM/L2 -> registers -> LDS in 128-key stages (double buffered,
-//     one barrier per stage) that all 256 rows share, so the K/V bytes per output
-//     row fall with the tile height.  A stage is computed as two 64-key steps;
-//     each step's part of the next stage is loaded before the step and written to
-//     the other buffer after it.  LDS rows are XOR-swizzled in 16-byte chunks
-//     (one pattern for K, one for V) so the operand reads hit distinct banks.
+//   * K and V go HBM/L2 -> LDS in 128-key stages (double buffered, one barrier
+//     per stage) that all 256 rows share, so the K/V bytes per output row fall
+//     with the tile height.  The loads write LDS directly (buffer loads with the
+//     LDS as destination: no registers, no LDS store instructions), the next
+//     stage's loads in flight during the whole current stage.  A stage is
+//     computed as two 64-key steps.  LDS rows are XOR-swizzled in 16-byte chunks
+//     (one pattern for K, one for V) so the operand reads hit distinct banks; a
+//     direct load writes lane i's 16 bytes at base + 16 i, so the swizzle is
+//     applied by choosing which global chunk each lane fetches.
 //   * Each wavefront owns 32 rows as two 16-row N tiles of
 //     v_mfma_f32_16x16x32_{bf16,f16}: S^T = K Q^T with the keys on the M axis
 //     (the K rows are read from LDS in the key order that leaves lane l holding
@@ -26,13 +29,14 @@
 //     row sums come out of the matrix core, from the same rounded P).  The V^T
 //     operand comes straight out of LDS through transpose reads.  Two wavefronts
 //     share a SIMD (at most 256 VGPRs each, no AGPR traffic).
-//   * P V precision: by default P is rounded to fp16 and V read as fp16 (bf16 V
-//     is converted while it is staged: exact for magnitudes in fp16's normal
-//     range), one product per step.  A bf16 stage whose largest |v| is not in
-//     [2^-10, 2^16) sends the rest of the tile's sweep to the split product (P as
-//     a high and a low part in the input format, V as given, two products),
-//     which the diagonal band always uses and which the caller can ask for
-//     everywhere.
+//   * P V precision: by default P is rounded to fp16 and V read as fp16, one
+//     product per step.  For bf16 input a pre-pass (vconv_kernel) writes an fp16
+//     copy of V into the workspace -- exact for magnitudes in fp16's normal range
+//     -- and flags every 128-token block whose largest |v| is not in
+//     [2^-10, 2^16); from the first stage that touches a flagged block on, a
+//     tile's sweep uses the split product (P as a high and a low part in the
+//     input format, V as given, two products), which the diagonal band always
+//     uses and which the caller can ask for everywhere.
 //   * The running maximum is allowed to lag the true one by up to 8 (log2
 //     units): the accumulators are rescaled only when some row of an N tile
 //     exceeds its reference by more, which removes almost every rescale of the
@@ -147,15 +151,26 @@ struct PrefillTile {
     static constexpr int VEC = D / 16;              // d elements per lane per V row
     static constexpr int CH = ROWB / 16;            // 16-byte chunks per key row
     static constexpr int kChunks = kStepKeys * CH;  // 16-byte chunks of one step's K (or V) rows
-    static constexpr int kPer = (kChunks + kPrefillThreads - 1) / kPrefillThreads;   // per thread
+    static constexpr int kPer = kChunks / kPrefillThreads;   // direct loads per wavefront per step and tensor
     static constexpr int kOff = 7;                  // exponent offset of P: p <= 2^(8 + 7)
     static constexpr int kTileBytes = kStageKeys * LROW;
-    // LDS regions of a stage: K and V.  The fast loop stages V in fp16 (for bf16
-    // input converted on the way), the masked / split loop V as given.
+    // LDS regions of a stage buffer: K, and V (fp16 in the fast loop, as given
+    // in the masked / split loop).
     static constexpr int kRegions = 2;
     static constexpr int kK = 0, kV = 1;
+    static_assert(kChunks % kPrefillThreads == 0, "whole direct loads per wavefront");
     static constexpr uint32_t kOnesF16 = 0x3c003c00u;
     static constexpr uint32_t kOnesIn = kHalf ? 0x3c003c00u : 0x3f803f80u;
+
+    // 16 bytes per lane from buffer `r` at byte `off` straight into LDS: lane i
+    // writes dst + 16 i (dst is the same for the whole wavefront); a lane whose
+    // bytes lie beyond the buffer's range writes zeros.
+    __device__ __forceinline__ static void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t off) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
+    }
+    // Waits for this wavefront's outstanding vector-memory loads (the direct LDS
+    // loads among them: their data is in LDS once the counter drops).
+    __device__ __forceinline__ static void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
 
     // LDS layout of a K or V tile: key row r at r * LROW, its 16-byte chunk c at
     // chunk position c ^ swz(r) (K) or c ^ swzv(r) (V).  One K operand read hits
@@ -176,23 +191,6 @@ struct PrefillTile {
         const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) v4s *)(const_cast<uint8_t *>(p)));
         return __builtin_bit_cast(uint2, r);
-    }
-
-    // bf16 -> fp16 of two packed values (exact inside fp16's range: bf16's 8-bit
-    // significand fits in fp16's 11).
-    __device__ __forceinline__ static uint32_t bf16x2_to_f16x2(uint32_t w) {
-        const f32x2_t f = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
-    }
-    // Range of a tile's V for the fp16 product, on bf16 magnitude bits (which
-    // order like the magnitudes): the thread keeps the largest magnitude of its
-    // chunks (packed 16-bit maximum, two operations per word) and tests it once:
-    //   >= 2^16 (0x4780): a value would overflow fp16;
-    //   >= 2^-10 (0x3a80): the tile's largest value keeps ~14 significant bits in
-    //   fp16 even where smaller values fall into fp16's subnormals.
-    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-    __device__ __forceinline__ static u16x2_t mag_max(u16x2_t m, uint32_t w) {
-        return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w & 0x7fff7fffu));
     }
 
     // One step: S^T = K Q^T for the N tiles, online softmax with the lagging
@@ -256,8 +254,7 @@ struct PrefillTile {
                     else
                         mx = fmaxf(mx, sv[nt][h][i]);
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max_over_rows(mx);
             mxs[nt] = mx == -INFINITY ? -INFINITY : mx * sl2;   // scaled, log2 units
             move |= mxs[nt] > m_ref[nt] + kLagLog2;
         }
@@ -340,8 +337,8 @@ struct PrefillTile {
     }
 
     // Tile `tile` of (sequence b at token offset off, length len; kv head j).
-    __device__ __forceinline__ static void run(const PrefillParams &P, uint8_t (*lds)[kRegions][kTileBytes],
-                                               int *flags, int64_t off, int len, int j, int tile) {
+    __device__ __forceinline__ static void run(const PrefillParams &P, uint8_t (*buf0)[kTileBytes],
+                                               uint8_t (*buf1)[kTileBytes], int64_t off, int len, int j, int tile) {
         const int tid = static_cast<int>(threadIdx.x);
         const int wave = uniform32(tid / kWave);
         const int lane = lane_id();
@@ -389,19 +386,17 @@ struct PrefillTile {
         const uint8_t *kbase = P.k + (off * P.h_kv + j) * ROWB;
         const uint8_t *vbase = P.v + (off * P.h_kv + j) * ROWB;
 
-        // Chunk c of a tile: key row c / CH, bytes 16 (c % CH).  With fewer chunks
-        // than threads (d_head 64) the extra threads load nothing.
-        uint32_t goff[kPer], loffk[kPer], loffv[kPer];
-        bool cok[kPer];
+        // Direct load i of this wavefront fills LDS chunks p = 64 (kPer wave + i) +
+        // lane of a step's K (or V) region: row r = p / CH at position p % CH,
+        // which holds the row's global chunk (p % CH) ^ swz(r) (swzv(r) for V).
+        uint32_t gk[kPer], gv[kPer];
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const int c = tid + i * kPrefillThreads;
-            cok[i] = c < kChunks;
-            const int r = (cok[i] ? c : 0) / CH;
-            const int col = (cok[i] ? c : 0) - r * CH;
-            goff[i] = static_cast<uint32_t>(r * rowstride + col * 16);
-            loffk[i] = static_cast<uint32_t>(r * LROW + (col ^ swz(r)) * 16);
-            loffv[i] = static_cast<uint32_t>(r * LROW + (col ^ swzv(r)) * 16);
+            const int p = (wave * kPer + i) * kWave + lane;
+            const int r = p / CH;
+            const int pos = p - r * CH;
+            gk[i] = static_cast<uint32_t>(r * rowstride + (pos ^ swz(r)) * 16);
+            gv[i] = static_cast<uint32_t>(r * rowstride + (pos ^ swzv(r)) * 16);
         }
         // Per-lane LDS offsets of the step's operands (fixed for the whole tile):
         // K operand of block b, piece p: row 8(m/4) + 4b + m%4, chunk 4p + kg.
@@ -422,78 +417,59 @@ struct PrefillTile {
             for (int cl = 0; cl < 4; ++cl)
                 voff[cl] = static_cast<uint32_t>((8 * kg + e) * LROW + 32 * (cl ^ e) + 16 * (q >> 1) + 8 * (q & 1));
         }
-        // Staging moves one step's rows (part `pt` of stage `sg`) at a time.
-        uint4 rk[kPer], rv[kPer];
-        auto fetch = [&](int sg, int pt) {
-            const int k0 = sg * kStageKeys + pt * kStepKeys;
-            const uint32_t bytes = k0 < len ? static_cast<uint32_t>(min(kStepKeys, len - k0) * rowstride) : 0u;
-            const int64_t boff = static_cast<int64_t>(k0) * rowstride;
-            const auto rsk = make_rsrc(kbase + boff, bytes);
-            const auto rsv = make_rsrc(vbase + boff, bytes);
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                rk[i] = buffer_load16<0>(rsk, goff[i]);
-                rv[i] = buffer_load16<0>(rsv, goff[i]);
-            }
-        };
-        // Stage tile st into buffer st & 1 for the fast loop: K, and V in fp16 (bf16
-        // input is converted on the way and the tile's range is recorded in flag
-        // slot st % 3: word 0 set if some |v| >= 2^16, word 1 set if some |v| >=
-        // 2^-10; the fp16 product is used only for tiles with word 0 clear and word
-        // 1 set).
-        auto stash_fast = [&](int st, int pt) {
-            uint8_t(*B)[kTileBytes] = lds[st & 1];
-            const uint32_t po = static_cast<uint32_t>(pt * kStepKeys * LROW);
-            u16x2_t mag = {0, 0};
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                if (cok[i]) {
-                    *reinterpret_cast<uint4 *>(B[kK] + po + loffk[i]) = rk[i];
-                    const uint4 x = rv[i];
-                    if constexpr (kHalf) {
-                        *reinterpret_cast<uint4 *>(B[kV] + po + loffv[i]) = x;
-                    } else {
-                        mag = mag_max(mag_max(mag_max(mag_max(mag, x.x), x.y), x.z), x.w);
-                        *reinterpret_cast<uint4 *>(B[kV] + po + loffv[i]) =
-                            make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
-                                       bf16x2_to_f16x2(x.w));
+        // Stages that run the fast (fp16 P V) loop: every stage below the tile's
+        // first token, up to the first stage touching a 128-token block of V that
+        // the pre-pass flagged (blocks at or beyond the copy's end count as
+        // flagged).  Stage s holds tokens off + 128 s .. + 127 of the packed axis.
+        const int nfull = min(nstages, (tstart + 1) / kStageKeys);
+        int nfast = 0;
+        if (!P.split_pv) {
+            if constexpr (kHalf) {
+                nfast = nfull;
+            } else if (nfull > 0) {
+                constexpr int VB = kPrefillVBlock;
+                const int64_t g_lo = off / VB;
+                const int64_t g_hi = (off + static_cast<int64_t>(nfull) * kStageKeys - 1) / VB;
+                int64_t g_bad = -1;
+                for (int64_t g = g_lo; g <= g_hi; g += kWave) {
+                    const int64_t gl = g + lane;
+                    const bool bad = gl <= g_hi && (gl >= P.nblk || P.vflags[j * P.nblk + gl] != 0);
+                    const unsigned long long mask = __ballot(bad);
+                    if (mask) {
+                        g_bad = g + (__ffsll(static_cast<long long>(mask)) - 1);
+                        break;
                     }
                 }
+                nfast = nfull;
+                if (g_bad >= 0) {
+                    const int64_t t = g_bad * VB - off - kStageKeys + 1;   // first stage reaching block g_bad
+                    const int64_t s_bad = t <= 0 ? 0 : (t + kStageKeys - 1) / kStageKeys;
+                    nfast = static_cast<int>(min(static_cast<int64_t>(nfull), s_bad));
+                }
+                nfast = uniform32(nfast);
             }
-            if constexpr (!kHalf) {
-                const unsigned m = mag.x > mag.y ? mag.x : mag.y;
-                if (m >= 0x4780u) flags[2 * (st % 3)] = 1;
-                if (m >= 0x3a80u) flags[2 * (st % 3) + 1] = 1;
-            }
-        };
-        // Stage tile st as given (the masked / split loop), or only its V (`v_only`:
-        // re-staging, over its fp16 copy, the tile the fast loop stopped at).
-        auto stash_raw = [&](int st, int pt, bool v_only) {
-            uint8_t(*B)[kTileBytes] = lds[st & 1];
-            const uint32_t po = static_cast<uint32_t>(pt * kStepKeys * LROW);
+        }
+        const uint8_t *vfast = nfast > 0 ? P.v16 + (off * P.h_kv + j) * ROWB : vbase;
+        // Loads stage sg into buffer B (both 64-key parts, K and V); rows at or
+        // beyond the sequence's end read as zero.  V comes from the fp16 copy for
+        // stages of the fast loop.
+        auto issue = [&](uint8_t (*B)[kTileBytes], int sg) {
+            const uint8_t *vsrc = sg < nfast ? vfast : vbase;
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                if (cok[i]) {
-                    if (!v_only) *reinterpret_cast<uint4 *>(B[kK] + po + loffk[i]) = rk[i];
-                    *reinterpret_cast<uint4 *>(B[kV] + po + loffv[i]) = rv[i];
+            for (int pt = 0; pt < kStageSteps; ++pt) {
+                const int k0 = sg * kStageKeys + pt * kStepKeys;
+                const uint32_t bytes = k0 < len ? static_cast<uint32_t>(min(kStepKeys, len - k0) * rowstride) : 0u;
+                const int64_t boff = static_cast<int64_t>(k0) * rowstride;
+                const auto rsk = make_rsrc(kbase + boff, bytes);
+                const auto rsv = make_rsrc(vsrc + boff, bytes);
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    const uint32_t lo = static_cast<uint32_t>(pt * kStepKeys * LROW + (wave * kPer + i) * kWave * 16);
+                    lds_load16(rsk, B[kK] + lo, gk[i]);
+                    lds_load16(rsv, B[kV] + lo, gv[i]);
                 }
             }
         };
-        // Slot st % 3 is written while tile st is staged (step st - 1), read in step
-        // st and cleared in step st + 1 -- each separated from the next use by a
-        // barrier.
-        auto tile_fast = [&](int st) -> bool {
-            if constexpr (kHalf) return true;
-            else return uniform32(flags[2 * (st % 3)]) == 0 && uniform32(flags[2 * (st % 3) + 1]) != 0;
-        };
-        auto clear_flag = [&](int st) {
-            if constexpr (!kHalf)
-                if (tid == 0) {
-                    flags[2 * ((st + 2) % 3)] = 0;
-                    flags[2 * ((st + 2) % 3) + 1] = 0;
-                }
-        };
-
         float m_ref[kNT];
         f32x4_t accl[kNT];
         f32x4_t acc[kNT][VEC];
@@ -504,63 +480,65 @@ struct PrefillTile {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) acc[nt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        if constexpr (!kHalf) {
-            if (tid < 4) flags[tid] = 0;   // slots of tiles 0 and 1
-            __syncthreads();
-        }
-#pragma unroll
-        for (int pt = 0; pt < kStageSteps; ++pt) {
-            fetch(0, pt);
-            stash_fast(0, pt);
-        }
+        issue(buf0, 0);
+        wait_loads();
         __syncthreads();
         // Steps whose keys every row of the tile sees (below the tile's first
         // token) run unmasked with fp16 P V; the rest -- the tile's diagonal band,
-        // and everything from a tile whose V range does not suit fp16 on -- masked
-        // with the exact split product, each wavefront skipping the steps beyond its
-        // own last token.  Two loops, so the fast one carries no masking or fallback
-        // code at all.
-        // One barrier per stage of kStageSteps steps, so the two wavefronts of a
-        // SIMD can drift apart within a stage.  Each step's part of the next stage
-        // is fetched before the step and staged after it (into the other buffer).
-        const int nfull = min(nstages, (tstart + 1) / kStageKeys);
-        int st = 0;
-        for (; st < nfull; ++st) {
-            if (P.split_pv || !tile_fast(st)) break;   // the same for the whole workgroup
-            clear_flag(st);
-            const int nx = min(st + 1, nstages - 1);
+        // and everything from the first stage whose V range does not suit fp16 on
+        // -- masked with the exact split product, each wavefront skipping the steps
+        // beyond its own last token.  Two loops, so the fast one carries no masking
+        // or fallback code at all.  Each stage starts the loads of the next one
+        // into the other buffer and ends with one barrier.  The buffers are two
+        // separate LDS arrays named at every use, so the compiler can tell that
+        // the operand reads of one never touch the loads in flight to the other.
+        auto stage_fast = [&](uint8_t (*cur)[kTileBytes], uint8_t (*nxt)[kTileBytes], int st) {
+            if (st + 1 < nstages) issue(nxt, st + 1);
 #pragma unroll
             for (int pt = 0; pt < kStageSteps; ++pt) {
-                fetch(nx, pt);
-                step<false, false>(lds[st & 1][kK] + pt * kStepKeys * LROW, lds[st & 1][kV] + pt * kStepKeys * LROW,
+                // Each step is scheduled on its own: interleaving two steps would
+                // need more than the 256 registers of two wavefronts per SIMD.
+                __builtin_amdgcn_sched_barrier(0);
+                step<false, false>(cur[kK] + pt * kStepKeys * LROW, cur[kV] + pt * kStepKeys * LROW,
                                    st * kStageKeys + pt * kStepKeys, koff, voff, qop, cap, sl2, m_ref, accl, acc);
-                stash_fast(st + 1, pt);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            wait_loads();
             __syncthreads();
-        }
-        // Stage st was staged for the fast loop; for bf16 input its V is put back as
-        // given (fetched again) before the masked / split loop reads it.
-        if constexpr (!kHalf) {
+        };
+        auto stage_slow = [&](uint8_t (*cur)[kTileBytes], uint8_t (*nxt)[kTileBytes], int st) {
+            if (st + 1 < nstages) issue(nxt, st + 1);
 #pragma unroll
             for (int pt = 0; pt < kStageSteps; ++pt) {
-                fetch(st, pt);
-                stash_raw(st, pt, true);
-            }
-            __syncthreads();
-        }
-        for (; st < nstages; ++st) {
-            const int nx = min(st + 1, nstages - 1);
-#pragma unroll
-            for (int pt = 0; pt < kStageSteps; ++pt) {
-                fetch(nx, pt);
+                __builtin_amdgcn_sched_barrier(0);
                 const int k0 = st * kStageKeys + pt * kStepKeys;
                 if (k0 < wkeys)
-                    step<true, true>(lds[st & 1][kK] + pt * kStepKeys * LROW, lds[st & 1][kV] + pt * kStepKeys * LROW,
-                                     k0, koff, voff, qop, cap, sl2, m_ref, accl, acc);
-                stash_raw(st + 1, pt, false);
+                    step<true, true>(cur[kK] + pt * kStepKeys * LROW, cur[kV] + pt * kStepKeys * LROW, k0, koff,
+                                     voff, qop, cap, sl2, m_ref, accl, acc);
             }
+            wait_loads();
             __syncthreads();
+        };
+        // Stage st computes from buffer st & 1; the loops go two stages at a time
+        // so that every call names its buffers statically.
+        int st = 0;
+        for (; st + 1 < nfast; st += 2) {
+            stage_fast(buf0, buf1, st);
+            stage_fast(buf1, buf0, st + 1);
         }
+        if (st < nfast) {
+            stage_fast(buf0, buf1, st);
+            ++st;
+        }
+        if (st < nstages && (st & 1)) {
+            stage_slow(buf1, buf0, st);
+            ++st;
+        }
+        for (; st + 1 < nstages; st += 2) {
+            stage_slow(buf0, buf1, st);
+            stage_slow(buf1, buf0, st + 1);
+        }
+        if (st < nstages) stage_slow(buf0, buf1, st);
 
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
@@ -582,8 +560,9 @@ struct PrefillTile {
 template <int kIn, int kOut, int D>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams P) {
     using T = PrefillTile<kIn, kOut, D>;
-    __shared__ __align__(16) uint8_t lds[2][T::kRegions][T::kTileBytes];
-    __shared__ int flags[6];
+    // The two stage buffers (K and V regions each) are separate arrays; see run().
+    __shared__ __align__(16) uint8_t buf0[T::kRegions][T::kTileBytes];
+    __shared__ __align__(16) uint8_t buf1[T::kRegions][T::kTileBytes];
     const int tt = kPrefillRows / P.G;
     const int64_t items = count_items(P.seq_lens, P.batch, tt, P.h_kv);
     const int64_t g = gridDim.x;
@@ -597,8 +576,66 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         const int ntile = static_cast<int>(tiles_of(len, tt));
         const int j = static_cast<int>(local / ntile);
         const int tile = ntile - 1 - static_cast<int>(local - static_cast<int64_t>(j) * ntile);   // longest first
-        T::run(P, lds, flags, off, len, j, tile);
+        T::run(P, buf0, buf1, off, len, j, tile);
     }
+}
+
+// fp16 copy of bf16 V and the range flags of its 128-token blocks: workgroup
+// j * nblk + g converts rows g * 128 .. + 127 (those below `total`) of kv head j
+// and sets flags[j * nblk + g] to 1 if the block's largest |v| is not in
+// [2^-10, 2^16) (or is not finite), else 0.  The conversion is exact for values
+// in fp16's normal range; flagged blocks are never read from the copy.
+template <int D>
+__global__ __launch_bounds__(kVconvThreads) void vconv_kernel(VconvParams p) {
+    constexpr int ROWB = D * 2;
+    constexpr int CH = ROWB / 16;
+    constexpr int kChunks = kPrefillVBlock * CH;
+    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+    const int64_t idx = blockIdx.x;
+    const int j = static_cast<int>(idx / p.nblk);
+    const int64_t g = idx - static_cast<int64_t>(j) * p.nblk;
+    const int tid = static_cast<int>(threadIdx.x);
+    u16x2_t mag = {0, 0};
+    for (int c = tid; c < kChunks; c += kVconvThreads) {
+        const int64_t row = g * kPrefillVBlock + c / CH;
+        if (row >= p.total) break;   // rows grow with c
+        const int64_t o = (row * p.h_kv + j) * ROWB + (c % CH) * 16;
+        const uint4 x = *reinterpret_cast<const uint4 *>(p.v + o);
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        uint32_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2_t, w[i] & 0x7fff7fffu));
+            const f32x2_t f = {__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xffff0000u)};
+            h[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+        }
+        *reinterpret_cast<uint4 *>(p.v16 + o) = make_uint4(h[0], h[1], h[2], h[3]);
+    }
+    // Largest magnitude bits of the block (bf16 magnitude bits order like the
+    // magnitudes; NaN and inf sort above every finite value).
+    unsigned m = mag.x > mag.y ? mag.x : mag.y;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const unsigned y = static_cast<unsigned>(__shfl_xor(static_cast<int>(m), d));
+        m = m > y ? m : y;
+    }
+    __shared__ unsigned wmax[kVconvThreads / kWave];
+    if (lane_id() == 0) wmax[tid / kWave] = m;
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int i = 1; i < kVconvThreads / kWave; ++i) m = m > wmax[i] ? m : wmax[i];
+        p.flags[idx] = (m >= 0x4780u || m < 0x3a80u) ? 1 : 0;
+    }
+}
+
+hipError_t launch_vconv_impl(const VconvParams &p, int D, int h_kv, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(p.nblk * h_kv));   // <= 2^30 by the total_tokens * h_kv limit
+    if (D == 128)
+        hipLaunchKernelGGL(vconv_kernel<128>, grid, dim3(kVconvThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(vconv_kernel<64>, grid, dim3(kVconvThreads), 0, stream, p);
+    return hipGetLastError();
 }
 
 template <int kIn, int kOut>
@@ -628,6 +665,10 @@ hipError_t launch_prefill(const PrefillParams &P, int in_dtype, int out_dtype, i
                                                      : launch_pio<kBf16, kF32>(P, D, blocks, stream);
     return out_dtype == kF16 ? launch_pio<kF16, kF16>(P, D, blocks, stream)
                              : launch_pio<kF16, kF32>(P, D, blocks, stream);
+}
+
+hipError_t launch_vconv(const VconvParams &p, int D, int h_kv, hipStream_t stream) {
+    return launch_vconv_impl(p, D, h_kv, stream);
 }
 
 hipError_t prefill_occupancy(int in_dtype, int out_dtype, int D, int *blocks_per_cu) {

@@ -31,7 +31,7 @@
 //     16 significant bits); for fp32 input v_mfma_f32_16x16x4_f32 takes one key
 //     per lane and stays in fp32.
 //   * The softmax state of query head g lives in lanes with lane % 16 == g; the
-//     block maximum is reduced across the 4 lane groups with two cross-lane
+//     block maximum is reduced across the 4 lane groups with two row-swap
 //     exchanges, l is kept per lane and reduced once per piece.  Scores are kept
 //     in the log2 domain (scale * log2 e folded in) and exponentiated with
 //     v_exp_f32; the partial m is stored in that domain and merged with exp2.
@@ -110,8 +110,7 @@ __device__ __forceinline__ void softmax_step(float (&sv)[N], float &m_run, float
     float mx = sv[0];
 #pragma unroll
     for (int i = 1; i < N; ++i) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_over_rows(mx);
     const float m_new = fmaxf(m_run, mx);
     // A row that has seen no key yet (all masked) keeps the identity (-inf, 0, 0):
     // exponentiate against 0 instead of -inf so that nothing becomes NaN.

@@ -27,8 +27,17 @@
  *
  * Supported: d_head in {64, 128}; G in 1..16; (in, out) dtypes (bf16, bf16),
  * (bf16, f32), (f16, f16), (f16, f32).  q, k, v, o 16-byte aligned, seq_lens
- * 4-byte aligned.  No workspace: every output row is written by exactly one
- * workgroup, so nothing is allocated and the call is capturable in a HIP graph.
+ * 4-byte aligned.  Every output row is written by exactly one workgroup (no
+ * cross-workgroup reduction).
+ *
+ * Workspace: only bf16 input with split_pv = 0 and total_tokens > 0 uses one --
+ * an fp16 copy of V (total_tokens * h_kv * d_head * 2 bytes) and one flag byte
+ * per 128-token block and kv head, both rewritten by every call (nothing needs
+ * initialising).  gqa_prefill_workspace_bytes() gives its size.  With workspace
+ * NULL the library uses its own, per (device, stream), grown with hipMalloc
+ * (not capturable in a HIP graph; freed by gqa_release()); a caller-provided
+ * workspace (256-byte aligned) makes the call capturable.  Calls sharing one
+ * workspace must be ordered (one stream).
  *
  * Asynchrony and errors as in gqa_decode.h: work is enqueued on `stream`, host
  * errors return a gqa_status before anything is enqueued (o untouched), and
@@ -51,13 +60,21 @@ extern "C" {
  *             0..2^20.  The result does not depend on it.
  * split_pv    Precision of the P V product.  0 (default): P is rounded to fp16
  *             (11 significant bits, times a common power of two that cancels) and
- *             V taken in fp16, one matrix-core product; for bf16 input a 128-key
- *             block of V whose largest magnitude is not in [2^-10, 2^16) switches
- *             the rest of that tile's sweep to the split product, so the fp16
- *             rounding of V never loses range or precision.  Typical error
- *             against the exact result: relative L2 ~1e-4.  1: P split into a
- *             high and a low 16-bit part everywhere (about 16 significant bits,
- *             two products, ~1.5x the matrix-core work); error ~1e-6.
+ *             V taken in fp16, one matrix-core product; for bf16 input V is read
+ *             from an fp16 copy made by the call, and a tile's sweep switches to
+ *             the split product from the first 128-key stage that touches a
+ *             128-token block of V whose largest magnitude is not in
+ *             [2^-10, 2^16), so the fp16 rounding of V never loses range or
+ *             precision.  Typical error against the exact result: relative L2
+ *             ~1e-4.  1: P split into a high and a low 16-bit part everywhere
+ *             (about 16 significant bits, two products, ~1.5x the matrix-core
+ *             work); error ~1e-6.  No workspace.
+ * total_tokens  Rows held by q, k, v and o: at least sum(seq_lens) (the fp16
+ *             copy covers V rows 0 .. total_tokens - 1, and V must hold them).
+ *             Used only by bf16 input with split_pv = 0; 0 there means unknown:
+ *             no copy is made and every stage uses the split product, as with
+ *             split_pv = 1.
+ * workspace, workspace_bytes  See above; ignored where no workspace is used.
  */
 typedef struct gqa_prefill_args {
     const void *q;
@@ -75,13 +92,18 @@ typedef struct gqa_prefill_args {
     int32_t num_blocks;
     void *stream;       /* hipStream_t; NULL = the null stream              */
     int32_t split_pv;   /* 0 or 1, see above                                */
+    int64_t total_tokens;
+    void *workspace;
+    size_t workspace_bytes;
 } gqa_prefill_args;
 
-/* gqa_prefill -- bf16 q/k/v in, bf16 o out.  Returns a gqa_status. */
+/* gqa_prefill -- bf16 q/k/v in, bf16 o out, total_tokens = sum(seq_lens) rows
+ * (the fp16 copy of V lives in the library's workspace).  Returns a gqa_status. */
 int gqa_prefill(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
-                int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream);
+                int32_t batch, int64_t total_tokens, int32_t h_q, int32_t h_kv, int32_t d_head, float scale,
+                void *stream);
 
-/* gqa_prefill_f16 -- IEEE fp16 q/k/v in, fp16 o out. */
+/* gqa_prefill_f16 -- IEEE fp16 q/k/v in, fp16 o out (no workspace). */
 int gqa_prefill_f16(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
                     int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream);
 
@@ -92,8 +114,14 @@ int gqa_prefill_ex(const gqa_prefill_args *args);
  * would return before enqueueing anything: GQA_ERR_NULL, GQA_ERR_SHAPE (batch,
  * h_q or h_kv <= 0, h_q not a multiple of h_kv), GQA_ERR_UNSUPPORTED (d_head, G,
  * h_kv above 65536 or the dtype pair), GQA_ERR_ALIGN, GQA_ERR_SCALE, GQA_ERR_ARG
- * (num_blocks out of range, split_pv not 0 or 1). */
+ * (num_blocks out of range, split_pv not 0 or 1, total_tokens negative or above
+ * 2^40), GQA_ERR_WORKSPACE (a caller workspace that is not 256-byte aligned or
+ * smaller than the call needs). */
 int gqa_prefill_validate(const gqa_prefill_args *args);
+
+/* Workspace bytes the call needs (0 where none is used), after the checks of
+ * gqa_prefill_validate except the workspace's own.  Host only. */
+int gqa_prefill_workspace_bytes(const gqa_prefill_args *args, size_t *bytes);
 
 #ifdef __cplusplus
 }

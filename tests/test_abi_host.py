@@ -233,4 +233,35 @@ def test_prefill_validation(lib):
 
 
 def test_prefill_args_struct_size(lib):
-    assert ctypes.sizeof(B.GqaPrefillArgs) == 5 * 8 + 4 * 4 + 4 + 3 * 4 + 8 + 8
+    # ... stream, split_pv (+4 bytes padding), total_tokens, workspace, workspace_bytes
+    assert ctypes.sizeof(B.GqaPrefillArgs) == 5 * 8 + 4 * 4 + 4 + 3 * 4 + 8 + 8 + 8 + 8 + 8
+    assert B.GqaPrefillArgs.total_tokens.offset == 88
+
+
+def test_prefill_total_tokens_and_workspace_rules(lib):
+    assert _pvalidate(total_tokens=-1) == B.GQA_ERR_ARG and "total_tokens" in B.last_error_message()
+    assert _pvalidate(total_tokens=1 << 37) == B.GQA_OK                       # h_kv 1
+    assert _pvalidate(total_tokens=(1 << 37) + 1) == B.GQA_ERR_ARG
+    assert _pvalidate(total_tokens=1 << 34, h_q=64, h_kv=8) == B.GQA_OK
+    assert _pvalidate(total_tokens=(1 << 34) + 1, h_q=64, h_kv=8) == B.GQA_ERR_ARG
+    # Workspace: an fp16 copy of V (rows x h_kv x d x 2 bytes, 256-aligned) then
+    # one flag byte per 128-token block and kv head, rounded up to 256 bytes.
+    a = _pargs(total_tokens=1000, h_q=8, h_kv=2)
+    copy = 1000 * 2 * 128 * 2
+    assert B.gqa_prefill_workspace_bytes(a) == copy + 256     # 8 blocks x 2 heads of flags
+    assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=129, d_head=64)) == 16640 + 256   # 16512 -> 16640
+    assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=1000, split_pv=1)) == 0
+    assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=0)) == 0
+    assert B.gqa_prefill_workspace_bytes(
+        _pargs(total_tokens=1000, in_dtype=B.GQA_DTYPE_F16, out_dtype=B.GQA_DTYPE_F16)) == 0
+    need = B.gqa_prefill_workspace_bytes(a)
+    assert _pvalidate(total_tokens=1000, h_q=8, h_kv=2, workspace=0x100000, workspace_bytes=need) == B.GQA_OK
+    assert _pvalidate(total_tokens=1000, h_q=8, h_kv=2, workspace=0x100000,
+                      workspace_bytes=need - 1) == B.GQA_ERR_WORKSPACE
+    assert _pvalidate(total_tokens=1000, h_q=8, h_kv=2, workspace=0x100080,
+                      workspace_bytes=need) == B.GQA_ERR_WORKSPACE and "aligned" in B.last_error_message()
+    # A workspace is not checked where the call uses none.
+    assert _pvalidate(total_tokens=1000, split_pv=1, workspace=0x100080, workspace_bytes=1) == B.GQA_OK
+    # The size query skips the caller workspace's own checks.
+    assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=1000, h_q=8, h_kv=2, workspace=0x100080,
+                                                workspace_bytes=1)) == need

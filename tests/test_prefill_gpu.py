@@ -143,6 +143,60 @@ def test_prefill_v_band_beyond_fp16_range():
     assert np.sqrt(((o - ref) ** 2).sum() / (ref ** 2).sum()) <= 1e-3
 
 
+def test_prefill_v_band_in_unaligned_sequences():
+    """Sequences that start off the 128-token blocks of the fp16 copy's range
+    flags (offsets 77 and 1077), with two key rows of magnitude ~2^20 inside the
+    second sequence: every stage that overlaps the flagged block must take the
+    exact product, the stages before it the fp16 one."""
+    import torch
+    lens = [77, 1000, 333]
+    c = _scaled_v(host_prefill_case(3, 8, 2, 128, lens, "bf16", seed=29), 20, rows=slice(600, 602))
+    ref = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    q, k, v, sl = upload(c)
+    row_scale = np.maximum(np.abs(ref).max(axis=-1, keepdims=True), 1.0)
+    for sp in (0, 1):
+        o = _run(q, k, v, sl, c.scale, torch.float32, split_pv=sp).cpu().numpy().astype(np.float64)
+        assert np.isfinite(o).all()
+        err = np.abs(o - ref) / row_scale
+        assert err.max() <= 2e-3, (sp, err.max())
+
+
+def test_prefill_caller_workspace_poisoned_and_reused():
+    """A caller workspace filled with NaN patterns gives the same bits as the
+    library's own, on two calls in a row (the second smaller, other values)."""
+    import torch
+    cases = [host_prefill_case(3, 16, 2, 128, [900, 333, 1], "bf16", seed=30),
+             host_prefill_case(2, 8, 1, 64, [129, 64], "bf16", seed=31)]
+    a0 = B.make_prefill_args(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 3, 16, 2, 128, 0.1, B.GQA_DTYPE_BF16,
+                             B.GQA_DTYPE_BF16, total_tokens=1234)
+    need = B.gqa_prefill_workspace_bytes(a0)
+    assert need == 1234 * 2 * 128 * 2 + 256           # copy (256-aligned) + 10 blocks x 2 heads of flags
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    for c in cases:
+        q, k, v, sl = upload(c)
+        ref = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+        own = _run(q, k, v, sl, c.scale, torch.float32)
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+        B.prefill(q, k, v, sl, scale=c.scale, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, own)
+        _check(out, ref, "caller workspace")
+
+
+def test_prefill_unknown_total_tokens_uses_split_product():
+    """bf16 with total_tokens = 0 makes no fp16 copy: the result is bit-identical
+    to split_pv = 1."""
+    import torch
+    c = host_prefill_case(2, 8, 2, 128, [500, 260], "bf16", seed=32)
+    q, k, v, sl = upload(c)
+    o0 = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    B.prefill(q, k, v, sl, scale=c.scale, out=o0, total_tokens=0)
+    o1 = _run(q, k, v, sl, c.scale, torch.float32, split_pv=1)
+    assert torch.equal(o0, o1)
+    o2 = _run(q, k, v, sl, c.scale, torch.float32)
+    assert not torch.equal(o2, o1)                    # the default does take the fp16 path
+
+
 def test_prefill_empty_and_single_token_sequences():
     import torch
     lens = [0, 1, 0, 1, 2]
@@ -200,7 +254,7 @@ def test_prefill_c_names():
     ref = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
     q, k, v, sl = upload(c)
     out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
-    B.gqa_prefill(q, k, v, out, sl, 2, 8, 2, 128, c.scale)
+    B.gqa_prefill(q, k, v, out, sl, 2, 140, 8, 2, 128, c.scale)
     torch.cuda.synchronize()
     _check(out, ref, "gqa_prefill")
     c16 = host_prefill_case(2, 8, 2, 128, [100, 40], "f16", seed=26)
