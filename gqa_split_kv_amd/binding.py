@@ -123,7 +123,7 @@ def lib() -> ctypes.CDLL:
     L.gqa_release.restype = None
     L.gqa_prefill.argtypes = [P, P, P, P, P, i32, ctypes.c_int64, i32, i32, i32, ctypes.c_float, P]
     L.gqa_prefill.restype = ctypes.c_int
-    L.gqa_prefill_f16.argtypes = sig
+    L.gqa_prefill_f16.argtypes = [P, P, P, P, P, i32, ctypes.c_int64, i32, i32, i32, ctypes.c_float, P]
     L.gqa_prefill_f16.restype = ctypes.c_int
     L.gqa_prefill_ex.argtypes = [ctypes.POINTER(GqaPrefillArgs)]
     L.gqa_prefill_ex.restype = ctypes.c_int
@@ -307,11 +307,11 @@ def gqa_prefill(q, k, v, o, seq_lens, batch: int, total_tokens: int, h_q: int, h
     return st
 
 
-def gqa_prefill_f16(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_head: int,
+def gqa_prefill_f16(q, k, v, o, seq_lens, batch: int, total_tokens: int, h_q: int, h_kv: int, d_head: int,
                     scale: float, stream=None) -> int:
     """Causal prefill, fp16 in / fp16 out."""
-    st = lib().gqa_prefill_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens), batch, h_q, h_kv,
-                               d_head, float(scale), _stream(stream))
+    st = lib().gqa_prefill_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens), batch, int(total_tokens), h_q,
+                               h_kv, d_head, float(scale), _stream(stream))
     _check(st)
     return st
 

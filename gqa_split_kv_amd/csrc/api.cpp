@@ -176,27 +176,28 @@ int prefill_ex(const gqa_prefill_args *a) {
     P.split_pv = a->split_pv;
     hipStream_t stream = reinterpret_cast<hipStream_t>(a->stream);
     const gqa::PrefillWorkspace W = gqa::prefill_workspace(a);
-    P.v16 = a->in_dtype == GQA_DTYPE_F16 ? P.v : nullptr;
+    P.vt = nullptr;
     P.vflags = nullptr;
-    P.nblk = 0;
+    P.nvb = 0;
     if (W.bytes > 0) {
         void *ws = a->workspace;
         if (!ws) {
             st = owned_workspace(dev, stream, W.bytes, &ws);
             if (st != GQA_OK) return st;
         }
-        gqa::VconvParams V;
+        gqa::VprepParams V;
         V.v = P.v;
-        V.v16 = static_cast<uint8_t *>(ws);
+        V.vt = static_cast<uint8_t *>(ws);
         V.flags = static_cast<uint8_t *>(ws) + W.flags_offset;
-        V.total = a->total_tokens;
-        V.nblk = W.nblk;
+        V.seq_lens = a->seq_lens;
+        V.batch = a->batch;
         V.h_kv = a->h_kv;
-        e = gqa::launch_vconv(V, a->d_head, a->h_kv, stream);
-        if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "V conversion kernel launch failed: %s", hipGetErrorString(e));
-        P.v16 = V.v16;
+        V.nvb = W.nvb;
+        e = gqa::launch_vprep(V, a->in_dtype, a->d_head, stream);
+        if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "V copy kernel launch failed: %s", hipGetErrorString(e));
+        P.vt = V.vt;
         P.vflags = V.flags;
-        P.nblk = W.nblk;
+        P.nvb = W.nvb;
     }
     e = gqa::launch_prefill(P, a->in_dtype, a->out_dtype, a->d_head, blocks, stream);
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "prefill kernel launch failed: %s", hipGetErrorString(e));
@@ -295,9 +296,10 @@ int gqa_prefill(const void *q, const void *k, const void *v, void *o, const int3
 }
 
 int gqa_prefill_f16(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
-                    int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream) {
-    const gqa_prefill_args a =
-        make_prefill_args(q, k, v, o, seq_lens, batch, 0, h_q, h_kv, d_head, scale, stream, GQA_DTYPE_F16);
+                    int32_t batch, int64_t total_tokens, int32_t h_q, int32_t h_kv, int32_t d_head, float scale,
+                    void *stream) {
+    const gqa_prefill_args a = make_prefill_args(q, k, v, o, seq_lens, batch, total_tokens, h_q, h_kv, d_head,
+                                                 scale, stream, GQA_DTYPE_F16);
     return gqa_prefill_ex(&a);
 }
 

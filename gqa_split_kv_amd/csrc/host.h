@@ -38,10 +38,10 @@ constexpr int kSplitMergeBelowBlocks = 256;
 #endif
 constexpr int kPrefillThreads = GQA_PREFILL_THREADS;
 constexpr int kPrefillRows = GQA_PREFILL_ROWS;
-// Tokens per range-checked block of the prefill's fp16 copy of bf16 V, and the
+// Keys per step of the prefill (one block of its transposed V copy), and the
 // workgroup size of the kernel that makes the copy.
-constexpr int kPrefillVBlock = 128;
-constexpr int kVconvThreads = 256;
+constexpr int kPrefillStepKeys = 64;
+constexpr int kVprepThreads = 256;
 constexpr int kMaxG = 16;           // rows (query heads x query tokens) per kv head in one 16-wide MFMA tile
 constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxPrefillBlocks = 1 << 20;
@@ -68,13 +68,14 @@ int validate(const gqa_decode_args *a);
 // workspace is checked too unless `check_workspace` is false.
 int validate_prefill(const gqa_prefill_args *a, bool check_workspace = true);
 
-// Prefill workspace: the fp16 copy of V [total_tokens, h_kv, D] at 0, the block
-// flags [h_kv][nblk] (bytes) at flags_offset.  bytes = 0 (and nblk = 0) when the
-// call makes no copy (fp16 input, split_pv = 1, or total_tokens = 0).
+// Prefill workspace: the transposed fp16 copy of V, [h_kv][nvb][D][64], at 0 and
+// the step flags [h_kv][nvb] (bytes) at flags_offset, nvb = ceil(total_tokens /
+// 64) + batch (at least the number of 64-key steps over all sequences).  bytes = 0
+// (and nvb = 0) when the call makes no copy (split_pv = 1 or total_tokens = 0).
 struct PrefillWorkspace {
     size_t flags_offset;
     size_t bytes;
-    int64_t nblk;
+    int64_t nvb;
 };
 PrefillWorkspace prefill_workspace(const gqa_prefill_args *a);
 constexpr int64_t kMaxPrefillRowsHeads = int64_t(1) << 37;   // total_tokens * h_kv limit

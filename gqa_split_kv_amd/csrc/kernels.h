@@ -49,23 +49,23 @@ struct PrefillParams {
     int32_t batch, h_q, h_kv, G;
     float scale_log2;          // scale * log2(e)
     int32_t split_pv;          // 1: split P V products everywhere
-    const uint8_t *v16;        // V in fp16 (the copy for bf16 input, v itself for fp16), or null
-    const uint8_t *vflags;     // [h_kv][nblk] 1 = 128-token block of V not fit for fp16 (bf16 input)
-    int64_t nblk;              // blocks in the copy (0: none)
+    const uint8_t *vt;         // [h_kv][nvb][D][64] fp16: V^T of every sequence's 64-key steps, or null
+    const uint8_t *vflags;     // [h_kv][nvb] 1 = that step's V is not fit for fp16 (bf16 input)
+    int64_t nvb;               // step blocks per kv head in vt (0: no copy)
 };
 
-// fp16 copy of bf16 V for the prefill's fast loop (vconv_kernel).
-struct VconvParams {
-    const uint8_t *v;          // [total, h_kv, D] bf16
-    uint8_t *v16;              // [total, h_kv, D] fp16
-    uint8_t *flags;            // [h_kv][nblk]
-    int64_t total;             // token rows
-    int64_t nblk;              // ceil(total / kPrefillVBlock)
-    int32_t h_kv;
+// Transposed fp16 copy of V for the prefill's fast loop (vprep_kernel).
+struct VprepParams {
+    const uint8_t *v;          // [sum(seq_lens), h_kv, D] in_dtype
+    uint8_t *vt;               // [h_kv][nvb][D][64] fp16
+    uint8_t *flags;            // [h_kv][nvb]
+    const int32_t *seq_lens;   // [batch]
+    int32_t batch, h_kv;
+    int64_t nvb;               // >= sum over sequences of ceil(len / 64)
 };
 
-// Enqueues vconv_kernel over nblk x h_kv workgroups.
-hipError_t launch_vconv(const VconvParams &p, int D, int h_kv, hipStream_t stream);
+// Enqueues vprep_kernel over h_kv * nvb workgroups.
+hipError_t launch_vprep(const VprepParams &p, int in_dtype, int D, hipStream_t stream);
 
 // Enqueues the prefill kernel: `blocks` workgroups of kPrefillThreads.
 hipError_t launch_prefill(const PrefillParams &P, int in_dtype, int out_dtype, int D, int blocks,

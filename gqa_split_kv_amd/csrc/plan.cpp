@@ -119,12 +119,11 @@ int validate(const gqa_decode_args *a) {
 
 PrefillWorkspace prefill_workspace(const gqa_prefill_args *a) {
     PrefillWorkspace W = {0, 0, 0};
-    if (a->in_dtype != GQA_DTYPE_BF16 || a->split_pv != 0 || a->total_tokens <= 0) return W;
-    W.nblk = (a->total_tokens + kPrefillVBlock - 1) / kPrefillVBlock;
-    const size_t copy = static_cast<size_t>(a->total_tokens) * static_cast<size_t>(a->h_kv) *
-                        static_cast<size_t>(a->d_head) * 2;
-    W.flags_offset = round_up(copy, 256);
-    W.bytes = round_up(W.flags_offset + static_cast<size_t>(W.nblk) * static_cast<size_t>(a->h_kv), 256);
+    if (a->split_pv != 0 || a->total_tokens <= 0) return W;
+    W.nvb = (a->total_tokens + kPrefillStepKeys - 1) / kPrefillStepKeys + a->batch;
+    const size_t blocks = static_cast<size_t>(W.nvb) * static_cast<size_t>(a->h_kv);
+    W.flags_offset = round_up(blocks * static_cast<size_t>(a->d_head) * kPrefillStepKeys * 2, 256);
+    W.bytes = round_up(W.flags_offset + blocks, 256);
     return W;
 }
 
@@ -160,6 +159,12 @@ int validate_prefill(const gqa_prefill_args *a, bool check_workspace) {
     if (a->total_tokens < 0 || (a->total_tokens > 0 && a->total_tokens > kMaxPrefillRowsHeads / a->h_kv))
         return fail(GQA_ERR_ARG, "total_tokens %lld out of range [0, 2^37 / h_kv]",
                     static_cast<long long>(a->total_tokens));
+    {
+        const PrefillWorkspace W = prefill_workspace(a);
+        if (W.nvb > 0 && W.nvb > static_cast<int64_t>(0x7fffffff) / a->h_kv)
+            return fail(GQA_ERR_ARG, "total_tokens %lld with batch %d and h_kv %d: the V copy needs more than 2^31 "
+                        "workgroups", static_cast<long long>(a->total_tokens), a->batch, a->h_kv);
+    }
     if (check_workspace && a->workspace) {
         const PrefillWorkspace W = prefill_workspace(a);
         if (W.bytes > 0) {

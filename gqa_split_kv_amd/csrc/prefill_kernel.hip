@@ -27,16 +27,18 @@
 //     (the K rows are read from LDS in the key order that leaves lane l holding
 //     keys 8*(l/16) .. +7 of its row), then O^T += V^T P^T and l += 1^T P^T (the
 //     row sums come out of the matrix core, from the same rounded P).  The V^T
-//     operand comes straight out of LDS through transpose reads.  Two wavefronts
-//     share a SIMD (at most 256 VGPRs each, no AGPR traffic).
+//     operand comes out of LDS with 16-byte loads from the transposed copy (fast
+//     loop) or through transpose loads from V as given (masked loop).  Two
+//     wavefronts share a SIMD (at most 256 VGPRs each, no AGPR traffic).
 //   * P V precision: by default P is rounded to fp16 and V read as fp16, one
-//     product per step.  For bf16 input a pre-pass (vconv_kernel) writes an fp16
-//     copy of V into the workspace -- exact for magnitudes in fp16's normal range
-//     -- and flags every 128-token block whose largest |v| is not in
-//     [2^-10, 2^16); from the first stage that touches a flagged block on, a
-//     tile's sweep uses the split product (P as a high and a low part in the
-//     input format, V as given, two products), which the diagonal band always
-//     uses and which the caller can ask for everywhere.
+//     product per step.  A pre-pass (vprep_kernel) writes every sequence's V, 64
+//     keys at a time, transposed and in fp16 into the workspace (bf16 is
+//     converted -- exactly for magnitudes in fp16's normal range -- and a block
+//     whose largest |v| is not in [2^-10, 2^16) is flagged), so that the fast
+//     loop reads the V^T operand with plain 16-byte LDS loads.  From the first
+//     flagged step on, a tile's sweep uses the split product (P as a high and a
+//     low part in the input format, V as given, two products), which the
+//     diagonal band always uses and which the caller can ask for everywhere.
 //   * The running maximum is allowed to lag the true one by up to 8 (log2
 //     units): the accumulators are rescaled only when some row of an N tile
 //     exceeds its reference by more, which removes almost every rescale of the
@@ -49,6 +51,8 @@
 //     which evens out the causal triangle's work.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -69,11 +73,6 @@ constexpr int kRowsPerWave = 16 * kNT;             // 32
 #define GQA_PREFILL_STEP_KEYS 64
 #endif
 constexpr int kStepKeys = GQA_PREFILL_STEP_KEYS;   // keys per compute step (a multiple of 32)
-#ifndef GQA_PREFILL_STAGE_STEPS
-#define GQA_PREFILL_STAGE_STEPS 2
-#endif
-constexpr int kStageSteps = GQA_PREFILL_STAGE_STEPS;   // compute steps per LDS stage (per barrier)
-constexpr int kStageKeys = kStepKeys * kStageSteps;
 constexpr float kLagLog2 = 8.f;                    // allowed lag of the running maximum
 static_assert(kWavesP * kRowsPerWave == kPrefillRows, "tile rows");
 
@@ -103,17 +102,20 @@ __device__ int64_t count_items(const int32_t *seq_lens, int batch, int tt, int h
 }
 
 // The sequence b holding work item `it`, with off = tokens before b, len = its
-// length and local = the item's index among b's items.
+// length, local = the item's index among b's items and steps = the 64-key steps
+// of the sequences before b (sum of ceil(len / 64)).  b = batch if there is none.
 __device__ void locate_item(const int32_t *seq_lens, int batch, int tt, int h_kv, int64_t it, int &b,
-                            int64_t &off, int &len, int64_t &local) {
+                            int64_t &off, int &len, int64_t &local, int64_t &steps) {
     const int lane = lane_id();
-    int64_t run_items = 0, run_len = 0;
+    int64_t run_items = 0, run_len = 0, run_steps = 0;
     for (int base = 0; base < batch; base += kWave) {
         const int i = base + lane;
         const int64_t li = (i < batch) ? seq_len_at(seq_lens, i) : 0;
         const int64_t ni = tiles_of(li, tt) * h_kv;
+        const int64_t si = tiles_of(li, kPrefillStepKeys);
         const int64_t inc_n = inclusive_scan64(ni);
         const int64_t inc_l = inclusive_scan64(li);
+        const int64_t inc_s = inclusive_scan64(si);
         const bool hit = (i < batch) && (run_items + inc_n > it);
         const unsigned long long mask = __ballot(hit);
         if (mask) {
@@ -122,15 +124,18 @@ __device__ void locate_item(const int32_t *seq_lens, int batch, int tt, int h_kv
             len = uniform32(static_cast<int>(shfl64(li, src)));
             off = uniform64(run_len + shfl64(inc_l, src) - len);
             local = uniform64(it - (run_items + shfl64(inc_n, src) - shfl64(ni, src)));
+            steps = uniform64(run_steps + shfl64(inc_s, src) - shfl64(si, src));
             return;
         }
         run_items += shfl64(inc_n, kWave - 1);
         run_len += shfl64(inc_l, kWave - 1);
+        run_steps += shfl64(inc_s, kWave - 1);
     }
     b = batch;
     off = run_len;
     len = 0;
     local = 0;
+    steps = run_steps;
 }
 
 // Stores 4 consecutive outputs, rounded to the output type.
@@ -153,11 +158,10 @@ struct PrefillTile {
     static constexpr int kChunks = kStepKeys * CH;  // 16-byte chunks of one step's K (or V) rows
     static constexpr int kPer = kChunks / kPrefillThreads;   // direct loads per wavefront per step and tensor
     static constexpr int kOff = 7;                  // exponent offset of P: p <= 2^(8 + 7)
-    static constexpr int kTileBytes = kStageKeys * LROW;
-    // LDS regions of a stage buffer: K, and V (fp16 in the fast loop, as given
-    // in the masked / split loop).
-    static constexpr int kRegions = 2;
-    static constexpr int kK = 0, kV = 1;
+    static constexpr int kSlotBytes = kStepKeys * LROW;   // one step's K (or V) rows in LDS
+    static constexpr int kVtRow = kStepKeys * 2;          // bytes of one d row of a transposed V step
+    static_assert(kStepKeys == kPrefillStepKeys, "the V copy's blocks are the kernel's steps");
+    static_assert(D * kVtRow == kSlotBytes, "a transposed V step fills one slot");
     static_assert(kChunks % kPrefillThreads == 0, "whole direct loads per wavefront");
     static constexpr uint32_t kOnesF16 = 0x3c003c00u;
     static constexpr uint32_t kOnesIn = kHalf ? 0x3c003c00u : 0x3f803f80u;
@@ -193,27 +197,12 @@ struct PrefillTile {
         return __builtin_bit_cast(uint2, r);
     }
 
-    // One step: S^T = K Q^T for the N tiles, online softmax with the lagging
-    // maximum, then O^T += V^T P^T and l += 1^T P^T (the row sums from the same
-    // rounded P as the product).
-    //   kDiag   some key of the step lies beyond some row's causal limit: mask
-    //           (chosen per wavefront and step; off the diagonal no row needs it).
-    //   kSplit  P in the input's 16-bit format as a high and a low part (two
-    //           products, V as given); otherwise P in fp16 (one product) against
-    //           V converted to fp16.
-    // sl2 > 0 (a negative scale is folded into Q).
-    template <bool kDiag, bool kSplit>
-    __device__ __forceinline__ static void step(const uint8_t *Kt, const uint8_t *Vt, int k0,
-                                                const uint32_t (&koff)[2][NKP], const uint32_t (&voff)[4],
-                                                const uint4 (&qop)[kNT][NKP], const int (&cap)[kNT],
-                                                float sl2, float (&m_ref)[kNT], f32x4_t (&accl)[kNT],
-                                                f32x4_t (&acc)[kNT][VEC]) {
-        constexpr bool kPvHalf = kSplit ? kHalf : true;   // element type of the P V product
-        constexpr int kH = kStepKeys / 32;                 // 32-key halves of the step
-        const int lane = lane_id();
-        const int kg = lane >> 4;
-        // S^T = K Q^T, half by half: lane holds keys k0 + 32h + 8kg + i of its rows.
-        float sv[kNT][kH][8];
+    static constexpr int kH = kStepKeys / 32;   // 32-key halves of a step
+
+    // S^T = K Q^T of one step for the N tiles, half by half: the lane holds keys
+    // k0 + 32h + 8kg + i of its rows in sv[nt][h][i].
+    __device__ __forceinline__ static void qk(const uint8_t *Kt, const uint32_t (&koff)[2][NKP],
+                                              const uint4 (&qop)[kNT][NKP], float (&sv)[kNT][kH][8]) {
 #pragma unroll
         for (int h = 0; h < kH; ++h) {
             uint4 kop[2][NKP];
@@ -226,24 +215,31 @@ struct PrefillTile {
             for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
-                    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+                    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int p = 0; p < NKP; ++p) s = mfma16<kHalf>(kop[b][p], qop[nt][p], s);
+                    for (int p = 0; p < NKP; ++p) sacc = mfma16<kHalf>(kop[b][p], qop[nt][p], sacc);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) sv[nt][h][4 * b + q] = s[q];
+                    for (int q = 0; q < 4; ++q) sv[nt][h][4 * b + q] = sacc[q];
                 }
         }
-        // Row maxima of the step and the (rare) move of the references, for both N
-        // tiles before any exponential, so that everything after it -- P for
-        // each half, the P V products, the row sums -- is one branch-free stretch
-        // the scheduler can interleave (the exponentials of half 1 with the
-        // products of half 0).
-        int lim[kNT];
+    }
+
+    // Row maxima of a step and the (rare) move of the references, for both N tiles
+    // before any exponential.  Moves the references only when some row's maximum
+    // passes its reference by more than the allowed lag (wave-uniform branch; rows
+    // that did not ask follow along, with alpha = 1 where nothing changes).
+    // Returns in nmu the exponent offsets of p = 2^(s*sl2 - m_ref + kOff) (a row
+    // with no visible key yet keeps the reference -inf and takes 0 in its place:
+    // its weights are masked to 0).  lim[nt]: key 32h + i of the lane is visible
+    // iff 32h + i < lim[nt] (used with kDiag only).
+    template <bool kDiag>
+    __device__ __forceinline__ static void references(const float (&sv)[kNT][kH][8], const int (&lim)[kNT], float sl2,
+                                                      float (&m_ref)[kNT], f32x4_t (&accl)[kNT],
+                                                      f32x4_t (&acc)[kNT][VEC], float (&nmu)[kNT]) {
         float mxs[kNT];
         bool move = false;
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
-            lim[nt] = cap[nt] - (k0 + 8 * kg);   // key 32h + i is visible iff 32h + i < lim
             float mx = -INFINITY;
 #pragma unroll
             for (int h = 0; h < kH; ++h)
@@ -258,9 +254,6 @@ struct PrefillTile {
             mxs[nt] = mx == -INFINITY ? -INFINITY : mx * sl2;   // scaled, log2 units
             move |= mxs[nt] > m_ref[nt] + kLagLog2;
         }
-        // Move the references only when some row's maximum passes its reference by
-        // more than the allowed lag (wave-uniform branch; rows that did not ask
-        // follow along, with alpha = 1 where nothing changes).
         if (__ballot(move)) {
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
@@ -272,13 +265,22 @@ struct PrefillTile {
                 m_ref[nt] = m_new;
             }
         }
-        // p = 2^(s*sl2 - m_ref + kOff); a row with no visible key yet keeps the
-        // reference -inf and takes 0 in its place (its weights are masked to 0).
-        float nmu[kNT];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt)
             nmu[nt] = static_cast<float>(kOff) - (m_ref[nt] == -INFINITY ? 0.f : m_ref[nt]);
-        uint4 bhi[kNT][kH], blo[kNT][kH];
+    }
+
+    // P = 2^(s*sl2 + nmu) of a step in the P V product's format (the row sums come
+    // from the same rounded P as the product).
+    //   kDiag   mask keys at or beyond each row's causal limit lim.
+    //   kSplit  P in the input's 16-bit format as a high and a low part (two
+    //           products, V as given); otherwise P in fp16 (one product) against
+    //           V in fp16.
+    template <bool kDiag, bool kSplit>
+    __device__ __forceinline__ static void exp_p(const float (&sv)[kNT][kH][8], const int (&lim)[kNT], float sl2,
+                                                 const float (&nmu)[kNT], uint4 (&bhi)[kNT][kH],
+                                                 uint4 (&blo)[kNT][kH]) {
+        constexpr bool kPvHalf = kSplit ? kHalf : true;   // element type of the P V product
 #pragma unroll
         for (int h = 0; h < kH; ++h) {
 #pragma unroll
@@ -310,14 +312,33 @@ struct PrefillTile {
                 bhi[nt][h] = make_uint4(phi[0], phi[1], phi[2], phi[3]);
                 if constexpr (kSplit) blo[nt][h] = make_uint4(plo[0], plo[1], plo[2], plo[3]);
             }
-            // O^T += V^T P^T for this half, d block c (d = 16c + M): the A operand is
-            // read transposed from LDS (keys 32h + 8kg + i, d = 16c + m).
+        }
+    }
+
+    // O^T += V^T P^T and l += 1^T P^T for a step, half by half (d block c: d =
+    // 16c + M; the A operand holds keys 32h + 8kg + i, d = 16c + m).
+    //   kVT     V is in the slot transposed (the fast loop's copy: row d holds the
+    //           step's 64 keys, 16-byte chunk k at position k ^ (d & 7)), read with
+    //           one 16-byte load per operand at voff[h]; otherwise V rows as
+    //           given, read with transpose loads at voff[c & 3].
+    template <bool kSplit, bool kVT>
+    __device__ __forceinline__ static void pv(const uint4 (&bhi)[kNT][kH], const uint4 (&blo)[kNT][kH],
+                                              const uint8_t *Vt, const uint32_t *voff, f32x4_t (&accl)[kNT],
+                                              f32x4_t (&acc)[kNT][VEC]) {
+        constexpr bool kPvHalf = kSplit ? kHalf : true;
+#pragma unroll
+        for (int h = 0; h < kH; ++h) {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) {
-                const uint8_t *base = Vt + h * 32 * LROW + (c >> 2) * 128 + voff[c & 3];
-                const uint2 lo = lds_read_tr16(base);
-                const uint2 hi = lds_read_tr16(base + 4 * LROW);
-                const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                uint4 av;
+                if constexpr (kVT) {
+                    av = *reinterpret_cast<const uint4 *>(Vt + c * 16 * kVtRow + voff[h]);
+                } else {
+                    const uint8_t *base = Vt + h * 32 * LROW + (c >> 2) * 128 + voff[c & 3];
+                    const uint2 lo = lds_read_tr16(base);
+                    const uint2 hi = lds_read_tr16(base + 4 * LROW);
+                    av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) {
                     acc[nt][c] = mfma16<kPvHalf>(av, bhi[nt][h], acc[nt][c]);
@@ -336,9 +357,34 @@ struct PrefillTile {
             }
     }
 
+    // Key limits of the lane's rows for a step at key k0 (see references()).
+    __device__ __forceinline__ static void limits(const int (&cap)[kNT], int k0, int (&lim)[kNT]) {
+        const int kg = lane_id() >> 4;
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) lim[nt] = cap[nt] - (k0 + 8 * kg);
+    }
+
+    // One unpipelined step (the masked / split loop): S, references, P V.
+    template <bool kDiag, bool kSplit>
+    __device__ __forceinline__ static void step(const uint8_t *Kt, const uint8_t *Vt, int k0,
+                                                const uint32_t (&koff)[2][NKP], const uint32_t (&voff)[4],
+                                                const uint4 (&qop)[kNT][NKP], const int (&cap)[kNT],
+                                                float sl2, float (&m_ref)[kNT], f32x4_t (&accl)[kNT],
+                                                f32x4_t (&acc)[kNT][VEC]) {
+        float sv[kNT][kH][8];
+        qk(Kt, koff, qop, sv);
+        int lim[kNT];
+        limits(cap, k0, lim);
+        float nmu[kNT];
+        references<kDiag>(sv, lim, sl2, m_ref, accl, acc, nmu);
+        uint4 bhi[kNT][kH], blo[kNT][kH];
+        exp_p<kDiag, kSplit>(sv, lim, sl2, nmu, bhi, blo);
+        pv<kSplit, false>(bhi, blo, Vt, voff, accl, acc);
+    }
+
     // Tile `tile` of (sequence b at token offset off, length len; kv head j).
-    __device__ __forceinline__ static void run(const PrefillParams &P, uint8_t (*buf0)[kTileBytes],
-                                               uint8_t (*buf1)[kTileBytes], int64_t off, int len, int j, int tile) {
+    __device__ __forceinline__ static void run(const PrefillParams &P, uint8_t *K0, uint8_t *K1, uint8_t *V0,
+                                               uint8_t *V1, int64_t off, int len, int j, int tile, int64_t vblk) {
         const int tid = static_cast<int>(threadIdx.x);
         const int wave = uniform32(tid / kWave);
         const int lane = lane_id();
@@ -382,92 +428,90 @@ struct PrefillTile {
         const int wtok_hi = min((wave * kRowsPerWave + kRowsPerWave - 1) / G, tcount - 1);
         const int wkeys = wtok_lo < tcount ? tstart + wtok_hi + 1 : 0;   // keys this wavefront needs
         const int nkeys = tstart + tcount;                                 // keys the tile needs
-        const int nstages = (nkeys + kStageKeys - 1) / kStageKeys;
+        const int nsteps = (nkeys + kStepKeys - 1) / kStepKeys;             // 64-key steps
         const uint8_t *kbase = P.k + (off * P.h_kv + j) * ROWB;
         const uint8_t *vbase = P.v + (off * P.h_kv + j) * ROWB;
 
         // Direct load i of this wavefront fills LDS chunks p = 64 (kPer wave + i) +
         // lane of a step's K (or V) region: row r = p / CH at position p % CH,
         // which holds the row's global chunk (p % CH) ^ swz(r) (swzv(r) for V).
-        uint32_t gk[kPer], gv[kPer];
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
+        auto raw_offset = [&](int i, bool is_v) -> uint32_t {
             const int p = (wave * kPer + i) * kWave + lane;
             const int r = p / CH;
             const int pos = p - r * CH;
-            gk[i] = static_cast<uint32_t>(r * rowstride + (pos ^ swz(r)) * 16);
-            gv[i] = static_cast<uint32_t>(r * rowstride + (pos ^ swzv(r)) * 16);
+            return static_cast<uint32_t>(r * rowstride + (pos ^ (is_v ? swzv(r) : swz(r))) * 16);
+        };
+        uint32_t gk[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) gk[i] = raw_offset(i, false);
+        // The same for a transposed V step (row d of 8 chunks, chunk k at position
+        // k ^ (d & 7)), and the lane's operand offsets in it: keys 32h + 8kg ..
+        // +7 of d row m (+ 16 c).
+        uint32_t gt[kPer], vto[kH];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int p = (wave * kPer + i) * kWave + lane;
+            const int r = p / 8;
+            const int pos = p - r * 8;
+            gt[i] = static_cast<uint32_t>(r * kVtRow + ((pos ^ (r & 7)) * 16));
         }
+#pragma unroll
+        for (int h = 0; h < kH; ++h)
+            vto[h] = static_cast<uint32_t>(m * kVtRow + (((4 * h + kg) ^ (m & 7)) & 7) * 16);
         // Per-lane LDS offsets of the step's operands (fixed for the whole tile):
         // K operand of block b, piece p: row 8(m/4) + 4b + m%4, chunk 4p + kg.
         // V (transposed read, t = 0, d block c = 4 ch + cl): lane 4e + q of group kg
         // addresses row 8kg + e (+ 4t), d = 16c + 4q, i.e. chunk 2c + q/2, bytes
         // 8 (q % 2); with the swizzle (2c + q/2) ^ 2e = 8ch + 2(cl ^ e) + q/2.
-        uint32_t koff[2][NKP], voff[4];
+        uint32_t koff[2][NKP];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int r = 8 * (m >> 2) + 4 * b + (m & 3);
 #pragma unroll
             for (int p = 0; p < NKP; ++p) koff[b][p] = static_cast<uint32_t>(r * LROW + ((4 * p + kg) ^ swz(r)) * 16);
         }
-        {
-            const int e = m >> 2;
-            const int q = m & 3;
-#pragma unroll
-            for (int cl = 0; cl < 4; ++cl)
-                voff[cl] = static_cast<uint32_t>((8 * kg + e) * LROW + 32 * (cl ^ e) + 16 * (q >> 1) + 8 * (q & 1));
-        }
-        // Stages that run the fast (fp16 P V) loop: every stage below the tile's
-        // first token, up to the first stage touching a 128-token block of V that
-        // the pre-pass flagged (blocks at or beyond the copy's end count as
-        // flagged).  Stage s holds tokens off + 128 s .. + 127 of the packed axis.
-        const int nfull = min(nstages, (tstart + 1) / kStageKeys);
+        // Steps that run the fast (fp16 P V, pipelined) loop: every step below the
+        // tile's first token, up to the first one whose V the copy flagged; none
+        // without a copy.  Step x holds the sequence's keys 64 x .. + 63, block
+        // vblk + x of the copy.
+        const int nfull = min(nsteps, (tstart + 1) / kStepKeys);
         int nfast = 0;
-        if (!P.split_pv) {
-            if constexpr (kHalf) {
-                nfast = nfull;
-            } else if (nfull > 0) {
-                constexpr int VB = kPrefillVBlock;
-                const int64_t g_lo = off / VB;
-                const int64_t g_hi = (off + static_cast<int64_t>(nfull) * kStageKeys - 1) / VB;
-                int64_t g_bad = -1;
-                for (int64_t g = g_lo; g <= g_hi; g += kWave) {
-                    const int64_t gl = g + lane;
-                    const bool bad = gl <= g_hi && (gl >= P.nblk || P.vflags[j * P.nblk + gl] != 0);
-                    const unsigned long long mask = __ballot(bad);
-                    if (mask) {
-                        g_bad = g + (__ffsll(static_cast<long long>(mask)) - 1);
-                        break;
-                    }
+        if (nfull > 0 && vblk + nfull <= P.nvb) {   // (a copy exists and covers these steps)
+            // First step whose V the copy flagged (bf16 input only sets flags).
+            const uint8_t *fl = P.vflags + j * P.nvb + vblk;
+            nfast = nfull;
+            for (int x0 = 0; x0 < nfull; x0 += kWave) {
+                const int x = x0 + lane;
+                const unsigned long long mask = __ballot(x < nfull && fl[x] != 0);
+                if (mask) {
+                    nfast = x0 + (__ffsll(static_cast<long long>(mask)) - 1);
+                    break;
                 }
-                nfast = nfull;
-                if (g_bad >= 0) {
-                    const int64_t t = g_bad * VB - off - kStageKeys + 1;   // first stage reaching block g_bad
-                    const int64_t s_bad = t <= 0 ? 0 : (t + kStageKeys - 1) / kStageKeys;
-                    nfast = static_cast<int>(min(static_cast<int64_t>(nfull), s_bad));
-                }
-                nfast = uniform32(nfast);
             }
+            nfast = uniform32(nfast);
         }
-        const uint8_t *vfast = nfast > 0 ? P.v16 + (off * P.h_kv + j) * ROWB : vbase;
-        // Loads stage sg into buffer B (both 64-key parts, K and V); rows at or
-        // beyond the sequence's end read as zero.  V comes from the fp16 copy for
-        // stages of the fast loop.
-        auto issue = [&](uint8_t (*B)[kTileBytes], int sg) {
-            const uint8_t *vsrc = sg < nfast ? vfast : vbase;
+        const uint8_t *vtb = nfast > 0 ? P.vt + (j * P.nvb + vblk) * kSlotBytes : vbase;
+        // Loads the K (or V) rows of step x into a slot; rows at or beyond the
+        // sequence's end read as zero.  V comes from the fp16 copy for the fast
+        // loop's steps.
+        auto issue_k = [&](uint8_t *dst, int x) {
+            const int k0 = x * kStepKeys;
+            const uint32_t bytes = k0 < len ? static_cast<uint32_t>(min(kStepKeys, len - k0) * rowstride) : 0u;
+            const auto rs = make_rsrc(kbase + static_cast<int64_t>(k0) * rowstride, bytes);
 #pragma unroll
-            for (int pt = 0; pt < kStageSteps; ++pt) {
-                const int k0 = sg * kStageKeys + pt * kStepKeys;
+            for (int i = 0; i < kPer; ++i) lds_load16(rs, dst + (wave * kPer + i) * kWave * 16, gk[i]);
+        };
+        auto issue_v = [&](uint8_t *dst, int x) {
+            if (x < nfast) {   // the transposed fp16 copy of step x (a full step)
+                const auto rs = make_rsrc(vtb + static_cast<int64_t>(x) * kSlotBytes, kSlotBytes);
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) lds_load16(rs, dst + (wave * kPer + i) * kWave * 16, gt[i]);
+            } else {
+                const int k0 = x * kStepKeys;
                 const uint32_t bytes = k0 < len ? static_cast<uint32_t>(min(kStepKeys, len - k0) * rowstride) : 0u;
-                const int64_t boff = static_cast<int64_t>(k0) * rowstride;
-                const auto rsk = make_rsrc(kbase + boff, bytes);
-                const auto rsv = make_rsrc(vsrc + boff, bytes);
+                const auto rs = make_rsrc(vbase + static_cast<int64_t>(k0) * rowstride, bytes);
 #pragma unroll
-                for (int i = 0; i < kPer; ++i) {
-                    const uint32_t lo = static_cast<uint32_t>(pt * kStepKeys * LROW + (wave * kPer + i) * kWave * 16);
-                    lds_load16(rsk, B[kK] + lo, gk[i]);
-                    lds_load16(rsv, B[kV] + lo, gv[i]);
-                }
+                for (int i = 0; i < kPer; ++i) lds_load16(rs, dst + (wave * kPer + i) * kWave * 16, raw_offset(i, true));
             }
         };
         float m_ref[kNT];
@@ -480,65 +524,85 @@ struct PrefillTile {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) acc[nt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        issue(buf0, 0);
+        // LDS slots: K of step x in K[x & 1], V of step x in V[x & 1]; the four
+        // slots are separate arrays named at every use, so the compiler can tell
+        // that operand reads never touch the loads in flight to another slot.
+        //
+        // Fast loop, software pipelined: iteration x holds S(x) from the previous
+        // one, and computes S(x+1) = K(x+1) Q^T on the matrix cores while the
+        // vector units turn S(x) into P(x) (the two are independent, so they
+        // interleave), then O += V(x) P(x).  At its start K(x+1) and V(x) are in
+        // LDS and the slot of K(x) is free; it loads K(x+2) and V(x+1) and ends
+        // with one barrier.  The S of the step after the fast loop is computed and
+        // dropped (the masked loop recomputes it).
+        //
+        // Masked / split loop: steps the diagonal band crosses, and every step from
+        // the first whose V range does not suit fp16 on; each wavefront skips the
+        // steps beyond its own last token.  Step x reads K(x), V(x), loads the
+        // next step's (K(x+1) may be there already) and ends with one barrier.
+        issue_k(K0, 0);
+        issue_v(V0, 0);
+        if (nsteps > 1) issue_k(K1, 1);
         wait_loads();
         __syncthreads();
-        // Steps whose keys every row of the tile sees (below the tile's first
-        // token) run unmasked with fp16 P V; the rest -- the tile's diagonal band,
-        // and everything from the first stage whose V range does not suit fp16 on
-        // -- masked with the exact split product, each wavefront skipping the steps
-        // beyond its own last token.  Two loops, so the fast one carries no masking
-        // or fallback code at all.  Each stage starts the loads of the next one
-        // into the other buffer and ends with one barrier.  The buffers are two
-        // separate LDS arrays named at every use, so the compiler can tell that
-        // the operand reads of one never touch the loads in flight to the other.
-        auto stage_fast = [&](uint8_t (*cur)[kTileBytes], uint8_t (*nxt)[kTileBytes], int st) {
-            if (st + 1 < nstages) issue(nxt, st + 1);
+        float sa[kNT][kH][8], sb[kNT][kH][8];
+        int lim0[kNT];
 #pragma unroll
-            for (int pt = 0; pt < kStageSteps; ++pt) {
-                // Each step is scheduled on its own: interleaving two steps would
-                // need more than the 256 registers of two wavefronts per SIMD.
-                __builtin_amdgcn_sched_barrier(0);
-                step<false, false>(cur[kK] + pt * kStepKeys * LROW, cur[kV] + pt * kStepKeys * LROW,
-                                   st * kStageKeys + pt * kStepKeys, koff, voff, qop, cap, sl2, m_ref, accl, acc);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int nt = 0; nt < kNT; ++nt) lim0[nt] = 0;   // unused by the unmasked references
+        if (nfast > 0) {
+            qk(K0, koff, qop, sa);
+            __syncthreads();   // every wavefront is done with K(0)
+        }
+        auto fast_iter = [&](uint8_t *Kfree, const uint8_t *Knext, const uint8_t *Vcur, uint8_t *Vnext, int x,
+                             float (&scur)[kNT][kH][8], float (&snext)[kNT][kH][8]) {
+            if (x + 2 < nsteps) issue_k(Kfree, x + 2);
+            if (x + 1 < nsteps) issue_v(Vnext, x + 1);
+            float nmu[kNT];
+            references<false>(scur, lim0, sl2, m_ref, accl, acc, nmu);
+            uint4 ph[kNT][kH], pl[kNT][kH];
+            qk(Knext, koff, qop, snext);
+            exp_p<false, false>(scur, lim0, sl2, nmu, ph, pl);
+            pv<false, true>(ph, pl, Vcur, vto, accl, acc);
             wait_loads();
             __syncthreads();
         };
-        auto stage_slow = [&](uint8_t (*cur)[kTileBytes], uint8_t (*nxt)[kTileBytes], int st) {
-            if (st + 1 < nstages) issue(nxt, st + 1);
-#pragma unroll
-            for (int pt = 0; pt < kStageSteps; ++pt) {
-                __builtin_amdgcn_sched_barrier(0);
-                const int k0 = st * kStageKeys + pt * kStepKeys;
-                if (k0 < wkeys)
-                    step<true, true>(cur[kK] + pt * kStepKeys * LROW, cur[kV] + pt * kStepKeys * LROW, k0, koff,
-                                     voff, qop, cap, sl2, m_ref, accl, acc);
+        {
+            int x = 0;
+            for (; x + 1 < nfast; x += 2) {
+                fast_iter(K0, K1, V0, V1, x, sa, sb);
+                fast_iter(K1, K0, V1, V0, x + 1, sb, sa);
             }
+            if (x < nfast) fast_iter(K0, K1, V0, V1, x, sa, sb);
+        }
+        int x = nfast;
+        const int kloaded = nfast + 1;   // K(0 .. kloaded) are loaded or being loaded
+        uint32_t voff[4];
+        {
+            const int e = m >> 2;
+            const int q = m & 3;
+#pragma unroll
+            for (int cl = 0; cl < 4; ++cl)
+                voff[cl] = static_cast<uint32_t>((8 * kg + e) * LROW + 32 * (cl ^ e) + 16 * (q >> 1) + 8 * (q & 1));
+        }
+        auto slow_iter = [&](const uint8_t *Kcur, uint8_t *Knext, const uint8_t *Vcur, uint8_t *Vnext, int x) {
+            if (x + 1 < nsteps) {
+                if (x + 1 > kloaded) issue_k(Knext, x + 1);
+                issue_v(Vnext, x + 1);
+            }
+            const int k0 = x * kStepKeys;
+            if (k0 < wkeys) step<true, true>(Kcur, Vcur, k0, koff, voff, qop, cap, sl2, m_ref, accl, acc);
             wait_loads();
             __syncthreads();
         };
-        // Stage st computes from buffer st & 1; the loops go two stages at a time
-        // so that every call names its buffers statically.
-        int st = 0;
-        for (; st + 1 < nfast; st += 2) {
-            stage_fast(buf0, buf1, st);
-            stage_fast(buf1, buf0, st + 1);
+        if (x < nsteps && (x & 1)) {
+            slow_iter(K1, K0, V1, V0, x);
+            ++x;
         }
-        if (st < nfast) {
-            stage_fast(buf0, buf1, st);
-            ++st;
+        for (; x + 1 < nsteps; x += 2) {
+            slow_iter(K0, K1, V0, V1, x);
+            slow_iter(K1, K0, V1, V0, x + 1);
         }
-        if (st < nstages && (st & 1)) {
-            stage_slow(buf1, buf0, st);
-            ++st;
-        }
-        for (; st + 1 < nstages; st += 2) {
-            stage_slow(buf0, buf1, st);
-            stage_slow(buf1, buf0, st + 1);
-        }
-        if (st < nstages) stage_slow(buf0, buf1, st);
+        if (x < nsteps) slow_iter(K0, K1, V0, V1, x);
 
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
@@ -560,9 +624,11 @@ struct PrefillTile {
 template <int kIn, int kOut, int D>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams P) {
     using T = PrefillTile<kIn, kOut, D>;
-    // The two stage buffers (K and V regions each) are separate arrays; see run().
-    __shared__ __align__(16) uint8_t buf0[T::kRegions][T::kTileBytes];
-    __shared__ __align__(16) uint8_t buf1[T::kRegions][T::kTileBytes];
+    // The K and V slots of two steps, four separate arrays; see run().
+    __shared__ __align__(16) uint8_t k0s[T::kSlotBytes];
+    __shared__ __align__(16) uint8_t k1s[T::kSlotBytes];
+    __shared__ __align__(16) uint8_t v0s[T::kSlotBytes];
+    __shared__ __align__(16) uint8_t v1s[T::kSlotBytes];
     const int tt = kPrefillRows / P.G;
     const int64_t items = count_items(P.seq_lens, P.batch, tt, P.h_kv);
     const int64_t g = gridDim.x;
@@ -571,70 +637,104 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         const int64_t it = r * g + ((r & 1) ? g - 1 - w : w);   // snake order
         if (it >= items) continue;
         int b, len;
-        int64_t off, local;
-        locate_item(P.seq_lens, P.batch, tt, P.h_kv, it, b, off, len, local);
+        int64_t off, local, steps;
+        locate_item(P.seq_lens, P.batch, tt, P.h_kv, it, b, off, len, local, steps);
         const int ntile = static_cast<int>(tiles_of(len, tt));
         const int j = static_cast<int>(local / ntile);
         const int tile = ntile - 1 - static_cast<int>(local - static_cast<int64_t>(j) * ntile);   // longest first
-        T::run(P, buf0, buf1, off, len, j, tile);
+        T::run(P, k0s, k1s, v0s, v1s, off, len, j, tile, steps);
     }
 }
 
-// fp16 copy of bf16 V and the range flags of its 128-token blocks: workgroup
-// j * nblk + g converts rows g * 128 .. + 127 (those below `total`) of kv head j
-// and sets flags[j * nblk + g] to 1 if the block's largest |v| is not in
-// [2^-10, 2^16) (or is not finite), else 0.  The conversion is exact for values
-// in fp16's normal range; flagged blocks are never read from the copy.
-template <int D>
-__global__ __launch_bounds__(kVconvThreads) void vconv_kernel(VconvParams p) {
-    constexpr int ROWB = D * 2;
-    constexpr int CH = ROWB / 16;
-    constexpr int kChunks = kPrefillVBlock * CH;
+// Transposed fp16 copy of V for the fast loop: workgroup j * nvb + blk takes
+// block blk of kv head j -- step x of sequence b, the keys 64 x .. + 63 (zeros
+// beyond the sequence's end) -- and writes it as D rows of 64 keys (row d holds
+// v[key, j, d] for the 64 keys, in fp16: bf16 input is converted, exactly for
+// magnitudes in fp16's normal range).  flags[j * nvb + blk] = 1 for bf16 input
+// whose block holds a largest |v| not in [2^-10, 2^16) (or a non-finite value):
+// that step must not take the fp16 product.  Blocks past the last step of the
+// last sequence are left alone.
+template <int kIn, int D>
+__global__ __launch_bounds__(kVprepThreads) void vprep_kernel(VprepParams p) {
+    constexpr int ROWB = D * 2;                    // bytes of one key row (one kv head)
+    constexpr int CH = ROWB / 16;                  // 16-byte chunks per key row
+    constexpr int K = kPrefillStepKeys;            // keys per block
+    constexpr int kPitch = ROWB + 16;              // LDS row pitch (keys x d tile)
     typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+    __shared__ __align__(16) uint8_t tile[K * kPitch];
+    __shared__ unsigned wmax[kVprepThreads / kWave];
     const int64_t idx = blockIdx.x;
-    const int j = static_cast<int>(idx / p.nblk);
-    const int64_t g = idx - static_cast<int64_t>(j) * p.nblk;
+    const int j = static_cast<int>(idx / p.nvb);
+    const int64_t blk = idx - static_cast<int64_t>(j) * p.nvb;
+    int b, len;
+    int64_t off, x, steps;
+    locate_item(p.seq_lens, p.batch, K, 1, blk, b, off, len, x, steps);
+    if (b >= p.batch) return;   // the same for the whole workgroup
     const int tid = static_cast<int>(threadIdx.x);
+    // Load the block's key rows (16 bytes a thread at a time) into LDS as fp16.
     u16x2_t mag = {0, 0};
-    for (int c = tid; c < kChunks; c += kVconvThreads) {
-        const int64_t row = g * kPrefillVBlock + c / CH;
-        if (row >= p.total) break;   // rows grow with c
-        const int64_t o = (row * p.h_kv + j) * ROWB + (c % CH) * 16;
-        const uint4 x = *reinterpret_cast<const uint4 *>(p.v + o);
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-        uint32_t h[4];
+    for (int c = tid; c < K * CH; c += kVprepThreads) {
+        const int key = c / CH;
+        const int dc = c - key * CH;
+        const int64_t row = x * K + key;
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (row < len) w = *reinterpret_cast<const uint4 *>(p.v + ((off + row) * p.h_kv + j) * ROWB + dc * 16);
+        if constexpr (kIn == kBf16) {
+            const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+            uint32_t h[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2_t, w[i] & 0x7fff7fffu));
-            const f32x2_t f = {__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xffff0000u)};
-            h[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+            for (int i = 0; i < 4; ++i) {
+                mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2_t, a[i] & 0x7fff7fffu));
+                const f32x2_t f = {__uint_as_float(a[i] << 16), __uint_as_float(a[i] & 0xffff0000u)};
+                h[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+            }
+            w = make_uint4(h[0], h[1], h[2], h[3]);
         }
-        *reinterpret_cast<uint4 *>(p.v16 + o) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4 *>(tile + key * kPitch + dc * 16) = w;
     }
-    // Largest magnitude bits of the block (bf16 magnitude bits order like the
-    // magnitudes; NaN and inf sort above every finite value).
-    unsigned m = mag.x > mag.y ? mag.x : mag.y;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const unsigned y = static_cast<unsigned>(__shfl_xor(static_cast<int>(m), d));
-        m = m > y ? m : y;
-    }
-    __shared__ unsigned wmax[kVconvThreads / kWave];
-    if (lane_id() == 0) wmax[tid / kWave] = m;
     __syncthreads();
-    if (tid == 0) {
+    // Write row d, keys 8 kc .. + 7, as one 16-byte chunk.
+    uint8_t *dst = p.vt + idx * (D * K * 2);
+    for (int c = tid; c < D * (K / 8); c += kVprepThreads) {
+        const int d = c / (K / 8);
+        const int kc = c - d * (K / 8);
+        uint32_t o[4];
 #pragma unroll
-        for (int i = 1; i < kVconvThreads / kWave; ++i) m = m > wmax[i] ? m : wmax[i];
-        p.flags[idx] = (m >= 0x4780u || m < 0x3a80u) ? 1 : 0;
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t lo = *reinterpret_cast<const uint16_t *>(tile + (8 * kc + 2 * t) * kPitch + d * 2);
+            const uint32_t hi = *reinterpret_cast<const uint16_t *>(tile + (8 * kc + 2 * t + 1) * kPitch + d * 2);
+            o[t] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint4 *>(dst + d * (K * 2) + kc * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    if constexpr (kIn == kBf16) {
+        // Largest magnitude bits of the block (bf16 magnitude bits order like the
+        // magnitudes; NaN and inf sort above every finite value).
+        unsigned mm = mag.x > mag.y ? mag.x : mag.y;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const unsigned y = static_cast<unsigned>(__shfl_xor(static_cast<int>(mm), d));
+            mm = mm > y ? mm : y;
+        }
+        if (lane_id() == 0) wmax[tid / kWave] = mm;
+        __syncthreads();
+        if (tid == 0) {
+#pragma unroll
+            for (int i = 1; i < kVprepThreads / kWave; ++i) mm = mm > wmax[i] ? mm : wmax[i];
+            p.flags[idx] = (mm >= 0x4780u || mm < 0x3a80u) ? 1 : 0;
+        }
+    } else {
+        if (tid == 0) p.flags[idx] = 0;
     }
 }
 
-hipError_t launch_vconv_impl(const VconvParams &p, int D, int h_kv, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(p.nblk * h_kv));   // <= 2^30 by the total_tokens * h_kv limit
+template <int kIn>
+hipError_t launch_vprep_in(const VprepParams &p, int D, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(p.nvb * p.h_kv));   // < 2^31 by the argument checks
     if (D == 128)
-        hipLaunchKernelGGL(vconv_kernel<128>, grid, dim3(kVconvThreads), 0, stream, p);
+        hipLaunchKernelGGL((vprep_kernel<kIn, 128>), grid, dim3(kVprepThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL(vconv_kernel<64>, grid, dim3(kVconvThreads), 0, stream, p);
+        hipLaunchKernelGGL((vprep_kernel<kIn, 64>), grid, dim3(kVprepThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -667,8 +767,8 @@ hipError_t launch_prefill(const PrefillParams &P, int in_dtype, int out_dtype, i
                              : launch_pio<kF16, kF32>(P, D, blocks, stream);
 }
 
-hipError_t launch_vconv(const VconvParams &p, int D, int h_kv, hipStream_t stream) {
-    return launch_vconv_impl(p, D, h_kv, stream);
+hipError_t launch_vprep(const VprepParams &p, int in_dtype, int D, hipStream_t stream) {
+    return in_dtype == kBf16 ? launch_vprep_in<kBf16>(p, D, stream) : launch_vprep_in<kF16>(p, D, stream);
 }
 
 hipError_t prefill_occupancy(int in_dtype, int out_dtype, int D, int *blocks_per_cu) {

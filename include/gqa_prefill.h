@@ -103,9 +103,10 @@ int gqa_prefill(const void *q, const void *k, const void *v, void *o, const int3
                 int32_t batch, int64_t total_tokens, int32_t h_q, int32_t h_kv, int32_t d_head, float scale,
                 void *stream);
 
-/* gqa_prefill_f16 -- IEEE fp16 q/k/v in, fp16 o out (no workspace). */
+/* gqa_prefill_f16 -- IEEE fp16 q/k/v in, fp16 o out, total_tokens as above. */
 int gqa_prefill_f16(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
-                    int32_t batch, int32_t h_q, int32_t h_kv, int32_t d_head, float scale, void *stream);
+                    int32_t batch, int64_t total_tokens, int32_t h_q, int32_t h_kv, int32_t d_head, float scale,
+                    void *stream);
 
 /* gqa_prefill_ex -- any supported dtype pair and grid size. */
 int gqa_prefill_ex(const gqa_prefill_args *args);

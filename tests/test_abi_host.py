@@ -240,20 +240,25 @@ def test_prefill_args_struct_size(lib):
 
 def test_prefill_total_tokens_and_workspace_rules(lib):
     assert _pvalidate(total_tokens=-1) == B.GQA_ERR_ARG and "total_tokens" in B.last_error_message()
-    assert _pvalidate(total_tokens=1 << 37) == B.GQA_OK                       # h_kv 1
+    assert _pvalidate(total_tokens=1 << 37, split_pv=1) == B.GQA_OK           # h_kv 1
     assert _pvalidate(total_tokens=(1 << 37) + 1) == B.GQA_ERR_ARG
-    assert _pvalidate(total_tokens=1 << 34, h_q=64, h_kv=8) == B.GQA_OK
+    assert _pvalidate(total_tokens=1 << 34, h_q=64, h_kv=8, split_pv=1) == B.GQA_OK
     assert _pvalidate(total_tokens=(1 << 34) + 1, h_q=64, h_kv=8) == B.GQA_ERR_ARG
-    # Workspace: an fp16 copy of V (rows x h_kv x d x 2 bytes, 256-aligned) then
-    # one flag byte per 128-token block and kv head, rounded up to 256 bytes.
+    # Workspace: V transposed in 64-key blocks, nvb = ceil(total / 64) + batch
+    # blocks per kv head of d x 64 fp16 values, then one flag byte per block and
+    # kv head, each part rounded up to 256 bytes.
     a = _pargs(total_tokens=1000, h_q=8, h_kv=2)
-    copy = 1000 * 2 * 128 * 2
-    assert B.gqa_prefill_workspace_bytes(a) == copy + 256     # 8 blocks x 2 heads of flags
-    assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=129, d_head=64)) == 16640 + 256   # 16512 -> 16640
+    nvb = 16 + 1
+    assert B.gqa_prefill_workspace_bytes(a) == 2 * nvb * 128 * 64 * 2 + 256
+    assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=129, d_head=64, batch=3)) == (3 + 3) * 64 * 64 * 2 + 256
     assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=1000, split_pv=1)) == 0
     assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=0)) == 0
     assert B.gqa_prefill_workspace_bytes(
-        _pargs(total_tokens=1000, in_dtype=B.GQA_DTYPE_F16, out_dtype=B.GQA_DTYPE_F16)) == 0
+        _pargs(total_tokens=1000, in_dtype=B.GQA_DTYPE_F16, out_dtype=B.GQA_DTYPE_F16)) == 2 * 0 + 17 * 128 * 64 * 2 + 256
+    # The V copy's grid (nvb x h_kv workgroups) must stay below 2^31.
+    assert _pvalidate(total_tokens=1 << 36, h_q=8, h_kv=2) == B.GQA_ERR_ARG and "2^31" in B.last_error_message()
+    assert _pvalidate(total_tokens=1 << 36, h_q=8, h_kv=1) == B.GQA_OK
+    assert _pvalidate(total_tokens=1 << 36, h_q=8, h_kv=2, split_pv=1) == B.GQA_OK
     need = B.gqa_prefill_workspace_bytes(a)
     assert _pvalidate(total_tokens=1000, h_q=8, h_kv=2, workspace=0x100000, workspace_bytes=need) == B.GQA_OK
     assert _pvalidate(total_tokens=1000, h_q=8, h_kv=2, workspace=0x100000,

@@ -170,7 +170,8 @@ def test_prefill_caller_workspace_poisoned_and_reused():
     a0 = B.make_prefill_args(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 3, 16, 2, 128, 0.1, B.GQA_DTYPE_BF16,
                              B.GQA_DTYPE_BF16, total_tokens=1234)
     need = B.gqa_prefill_workspace_bytes(a0)
-    assert need == 1234 * 2 * 128 * 2 + 256           # copy (256-aligned) + 10 blocks x 2 heads of flags
+    nvb = -(-1234 // 64) + 3                          # 64-key blocks: ceil(total / 64) + batch
+    assert need == 2 * nvb * 128 * 64 * 2 + 256       # transposed copy + one flag byte per block and head
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     for c in cases:
         q, k, v, sl = upload(c)
@@ -183,11 +184,12 @@ def test_prefill_caller_workspace_poisoned_and_reused():
         _check(out, ref, "caller workspace")
 
 
-def test_prefill_unknown_total_tokens_uses_split_product():
-    """bf16 with total_tokens = 0 makes no fp16 copy: the result is bit-identical
-    to split_pv = 1."""
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_unknown_total_tokens_uses_split_product(dtype):
+    """total_tokens = 0 makes no copy of V: the result is bit-identical to
+    split_pv = 1."""
     import torch
-    c = host_prefill_case(2, 8, 2, 128, [500, 260], "bf16", seed=32)
+    c = host_prefill_case(2, 8, 2, 128, [500, 260], dtype, seed=32)
     q, k, v, sl = upload(c)
     o0 = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
     B.prefill(q, k, v, sl, scale=c.scale, out=o0, total_tokens=0)
@@ -261,6 +263,6 @@ def test_prefill_c_names():
     ref16 = oracle.gqa_prefill_f64(c16.q, c16.k, c16.v, c16.seq_lens, c16.scale)
     q, k, v, sl = upload(c16)
     out = torch.full(q.shape, float("nan"), dtype=torch.float16, device="cuda")
-    B.gqa_prefill_f16(q, k, v, out, sl, 2, 8, 2, 128, c16.scale)
+    B.gqa_prefill_f16(q, k, v, out, sl, 2, 140, 8, 2, 128, c16.scale)
     torch.cuda.synchronize()
     _check(out, ref16, "gqa_prefill_f16")
