@@ -30,14 +30,15 @@
  * 4-byte aligned.  Every output row is written by exactly one workgroup (no
  * cross-workgroup reduction).
  *
- * Workspace: only bf16 input with split_pv = 0 and total_tokens > 0 uses one --
- * an fp16 copy of V (total_tokens * h_kv * d_head * 2 bytes) and one flag byte
- * per 128-token block and kv head, both rewritten by every call (nothing needs
- * initialising).  gqa_prefill_workspace_bytes() gives its size.  With workspace
- * NULL the library uses its own, per (device, stream), grown with hipMalloc
- * (not capturable in a HIP graph; freed by gqa_release()); a caller-provided
- * workspace (256-byte aligned) makes the call capturable.  Calls sharing one
- * workspace must be ordered (one stream).
+ * Workspace: the default precision mode (split_pv = 0) with total_tokens > 0
+ * uses one -- V transposed and in fp16, 64 keys of one sequence at a time
+ * (nvb = ceil(total_tokens / 64) + batch blocks of d_head x 64 values per kv
+ * head), and one flag byte per block and kv head, both rewritten by every call
+ * (nothing needs initialising).  gqa_prefill_workspace_bytes() gives its size.
+ * With workspace NULL the library uses its own, per (device, stream), grown
+ * with hipMalloc (not capturable in a HIP graph; freed by gqa_release()); a
+ * caller-provided workspace (256-byte aligned) makes the call capturable.  Calls
+ * sharing one workspace must be ordered (one stream).
  *
  * Asynchrony and errors as in gqa_decode.h: work is enqueued on `stream`, host
  * errors return a gqa_status before anything is enqueued (o untouched), and
@@ -60,20 +61,18 @@ extern "C" {
  *             0..2^20.  The result does not depend on it.
  * split_pv    Precision of the P V product.  0 (default): P is rounded to fp16
  *             (11 significant bits, times a common power of two that cancels) and
- *             V taken in fp16, one matrix-core product; for bf16 input V is read
- *             from an fp16 copy made by the call, and a tile's sweep switches to
- *             the split product from the first 128-key stage that touches a
- *             128-token block of V whose largest magnitude is not in
- *             [2^-10, 2^16), so the fp16 rounding of V never loses range or
+ *             V taken in fp16, one matrix-core product, V read from the call's
+ *             transposed fp16 copy (bf16 converted); for bf16 input a tile's
+ *             sweep switches to the split product from the first 64-key step
+ *             whose V has a largest magnitude not in [2^-10, 2^16) (or a
+ *             non-finite value), so the fp16 rounding of V never loses range or
  *             precision.  Typical error against the exact result: relative L2
  *             ~1e-4.  1: P split into a high and a low 16-bit part everywhere
  *             (about 16 significant bits, two products, ~1.5x the matrix-core
  *             work); error ~1e-6.  No workspace.
- * total_tokens  Rows held by q, k, v and o: at least sum(seq_lens) (the fp16
- *             copy covers V rows 0 .. total_tokens - 1, and V must hold them).
- *             Used only by bf16 input with split_pv = 0; 0 there means unknown:
- *             no copy is made and every stage uses the split product, as with
- *             split_pv = 1.
+ * total_tokens  Rows held by q, k, v and o: at least sum(seq_lens).  Sizes the
+ *             copy of V; 0 means unknown: no copy is made and every step uses
+ *             the split product, as with split_pv = 1.  Unused with split_pv = 1.
  * workspace, workspace_bytes  See above; ignored where no workspace is used.
  */
 typedef struct gqa_prefill_args {
@@ -98,7 +97,7 @@ typedef struct gqa_prefill_args {
 } gqa_prefill_args;
 
 /* gqa_prefill -- bf16 q/k/v in, bf16 o out, total_tokens = sum(seq_lens) rows
- * (the fp16 copy of V lives in the library's workspace).  Returns a gqa_status. */
+ * (the copy of V lives in the library's workspace).  Returns a gqa_status. */
 int gqa_prefill(const void *q, const void *k, const void *v, void *o, const int32_t *seq_lens,
                 int32_t batch, int64_t total_tokens, int32_t h_q, int32_t h_kv, int32_t d_head, float scale,
                 void *stream);
@@ -115,9 +114,10 @@ int gqa_prefill_ex(const gqa_prefill_args *args);
  * would return before enqueueing anything: GQA_ERR_NULL, GQA_ERR_SHAPE (batch,
  * h_q or h_kv <= 0, h_q not a multiple of h_kv), GQA_ERR_UNSUPPORTED (d_head, G,
  * h_kv above 65536 or the dtype pair), GQA_ERR_ALIGN, GQA_ERR_SCALE, GQA_ERR_ARG
- * (num_blocks out of range, split_pv not 0 or 1, total_tokens negative or above
- * 2^40), GQA_ERR_WORKSPACE (a caller workspace that is not 256-byte aligned or
- * smaller than the call needs). */
+ * (num_blocks out of range, split_pv not 0 or 1, total_tokens negative,
+ * total_tokens * h_kv above 2^37, or a copy of V needing 2^31 or more
+ * workgroups), GQA_ERR_WORKSPACE (a caller workspace that is not 256-byte
+ * aligned or smaller than the call needs). */
 int gqa_prefill_validate(const gqa_prefill_args *args);
 
 /* Workspace bytes the call needs (0 where none is used), after the checks of
