@@ -199,29 +199,44 @@ struct PrefillTile {
 
     static constexpr int kH = kStepKeys / 32;   // 32-key halves of a step
 
-    // S^T = K Q^T of one step for the N tiles, half by half: the lane holds keys
-    // k0 + 32h + 8kg + i of its rows in sv[nt][h][i].
+    // S^T = K Q^T of one step for the N tiles: the lane holds keys k0 + 32h + 8kg +
+    // i of its rows in sv[nt][h][i].  The contraction over d runs in the outer
+    // loop, so the 2 kNT kH accumulators -- the score registers themselves -- form
+    // independent chains that the matrix core interleaves (a chain of dependent
+    // products issues at a fraction of the rate), and each piece of the K operand
+    // is read from LDS just before its products.
     __device__ __forceinline__ static void qk(const uint8_t *Kt, const uint32_t (&koff)[2][NKP],
                                               const uint4 (&qop)[kNT][NKP], float (&sv)[kNT][kH][8]) {
+        f32x4_t sacc[kNT][kH][2];
 #pragma unroll
-        for (int h = 0; h < kH; ++h) {
-            uint4 kop[2][NKP];
+        for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int h = 0; h < kH; ++h)
 #pragma unroll
-                for (int p = 0; p < NKP; ++p)
-                    kop[b][p] = *reinterpret_cast<const uint4 *>(Kt + h * 32 * LROW + koff[b][p]);
+                for (int b = 0; b < 2; ++b) sacc[nt][h][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt)
+        for (int p = 0; p < NKP; ++p) {
+            uint4 kop[kH][2];
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+            for (int h = 0; h < kH; ++h)
 #pragma unroll
-                    for (int p = 0; p < NKP; ++p) sacc = mfma16<kHalf>(kop[b][p], qop[nt][p], sacc);
+                for (int b = 0; b < 2; ++b)
+                    kop[h][b] = *reinterpret_cast<const uint4 *>(Kt + h * 32 * LROW + koff[b][p]);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) sv[nt][h][4 * b + q] = sacc[q];
-                }
+            for (int h = 0; h < kH; ++h)
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) sacc[nt][h][b] = mfma16<kHalf>(kop[h][b], qop[nt][p], sacc[nt][h][b]);
         }
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+            for (int h = 0; h < kH; ++h)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) sv[nt][h][4 * b + q] = sacc[nt][h][b][q];
     }
 
     // Row maxima of a step and the (rare) move of the references, for both N tiles
@@ -340,21 +355,22 @@ struct PrefillTile {
                     av = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 }
 #pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) {
-                    acc[nt][c] = mfma16<kPvHalf>(av, bhi[nt][h], acc[nt][c]);
-                    if constexpr (kSplit) acc[nt][c] = mfma16<kPvHalf>(av, blo[nt][h], acc[nt][c]);
+                for (int nt = 0; nt < kNT; ++nt) acc[nt][c] = mfma16<kPvHalf>(av, bhi[nt][h], acc[nt][c]);
+                if constexpr (kSplit) {
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt) acc[nt][c] = mfma16<kPvHalf>(av, blo[nt][h], acc[nt][c]);
                 }
             }
-        }
-        const uint32_t one = kPvHalf ? kOnesF16 : kOnesIn;
-        const uint4 ones = make_uint4(one, one, one, one);
+            // Row sums of this half (after the half's products, so the two
+            // updates of accl[nt] are far apart).
+            const uint32_t one = kPvHalf ? kOnesF16 : kOnesIn;
+            const uint4 ones = make_uint4(one, one, one, one);
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-            for (int h = 0; h < kH; ++h) {
+            for (int nt = 0; nt < kNT; ++nt) {
                 accl[nt] = mfma16<kPvHalf>(ones, bhi[nt][h], accl[nt]);
                 if constexpr (kSplit) accl[nt] = mfma16<kPvHalf>(ones, blo[nt][h], accl[nt]);
             }
+        }
     }
 
     // Key limits of the lane's rows for a step at key k0 (see references()).
