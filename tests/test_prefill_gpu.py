@@ -89,6 +89,21 @@ def test_prefill_longer_ragged_batch_and_grid_independence():
             assert torch.equal(o, outs[0])
 
 
+def test_prefill_70b_heads_long_sequences():
+    """64 query heads over 8 kv heads (the 70B grouping), two sequences long
+    enough for dozens of fast-loop steps per tile, both P V modes."""
+    import torch
+    lens = [2500, 640]
+    c = host_prefill_case(2, 64, 8, 128, lens, "bf16", seed=33)
+    _say("oracle: 70B heads, lens", lens)
+    ref = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    q, k, v, sl = upload(c)
+    for sp in (0, 1):
+        o = _run(q, k, v, sl, c.scale, torch.float32, split_pv=sp)
+        e, r = _check(o, ref, "70B heads split=%d" % sp, sp)
+        _say("  split_pv %d max|err| %.3g rel-L2 %.3g" % (sp, e, r))
+
+
 def test_prefill_peaked_keys():
     import torch
     lens = [2048, 600]
