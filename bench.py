@@ -194,8 +194,9 @@ def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
         for e in ev_steps + [ev]:
             hip.destroy(e[0])
             hip.destroy(e[1])
+        # The blocks stay in torch's cache for the next form: handing them back to
+        # the driver and allocating afresh measured ~4% slower sweeps on this machine.
         del q, k, v, out, ws, timed, warm
-        torch.cuda.empty_cache()
     return rows
 
 
