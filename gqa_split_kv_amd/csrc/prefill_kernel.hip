@@ -13,15 +13,17 @@
 //     query heads of one (sequence, kv head), and sweeps the keys 0 .. its last
 //     token with the page's online-softmax fold; the rows are disjoint, so every
 //     tile normalises and stores its own outputs.
-//   * K and V go HBM/L2 -> LDS in 128-key stages (double buffered, one barrier
-//     per stage) that all 256 rows share, so the K/V bytes per output row fall
-//     with the tile height.  The loads write LDS directly (buffer loads with the
-//     LDS as destination: no registers, no LDS store instructions), the next
-//     stage's loads in flight during the whole current stage.  A stage is
-//     computed as two 64-key steps.  LDS rows are XOR-swizzled in 16-byte chunks
-//     (one pattern for K, one for V) so the operand reads hit distinct banks; a
-//     direct load writes lane i's 16 bytes at base + 16 i, so the swizzle is
-//     applied by choosing which global chunk each lane fetches.
+//   * The keys are swept in 64-key steps.  K and V go HBM/L2 -> LDS into four
+//     slots (K and V of two steps) that all 256 rows share, so the K/V bytes per
+//     output row fall with the tile height.  The loads write LDS directly (buffer
+//     loads with the LDS as destination: no registers, no LDS store
+//     instructions) and run a step ahead of their use; one barrier per step.
+//     LDS rows are XOR-swizzled in 16-byte chunks so the operand reads hit
+//     distinct banks; a direct load writes lane i's 16 bytes at base + 16 i, so
+//     the swizzle is applied by choosing which global chunk each lane fetches.
+//   * The fast loop is software pipelined: while the vector units turn the
+//     scores of step x into P, the matrix cores compute the scores of step x+1;
+//     then O += V P for step x.
 //   * Each wavefront owns 32 rows as two 16-row N tiles of
 //     v_mfma_f32_16x16x32_{bf16,f16}: S^T = K Q^T with the keys on the M axis
 //     (the K rows are read from LDS in the key order that leaves lane l holding
@@ -51,8 +53,6 @@
 //     which evens out the causal triangle's work.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -176,11 +176,13 @@ struct PrefillTile {
     // loads among them: their data is in LDS once the counter drops).
     __device__ __forceinline__ static void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
 
-    // LDS layout of a K or V tile: key row r at r * LROW, its 16-byte chunk c at
-    // chunk position c ^ swz(r) (K) or c ^ swzv(r) (V).  One K operand read hits
-    // rows {0-3, 8-11, 16-19, 24-27} (+4 for the second block) at one chunk; one
-    // transposed V read (see v_operand) hits 4 consecutive rows at 2 chunks.  The
-    // swizzles spread both over distinct banks.
+    // LDS layout of a K slot, or of a V slot holding V as given: key row r at
+    // r * LROW, its 16-byte chunk c at chunk position c ^ swz(r) (K) or c ^ swzv(r)
+    // (V).  One K operand read hits rows {0-3, 8-11, 16-19, 24-27} (+4 for the
+    // second block) at one chunk; one transposed V read (pv() with V as given)
+    // hits 4 consecutive rows at 2 chunks.  The swizzles spread both over
+    // distinct banks.  (A slot holding the transposed copy has its own layout:
+    // see pv().)
     __device__ __forceinline__ static int swz(int r) { return ((r & 3) | ((r >> 1) & 12)) & (CH - 1); }
     __device__ __forceinline__ static int swzv(int r) { return (2 * (r & 3)) & (CH - 1); }
 
