@@ -41,12 +41,14 @@
 //     flagged step on, a tile's sweep uses the split product (P as a high and a
 //     low part in the input format, V as given, two products), which the
 //     diagonal band always uses and which the caller can ask for everywhere.
-//   * The running maximum is allowed to lag the true one by up to 8 (log2
-//     units): the accumulators are rescaled only when some row of an N tile
-//     exceeds its reference by more, which removes almost every rescale of the
-//     accumulators.  Weights are then at most 2^(8+7) (the 2^7 keeps small
-//     weights inside fp16's exponent range), and the common factor cancels in
-//     O / l.
+//   * The running maximum is allowed to lag the true one: the accumulators are
+//     rescaled only when some row's scores pass its reference by more than 8
+//     (log2 units; the masked loop computes the row maxima every step) or make
+//     an fp16 weight overflow (the fast loop computes the maxima only for a
+//     tile's first step and then watches each step's row sums for infinity,
+//     recomputing that step with moved references when one appears).  Weights
+//     are then below 2^16 (the exponent offset 2^7 keeps small weights inside
+//     fp16's range), and the common factor cancels in O / l.
 //   * Tiles are handed out in a fixed snake order over a persistent grid: the
 //     tiles of a (sequence, kv head) are enumerated last token first (longest
 //     first), and workgroup w takes tiles w, 2g-1-w, 2g+w, ... (g = grid size),
@@ -338,7 +340,8 @@ struct PrefillTile {
     //           step's 64 keys, 16-byte chunk k at position k ^ (d & 7)), read with
     //           one 16-byte load per operand at voff[h]; otherwise V rows as
     //           given, read with transpose loads at voff[c & 3].
-    template <bool kSplit, bool kVT>
+    //   kRowSum also accumulate the row sums into accl (otherwise row_sums() does).
+    template <bool kSplit, bool kVT, bool kRowSum = true>
     __device__ __forceinline__ static void pv(const uint4 (&bhi)[kNT][kH], const uint4 (&blo)[kNT][kH],
                                               const uint8_t *Vt, const uint32_t *voff, f32x4_t (&accl)[kNT],
                                               f32x4_t (&acc)[kNT][VEC]) {
@@ -365,14 +368,28 @@ struct PrefillTile {
             }
             // Row sums of this half (after the half's products, so the two
             // updates of accl[nt] are far apart).
-            const uint32_t one = kPvHalf ? kOnesF16 : kOnesIn;
-            const uint4 ones = make_uint4(one, one, one, one);
+            if constexpr (kRowSum) {
+                const uint32_t one = kPvHalf ? kOnesF16 : kOnesIn;
+                const uint4 ones = make_uint4(one, one, one, one);
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                accl[nt] = mfma16<kPvHalf>(ones, bhi[nt][h], accl[nt]);
-                if constexpr (kSplit) accl[nt] = mfma16<kPvHalf>(ones, blo[nt][h], accl[nt]);
+                for (int nt = 0; nt < kNT; ++nt) {
+                    accl[nt] = mfma16<kPvHalf>(ones, bhi[nt][h], accl[nt]);
+                    if constexpr (kSplit) accl[nt] = mfma16<kPvHalf>(ones, blo[nt][h], accl[nt]);
+                }
             }
         }
+    }
+
+    // Row sums of one step's fp16 P (every element of rs[nt] is the sum of the
+    // lane's row).
+    __device__ __forceinline__ static void row_sums(const uint4 (&bhi)[kNT][kH], f32x4_t (&rs)[kNT]) {
+        const uint4 ones = make_uint4(kOnesF16, kOnesF16, kOnesF16, kOnesF16);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) rs[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < kH; ++h)
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) rs[nt] = mfma16<true>(ones, bhi[nt][h], rs[nt]);
     }
 
     // Key limits of the lane's rows for a step at key k0 (see references()).
@@ -567,20 +584,37 @@ struct PrefillTile {
         int lim0[kNT];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) lim0[nt] = 0;   // unused by the unmasked references
+        float nmu[kNT];
         if (nfast > 0) {
             qk(K0, koff, qop, sa);
+            references<false>(sa, lim0, sl2, m_ref, accl, acc, nmu);   // references from step 0's maxima
             __syncthreads();   // every wavefront is done with K(0)
         }
+        // After step 0 the fast loop does not compute row maxima: a score more than
+        // ~9 (log2 units) above its row's reference makes its fp16 weight, and so
+        // the step's row sum, infinite, and only then are the maxima computed, the
+        // references moved and P recomputed (rare; the accumulators still hold
+        // the previous steps only).  Otherwise the weights stay below 2^16.
         auto fast_iter = [&](uint8_t *Kfree, const uint8_t *Knext, const uint8_t *Vcur, uint8_t *Vnext, int x,
                              float (&scur)[kNT][kH][8], float (&snext)[kNT][kH][8]) {
             if (x + 2 < nsteps) issue_k(Kfree, x + 2);
             if (x + 1 < nsteps) issue_v(Vnext, x + 1);
-            float nmu[kNT];
-            references<false>(scur, lim0, sl2, m_ref, accl, acc, nmu);
             uint4 ph[kNT][kH], pl[kNT][kH];
             qk(Knext, koff, qop, snext);
             exp_p<false, false>(scur, lim0, sl2, nmu, ph, pl);
-            pv<false, true>(ph, pl, Vcur, vto, accl, acc);
+            f32x4_t rs[kNT];
+            row_sums(ph, rs);
+            bool bad = false;
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) bad |= !(fabsf(rs[nt][0]) < INFINITY);   // inf or NaN
+            if (__ballot(bad)) {
+                references<false>(scur, lim0, sl2, m_ref, accl, acc, nmu);
+                exp_p<false, false>(scur, lim0, sl2, nmu, ph, pl);
+                row_sums(ph, rs);
+            }
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) accl[nt] += rs[nt];
+            pv<false, true, false>(ph, pl, Vcur, vto, accl, acc);
             wait_loads();
             __syncthreads();
         };
