@@ -613,7 +613,7 @@ struct PrefillTile {
                 row_sums(ph, rs);
             }
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) accl[nt] += rs[nt];
+            for (int nt = 0; nt < kNT; ++nt) accl[nt][0] += rs[nt][0];   // element 0 is the one read at the end
             pv<false, true, false>(ph, pl, Vcur, vto, accl, acc);
             wait_loads();
             __syncthreads();
@@ -658,7 +658,7 @@ struct PrefillTile {
 
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
-            const float l_tot = accl[nt][0];   // every element of the ones product is the row sum
+            const float l_tot = accl[nt][0];   // the row sum (the fast loop adds to element 0 only)
             const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
             // acc[nt][c][q] is O[row][d = 16c + 4kg + q].
             if (cap[nt] > 0) {
