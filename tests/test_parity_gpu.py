@@ -378,9 +378,9 @@ def test_runs_on_the_given_stream_and_is_deterministic():
 # ------------------------------------------------------------------ measurement probes
 
 
-def test_probe_copy_and_read_are_exact():
+@pytest.mark.parametrize("n", [16, 1024 + 48, (37 << 20) + 48])
+def test_probe_copy_and_read_are_exact(n):
     import torch
-    n = (37 << 20) + 48
     src = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
     dst = torch.zeros_like(src)
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")     # GQA_PROBE_SINK_WORDS
