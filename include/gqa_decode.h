@@ -119,7 +119,10 @@ int gqa_decode_f16(const void *q, const void *k, const void *v, void *o,
  *             caller and not used concurrently by another call.  NULL = a
  *             library-owned buffer per (device, stream), grown with hipMalloc on
  *             demand and freed by gqa_release(); callers that capture HIP graphs
- *             must pass their own.
+ *             must pass their own, and make one uncaptured call of the same dtypes
+ *             and d_head on the device first (it caches the device's compute-unit
+ *             count and occupancy); the captured call then enqueues kernel
+ *             launches only.
  * sweep_events  See the field's comment; leave NULL outside profiling.
  * t_q         See the field's comment; 0 for the single-token decode.
  */

@@ -37,8 +37,9 @@
  * (nothing needs initialising).  gqa_prefill_workspace_bytes() gives its size.
  * With workspace NULL the library uses its own, per (device, stream), grown
  * with hipMalloc (not capturable in a HIP graph; freed by gqa_release()); a
- * caller-provided workspace (256-byte aligned) makes the call capturable.  Calls
- * sharing one workspace must be ordered (one stream).
+ * caller-provided workspace (256-byte aligned) makes the call capturable, after
+ * one uncaptured call of the same dtypes and d_head on the device (as for
+ * gqa_decode_ex).  Calls sharing one workspace must be ordered (one stream).
  *
  * Asynchrony and errors as in gqa_decode.h: work is enqueued on `stream`, host
  * errors return a gqa_status before anything is enqueued (o untouched), and
