@@ -20,6 +20,9 @@ Prints one JSON line:
   cpu_baseline   the fp64 CPU oracle on the same inputs, on the host cores
   decode_variants  the same batch with fp16 q/k/v and with two query tokens per
                  sequence (t_q = 2): step time, GB/s and the sweep kernel's roofline
+  other_workloads  the same step on every other named workload (tiny fp32,
+                 8B-shaped, single KV group, long-context stress) at its automatic
+                 plan: step time, GB/s, % of the HBM peak, the sweep kernel's time
   prefill        the causal prefill row at its own workload (one KV group, 32768
                  tokens, h_q 8, d_head 128, bf16): ms per call and TFLOP/s of
                  the algorithmic causal work against the bf16 matrix-core peak,
@@ -200,6 +203,64 @@ def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
     return rows
 
 
+def other_workloads(hip, stream, skip: int, steps: int):
+    """The decode step on every other named workload at its automatic plan: mean
+    step time over `steps` back-to-back calls (HIP events), K/V GB/s and its
+    fraction of the HBM peak, and the sweep kernel's own time.  Workloads whose
+    K and V fit in the caches cycle through copies of their inputs totalling
+    about 1 GiB, so every step reads its K and V from HBM."""
+    import torch
+    import gqa_split_kv_amd as gqa
+    from gqa_split_kv_amd.inputs import WORKLOADS, device_workload
+    rows = {}
+    for cfg, w in sorted(WORKLOADS.items()):
+        if cfg == skip:
+            continue
+        log("workload %d (%s)" % (cfg, w.name))
+        kv_bytes = w.kv_bytes()
+        rotate = 1 if kv_bytes >= (1 << 30) else min(64, -(-(1 << 30) // max(kv_bytes, 1)))
+        d = device_workload(w)
+        sets = [d] + [type(d)(d.q.clone(), d.k.clone(), d.v.clone(), d.seq_lens.clone(), d.seq_lens_host,
+                              d.scale, d.dtype) for _ in range(rotate - 1)]
+        kv_bytes = w.kv_bytes(d.seq_lens_host)
+        code = gqa.GQA_DTYPE_BF16 if w.dtype == "bf16" else gqa.GQA_DTYPE_F32
+        out = torch.empty((w.batch, w.h_q, w.d), dtype=d.q.dtype, device="cuda")
+        probe = gqa.make_args(d.q, d.k, d.v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale, code, code,
+                              stream=stream)
+        ws_bytes = gqa.gqa_decode_workspace_bytes(probe)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        ev_steps = [(hip.event(), hip.event()) for _ in range(steps)]
+
+        def args_for(i, events=None):
+            c = sets[i % rotate]
+            return gqa.make_args(c.q, c.k, c.v, out, c.seq_lens, w.batch, w.h_q, w.h_kv, w.d, c.scale, code,
+                                 code, 0, 0, ws, ws_bytes, stream, sweep_events=events)
+        warm = [args_for(i) for i in range(rotate)]
+        timed = [args_for(i, ev_steps[i]) for i in range(steps)]
+        for i in range(max(rotate, 3)):
+            gqa.gqa_decode_ex(warm[i % rotate])
+        torch.cuda.synchronize()
+        ev = (hip.event(), hip.event())
+        hip.record(ev[0], stream)
+        for a in timed:
+            gqa.gqa_decode_ex(a)
+        hip.record(ev[1], stream)
+        hip.sync(ev[1])
+        ms = hip.ms(*ev) / steps
+        sweep_ms = sum(hip.ms(a, b) for a, b in ev_steps) / steps
+        gbs = kv_bytes / (ms / 1e3) / 1e9
+        rows[w.name] = {"dtype": w.dtype, "kv_bytes_per_step": kv_bytes, "rotate": rotate,
+                        "us_per_step": round(ms * 1e3, 2), "gb_s": round(gbs, 2),
+                        "pct_of_peak_hbm": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+                        "sweep_kernel_us": round(sweep_ms * 1e3, 2),
+                        "us_at_hbm_peak": round(kv_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 3)}
+        for e in ev_steps + [ev]:
+            hip.destroy(e[0])
+            hip.destroy(e[1])
+        del d, sets, out, ws, warm, timed
+    return rows
+
+
 def prefill_flops(seq_lens, h_q: int, d: int) -> float:
     """Algorithmic causal-prefill work: token t of a sequence meets t + 1 keys, each
     costing 2d flops for q.k and 2d for the weighted V sum, per query head."""
@@ -276,6 +337,8 @@ def main():
                     help="timed calls of the causal prefill row (0 skips it)")
     ap.add_argument("--variant-steps", type=int, default=20,
                     help="timed steps of each other decode form (fp16, t_q = 2) on the same batch; 0 skips")
+    ap.add_argument("--workload-steps", type=int, default=50,
+                    help="timed steps of the decode on each other named workload; 0 skips")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (profiler calibration)")
     args = ap.parse_args()
@@ -414,6 +477,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline(d, w, args.cpu_budget)
     if args.variant_steps > 0:
         result["decode_variants"] = decode_variants(hip, stream, w, d, kv_bytes, args.variant_steps)
+    if args.workload_steps > 0:
+        result["other_workloads"] = other_workloads(hip, stream, args.workload, args.workload_steps)
     if args.prefill_steps > 0:
         result["prefill"] = prefill_row(hip, stream, args.prefill_steps, not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
