@@ -205,10 +205,13 @@ def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
 
 def other_workloads(hip, stream, skip: int, steps: int):
     """The decode step on every other named workload at its automatic plan: mean
-    step time over `steps` back-to-back calls (HIP events), K/V GB/s and its
-    fraction of the HBM peak, and the sweep kernel's own time.  Workloads whose
-    K and V fit in the caches cycle through copies of their inputs totalling
-    about 1 GiB, so every step reads its K and V from HBM."""
+    step time over `steps` back-to-back calls (HIP events around the loop only),
+    K/V GB/s and its fraction of the HBM peak, and the sweep kernel's own time
+    from a second pass with events around each sweep launch (each event record
+    costs the GPU ~3 us between kernels, which would swamp a ~16 us step, so the
+    step loop has none).  Workloads whose K and V fit in the caches cycle
+    through copies of their inputs totalling about 1 GiB, so every step reads
+    its K and V from HBM."""
     import torch
     import gqa_split_kv_amd as gqa
     from gqa_split_kv_amd.inputs import WORKLOADS, device_workload
@@ -236,7 +239,8 @@ def other_workloads(hip, stream, skip: int, steps: int):
             return gqa.make_args(c.q, c.k, c.v, out, c.seq_lens, w.batch, w.h_q, w.h_kv, w.d, c.scale, code,
                                  code, 0, 0, ws, ws_bytes, stream, sweep_events=events)
         warm = [args_for(i) for i in range(rotate)]
-        timed = [args_for(i, ev_steps[i]) for i in range(steps)]
+        timed = [warm[i % rotate] for i in range(steps)]
+        marked = [args_for(i, ev_steps[i]) for i in range(steps)]
         for i in range(max(rotate, 3)):
             gqa.gqa_decode_ex(warm[i % rotate])
         torch.cuda.synchronize()
@@ -247,6 +251,9 @@ def other_workloads(hip, stream, skip: int, steps: int):
         hip.record(ev[1], stream)
         hip.sync(ev[1])
         ms = hip.ms(*ev) / steps
+        for a in marked:
+            gqa.gqa_decode_ex(a)
+        torch.cuda.synchronize()
         sweep_ms = sum(hip.ms(a, b) for a, b in ev_steps) / steps
         gbs = kv_bytes / (ms / 1e3) / 1e9
         rows[w.name] = {"dtype": w.dtype, "kv_bytes_per_step": kv_bytes, "rotate": rotate,
@@ -257,7 +264,7 @@ def other_workloads(hip, stream, skip: int, steps: int):
         for e in ev_steps + [ev]:
             hip.destroy(e[0])
             hip.destroy(e[1])
-        del d, sets, out, ws, warm, timed
+        del d, sets, out, ws, warm, timed, marked
     return rows
 
 

@@ -383,25 +383,26 @@ __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int 
     // step st sits at position abase - off + kKeys*st + i) the bound is cap - kKeys*st.
     const int cap = len - P.t_q + t + 1 - static_cast<int>(abase - off);
 
+    // A step at or past nstep gets an empty range: its loads return zeros without
+    // a memory access (the pipeline's prefetches past the piece cost no round trip).
     auto load_step = [&](typename S::Buf &B, int st) {
-        const int hi = min(S::kKeys, span - st * S::kKeys);
-        const int64_t boff = static_cast<int64_t>(st) * S::kKeys * rowstride;
+        const int hi = max(0, min(S::kKeys, span - st * S::kKeys));
+        const int64_t boff = hi > 0 ? static_cast<int64_t>(st) * S::kKeys * rowstride : 0;
         const uint32_t bytes = static_cast<uint32_t>(hi * rowstride);
         S::load(B, buffer_rsrc(kbase + boff, bytes), buffer_rsrc(vbase + boff, bytes), lo);
     };
 
     // Software pipeline over kDepth register buffers: the loads of the next
-    // kDepth-1 steps are in flight while a step is computed.  Prefetch indices
-    // are clamped so every load is unconditional (the last step is fetched again,
-    // from cache, instead of branching).
+    // kDepth-1 steps are in flight while a step is computed.  Every load is
+    // unconditional: prefetches past the last step read an empty range.
     typename S::Buf buf[kDepth];
 #pragma unroll
-    for (int u = 0; u + 1 < kDepth; ++u) load_step(buf[u], min(u, nstep - 1));
+    for (int u = 0; u + 1 < kDepth; ++u) load_step(buf[u], u);
     int st = 0;
     while (true) {
 #pragma unroll
         for (int u = 0; u < kDepth; ++u) {
-            load_step(buf[(u + kDepth - 1) % kDepth], min(st + kDepth - 1, nstep - 1));
+            load_step(buf[(u + kDepth - 1) % kDepth], st + kDepth - 1);
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
             S::compute(buf[u], qop, st == 0 ? lead : 0,
                        min(min(S::kKeys, span - st * S::kKeys), cap - st * S::kKeys), kg, sl2, m_run,
