@@ -274,8 +274,10 @@ def prefill_flops(seq_lens, h_q: int, d: int) -> float:
     return float(sum(4.0 * d * h_q * S * (S + 1) / 2 for S in seq_lens))
 
 
-def prefill_row(hip, stream, steps: int, with_oracle: bool):
-    """Times gqa_prefill_ex on the 32K-token single-KV-group workload."""
+def prefill_row(hip, stream, steps: int, with_oracle: bool, warmup: int = 10):
+    """Times gqa_prefill_ex on the 32K-token single-KV-group workload: `warmup`
+    untimed calls per mode first (the matrix-core clocks ramp up over the first
+    few milliseconds of sustained work), then `steps` timed calls."""
     import torch
     import gqa_split_kv_amd as gqa
     from gqa_split_kv_amd.inputs import PREFILL_32K, device_prefill_case
@@ -291,7 +293,7 @@ def prefill_row(hip, stream, steps: int, with_oracle: bool):
         a = gqa.make_prefill_args(c.q, c.k, c.v, out, c.seq_lens, w.batch, w.h_q, w.h_kv, w.d, c.scale,
                                   gqa.GQA_DTYPE_BF16, gqa.GQA_DTYPE_BF16, 0, stream, split,
                                   total_tokens=c.q.shape[0])
-        for _ in range(2):
+        for _ in range(warmup):
             gqa.gqa_prefill_ex(a)
         torch.cuda.synchronize()
         ev = (hip.event(), hip.event())

@@ -121,6 +121,43 @@ __device__ void locate(const int32_t *seq_lens, int batch, int h_kv, int64_t pos
     len = 0;
 }
 
+// Value of x in lane src (src the same in every lane), as a wave-uniform value.
+__device__ __forceinline__ int64_t lane64(int64_t x, int src) {
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x)), src);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(x >> 32), src);
+    return (static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo);
+}
+
+// The lengths of a batch of at most 64 sequences held in registers: lane i has
+// sequence i's clamped length li (0 past the batch) and the inclusive sum incl of
+// lengths 0 .. i.  One load and one scan answer every seq_lens question the
+// decode kernels ask (the total, a sequence's length and offset, and which
+// sequence holds a key), where the loops above would each read seq_lens again.
+struct FirstLens {
+    int64_t li = 0, incl = 0;
+    __device__ void load(const int32_t *seq_lens, int batch) {
+        const int i = lane_id();
+        li = (i < batch) ? seq_len_at(seq_lens, i) : 0;
+        incl = inclusive_scan64(li);
+    }
+    __device__ int64_t total() const { return lane64(incl, kWave - 1); }
+    __device__ int len(int b) const { return static_cast<int>(lane64(li, b)); }      // b < 64
+    __device__ int64_t prefix(int b) const { return lane64(incl, b) - lane64(li, b); }   // b < 64
+    // locate() over these lengths.
+    __device__ void locate(int batch, int h_kv, int64_t pos, int &b, int64_t &off, int &len) const {
+        const unsigned long long mask = __ballot(lane_id() < batch && incl * h_kv > pos);
+        if (mask) {
+            b = __ffsll(static_cast<long long>(mask)) - 1;
+            len = static_cast<int>(lane64(li, b));
+            off = lane64(incl, b) - len;
+        } else {
+            b = batch;
+            off = total();
+            len = 0;
+        }
+    }
+};
+
 // Keys per range: max(min_chunk, ceil(total / num_chunks)).  The partial and the
 // merge kernel must agree on it exactly.
 __device__ __forceinline__ int64_t chunk_keys(int64_t total, int num_chunks, int min_chunk) {

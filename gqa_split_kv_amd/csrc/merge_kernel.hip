@@ -110,16 +110,20 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
     const bool active = g < R;
     const int tq = (active ? g : R - 1) / G;
     const int gh = (active ? g : R - 1) - tq * G;
-    const int len = uniform32(seq_len_at(P.seq_lens, b));
+    // Up to 64 sequences: one read of seq_lens gives the length, total and prefix.
+    const bool few = P.batch <= kWave;
+    FirstLens fl;
+    if (few) fl.load(P.seq_lens, P.batch);
+    const int len = few ? fl.len(b) : uniform32(seq_len_at(P.seq_lens, b));
     uint8_t *orow = P.o + ((static_cast<int64_t>(b) * P.t_q + tq) * P.h_q + j * G + gh) * D *
                               (kOut == kF32 ? 4 : 2);
     if (len == 0) {
         if (pl == 0 && active) store_quad<kOut>(orow, eq, make_float4(0.f, 0.f, 0.f, 0.f));
         return;
     }
-    const int64_t total = total_len(P.seq_lens, P.batch);
+    const int64_t total = few ? fl.total() : total_len(P.seq_lens, P.batch);
     const int64_t chunk = chunk_keys(total, P.num_chunks / P.h_kv, P.min_chunk);
-    const int64_t ustart = prefix_len(P.seq_lens, b);
+    const int64_t ustart = few ? fl.prefix(b) : prefix_len(P.seq_lens, b);
     const int64_t ca = ustart / chunk;   // token ranges holding this sequence
     const int64_t cb = (ustart + len - 1) / chunk;
     if (ca == cb) return;                // written whole by the sweep kernel

@@ -455,14 +455,21 @@ __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
     // adjacent kv-head slices of the same key rows at the same time.
     const int j = w % P.h_kv;
     const int c = w / P.h_kv;
-    const int64_t total = total_len(P.seq_lens, P.batch);
+    // Up to 64 sequences: their lengths stay in registers (one read of seq_lens).
+    const bool few = P.batch <= kWave;
+    FirstLens fl;
+    if (few) fl.load(P.seq_lens, P.batch);
+    const int64_t total = few ? fl.total() : total_len(P.seq_lens, P.batch);
     const int64_t chunk = chunk_keys(total, P.num_chunks / P.h_kv, P.min_chunk);
     int64_t pos = static_cast<int64_t>(c) * chunk;
     if (pos >= total) return;
     const int64_t end = pos + chunk < total ? pos + chunk : total;
     int b, len;
     int64_t off;
-    locate(P.seq_lens, P.batch, 1, pos, b, off, len);
+    if (few)
+        fl.locate(P.batch, 1, pos, b, off, len);
+    else
+        locate(P.seq_lens, P.batch, 1, pos, b, off, len);
     while (true) {
         const int t0 = uniform32(static_cast<int>(pos - off));
         const int64_t lim = end - off;
@@ -473,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
         off += len;   // next non-empty sequence (one exists: pos < total)
         do {
             ++b;
-            len = uniform32(seq_len_at(P.seq_lens, b));
+            len = few ? fl.len(b) : uniform32(seq_len_at(P.seq_lens, b));
         } while (len == 0);
     }
 }
