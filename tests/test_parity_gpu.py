@@ -95,6 +95,26 @@ def test_long_context_peaked_workload_full_size():
     compare(out16, ref, "cfg5 bf16 out")
 
 
+def test_sequence_beyond_2_pow_25_keys():
+    """A sequence of 2^25 + 3 keys between two short ones (d 64, one kv head, G 2):
+    the long one is cut into many ranges and merged, and the short one after it
+    starts past 2^25 key rows, at the offset the kernels' table of lengths gives."""
+    import torch
+    from gqa_split_kv_amd.inputs import device_case
+    import oracle
+    lens = [5, (1 << 25) + 3, 7]
+    _say("generating 3 sequences, %d keys" % sum(lens))
+    d = device_case(3, 2, 1, 64, lens, "bf16", seed=2525)
+    o32 = run_hip(d.q, d.k, d.v, d.seq_lens, d.scale, out_dtype=torch.float32)
+    o16 = run_hip(d.q, d.k, d.v, d.seq_lens, d.scale)
+    _say("copying inputs to the host and running the oracle")
+    ref = oracle.gqa_decode_f64(to_host_bits(d.q), to_host_bits(d.k), to_host_bits(d.v), d.seq_lens_host,
+                                d.scale)
+    e, r = compare(o32, ref, "2^25+3 keys f32 out")
+    _say("fp32 out: max|err| %.3g rel-L2 %.3g" % (e, r))
+    compare(o16, ref, "2^25+3 keys bf16 out")
+
+
 # ------------------------------------------------------------------ shapes and plans
 
 
