@@ -89,6 +89,29 @@ def test_prefill_longer_ragged_batch_and_grid_independence():
             assert torch.equal(o, outs[0])
 
 
+def test_prefill_batch_of_more_than_64_sequences():
+    """150 sequences (lengths 0 .. 400, some empty, some past a 64-key step):
+    the work-item count and the search for a tile's sequence run over several
+    64-sequence blocks, and the V copy's step blocks follow every sequence."""
+    import torch
+    rng = np.random.default_rng(150)
+    lens = [int(x) for x in rng.integers(0, 401, size=150)]
+    lens[3] = 0
+    lens[70] = 0
+    lens[64] = 65
+    c = host_prefill_case(len(lens), 8, 2, 128, lens, "bf16", seed=150)
+    _say("oracle: 150 sequences, %d tokens" % sum(lens))
+    ref = oracle.gqa_prefill_f64(c.q, c.k, c.v, c.seq_lens, c.scale)
+    q, k, v, sl = upload(c)
+    for nb, sp in ((0, 0), (7, 0), (0, 1)):
+        _say("prefill 150 sequences, num_blocks", nb, "split_pv", sp)
+        o = _run(q, k, v, sl, c.scale, torch.float32, nb, sp)
+        e, r = _check(o, ref, "150 sequences nb=%d split=%d" % (nb, sp), sp)
+        _say("  max|err| %.3g rel-L2 %.3g" % (e, r))
+    o16 = _run(q, k, v, sl, c.scale)
+    _check(o16, ref, "150 sequences bf16 out")
+
+
 def test_prefill_70b_heads_long_sequences():
     """64 query heads over 8 kv heads (the 70B grouping), two sequences long
     enough for dozens of fast-loop steps per tile, both P V modes."""
