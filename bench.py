@@ -113,6 +113,18 @@ def committed_traffic():
     return float(t.group(1)), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-kernel scaled"
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(d, w, budget_s: float):
     """Times the fp64 oracle on the host over whole sequences of the same inputs."""
     import numpy as np
@@ -139,7 +151,7 @@ def cpu_baseline(d, w, budget_s: float):
     nbytes = rows * w.h_kv * w.d * 2 * 2
     return {
         "value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-        "seconds": dt,
+        "cpu": cpu_model(), "seconds": dt,
         "sample": "first %d of %d sequences (%d keys, %.3g GB of K+V), same seeded inputs, "
                   "fp64 direct softmax(qK^T*scale)V per head, OpenMP over (sequence, kv head)"
                   % (n, len(sl), rows, nbytes / 1e9),
@@ -323,7 +335,8 @@ def prefill_row(hip, stream, steps: int, with_oracle: bool, warmup: int = 10):
         dt = time.perf_counter() - t
         sample_flops = sum(4.0 * w.d * w.h_q * (tk + 1) for tk in toks)
         row["cpu_baseline"] = {"value": round(sample_flops / dt / 1e12, 6), "unit": "TFLOP/s",
-                               "cores": oracle.num_threads(), "kind": "oracle", "seconds": round(dt, 3),
+                               "cores": oracle.num_threads(), "kind": "oracle", "cpu": cpu_model(),
+                               "seconds": round(dt, 3),
                                "sample": "the last 8 of 32768 tokens (all 8 heads), fp64, one token at a time"}
     return row
 
