@@ -642,7 +642,13 @@ struct PrefillTile {
                 issue_v(Vnext, x + 1);
             }
             const int k0 = x * kStepKeys;
-            if (k0 < wkeys) step<true, true>(Kcur, Vcur, k0, koff, voff, qop, cap, sl2, m_ref, accl, acc);
+            // A step below the tile's first token is visible to every row: no mask.
+            if (k0 < wkeys) {
+                if (x < nfull)
+                    step<false, true>(Kcur, Vcur, k0, koff, voff, qop, cap, sl2, m_ref, accl, acc);
+                else
+                    step<true, true>(Kcur, Vcur, k0, koff, voff, qop, cap, sl2, m_ref, accl, acc);
+            }
             wait_loads();
             __syncthreads();
         };
