@@ -18,8 +18,9 @@ Prints one JSON line:
                  traffic = HBM bytes per launch from the committed rocprofv3
                  counter summary if it was taken on the current kernel source
   cpu_baseline   the fp64 CPU oracle on the same inputs, on the host cores
-  decode_variants  the same batch with fp16 q/k/v and with two query tokens per
-                 sequence (t_q = 2): step time, GB/s and the sweep kernel's roofline
+  decode_variants  the same batch with fp16 q/k/v and with two or four query
+                 tokens per sequence (t_q = 2, 4): step time, GB/s and the sweep
+                 kernel's roofline
   other_workloads  the same step on every other named workload (tiny fp32,
                  8B-shaped, single KV group, long-context stress) at its automatic
                  plan: step time, GB/s, % of the HBM peak, the sweep kernel's time
@@ -160,9 +161,10 @@ def cpu_baseline(d, w, budget_s: float):
 
 def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
     """The decode path's other input forms on the same batch and K/V bytes:
-    fp16 q/k/v (gqa_decode_f16's kernels, fp16 out) and two query tokens per
-    sequence (bf16, t_q = 2: every sequence's last two tokens, causal between
-    them; G * t_q = 16 rows per kv head).  Each is timed like the headline step,
+    fp16 q/k/v (gqa_decode_f16's kernels, fp16 out) and two or four query tokens
+    per sequence (bf16, t_q = 2: every sequence's last two tokens, causal between
+    them, G * t_q = 16 rows per kv head; t_q = 4: 32 rows, two wavefronts per
+    key range and kv head).  Each is timed like the headline step,
     with the sweep kernel's own HIP events."""
     import torch
     import gqa_split_kv_amd as gqa
@@ -173,6 +175,8 @@ def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
          gqa.GQA_DTYPE_F16, 0),
         ("bf16_t_q2", lambda: (device_queries(w.batch, 2, w.h_q, w.d, "bf16", seed=w.seed + 7), d.k, d.v),
          gqa.GQA_DTYPE_BF16, 2),
+        ("bf16_t_q4", lambda: (device_queries(w.batch, 4, w.h_q, w.d, "bf16", seed=w.seed + 9), d.k, d.v),
+         gqa.GQA_DTYPE_BF16, 4),
     ]
     for name, make, code, t_q in forms:
         log("decode variant %s" % name)

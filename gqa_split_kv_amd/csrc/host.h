@@ -42,7 +42,9 @@ constexpr int kPrefillRows = GQA_PREFILL_ROWS;
 // workgroup size of the kernel that makes the copy.
 constexpr int kPrefillStepKeys = 64;
 constexpr int kVprepThreads = 256;
-constexpr int kMaxG = 16;           // rows (query heads x query tokens) per kv head in one 16-wide MFMA tile
+constexpr int kMaxG = 16;           // prefill: query heads per kv head (one 16-wide MFMA tile of rows)
+constexpr int kRowTile = 16;        // decode: rows (query tokens x query heads) per sweep wavefront
+constexpr int kMaxRows = 64;        // decode: rows per kv head, G * t_q (up to 4 wavefronts per range)
 constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxPrefillBlocks = 1 << 20;
 constexpr int kMaxHeadsKv = 1 << 16;   // keeps 16 key rows of lane offsets within 32 bits
@@ -80,14 +82,18 @@ struct PrefillWorkspace {
 PrefillWorkspace prefill_workspace(const gqa_prefill_args *a);
 constexpr int64_t kMaxPrefillRowsHeads = int64_t(1) << 37;   // total_tokens * h_kv limit
 
-// Workspace layout for `num_chunks` wavefronts: two partial-triple slots per
-// wavefront, each R = G * t_q rows of (O[D] fp32) plus (m, l) fp32.
+// Workspace layout for `units` (token range, kv head) units: two partial-triple
+// slots per unit, each R = G * t_q rows of (O[D] fp32) plus (m, l) fp32.  A unit
+// is swept by row_groups() wavefronts, 16 of its rows each.
 struct WorkspaceLayout {
-    size_t o_offset;    // float  [num_chunks][2][G][D]
-    size_t ml_offset;   // float2 [num_chunks][2][G]
+    size_t o_offset;    // float  [units][2][R][D]
+    size_t ml_offset;   // float2 [units][2][R]
     size_t bytes;
 };
-WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D);
+WorkspaceLayout workspace_layout(int64_t units, int rows, int D);
+
+// Wavefronts per (token range, kv head) of a decode call: ceil(G * t_q / 16).
+int row_groups(const gqa_decode_args *a);
 
 int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decode_plan *plan);
 

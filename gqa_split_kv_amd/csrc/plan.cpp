@@ -38,9 +38,9 @@ static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D) {
+WorkspaceLayout workspace_layout(int64_t units, int rows, int D) {
     WorkspaceLayout L;
-    const size_t slots = static_cast<size_t>(num_chunks) * 2 * static_cast<size_t>(rows);
+    const size_t slots = static_cast<size_t>(units) * 2 * static_cast<size_t>(rows);
     L.o_offset = 0;
     L.ml_offset = round_up(slots * static_cast<size_t>(D) * sizeof(float), 256);
     L.bytes = round_up(L.ml_offset + slots * 2 * sizeof(float), 256);
@@ -51,6 +51,8 @@ WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D) {
 static int rows_per_kv_head(const gqa_decode_args *a) {
     return (a->h_q / a->h_kv) * (a->t_q > 0 ? a->t_q : 1);
 }
+
+int row_groups(const gqa_decode_args *a) { return (rows_per_kv_head(a) + kRowTile - 1) / kRowTile; }
 
 static int check_basic(const gqa_decode_args *a) {
     if (!a) return fail(GQA_ERR_NULL, "args is NULL");
@@ -66,12 +68,12 @@ static int check_basic(const gqa_decode_args *a) {
     if (a->h_kv > kMaxHeadsKv)
         return fail(GQA_ERR_UNSUPPORTED, "h_kv %d exceeds %d", a->h_kv, kMaxHeadsKv);
     const int G = a->h_q / a->h_kv;
-    if (G > kMaxG)
-        return fail(GQA_ERR_UNSUPPORTED, "G = h_q/h_kv = %d exceeds %d", G, kMaxG);
+    if (G > kMaxRows)
+        return fail(GQA_ERR_UNSUPPORTED, "G = h_q/h_kv = %d exceeds %d", G, kMaxRows);
     if (a->t_q < 0) return fail(GQA_ERR_SHAPE, "t_q %d is negative", a->t_q);
     const int tq = a->t_q > 0 ? a->t_q : 1;
-    if (static_cast<int64_t>(G) * tq > kMaxG)
-        return fail(GQA_ERR_UNSUPPORTED, "G * t_q = %d * %d exceeds %d rows", G, tq, kMaxG);
+    if (static_cast<int64_t>(G) * tq > kMaxRows)
+        return fail(GQA_ERR_UNSUPPORTED, "G * t_q = %d * %d exceeds %d rows", G, tq, kMaxRows);
     if (static_cast<int64_t>(a->batch) * tq * a->h_q > 0x7fffffff)
         return fail(GQA_ERR_SHAPE, "batch * t_q * h_q exceeds 2^31-1");
     if (a->d_head != 64 && a->d_head != 128)
@@ -108,9 +110,10 @@ int validate(const gqa_decode_args *a) {
     int st = check_basic(a);
     if (st != GQA_OK) return st;
     if (a->num_chunks > 0) {
-        int64_t chunks = static_cast<int64_t>(a->num_chunks) / a->h_kv * a->h_kv;
-        if (chunks < a->h_kv) chunks = a->h_kv;
-        const WorkspaceLayout L = workspace_layout(chunks, rows_per_kv_head(a), a->d_head);
+        const int64_t per = static_cast<int64_t>(a->h_kv) * row_groups(a);
+        int64_t chunks = static_cast<int64_t>(a->num_chunks) / per * per;
+        if (chunks < per) chunks = per;
+        const WorkspaceLayout L = workspace_layout(chunks / row_groups(a), rows_per_kv_head(a), a->d_head);
         st = check_workspace(a, L.bytes);
         if (st != GQA_OK) return st;
     }
@@ -189,18 +192,22 @@ int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decod
         chunks = static_cast<int64_t>(num_cus) * (waves_per_cu < kAutoWavesPerCu ? waves_per_cu : kAutoWavesPerCu);
         if (chunks > kMaxChunks) chunks = kMaxChunks;
     }
-    // One wavefront per kv head of every token range: a multiple of h_kv.
-    chunks = chunks / a->h_kv * a->h_kv;
-    if (chunks < a->h_kv) chunks = a->h_kv;
-    if (chunks > kMaxChunks) return fail(GQA_ERR_ARG, "h_kv %d needs more than %d wavefronts", a->h_kv, kMaxChunks);
-    const WorkspaceLayout L = workspace_layout(chunks, rows_per_kv_head(a), a->d_head);
+    // NG wavefronts (16 rows each) per kv head of every token range: a multiple of h_kv * NG.
+    const int NG = row_groups(a);
+    const int64_t per = static_cast<int64_t>(a->h_kv) * NG;
+    chunks = chunks / per * per;
+    if (chunks < per) chunks = per;
+    if (chunks > kMaxChunks)
+        return fail(GQA_ERR_ARG, "h_kv %d with %d rows per kv head needs more than %d wavefronts", a->h_kv,
+                    rows_per_kv_head(a), kMaxChunks);
+    const WorkspaceLayout L = workspace_layout(chunks / NG, rows_per_kv_head(a), a->d_head);
     st = check_workspace(a, L.bytes);
     if (st != GQA_OK) return st;
     plan->num_chunks = static_cast<int32_t>(chunks);
     plan->min_chunk = a->min_chunk > 0 ? a->min_chunk : kAutoMinChunk;
     plan->split_blocks = static_cast<int32_t>((chunks + kWavesPerBlock - 1) / kWavesPerBlock);
     // Expected pieces per sequence: token ranges per sequence on average.
-    const int64_t ranges = chunks / a->h_kv;
+    const int64_t ranges = chunks / per;
     const int R = rows_per_kv_head(a);
     const bool wide = ranges / a->batch > kWideMergePieces;
     const bool split = wide && static_cast<int64_t>(a->batch) * a->h_kv * R < kSplitMergeBelowBlocks;

@@ -35,7 +35,9 @@
  *   seq_lens  int32[batch]  (device memory; read by the kernels, never by the host,
  *             so a call needs no host synchronisation)
  *
- * Supported: d_head in {64, 128}; G = h_q / h_kv in 1..16; (in, out) dtypes
+ * Supported: d_head in {64, 128}; G = h_q / h_kv in 1..64 (G * t_q <= 64 rows per kv
+ * head; more than 16 rows are swept by ceil(rows / 16) wavefronts per key range, each
+ * reading the same keys); (in, out) dtypes
  * (bf16, bf16), (bf16, f32), (f16, f16), (f16, f32) and (f32, f32).  q, k, v, o must be 16-byte aligned,
  * seq_lens 4-byte aligned.
  *
@@ -68,7 +70,7 @@ typedef enum gqa_status {
     GQA_ERR_NULL = 1,        /* a required pointer is NULL                              */
     GQA_ERR_SHAPE = 2,       /* batch, h_q or h_kv <= 0, h_q not a multiple of h_kv,    *
                               * t_q < 0, or batch * t_q * h_q above 2^31-1              */
-    GQA_ERR_UNSUPPORTED = 3, /* d_head not 64/128, G * t_q > 16, or dtype pair          *
+    GQA_ERR_UNSUPPORTED = 3, /* d_head not 64/128, G * t_q > 64, or dtype pair          *
                               * not supported                                           */
     GQA_ERR_ALIGN = 4,       /* q/k/v/o not 16-byte aligned or seq_lens not 4-byte      */
     GQA_ERR_SCALE = 5,       /* scale is not finite                                     */
@@ -101,15 +103,16 @@ int gqa_decode_f16(const void *q, const void *k, const void *v, void *o,
 /*
  * Full argument block.  Zero-initialise it, then set the fields.
  *
- * num_chunks  Wavefronts of the sweep.  The token axis -- the key rows of all
+ * num_chunks  Wavefronts of the sweep.  With NG = ceil(G * t_q / 16) wavefronts
+ *             per kv head (16 rows each), the token axis -- the key rows of all
  *             sequences end to end, sum(seq_lens) rows -- is cut into
- *             num_chunks / h_kv equal ranges of `chunk` rows, where
- *               chunk = max(min_chunk, ceil(sum(seq_lens) / (num_chunks / h_kv)))
+ *             num_chunks / (h_kv NG) equal ranges of `chunk` rows, where
+ *               chunk = max(min_chunk, ceil(sum(seq_lens) / (num_chunks / (h_kv NG))))
  *             is computed on the device from seq_lens, and each range is swept by
- *             h_kv wavefronts, one per kv head.  A range that holds a whole
+ *             h_kv NG wavefronts.  A range that holds a whole
  *             sequence writes its o rows directly; the pieces of a sequence that
  *             spans several ranges are merged by a second kernel.  Rounded down to
- *             a multiple of h_kv (at least h_kv).  0 = automatic (compute units x
+ *             a multiple of h_kv NG (at least h_kv NG).  0 = automatic (compute units x
  *             resident wavefronts per compute unit).  Range: 0..2^24.
  * min_chunk   Smallest range in key rows; 0 = automatic.  Range: 0..2^30.
  *             min_chunk = 1024 with a large num_chunks reproduces the page's
@@ -153,7 +156,7 @@ typedef struct gqa_decode_args {
      * 0 or 1 = one.  With t_q > 1, q and o are [batch, t_q, h_q, d_head], the last
      * t_q key rows of every sequence belong to the new tokens, and query token t
      * attends to the keys at positions 0 .. seq_len - t_q + t (causal among the new
-     * tokens; a token that sees no key gives 0).  G * t_q must not exceed 16. */
+     * tokens; a token that sees no key gives 0).  G * t_q must not exceed 64. */
     int32_t t_q;
 } gqa_decode_args;
 

@@ -80,7 +80,7 @@ def test_shape_errors(lib, kw):
 
 
 @pytest.mark.parametrize("kw", [dict(d_head=96), dict(d_head=256), dict(d_head=0),
-                                dict(h_q=32 * 8, h_kv=8), dict(h_q=17, h_kv=1),
+                                dict(h_q=65 * 8, h_kv=8), dict(h_q=65, h_kv=1),
                                 dict(in_dtype=B.GQA_DTYPE_F32, out_dtype=B.GQA_DTYPE_BF16),
                                 dict(in_dtype=B.GQA_DTYPE_F32, out_dtype=B.GQA_DTYPE_F16),
                                 dict(in_dtype=B.GQA_DTYPE_F16, out_dtype=B.GQA_DTYPE_BF16),
@@ -92,13 +92,32 @@ def test_unsupported(lib, kw):
 
 def test_multi_token_limits(lib):
     assert _validate(t_q=2, h_q=64, h_kv=8) == B.GQA_OK          # G 8 x 2 tokens = 16 rows
-    assert _validate(t_q=3, h_q=64, h_kv=8) == B.GQA_ERR_UNSUPPORTED
-    assert _validate(t_q=16, h_q=8, h_kv=8) == B.GQA_OK
+    assert _validate(t_q=8, h_q=64, h_kv=8) == B.GQA_OK          # 64 rows: 4 wavefronts per range
+    assert _validate(t_q=9, h_q=64, h_kv=8) == B.GQA_ERR_UNSUPPORTED
+    assert _validate(t_q=64, h_q=8, h_kv=8) == B.GQA_OK
+    assert _validate(t_q=65, h_q=8, h_kv=8) == B.GQA_ERR_UNSUPPORTED
+    assert _validate(h_q=64, h_kv=1) == B.GQA_OK                 # G 64
     assert _validate(t_q=-1) == B.GQA_ERR_SHAPE
     st, p1 = B.gqa_decode_make_plan(_args(num_chunks=64), 256, 4)
     st2, p4 = B.gqa_decode_make_plan(_args(num_chunks=64, t_q=4), 256, 4)
     assert st == st2 == B.GQA_OK
     assert p4.workspace_bytes >= 4 * p1.workspace_bytes - 256
+
+
+def test_row_groups_share_token_ranges(lib):
+    """More than 16 rows per kv head: ceil(rows / 16) wavefronts per (token range,
+    kv head), so the wavefront count is a multiple of h_kv times that, and the
+    workspace holds one unit of slots per (token range, kv head)."""
+    st, p = B.gqa_decode_make_plan(_args(h_q=64, h_kv=8, t_q=4), 256, 4)       # 32 rows: 2 groups
+    assert st == B.GQA_OK and p.num_chunks == 1024 and p.split_blocks == 256
+    st, p = B.gqa_decode_make_plan(_args(h_q=48, h_kv=1, t_q=1, num_chunks=10), 256, 4)   # 48 rows: 3
+    assert st == B.GQA_OK and p.num_chunks == 9
+    st, p = B.gqa_decode_make_plan(_args(h_q=48, h_kv=1, num_chunks=2), 256, 4)
+    assert st == B.GQA_OK and p.num_chunks == 3                  # at least one range
+    # Units = wavefronts / groups: 2 groups of 16 rows hold as many slots as 1 of 32.
+    st, p32 = B.gqa_decode_make_plan(_args(h_q=32, h_kv=1, num_chunks=64), 256, 4)
+    st, p16 = B.gqa_decode_make_plan(_args(h_q=16, h_kv=1, num_chunks=64), 256, 4)
+    assert p32.workspace_bytes == p16.workspace_bytes
 
 
 @pytest.mark.parametrize("field", ["q", "k", "v", "o"])

@@ -225,6 +225,48 @@ def test_multi_token_70b_shaped_ragged_full_size_sampled():
         compare(out16[b:b + 1], ref, "t_q=2 seq %d bf16" % b)
 
 
+@pytest.mark.parametrize("G,h_kv,t_q", [(8, 2, 4), (16, 1, 3), (8, 1, 8), (32, 2, 1), (64, 1, 1),
+                                        (24, 1, 2), (17, 1, 1), (3, 3, 7)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"),
+                                       ("f16", "f16")])
+def test_more_than_16_rows_per_kv_head(G, h_kv, t_q, d, dtype, out):
+    """G * t_q from 17 to 64 rows per kv head: ceil(rows / 16) wavefronts sweep each
+    (token range, kv head), 16 rows each, and leave their partials in the same
+    workspace unit; short sequences leave tokens that see no key (output 0)."""
+    import torch
+    lens = [37, 0, 300, 2, 1, 16, 129]
+    c = host_case(len(lens), G * h_kv, h_kv, d, lens, dtype, seed=G * 37 + t_q * 5 + d + h_kv, t_q=t_q)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    odt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out]
+    for nc, mc in [(0, 0), (5, 1), (64, 16), (1000, 1)]:
+        _say("rows", G * t_q, "t_q", t_q, "G", G, "h_kv", h_kv, "d", d, dtype, "->", out, "nc", nc, "mc", mc)
+        o = run_hip(q, k, v, sl, c.scale, out_dtype=odt, num_chunks=nc, min_chunk=mc)
+        assert o.shape == (len(lens), t_q, G * h_kv, d)
+        compare(o, ref, "rows=%d t_q=%d G=%d h_kv=%d d=%d %s->%s nc=%d mc=%d" % (G * t_q, t_q, G, h_kv, d,
+                                                                                 dtype, out, nc, mc))
+
+
+def test_more_than_16_rows_70b_heads_ragged_batch():
+    """Four speculative tokens on the 70B grouping (G 8, h_kv 8: 32 rows per kv
+    head) over a ragged batch of 12 sequences up to 3000 keys, and one token on 64
+    query heads over one kv head (G 64), against the oracle."""
+    import torch
+    rng = np.random.default_rng(4)
+    lens = [int(x) for x in rng.integers(0, 3001, size=12)]
+    for h_q, h_kv, t_q in ((64, 8, 4), (64, 1, 1)):
+        c = host_case(len(lens), h_q, h_kv, 128, lens, "bf16", seed=400 + h_kv + t_q, t_q=t_q)
+        ref = oracle_of(c)
+        q, k, v, sl = upload(c)
+        for nc, mc in [(0, 0), (7, 1), (4096, 1)]:
+            _say("70B heads ragged, h_q", h_q, "h_kv", h_kv, "t_q", t_q, "nc", nc)
+            o32 = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=mc)
+            compare(o32, ref, "h_q=%d h_kv=%d t_q=%d nc=%d f32" % (h_q, h_kv, t_q, nc))
+            o16 = run_hip(q, k, v, sl, c.scale, num_chunks=nc, min_chunk=mc)
+            compare(o16, ref, "h_q=%d h_kv=%d t_q=%d nc=%d bf16" % (h_q, h_kv, t_q, nc))
+
+
 def test_multi_token_short_sequences_give_zero_for_unseen_tokens():
     import torch
     lens = [0, 1, 2, 3, 4, 5]
