@@ -267,6 +267,24 @@ def test_more_than_16_rows_70b_heads_ragged_batch():
             compare(o16, ref, "h_q=%d h_kv=%d t_q=%d nc=%d bf16" % (h_q, h_kv, t_q, nc))
 
 
+def test_more_than_16_rows_more_than_64_sequences():
+    """Row groups (G 32, two wavefronts per key range) over 90 sequences, where the
+    kernels take the lengths from seq_lens block by block instead of one register
+    table, with the automatic and forced plans."""
+    import torch
+    rng = np.random.default_rng(90)
+    lens = [int(x) for x in rng.integers(0, 400, size=90)]
+    lens[0] = 0
+    lens[64] = 1
+    c = host_case(len(lens), 64, 2, 128, lens, "bf16", seed=90, t_q=1)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    for nc, mc in [(0, 0), (6, 1), (2000, 1)]:
+        _say("90 sequences, G 32, nc", nc, "mc", mc)
+        o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=mc)
+        compare(o, ref, "90 sequences G=32 nc=%d mc=%d" % (nc, mc))
+
+
 def test_multi_token_short_sequences_give_zero_for_unseen_tokens():
     import torch
     lens = [0, 1, 2, 3, 4, 5]
