@@ -44,7 +44,7 @@ constexpr int kPrefillStepKeys = 64;
 constexpr int kVprepThreads = 256;
 constexpr int kMaxG = 16;           // prefill: query heads per kv head (one 16-wide MFMA tile of rows)
 constexpr int kRowTile = 16;        // decode: rows (query tokens x query heads) per sweep wavefront
-constexpr int kMaxRows = 64;        // decode: rows per kv head, G * t_q (up to 4 wavefronts per range)
+constexpr int kMaxRows = 64;        // decode: rows per kv head, G * t_q (up to 2 wavefronts of 2 tiles per range)
 constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxPrefillBlocks = 1 << 20;
 constexpr int kMaxHeadsKv = 1 << 16;   // keeps 16 key rows of lane offsets within 32 bits
@@ -92,7 +92,8 @@ struct WorkspaceLayout {
 };
 WorkspaceLayout workspace_layout(int64_t units, int rows, int D);
 
-// Wavefronts per (token range, kv head) of a decode call: ceil(G * t_q / 16).
+// Wavefronts per (token range, kv head) of a decode call: 1 up to 16 rows (G * t_q),
+// else ceil(rows / 32) (two 16-row tiles per wavefront).
 int row_groups(const gqa_decode_args *a);
 
 int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decode_plan *plan);

@@ -20,7 +20,7 @@ struct DecodeParams {
     int32_t batch, h_q, h_kv, G;
     int32_t t_q;               // query tokens per sequence
     int32_t R;                 // rows per kv head: G * t_q (row = t * G + g)
-    int32_t NG;                // wavefronts per (token range, kv head): ceil(R / 16), 16 rows each
+    int32_t NG;                // wavefronts per (token range, kv head): 1 up to 16 rows, else ceil(R / 32)
     int32_t num_chunks, min_chunk;
     float scale_log2;          // scale * log2(e)
 };

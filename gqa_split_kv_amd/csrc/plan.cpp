@@ -52,7 +52,12 @@ static int rows_per_kv_head(const gqa_decode_args *a) {
     return (a->h_q / a->h_kv) * (a->t_q > 0 ? a->t_q : 1);
 }
 
-int row_groups(const gqa_decode_args *a) { return (rows_per_kv_head(a) + kRowTile - 1) / kRowTile; }
+// Wavefronts per (token range, kv head): one 16-row tile each up to 16 rows, two
+// tiles each beyond.
+int row_groups(const gqa_decode_args *a) {
+    const int R = rows_per_kv_head(a);
+    return R <= kRowTile ? 1 : (R + 2 * kRowTile - 1) / (2 * kRowTile);
+}
 
 static int check_basic(const gqa_decode_args *a) {
     if (!a) return fail(GQA_ERR_NULL, "args is NULL");
@@ -192,7 +197,7 @@ int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decod
         chunks = static_cast<int64_t>(num_cus) * (waves_per_cu < kAutoWavesPerCu ? waves_per_cu : kAutoWavesPerCu);
         if (chunks > kMaxChunks) chunks = kMaxChunks;
     }
-    // NG wavefronts (16 rows each) per kv head of every token range: a multiple of h_kv * NG.
+    // NG wavefronts (one or two 16-row tiles each) per kv head of every token range: a multiple of h_kv * NG.
     const int NG = row_groups(a);
     const int64_t per = static_cast<int64_t>(a->h_kv) * NG;
     chunks = chunks / per * per;

@@ -55,7 +55,7 @@ constexpr int kSweepDepth = GQA_SWEEP_DEPTH;   // register buffers in the sweep 
 // Cache policy of the K/V stream loads (buffer-instruction cache-policy bits).
 // With one wavefront per (token range, kv head), K and V are read exactly once,
 // so they are loaded non-temporally (nt) and do not displace the partials, q and
-// seq_lens from the caches.  When NG > 1 wavefronts (16 rows each) sweep the same
+// seq_lens from the caches.  When NG > 1 wavefronts (32 rows each) sweep the same
 // range, the loads keep the default policy so that the repeats find the lines in
 // the caches (measured with four query tokens on the 70B grouping: 1189 us with
 // nt, 827 us cached; one token: 619 us nt, 705 us cached).
@@ -337,41 +337,19 @@ __device__ __forceinline__ void store_row(uint8_t *dst, const float *x, int n) {
 }
 
 // One piece: keys [t0, t1) of (sequence b, kv head j); off = keys before b.  The
-// wavefront takes rows 16 rg .. 16 rg + 15 of the kv head; u = its (token range,
-// kv head) unit, which indexes the workspace slots.
-template <int kIn, int kOut, int D, int kDepth, int kCpol>
+// wavefront takes kNT 16-row tiles of the kv head, rows 16 (kNT rg + nt) ..
+// + 15 for nt < kNT, and computes each step once per tile on the same loaded
+// keys; `unit` = its (token range, kv head) unit, which indexes the workspace.
+template <int kIn, int kOut, int D, int kDepth, int kCpol, int kNT>
 __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int j, int64_t off,
-                                              int t0, int t1, int len, int u, int rg) {
+                                              int t0, int t1, int len, int unit, int rg) {
     using S = Step<kIn, D>;
     constexpr int VEC = S::VEC;
     const int lane = lane_id();
-    const int r = 16 * rg + (lane & 15);   // row of the kv head: query token t and head g
     const int kg = lane >> 4;
     const int G = P.G;
     const int R = P.R;              // rows in use: G * t_q
-    const bool row_ok = r < R;
-    const int t = (row_ok ? r : R - 1) / G;
-    const int g = (row_ok ? r : R - 1) - t * G;
-    const int64_t qo_row = (static_cast<int64_t>(b) * P.t_q + t) * P.h_q + j * G + g;   // q and o row
     const int rowstride = P.h_kv * S::ROWB;
-
-    // Q operand: query row (t, g), bytes [64p + 16kg, +16) of it (zero for unused rows):
-    // the same d permutation as the K rows, so the contraction covers every d once.
-    uint4 qop[S::NKP];
-    {
-        const uint8_t *qrow = P.q + qo_row * S::ROWB + 16 * kg;
-#pragma unroll
-        for (int p = 0; p < S::NKP; ++p) {
-            qop[p] = *reinterpret_cast<const uint4 *>(qrow + 64 * p);
-            if (!row_ok) qop[p] = make_uint4(0, 0, 0, 0);
-        }
-    }
-
-    f32x4_t acc[VEC];
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
 
     // Steps cover key rows aligned to kKeys in the packed K/V (absolute row index),
     // so a step never straddles a kKeys-row boundary of the cache: the first step
@@ -383,15 +361,52 @@ __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int 
     const int lead = static_cast<int>(first - abase);            // masked rows of step 0
     const int span = lead + (t1 - t0);                           // keys from abase to the end
     const int nstep = (span + S::kKeys - 1) / S::kKeys;
+
+    // The lane's row in each tile: query token t and head g, its q and o row, and
+    // the causal limit of token t among the t_q new tokens -- it sees the keys at
+    // sequence positions below len - t_q + t + 1, i.e. (key i of step st sits at
+    // position abase - off + kKeys*st + i) below cap - kKeys*st in step coordinates.
+    int r[kNT], cap[kNT];
+    bool row_ok[kNT];
+    int64_t qo_row[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        r[nt] = 16 * (kNT * rg + nt) + (lane & 15);
+        row_ok[nt] = r[nt] < R;
+        const int t = (row_ok[nt] ? r[nt] : R - 1) / G;
+        const int g = (row_ok[nt] ? r[nt] : R - 1) - t * G;
+        qo_row[nt] = (static_cast<int64_t>(b) * P.t_q + t) * P.h_q + j * G + g;
+        cap[nt] = len - P.t_q + t + 1 - static_cast<int>(abase - off);
+    }
+
+    // Q operand: query row (t, g), bytes [64p + 16kg, +16) of it (zero for unused rows):
+    // the same d permutation as the K rows, so the contraction covers every d once.
+    uint4 qop[kNT][S::NKP];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const uint8_t *qrow = P.q + qo_row[nt] * S::ROWB + 16 * kg;
+#pragma unroll
+        for (int p = 0; p < S::NKP; ++p) {
+            qop[nt][p] = *reinterpret_cast<const uint4 *>(qrow + 64 * p);
+            if (!row_ok[nt]) qop[nt][p] = make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    f32x4_t acc[kNT][VEC];
+    float m_run[kNT], l_run[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) acc[nt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_run[nt] = -INFINITY;
+        l_run[nt] = 0.f;
+    }
+
     const int64_t row0 = abase * P.h_kv + j;
     const uint8_t *kbase = P.k + row0 * S::ROWB;
     const uint8_t *vbase = P.v + row0 * S::ROWB;
     const float sl2 = P.scale_log2;
     const typename S::Lanes lo(rowstride);
-    // Causal limit of query token t among the t_q new tokens: it sees the keys at
-    // sequence positions below len - t_q + t + 1.  In step coordinates (key i of
-    // step st sits at position abase - off + kKeys*st + i) the bound is cap - kKeys*st.
-    const int cap = len - P.t_q + t + 1 - static_cast<int>(abase - off);
 
     // A step at or past nstep gets an empty range: its loads return zeros without
     // a memory access (the pipeline's prefetches past the piece cost no round trip).
@@ -407,63 +422,69 @@ __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int 
     // unconditional: prefetches past the last step read an empty range.
     typename S::Buf buf[kDepth];
 #pragma unroll
-    for (int u = 0; u + 1 < kDepth; ++u) load_step(buf[u], u);
+    for (int ub = 0; ub + 1 < kDepth; ++ub) load_step(buf[ub], ub);
     int st = 0;
     while (true) {
 #pragma unroll
-        for (int u = 0; u < kDepth; ++u) {
-            load_step(buf[(u + kDepth - 1) % kDepth], st + kDepth - 1);
+        for (int ub = 0; ub < kDepth; ++ub) {
+            load_step(buf[(ub + kDepth - 1) % kDepth], st + kDepth - 1);
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
-            S::compute(buf[u], qop, st == 0 ? lead : 0,
-                       min(min(S::kKeys, span - st * S::kKeys), cap - st * S::kKeys), kg, sl2, m_run,
-                       l_run, acc);
+            const int hi = min(S::kKeys, span - st * S::kKeys);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt)
+                S::compute(buf[ub], qop[nt], st == 0 ? lead : 0, min(hi, cap[nt] - st * S::kKeys), kg, sl2,
+                           m_run[nt], l_run[nt], acc[nt]);
             if (++st == nstep) goto swept;
         }
     }
 swept:
 
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 16);
+        l_tot += __shfl_xor(l_tot, 32);
 
-    // The lane's outputs: O[row][d] for d in [4*VEC*kg, 4*VEC*kg + 4*VEC), index q*VEC + c.
-    float out[4 * VEC];
-    if (t0 == 0 && t1 == len) {
-        // The whole sequence was in this range: normalise and store (a query token
-        // that sees no key gives 0).
-        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        // The lane's outputs: O[row][d] for d in [4*VEC*kg, 4*VEC*kg + 4*VEC), index q*VEC + c.
+        float out[4 * VEC];
+        if (t0 == 0 && t1 == len) {
+            // The whole sequence was in this range: normalise and store (a query
+            // token that sees no key gives 0).
+            const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[c][q] * inv;
-        if (row_ok) {
-            uint8_t *dst = P.o + (qo_row * D + 4 * VEC * kg) * (kOut == kF32 ? 4 : 2);
-            store_row<kOut>(dst, out, 4 * VEC);
-        }
-    } else {
-        // Slot 0: a piece of a sequence that began before this range; slot 1: the
-        // first piece of a sequence that continues past it.
-        const int slot = (t0 > 0) ? 0 : 1;
+                for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[nt][c][q] * inv;
+            if (row_ok[nt]) {
+                uint8_t *dst = P.o + (qo_row[nt] * D + 4 * VEC * kg) * (kOut == kF32 ? 4 : 2);
+                store_row<kOut>(dst, out, 4 * VEC);
+            }
+        } else {
+            // Slot 0: a piece of a sequence that began before this range; slot 1:
+            // the first piece of a sequence that continues past it.
+            const int slot = (t0 > 0) ? 0 : 1;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[c][q];
-        if (row_ok) {
-            const int64_t srow = (static_cast<int64_t>(u) * 2 + slot) * R + r;
-            store_row<kF32>(reinterpret_cast<uint8_t *>(P.ws_o + srow * D + 4 * VEC * kg), out, 4 * VEC);
-            if (kg == 0) P.ws_ml[srow] = make_float2(m_run, l_tot);
+                for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[nt][c][q];
+            if (row_ok[nt]) {
+                const int64_t srow = (static_cast<int64_t>(unit) * 2 + slot) * R + r[nt];
+                store_row<kF32>(reinterpret_cast<uint8_t *>(P.ws_o + srow * D + 4 * VEC * kg), out, 4 * VEC);
+                if (kg == 0) P.ws_ml[srow] = make_float2(m_run[nt], l_tot);
+            }
         }
     }
 }
 
-template <int kIn, int kOut, int D, int kDepth, int kCpol>
+template <int kIn, int kOut, int D, int kDepth, int kCpol, int kNT>
 __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
     const int w = uniform32(static_cast<int>(blockIdx.x) * kWavesPerBlock +
                             static_cast<int>(threadIdx.x) / kWave);
     if (w >= P.num_chunks) return;
-    // Wavefront w takes row group rg of kv head j over token range c of the
-    // flattened token axis; the h_kv * NG wavefronts of one range are consecutive,
-    // so they stream the adjacent kv-head slices of the same key rows at the same
-    // time (the NG row groups of one kv head read the same slice).
+    // Wavefront w takes row group rg (kNT tiles of 16 rows) of kv head j over
+    // token range c of the flattened token axis; the h_kv * NG wavefronts of one
+    // range are consecutive, so they stream the adjacent kv-head slices of the same
+    // key rows at the same time (the NG row groups of one kv head read the same
+    // slice).
     const int u = P.NG == 1 ? w : w / P.NG;   // (a division by a run-time value costs ~40 instructions)
     const int rg = w - u * P.NG;
     const int j = u % P.h_kv;
@@ -487,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
         const int t0 = uniform32(static_cast<int>(pos - off));
         const int64_t lim = end - off;
         const int t1 = uniform32(static_cast<int>(lim < len ? lim : len));
-        process_piece<kIn, kOut, D, kDepth, kCpol>(P, b, j, off, t0, t1, len, u, rg);
+        process_piece<kIn, kOut, D, kDepth, kCpol, kNT>(P, b, j, off, t0, t1, len, u, rg);
         pos = off + t1;
         if (pos >= end) break;
         off += len;   // next non-empty sequence (one exists: pos < total)
@@ -498,31 +519,37 @@ __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
     }
 }
 
-template <int kIn, int kOut, int kCpol>
+template <int kIn, int kOut, int kCpol, int kNT>
 void launch_iop(const DecodeParams &P, int D, int blocks, hipStream_t stream) {
     if (D == 128)
-        hipLaunchKernelGGL((split_kernel<kIn, kOut, 128, kSweepDepth, kCpol>), dim3(blocks), dim3(kThreads), 0,
+        hipLaunchKernelGGL((split_kernel<kIn, kOut, 128, kSweepDepth, kCpol, kNT>), dim3(blocks), dim3(kThreads), 0,
                            stream, P);
     else
-        hipLaunchKernelGGL((split_kernel<kIn, kOut, 64, kSweepDepth, kCpol>), dim3(blocks), dim3(kThreads), 0,
+        hipLaunchKernelGGL((split_kernel<kIn, kOut, 64, kSweepDepth, kCpol, kNT>), dim3(blocks), dim3(kThreads), 0,
                            stream, P);
 }
 
+// Up to 16 rows per kv head: one tile per wavefront, non-temporal loads.  More:
+// two tiles per wavefront (each step computed twice on one load of the keys),
+// NG = ceil(R / 32) wavefronts per key range; with NG > 1 they re-read the same
+// keys, so the loads keep the cached policy.
 template <int kIn, int kOut>
 hipError_t launch_io(const DecodeParams &P, int D, int blocks, hipStream_t stream) {
-    if (P.NG > 1)
-        launch_iop<kIn, kOut, kKvCachePolicyShared>(P, D, blocks, stream);
+    if (P.R <= 16)
+        launch_iop<kIn, kOut, kKvCachePolicy, 1>(P, D, blocks, stream);
+    else if (P.NG == 1)
+        launch_iop<kIn, kOut, kKvCachePolicy, 2>(P, D, blocks, stream);
     else
-        launch_iop<kIn, kOut, kKvCachePolicy>(P, D, blocks, stream);
+        launch_iop<kIn, kOut, kKvCachePolicyShared, 2>(P, D, blocks, stream);
     return hipGetLastError();
 }
 
 template <int kIn, int kOut>
 hipError_t occupancy_io(int D, int *blocks_per_cu) {
     return D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                          blocks_per_cu, split_kernel<kIn, kOut, 128, kSweepDepth, kKvCachePolicy>, kThreads, 0)
+                          blocks_per_cu, split_kernel<kIn, kOut, 128, kSweepDepth, kKvCachePolicy, 1>, kThreads, 0)
                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                          blocks_per_cu, split_kernel<kIn, kOut, 64, kSweepDepth, kKvCachePolicy>, kThreads, 0);
+                          blocks_per_cu, split_kernel<kIn, kOut, 64, kSweepDepth, kKvCachePolicy, 1>, kThreads, 0);
 }
 
 }  // namespace

@@ -36,8 +36,8 @@
  *             so a call needs no host synchronisation)
  *
  * Supported: d_head in {64, 128}; G = h_q / h_kv in 1..64 (G * t_q <= 64 rows per kv
- * head; more than 16 rows are swept by ceil(rows / 16) wavefronts per key range, each
- * reading the same keys); (in, out) dtypes
+ * head; more than 16 rows are swept by wavefronts of two 16-row tiles, ceil(rows / 32)
+ * per key range, each reading the range's keys once); (in, out) dtypes
  * (bf16, bf16), (bf16, f32), (f16, f16), (f16, f32) and (f32, f32).  q, k, v, o must be 16-byte aligned,
  * seq_lens 4-byte aligned.
  *
@@ -103,8 +103,8 @@ int gqa_decode_f16(const void *q, const void *k, const void *v, void *o,
 /*
  * Full argument block.  Zero-initialise it, then set the fields.
  *
- * num_chunks  Wavefronts of the sweep.  With NG = ceil(G * t_q / 16) wavefronts
- *             per kv head (16 rows each), the token axis -- the key rows of all
+ * num_chunks  Wavefronts of the sweep.  With NG wavefronts per kv head (NG = 1
+ *             for G * t_q <= 16 rows, else ceil(G * t_q / 32)), the token axis -- the key rows of all
  *             sequences end to end, sum(seq_lens) rows -- is cut into
  *             num_chunks / (h_kv NG) equal ranges of `chunk` rows, where
  *               chunk = max(min_chunk, ceil(sum(seq_lens) / (num_chunks / (h_kv NG))))

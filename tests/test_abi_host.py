@@ -105,19 +105,19 @@ def test_multi_token_limits(lib):
 
 
 def test_row_groups_share_token_ranges(lib):
-    """More than 16 rows per kv head: ceil(rows / 16) wavefronts per (token range,
-    kv head), so the wavefront count is a multiple of h_kv times that, and the
-    workspace holds one unit of slots per (token range, kv head)."""
-    st, p = B.gqa_decode_make_plan(_args(h_q=64, h_kv=8, t_q=4), 256, 4)       # 32 rows: 2 groups
+    """More than 16 rows per kv head: wavefronts of two 16-row tiles, ceil(rows / 32)
+    of them per (token range, kv head), so the wavefront count is a multiple of h_kv
+    times that, and the workspace holds one unit of slots per (token range, kv head)."""
+    st, p = B.gqa_decode_make_plan(_args(h_q=64, h_kv=8, t_q=4), 256, 4)       # 32 rows: 1 group
     assert st == B.GQA_OK and p.num_chunks == 1024 and p.split_blocks == 256
-    st, p = B.gqa_decode_make_plan(_args(h_q=48, h_kv=1, t_q=1, num_chunks=10), 256, 4)   # 48 rows: 3
-    assert st == B.GQA_OK and p.num_chunks == 9
-    st, p = B.gqa_decode_make_plan(_args(h_q=48, h_kv=1, num_chunks=2), 256, 4)
-    assert st == B.GQA_OK and p.num_chunks == 3                  # at least one range
-    # Units = wavefronts / groups: 2 groups of 16 rows hold as many slots as 1 of 32.
+    st, p = B.gqa_decode_make_plan(_args(h_q=48, h_kv=1, t_q=1, num_chunks=11), 256, 4)   # 48 rows: 2
+    assert st == B.GQA_OK and p.num_chunks == 10
+    st, p = B.gqa_decode_make_plan(_args(h_q=64, h_kv=1, num_chunks=1), 256, 4)
+    assert st == B.GQA_OK and p.num_chunks == 2                  # at least one range
+    # Units = wavefronts / groups: 2 groups for 64 rows hold as many slots as 1 for 32.
+    st, p64 = B.gqa_decode_make_plan(_args(h_q=64, h_kv=1, num_chunks=64), 256, 4)
     st, p32 = B.gqa_decode_make_plan(_args(h_q=32, h_kv=1, num_chunks=64), 256, 4)
-    st, p16 = B.gqa_decode_make_plan(_args(h_q=16, h_kv=1, num_chunks=64), 256, 4)
-    assert p32.workspace_bytes == p16.workspace_bytes
+    assert p64.workspace_bytes == p32.workspace_bytes
 
 
 @pytest.mark.parametrize("field", ["q", "k", "v", "o"])

@@ -231,9 +231,9 @@ def test_multi_token_70b_shaped_ragged_full_size_sampled():
 @pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"),
                                        ("f16", "f16")])
 def test_more_than_16_rows_per_kv_head(G, h_kv, t_q, d, dtype, out):
-    """G * t_q from 17 to 64 rows per kv head: ceil(rows / 16) wavefronts sweep each
-    (token range, kv head), 16 rows each, and leave their partials in the same
-    workspace unit; short sequences leave tokens that see no key (output 0)."""
+    """G * t_q from 17 to 64 rows per kv head: wavefronts of two 16-row tiles,
+    ceil(rows / 32) of them per (token range, kv head), leave their partials in the
+    same workspace unit; short sequences leave tokens that see no key (output 0)."""
     import torch
     lens = [37, 0, 300, 2, 1, 16, 129]
     c = host_case(len(lens), G * h_kv, h_kv, d, lens, dtype, seed=G * 37 + t_q * 5 + d + h_kv, t_q=t_q)
@@ -268,7 +268,7 @@ def test_more_than_16_rows_70b_heads_ragged_batch():
 
 
 def test_more_than_16_rows_more_than_64_sequences():
-    """Row groups (G 32, two wavefronts per key range) over 90 sequences, where the
+    """Row groups (G 48: two wavefronts of two tiles per key range) over 90 sequences, where the
     kernels take the lengths from seq_lens block by block instead of one register
     table, with the automatic and forced plans."""
     import torch
@@ -276,13 +276,13 @@ def test_more_than_16_rows_more_than_64_sequences():
     lens = [int(x) for x in rng.integers(0, 400, size=90)]
     lens[0] = 0
     lens[64] = 1
-    c = host_case(len(lens), 64, 2, 128, lens, "bf16", seed=90, t_q=1)
+    c = host_case(len(lens), 96, 2, 128, lens, "bf16", seed=90, t_q=1)
     ref = oracle_of(c)
     q, k, v, sl = upload(c)
     for nc, mc in [(0, 0), (6, 1), (2000, 1)]:
-        _say("90 sequences, G 32, nc", nc, "mc", mc)
+        _say("90 sequences, G 48, nc", nc, "mc", mc)
         o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=mc)
-        compare(o, ref, "90 sequences G=32 nc=%d mc=%d" % (nc, mc))
+        compare(o, ref, "90 sequences G=48 nc=%d mc=%d" % (nc, mc))
 
 
 def test_multi_token_short_sequences_give_zero_for_unseen_tokens():
