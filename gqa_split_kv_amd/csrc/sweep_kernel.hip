@@ -57,8 +57,9 @@ constexpr int kSweepDepth = GQA_SWEEP_DEPTH;   // register buffers in the sweep 
 // so they are loaded non-temporally (nt) and do not displace the partials, q and
 // seq_lens from the caches.  When NG > 1 wavefronts (32 rows each) sweep the same
 // range, the loads keep the default policy so that the repeats find the lines in
-// the caches (measured with four query tokens on the 70B grouping: 1189 us with
-// nt, 827 us cached; one token: 619 us nt, 705 us cached).
+// the caches (measured on the 70B-shaped batch with two wavefronts re-reading
+// every range: 1189 us per step with nt loads, 827 us cached; with one wavefront
+// per range the cached policy costs 619 -> 705 us).
 #ifndef GQA_KV_CPOL
 #define GQA_KV_CPOL 2
 #endif
