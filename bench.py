@@ -164,7 +164,7 @@ def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
     fp16 q/k/v (gqa_decode_f16's kernels, fp16 out) and two or four query tokens
     per sequence (bf16, t_q = 2: every sequence's last two tokens, causal between
     them, G * t_q = 16 rows per kv head; t_q = 4: 32 rows, two 16-row tiles per
-    wavefront).  Each is timed like the headline step,
+    wavefront over one load of the keys).  Each is timed like the headline step,
     with the sweep kernel's own HIP events."""
     import torch
     import gqa_split_kv_amd as gqa

@@ -100,8 +100,7 @@ int decode_ex(const gqa_decode_args *a) {
         if (st != GQA_OK) return st;
     }
     const int G = a->h_q / a->h_kv;
-    const int NG = gqa::row_groups(a);
-    const gqa::WorkspaceLayout L = gqa::workspace_layout(plan.num_chunks / NG, G * (a->t_q > 0 ? a->t_q : 1), a->d_head);
+    const gqa::WorkspaceLayout L = gqa::workspace_layout(plan.num_chunks, G * (a->t_q > 0 ? a->t_q : 1), a->d_head);
     gqa::DecodeParams P;
     P.q = static_cast<const uint8_t *>(a->q);
     P.k = static_cast<const uint8_t *>(a->k);
@@ -116,7 +115,6 @@ int decode_ex(const gqa_decode_args *a) {
     P.G = G;
     P.t_q = a->t_q > 0 ? a->t_q : 1;
     P.R = G * P.t_q;
-    P.NG = NG;
     P.num_chunks = plan.num_chunks;
     P.min_chunk = plan.min_chunk;
     P.scale_log2 = static_cast<float>(static_cast<double>(a->scale) * 1.4426950408889634074);

@@ -43,8 +43,7 @@ constexpr int kPrefillRows = GQA_PREFILL_ROWS;
 constexpr int kPrefillStepKeys = 64;
 constexpr int kVprepThreads = 256;
 constexpr int kMaxG = 16;           // prefill: query heads per kv head (one 16-wide MFMA tile of rows)
-constexpr int kRowTile = 16;        // decode: rows (query tokens x query heads) per sweep wavefront
-constexpr int kMaxRows = 64;        // decode: rows per kv head, G * t_q (up to 2 wavefronts of 2 tiles per range)
+constexpr int kMaxRows = 64;        // decode: rows per kv head, G * t_q (up to four 16-row tiles per wavefront)
 constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxPrefillBlocks = 1 << 20;
 constexpr int kMaxHeadsKv = 1 << 16;   // keeps 16 key rows of lane offsets within 32 bits
@@ -82,19 +81,14 @@ struct PrefillWorkspace {
 PrefillWorkspace prefill_workspace(const gqa_prefill_args *a);
 constexpr int64_t kMaxPrefillRowsHeads = int64_t(1) << 37;   // total_tokens * h_kv limit
 
-// Workspace layout for `units` (token range, kv head) units: two partial-triple
-// slots per unit, each R = G * t_q rows of (O[D] fp32) plus (m, l) fp32.  A unit
-// is swept by row_groups() wavefronts, 16 of its rows each.
+// Workspace layout for `num_chunks` wavefronts: two partial-triple slots per
+// wavefront, each R = G * t_q rows of (O[D] fp32) plus (m, l) fp32.
 struct WorkspaceLayout {
-    size_t o_offset;    // float  [units][2][R][D]
-    size_t ml_offset;   // float2 [units][2][R]
+    size_t o_offset;    // float  [num_chunks][2][R][D]
+    size_t ml_offset;   // float2 [num_chunks][2][R]
     size_t bytes;
 };
-WorkspaceLayout workspace_layout(int64_t units, int rows, int D);
-
-// Wavefronts per (token range, kv head) of a decode call: 1 up to 16 rows (G * t_q),
-// else ceil(rows / 32) (two 16-row tiles per wavefront).
-int row_groups(const gqa_decode_args *a);
+WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D);
 
 int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decode_plan *plan);
 

@@ -15,12 +15,11 @@ struct DecodeParams {
     const uint8_t *v;
     uint8_t *o;                // [batch, t_q, h_q, D] out_dtype
     const int32_t *seq_lens;   // [batch]
-    float *ws_o;               // [num_chunks / NG][2][R][D]   unnormalised O of a piece
-    float2 *ws_ml;             // [num_chunks / NG][2][R]      (m in log2 units, l)
+    float *ws_o;               // [num_chunks][2][R][D]   unnormalised O of a piece
+    float2 *ws_ml;             // [num_chunks][2][R]      (m in log2 units, l)
     int32_t batch, h_q, h_kv, G;
     int32_t t_q;               // query tokens per sequence
-    int32_t R;                 // rows per kv head: G * t_q (row = t * G + g)
-    int32_t NG;                // wavefronts per (token range, kv head): 1 up to 16 rows, else ceil(R / 32)
+    int32_t R;                 // rows per kv head: G * t_q (row = t * G + g), up to 64
     int32_t num_chunks, min_chunk;
     float scale_log2;          // scale * log2(e)
 };

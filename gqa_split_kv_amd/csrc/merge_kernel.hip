@@ -2,8 +2,9 @@
 // the workspace when its keys were cut across several sweep ranges.
 //
 // For row (query token t, query head g) of (sequence b, kv head j) with pieces
-// s = ca .. cb (range s of kv head j is unit s*h_kv + j of the workspace; the
-// first piece sits in slot 1 of its unit, the rest in slot 0):
+// s = ca .. cb (range s
+// was swept by wavefront s*h_kv + j; the first piece sits in slot 1 of its
+// wavefront, the rest in slot 0):
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s O_s 2^(m_s - M) / L
 // (kernbench2 page "_gqa_attention_decode_long.py", `_merge_running`: the
 // pairwise rule applied to all pieces at once with their common maximum, which
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
         return;
     }
     const int64_t total = few ? fl.total() : total_len(P.seq_lens, P.batch);
-    const int64_t chunk = chunk_keys(total, P.num_chunks / (P.h_kv * P.NG), P.min_chunk);
+    const int64_t chunk = chunk_keys(total, P.num_chunks / P.h_kv, P.min_chunk);
     const int64_t ustart = few ? fl.prefix(b) : prefix_len(P.seq_lens, b);
     const int64_t ca = ustart / chunk;   // token ranges holding this sequence
     const int64_t cb = (ustart + len - 1) / chunk;

@@ -38,9 +38,9 @@ static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-WorkspaceLayout workspace_layout(int64_t units, int rows, int D) {
+WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D) {
     WorkspaceLayout L;
-    const size_t slots = static_cast<size_t>(units) * 2 * static_cast<size_t>(rows);
+    const size_t slots = static_cast<size_t>(num_chunks) * 2 * static_cast<size_t>(rows);
     L.o_offset = 0;
     L.ml_offset = round_up(slots * static_cast<size_t>(D) * sizeof(float), 256);
     L.bytes = round_up(L.ml_offset + slots * 2 * sizeof(float), 256);
@@ -54,10 +54,6 @@ static int rows_per_kv_head(const gqa_decode_args *a) {
 
 // Wavefronts per (token range, kv head): one 16-row tile each up to 16 rows, two
 // tiles each beyond.
-int row_groups(const gqa_decode_args *a) {
-    const int R = rows_per_kv_head(a);
-    return R <= kRowTile ? 1 : (R + 2 * kRowTile - 1) / (2 * kRowTile);
-}
 
 static int check_basic(const gqa_decode_args *a) {
     if (!a) return fail(GQA_ERR_NULL, "args is NULL");
@@ -115,10 +111,9 @@ int validate(const gqa_decode_args *a) {
     int st = check_basic(a);
     if (st != GQA_OK) return st;
     if (a->num_chunks > 0) {
-        const int64_t per = static_cast<int64_t>(a->h_kv) * row_groups(a);
-        int64_t chunks = static_cast<int64_t>(a->num_chunks) / per * per;
-        if (chunks < per) chunks = per;
-        const WorkspaceLayout L = workspace_layout(chunks / row_groups(a), rows_per_kv_head(a), a->d_head);
+        int64_t chunks = static_cast<int64_t>(a->num_chunks) / a->h_kv * a->h_kv;
+        if (chunks < a->h_kv) chunks = a->h_kv;
+        const WorkspaceLayout L = workspace_layout(chunks, rows_per_kv_head(a), a->d_head);
         st = check_workspace(a, L.bytes);
         if (st != GQA_OK) return st;
     }
@@ -197,22 +192,18 @@ int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decod
         chunks = static_cast<int64_t>(num_cus) * (waves_per_cu < kAutoWavesPerCu ? waves_per_cu : kAutoWavesPerCu);
         if (chunks > kMaxChunks) chunks = kMaxChunks;
     }
-    // NG wavefronts (one or two 16-row tiles each) per kv head of every token range: a multiple of h_kv * NG.
-    const int NG = row_groups(a);
-    const int64_t per = static_cast<int64_t>(a->h_kv) * NG;
-    chunks = chunks / per * per;
-    if (chunks < per) chunks = per;
-    if (chunks > kMaxChunks)
-        return fail(GQA_ERR_ARG, "h_kv %d with %d rows per kv head needs more than %d wavefronts", a->h_kv,
-                    rows_per_kv_head(a), kMaxChunks);
-    const WorkspaceLayout L = workspace_layout(chunks / NG, rows_per_kv_head(a), a->d_head);
+    // One wavefront per kv head of every token range: a multiple of h_kv.
+    chunks = chunks / a->h_kv * a->h_kv;
+    if (chunks < a->h_kv) chunks = a->h_kv;
+    if (chunks > kMaxChunks) return fail(GQA_ERR_ARG, "h_kv %d needs more than %d wavefronts", a->h_kv, kMaxChunks);
+    const WorkspaceLayout L = workspace_layout(chunks, rows_per_kv_head(a), a->d_head);
     st = check_workspace(a, L.bytes);
     if (st != GQA_OK) return st;
     plan->num_chunks = static_cast<int32_t>(chunks);
     plan->min_chunk = a->min_chunk > 0 ? a->min_chunk : kAutoMinChunk;
     plan->split_blocks = static_cast<int32_t>((chunks + kWavesPerBlock - 1) / kWavesPerBlock);
     // Expected pieces per sequence: token ranges per sequence on average.
-    const int64_t ranges = chunks / per;
+    const int64_t ranges = chunks / a->h_kv;
     const int R = rows_per_kv_head(a);
     const bool wide = ranges / a->batch > kWideMergePieces;
     const bool split = wide && static_cast<int64_t>(a->batch) * a->h_kv * R < kSplitMergeBelowBlocks;

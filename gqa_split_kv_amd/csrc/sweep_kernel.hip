@@ -53,18 +53,12 @@ using namespace dev;
 #endif
 constexpr int kSweepDepth = GQA_SWEEP_DEPTH;   // register buffers in the sweep pipeline
 // Cache policy of the K/V stream loads (buffer-instruction cache-policy bits).
-// With one wavefront per (token range, kv head), K and V are read exactly once,
-// so they are loaded non-temporally (nt) and do not displace the partials, q and
-// seq_lens from the caches.  When NG > 1 wavefronts (32 rows each) sweep the same
-// range, the loads keep the default policy so that the repeats find the lines in
-// the caches (measured on the 70B-shaped batch with two wavefronts re-reading
-// every range: 1189 us per step with nt loads, 827 us cached; with one wavefront
-// per range the cached policy costs 619 -> 705 us).
+// K and V are read exactly once, so they are loaded non-temporally (nt) and do
+// not displace the partials, q and seq_lens from the caches.
 #ifndef GQA_KV_CPOL
 #define GQA_KV_CPOL 2
 #endif
 constexpr int kKvCachePolicy = GQA_KV_CPOL;
-constexpr int kKvCachePolicyShared = 0;
 
 // ------------------------------------------------------------------ loads
 
@@ -78,22 +72,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t *bas
                                              uniform32(static_cast<int>(bytes)), 0x00020000);
 }
 
-template <int kCpol>
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpol);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kKvCachePolicy);
     return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
-template <int NW, int kCpol>
+template <int NW>
 __device__ __forceinline__ void load_words(uint32_t (&dst)[NW], __amdgpu_buffer_rsrc_t r, uint32_t off) {
     if constexpr (NW == 2) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpol);
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kKvCachePolicy);
         dst[0] = x[0];
         dst[1] = x[1];
     } else {
 #pragma unroll
         for (int i = 0; i < NW / 4; ++i) {
-            const uint4 x = load16<kCpol>(r, off + 16 * i);
+            const uint4 x = load16(r, off + 16 * i);
             dst[4 * i + 0] = x.x;
             dst[4 * i + 1] = x.y;
             dst[4 * i + 2] = x.z;
@@ -186,15 +179,14 @@ struct Packed16Step {
                 v[i] = static_cast<uint32_t>((8 * kg + i) * rowstride + m * VEC * ES);
         }
     };
-    template <int kCpol>
     __device__ __forceinline__ static void load(Buf &B, __amdgpu_buffer_rsrc_t rk,
                                                 __amdgpu_buffer_rsrc_t rv, const Lanes &lo) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int p = 0; p < NKP; ++p) B.k[b][p] = load16<kCpol>(rk, lo.k[b] + 64 * p);
+            for (int p = 0; p < NKP; ++p) B.k[b][p] = load16(rk, lo.k[b] + 64 * p);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) load_words<VW, kCpol>(B.v[i], rv, lo.v[i]);
+        for (int i = 0; i < 8; ++i) load_words<VW>(B.v[i], rv, lo.v[i]);
     }
     __device__ __forceinline__ static void compute(const Buf &B, const uint4 (&qop)[NKP], int lo, int hi,
                                                    int kg, float sl2, float &m_run, float &l_run,
@@ -279,13 +271,12 @@ struct F32Step {
             for (int r = 0; r < 4; ++r) v[r] = static_cast<uint32_t>((4 * kg + r) * rowstride + m * VEC * ES);
         }
     };
-    template <int kCpol>
     __device__ __forceinline__ static void load(Buf &B, __amdgpu_buffer_rsrc_t rk,
                                                 __amdgpu_buffer_rsrc_t rv, const Lanes &lo) {
 #pragma unroll
-        for (int p = 0; p < NKP; ++p) B.k[p] = load16<kCpol>(rk, lo.k + 64 * p);
+        for (int p = 0; p < NKP; ++p) B.k[p] = load16(rk, lo.k + 64 * p);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) load_words<VW, kCpol>(B.v[r], rv, lo.v[r]);
+        for (int r = 0; r < 4; ++r) load_words<VW>(B.v[r], rv, lo.v[r]);
     }
     __device__ __forceinline__ static void compute(const Buf &B, const uint4 (&qop)[NKP], int lo, int hi,
                                                    int kg, float sl2, float &m_run, float &l_run,
@@ -338,12 +329,12 @@ __device__ __forceinline__ void store_row(uint8_t *dst, const float *x, int n) {
 }
 
 // One piece: keys [t0, t1) of (sequence b, kv head j); off = keys before b.  The
-// wavefront takes kNT 16-row tiles of the kv head, rows 16 (kNT rg + nt) ..
-// + 15 for nt < kNT, and computes each step once per tile on the same loaded
-// keys; `unit` = its (token range, kv head) unit, which indexes the workspace.
-template <int kIn, int kOut, int D, int kDepth, int kCpol, int kNT>
+// wavefront takes the kv head's rows as kNT tiles of 16 (rows 16 nt .. 16 nt + 15)
+// and computes each step once per tile on the same loaded keys; w = the
+// wavefront, which indexes the workspace slots.
+template <int kIn, int kOut, int D, int kDepth, int kNT>
 __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int j, int64_t off,
-                                              int t0, int t1, int len, int unit, int rg) {
+                                              int t0, int t1, int len, int w) {
     using S = Step<kIn, D>;
     constexpr int VEC = S::VEC;
     const int lane = lane_id();
@@ -372,7 +363,7 @@ __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int 
     int64_t qo_row[kNT];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-        r[nt] = 16 * (kNT * rg + nt) + (lane & 15);
+        r[nt] = 16 * nt + (lane & 15);
         row_ok[nt] = r[nt] < R;
         const int t = (row_ok[nt] ? r[nt] : R - 1) / G;
         const int g = (row_ok[nt] ? r[nt] : R - 1) - t * G;
@@ -415,7 +406,7 @@ __device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int 
         const int hi = max(0, min(S::kKeys, span - st * S::kKeys));
         const int64_t boff = hi > 0 ? static_cast<int64_t>(st) * S::kKeys * rowstride : 0;
         const uint32_t bytes = static_cast<uint32_t>(hi * rowstride);
-        S::template load<kCpol>(B, buffer_rsrc(kbase + boff, bytes), buffer_rsrc(vbase + boff, bytes), lo);
+        S::load(B, buffer_rsrc(kbase + boff, bytes), buffer_rsrc(vbase + boff, bytes), lo);
     };
 
     // Software pipeline over kDepth register buffers: the loads of the next
@@ -468,7 +459,7 @@ swept:
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[nt][c][q];
             if (row_ok[nt]) {
-                const int64_t srow = (static_cast<int64_t>(unit) * 2 + slot) * R + r[nt];
+                const int64_t srow = (static_cast<int64_t>(w) * 2 + slot) * R + r[nt];
                 store_row<kF32>(reinterpret_cast<uint8_t *>(P.ws_o + srow * D + 4 * VEC * kg), out, 4 * VEC);
                 if (kg == 0) P.ws_ml[srow] = make_float2(m_run[nt], l_tot);
             }
@@ -476,26 +467,22 @@ swept:
     }
 }
 
-template <int kIn, int kOut, int D, int kDepth, int kCpol, int kNT>
+template <int kIn, int kOut, int D, int kDepth, int kNT>
 __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
     const int w = uniform32(static_cast<int>(blockIdx.x) * kWavesPerBlock +
                             static_cast<int>(threadIdx.x) / kWave);
     if (w >= P.num_chunks) return;
-    // Wavefront w takes row group rg (kNT tiles of 16 rows) of kv head j over
-    // token range c of the flattened token axis; the h_kv * NG wavefronts of one
-    // range are consecutive, so they stream the adjacent kv-head slices of the same
-    // key rows at the same time (the NG row groups of one kv head read the same
-    // slice).
-    const int u = P.NG == 1 ? w : w / P.NG;   // (a division by a run-time value costs ~40 instructions)
-    const int rg = w - u * P.NG;
-    const int j = u % P.h_kv;
-    const int c = u / P.h_kv;
+    // Wavefront w sweeps kv head j over token range c of the flattened token axis;
+    // the h_kv wavefronts of one range are consecutive, so they stream the
+    // adjacent kv-head slices of the same key rows at the same time.
+    const int j = w % P.h_kv;
+    const int c = w / P.h_kv;
     // Up to 64 sequences: their lengths stay in registers (one read of seq_lens).
     const bool few = P.batch <= kWave;
     FirstLens fl;
     if (few) fl.load(P.seq_lens, P.batch);
     const int64_t total = few ? fl.total() : total_len(P.seq_lens, P.batch);
-    const int64_t chunk = chunk_keys(total, P.num_chunks / (P.h_kv * P.NG), P.min_chunk);
+    const int64_t chunk = chunk_keys(total, P.num_chunks / P.h_kv, P.min_chunk);
     int64_t pos = static_cast<int64_t>(c) * chunk;
     if (pos >= total) return;
     const int64_t end = pos + chunk < total ? pos + chunk : total;
@@ -509,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
         const int t0 = uniform32(static_cast<int>(pos - off));
         const int64_t lim = end - off;
         const int t1 = uniform32(static_cast<int>(lim < len ? lim : len));
-        process_piece<kIn, kOut, D, kDepth, kCpol, kNT>(P, b, j, off, t0, t1, len, u, rg);
+        process_piece<kIn, kOut, D, kDepth, kNT>(P, b, j, off, t0, t1, len, w);
         pos = off + t1;
         if (pos >= end) break;
         off += len;   // next non-empty sequence (one exists: pos < total)
@@ -520,37 +507,34 @@ __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
     }
 }
 
-template <int kIn, int kOut, int kCpol, int kNT>
-void launch_iop(const DecodeParams &P, int D, int blocks, hipStream_t stream) {
+template <int kIn, int kOut, int kNT>
+void launch_iot(const DecodeParams &P, int D, int blocks, hipStream_t stream) {
     if (D == 128)
-        hipLaunchKernelGGL((split_kernel<kIn, kOut, 128, kSweepDepth, kCpol, kNT>), dim3(blocks), dim3(kThreads), 0,
-                           stream, P);
+        hipLaunchKernelGGL((split_kernel<kIn, kOut, 128, kSweepDepth, kNT>), dim3(blocks), dim3(kThreads), 0, stream,
+                           P);
     else
-        hipLaunchKernelGGL((split_kernel<kIn, kOut, 64, kSweepDepth, kCpol, kNT>), dim3(blocks), dim3(kThreads), 0,
-                           stream, P);
+        hipLaunchKernelGGL((split_kernel<kIn, kOut, 64, kSweepDepth, kNT>), dim3(blocks), dim3(kThreads), 0, stream, P);
 }
 
-// Up to 16 rows per kv head: one tile per wavefront, non-temporal loads.  More:
-// two tiles per wavefront (each step computed twice on one load of the keys),
-// NG = ceil(R / 32) wavefronts per key range; with NG > 1 they re-read the same
-// keys, so the loads keep the cached policy.
+// 16-row tiles per wavefront: 1 up to 16 rows per kv head (G * t_q), 2 up to 32,
+// 4 up to 64 (the keys of a step are loaded once for all of them).
 template <int kIn, int kOut>
 hipError_t launch_io(const DecodeParams &P, int D, int blocks, hipStream_t stream) {
     if (P.R <= 16)
-        launch_iop<kIn, kOut, kKvCachePolicy, 1>(P, D, blocks, stream);
-    else if (P.NG == 1)
-        launch_iop<kIn, kOut, kKvCachePolicy, 2>(P, D, blocks, stream);
+        launch_iot<kIn, kOut, 1>(P, D, blocks, stream);
+    else if (P.R <= 32)
+        launch_iot<kIn, kOut, 2>(P, D, blocks, stream);
     else
-        launch_iop<kIn, kOut, kKvCachePolicyShared, 2>(P, D, blocks, stream);
+        launch_iot<kIn, kOut, 4>(P, D, blocks, stream);
     return hipGetLastError();
 }
 
 template <int kIn, int kOut>
 hipError_t occupancy_io(int D, int *blocks_per_cu) {
     return D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                          blocks_per_cu, split_kernel<kIn, kOut, 128, kSweepDepth, kKvCachePolicy, 1>, kThreads, 0)
+                          blocks_per_cu, split_kernel<kIn, kOut, 128, kSweepDepth, 1>, kThreads, 0)
                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                          blocks_per_cu, split_kernel<kIn, kOut, 64, kSweepDepth, kKvCachePolicy, 1>, kThreads, 0);
+                          blocks_per_cu, split_kernel<kIn, kOut, 64, kSweepDepth, 1>, kThreads, 0);
 }
 
 }  // namespace

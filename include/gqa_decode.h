@@ -36,8 +36,8 @@
  *             so a call needs no host synchronisation)
  *
  * Supported: d_head in {64, 128}; G = h_q / h_kv in 1..64 (G * t_q <= 64 rows per kv
- * head; more than 16 rows are swept by wavefronts of two 16-row tiles, ceil(rows / 32)
- * per key range, each reading the range's keys once); (in, out) dtypes
+ * head, swept as one, two or four 16-row tiles per wavefront over one read of the
+ * keys); (in, out) dtypes
  * (bf16, bf16), (bf16, f32), (f16, f16), (f16, f32) and (f32, f32).  q, k, v, o must be 16-byte aligned,
  * seq_lens 4-byte aligned.
  *
@@ -103,16 +103,15 @@ int gqa_decode_f16(const void *q, const void *k, const void *v, void *o,
 /*
  * Full argument block.  Zero-initialise it, then set the fields.
  *
- * num_chunks  Wavefronts of the sweep.  With NG wavefronts per kv head (NG = 1
- *             for G * t_q <= 16 rows, else ceil(G * t_q / 32)), the token axis -- the key rows of all
+ * num_chunks  Wavefronts of the sweep.  The token axis -- the key rows of all
  *             sequences end to end, sum(seq_lens) rows -- is cut into
- *             num_chunks / (h_kv NG) equal ranges of `chunk` rows, where
- *               chunk = max(min_chunk, ceil(sum(seq_lens) / (num_chunks / (h_kv NG))))
+ *             num_chunks / h_kv equal ranges of `chunk` rows, where
+ *               chunk = max(min_chunk, ceil(sum(seq_lens) / (num_chunks / h_kv)))
  *             is computed on the device from seq_lens, and each range is swept by
- *             h_kv NG wavefronts.  A range that holds a whole
+ *             h_kv wavefronts, one per kv head.  A range that holds a whole
  *             sequence writes its o rows directly; the pieces of a sequence that
  *             spans several ranges are merged by a second kernel.  Rounded down to
- *             a multiple of h_kv NG (at least h_kv NG).  0 = automatic (compute units x
+ *             a multiple of h_kv (at least h_kv).  0 = automatic (compute units x
  *             resident wavefronts per compute unit).  Range: 0..2^24.
  * min_chunk   Smallest range in key rows; 0 = automatic.  Range: 0..2^30.
  *             min_chunk = 1024 with a large num_chunks reproduces the page's

@@ -231,9 +231,9 @@ def test_multi_token_70b_shaped_ragged_full_size_sampled():
 @pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"),
                                        ("f16", "f16")])
 def test_more_than_16_rows_per_kv_head(G, h_kv, t_q, d, dtype, out):
-    """G * t_q from 17 to 64 rows per kv head: wavefronts of two 16-row tiles,
-    ceil(rows / 32) of them per (token range, kv head), leave their partials in the
-    same workspace unit; short sequences leave tokens that see no key (output 0)."""
+    """G * t_q from 17 to 64 rows per kv head: a wavefront holds two or four 16-row
+    tiles and computes each step once per tile on one load of the keys; short
+    sequences leave tokens that see no key (output 0)."""
     import torch
     lens = [37, 0, 300, 2, 1, 16, 129]
     c = host_case(len(lens), G * h_kv, h_kv, d, lens, dtype, seed=G * 37 + t_q * 5 + d + h_kv, t_q=t_q)
@@ -268,7 +268,7 @@ def test_more_than_16_rows_70b_heads_ragged_batch():
 
 
 def test_more_than_16_rows_more_than_64_sequences():
-    """Row groups (G 48: two wavefronts of two tiles per key range) over 90 sequences, where the
+    """Four 16-row tiles per wavefront (G 48) over 90 sequences, where the
     kernels take the lengths from seq_lens block by block instead of one register
     table, with the automatic and forced plans."""
     import torch
