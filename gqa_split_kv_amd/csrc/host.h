@@ -42,7 +42,6 @@ constexpr int kPrefillRows = GQA_PREFILL_ROWS;
 // workgroup size of the kernel that makes the copy.
 constexpr int kPrefillStepKeys = 64;
 constexpr int kVprepThreads = 256;
-constexpr int kMaxG = 16;           // prefill: query heads per kv head (one 16-wide MFMA tile of rows)
 constexpr int kMaxRows = 64;        // decode: rows per kv head, G * t_q (up to four 16-row tiles per wavefront)
 constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxPrefillBlocks = 1 << 20;

@@ -142,7 +142,7 @@ int validate_prefill(const gqa_prefill_args *a, bool check_workspace) {
     if (a->h_kv > kMaxHeadsKv)
         return fail(GQA_ERR_UNSUPPORTED, "h_kv %d exceeds %d", a->h_kv, kMaxHeadsKv);
     const int G = a->h_q / a->h_kv;
-    if (G > kMaxG) return fail(GQA_ERR_UNSUPPORTED, "G = h_q/h_kv = %d exceeds %d", G, kMaxG);
+    if (G > kMaxRows) return fail(GQA_ERR_UNSUPPORTED, "G = h_q/h_kv = %d exceeds %d", G, kMaxRows);
     if (a->d_head != 64 && a->d_head != 128)
         return fail(GQA_ERR_UNSUPPORTED, "d_head %d not supported (64 or 128)", a->d_head);
     const bool pair_ok = (a->in_dtype == GQA_DTYPE_BF16 && a->out_dtype == GQA_DTYPE_BF16) ||

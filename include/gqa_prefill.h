@@ -25,7 +25,8 @@
  *   k, v      [sum(seq_lens), h_kv, d_head]   in_dtype, packed the same way
  *   seq_lens  int32[batch], device memory, read only by the kernel
  *
- * Supported: d_head in {64, 128}; G in 1..16; (in, out) dtypes (bf16, bf16),
+ * Supported: d_head in {64, 128}; G in 1..64 (a 256-row tile holds floor(256 / G)
+ * tokens x G heads); (in, out) dtypes (bf16, bf16),
  * (bf16, f32), (f16, f16), (f16, f32).  q, k, v, o 16-byte aligned, seq_lens
  * 4-byte aligned.  Every output row is written by exactly one workgroup (no
  * cross-workgroup reduction).

@@ -234,7 +234,8 @@ def test_prefill_validation(lib):
     assert B.lib().gqa_prefill_validate(None) == B.GQA_ERR_NULL
     assert _pvalidate(batch=0) == B.GQA_ERR_SHAPE
     assert _pvalidate(h_q=12, h_kv=8) == B.GQA_ERR_SHAPE
-    assert _pvalidate(h_q=32, h_kv=1) == B.GQA_ERR_UNSUPPORTED      # G = 32
+    assert _pvalidate(h_q=64, h_kv=1) == B.GQA_OK                   # G = 64
+    assert _pvalidate(h_q=65, h_kv=1) == B.GQA_ERR_UNSUPPORTED      # G = 65
     assert _pvalidate(h_q=70000, h_kv=70000) == B.GQA_ERR_UNSUPPORTED
     assert _pvalidate(d_head=96) == B.GQA_ERR_UNSUPPORTED
     assert _pvalidate(o=0x40008) == B.GQA_ERR_ALIGN

@@ -53,7 +53,7 @@ def _check(o, ref, what, split_pv=0):
     return compare(o, ref, what, slack=None if split_pv else MAX_ABS)
 
 
-@pytest.mark.parametrize("G,h_kv", [(8, 1), (4, 2), (1, 2), (16, 1), (3, 2), (2, 1)])
+@pytest.mark.parametrize("G,h_kv", [(8, 1), (4, 2), (1, 2), (16, 1), (3, 2), (2, 1), (32, 1), (64, 1), (24, 2)])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "f32"), ("f16", "f16"), ("f16", "f32")])
 def test_prefill_heads_dims_dtypes(G, h_kv, d, dtype, out):
