@@ -46,9 +46,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16 matrix-core peak of one MI355X
 METRIC = "µs/decode step + K/V HBM GB/s (% of peak), GQA h_q=64 h_kv=8 d=128 @32K"
-# Sources that define the sweep kernel's code (its counter data is tied to them).
+# Sources that define the sweep kernel's code and its launch plan (num_chunks,
+# min_chunk and the workspace layout set the traffic per launch), so its counter
+# data is tied to them.
 KERNEL_SRCS = [os.path.join(ROOT, "gqa_split_kv_amd", "csrc", f)
-               for f in ("sweep_kernel.hip", "device_common.h", "kernels.h", "host.h")]
+               for f in ("sweep_kernel.hip", "device_common.h", "kernels.h", "host.h", "plan.cpp", "api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_kernel_70b_ragged_traffic.md")
 
 

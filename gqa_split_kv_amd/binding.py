@@ -270,13 +270,71 @@ def gqa_release() -> None:
 # ------------------------------------------------------------------ convenience
 
 
+# Device type the convenience wrappers accept (the library's kernels need HIP
+# device memory; torch names that device type "cuda").
+_DEVICE_TYPE = "cuda"
+
+
+def _check_tensors(what: str, q, k, v, seq_lens, out, workspace, batch: int) -> None:
+    """Host-side checks of the tensors a convenience call hands to the library.
+
+    The C ABI takes bare pointers, so it cannot see a dtype, a device, strides or
+    a tensor's size; a mismatch there would make the kernels read or write outside
+    the caller's buffers.  Everything checked here is tensor metadata: no device
+    access, no synchronisation (the lengths in seq_lens stay unread, so k and v
+    must hold at least sum(seq_lens) rows, as the header states)."""
+    import torch
+    names = ("q", "k", "v")
+    for name, t in zip(names, (q, k, v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s: %s must be a torch.Tensor" % (what, name))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("%s: q, k and v must share one dtype (got %s, %s, %s)" % (what, q.dtype, k.dtype, v.dtype))
+    _dtype_code(q)
+    dev = q.device
+    if dev.type != _DEVICE_TYPE:
+        raise ValueError("%s: q must be a %s (HIP device) tensor, got device %s" % (what, _DEVICE_TYPE, dev))
+    for name, t in zip(names, (q, k, v)):
+        if t.device != dev:
+            raise ValueError("%s: %s is on %s, q on %s" % (what, name, t.device, dev))
+        if not t.is_contiguous():
+            raise ValueError("%s: %s must be contiguous" % (what, name))
+    if k.shape != v.shape:
+        raise ValueError("%s: k %s and v %s must have one shape" % (what, tuple(k.shape), tuple(v.shape)))
+    if k.shape[2] != q.shape[-1]:
+        raise ValueError("%s: d_head of k (%d) differs from q's (%d)" % (what, k.shape[2], q.shape[-1]))
+    if not isinstance(seq_lens, torch.Tensor) or seq_lens.dtype != torch.int32:
+        raise ValueError("%s: seq_lens must be an int32 tensor" % what)
+    if seq_lens.device != dev or not seq_lens.is_contiguous():
+        raise ValueError("%s: seq_lens must be a contiguous tensor on %s" % (what, dev))
+    if seq_lens.numel() != batch:
+        raise ValueError("%s: seq_lens holds %d lengths, the batch is %d" % (what, seq_lens.numel(), batch))
+    if out is not None:
+        if not isinstance(out, torch.Tensor):
+            raise TypeError("%s: out must be a torch.Tensor" % what)
+        if out.shape != q.shape:
+            raise ValueError("%s: out %s must have q's shape %s" % (what, tuple(out.shape), tuple(q.shape)))
+        if out.dtype not in (q.dtype, torch.float32):
+            raise ValueError("%s: out must be %s or float32, got %s" % (what, q.dtype, out.dtype))
+        if out.device != dev or not out.is_contiguous():
+            raise ValueError("%s: out must be a contiguous tensor on %s" % (what, dev))
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor):
+            raise TypeError("%s: workspace must be a torch.Tensor" % what)
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("%s: workspace must be a contiguous tensor on %s" % (what, dev))
+
+
 def decode(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype=None,
            num_chunks: int = 0, min_chunk: int = 0, workspace=None, stream=None):
     """o = GQA decode of q [batch, h_q, d] (or [batch, t_q, h_q, d] for t_q query
     tokens per sequence) against packed k, v [sum(seq_lens), h_kv, d].
 
-    seq_lens is an int32 device tensor.  out_dtype defaults to q's dtype; pass
-    torch.float32 with 16-bit inputs for the fp32 result.  Returns `out`.
+    q, k and v share one dtype and one CUDA device and are contiguous; seq_lens
+    is a contiguous int32 tensor on that device with one length per sequence.
+    out_dtype defaults to q's dtype; pass torch.float32 with 16-bit inputs for the
+    fp32 result.  Raises ValueError/TypeError before any device work when the
+    tensors do not fit these rules.  Returns `out`.
     """
     import torch
     if q.dim() not in (3, 4) or k.dim() != 3 or v.dim() != 3:
@@ -284,6 +342,9 @@ def decode(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype
     t_q = q.shape[1] if q.dim() == 4 else 0
     batch, h_q, d = q.shape[0], q.shape[-2], q.shape[-1]
     h_kv = k.shape[1]
+    _check_tensors("decode", q, k, v, seq_lens, out, workspace, batch)
+    if out is None and out_dtype not in (None, q.dtype, torch.float32):
+        raise ValueError("decode: out_dtype must be %s or float32, got %s" % (q.dtype, out_dtype))
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
     if out is None:
@@ -355,20 +416,31 @@ def prefill(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtyp
             num_blocks: int = 0, stream=None, split_pv: int = 0, workspace=None, total_tokens=None):
     """o = causal GQA prefill of q [sum(seq_lens), h_q, d] against k, v
     [sum(seq_lens), h_kv, d] (each token sees its sequence's keys up to itself).
-    seq_lens is an int32 device tensor; total_tokens defaults to q's row count;
-    workspace (a device byte tensor) defaults to the library's own.  Returns `out`."""
+    q, k, v share one dtype and CUDA device, are contiguous and hold the same rows;
+    seq_lens is a contiguous int32 tensor on that device; total_tokens defaults to
+    q's row count (and may not exceed it); workspace (a device byte tensor)
+    defaults to the library's own.  Raises ValueError/TypeError before any device
+    work when the tensors do not fit these rules.  Returns `out`."""
     import torch
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q must be [sum(seq_lens), h_q, d]; k, v [sum(seq_lens), h_kv, d]")
     h_q, d = q.shape[1], q.shape[2]
     h_kv = k.shape[1]
-    batch = int(seq_lens.numel())
+    batch = int(seq_lens.numel()) if isinstance(seq_lens, torch.Tensor) else -1
+    _check_tensors("prefill", q, k, v, seq_lens, out, workspace, batch)
+    if k.shape[0] != q.shape[0]:
+        raise ValueError("prefill: q holds %d rows, k and v %d (the sequences are packed the same way)"
+                         % (q.shape[0], k.shape[0]))
+    if out is None and out_dtype not in (None, q.dtype, torch.float32):
+        raise ValueError("prefill: out_dtype must be %s or float32, got %s" % (q.dtype, out_dtype))
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if total_tokens is None:
         total_tokens = q.shape[0]
+    if not 0 <= int(total_tokens) <= q.shape[0]:
+        raise ValueError("prefill: total_tokens %d outside [0, %d] (the rows q holds)" % (int(total_tokens), q.shape[0]))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = make_prefill_args(q, k, v, out, seq_lens, batch, h_q, h_kv, d, scale, _dtype_code(q),
                              _dtype_code(out), num_blocks, _stream(stream), split_pv, total_tokens, workspace,

@@ -1,6 +1,7 @@
 // host.h -- internal host-side declarations shared by the C-ABI layer (api.cpp),
-// the pure-C++ validation/planning (plan.cpp) and the kernel launcher
-// (decode_kernels.hip).  Not part of the public interface.
+// the pure-C++ validation/planning (plan.cpp) and the kernel launchers
+// (sweep_kernel.hip, merge_kernel.hip, prefill_kernel.hip).  Not part of the
+// public interface.
 #pragma once
 
 #include <stddef.h>

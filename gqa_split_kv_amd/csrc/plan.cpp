@@ -52,9 +52,6 @@ static int rows_per_kv_head(const gqa_decode_args *a) {
     return (a->h_q / a->h_kv) * (a->t_q > 0 ? a->t_q : 1);
 }
 
-// Wavefronts per (token range, kv head): one 16-row tile each up to 16 rows, two
-// tiles each beyond.
-
 static int check_basic(const gqa_decode_args *a) {
     if (!a) return fail(GQA_ERR_NULL, "args is NULL");
     if (!a->q || !a->k || !a->v || !a->o || !a->seq_lens)

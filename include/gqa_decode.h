@@ -112,7 +112,7 @@ int gqa_decode_f16(const void *q, const void *k, const void *v, void *o,
  *             sequence writes its o rows directly; the pieces of a sequence that
  *             spans several ranges are merged by a second kernel.  Rounded down to
  *             a multiple of h_kv (at least h_kv).  0 = automatic (compute units x
- *             resident wavefronts per compute unit).  Range: 0..2^24.
+ *             min(resident wavefronts per compute unit, 4)).  Range: 0..2^24.
  * min_chunk   Smallest range in key rows; 0 = automatic.  Range: 0..2^30.
  *             min_chunk = 1024 with a large num_chunks reproduces the page's
  *             1024-key tiles as the split granularity.
@@ -174,7 +174,8 @@ int gqa_decode_validate(const gqa_decode_args *args);
 /*
  * Resolved launch plan of a call (pure host arithmetic, no device access).
  * num_cus and waves_per_cu describe the device: the automatic num_chunks is
- * num_cus * waves_per_cu.  Returns GQA_OK or the validation status.
+ * num_cus * min(waves_per_cu, 4) (at most one sweep wavefront per SIMD), rounded
+ * down to a multiple of h_kv.  Returns GQA_OK or the validation status.
  */
 typedef struct gqa_decode_plan {
     int32_t num_chunks;      /* wavefronts launched (h_kv per token range)         */
@@ -192,7 +193,12 @@ int gqa_decode_make_plan(const gqa_decode_args *args, int32_t num_cus, int32_t w
 /*
  * gqa_decode_workspace_bytes -- bytes of workspace a gqa_decode_ex call with these
  * arguments needs, in *bytes.  With num_chunks = 0 it queries the current
- * device's compute-unit count.  Returns a status.
+ * device's compute-unit count.  Returns a status: GQA_ERR_NULL when `bytes` is
+ * NULL, the validation status of the arguments, or GQA_ERR_HIP when the device
+ * query fails; *bytes is written only on GQA_OK.  The size comes back through a
+ * pointer rather than as the return value because the query can fail in these
+ * ways, and a size_t return would have no value that reads unambiguously as an
+ * error (0 is a valid size: a call whose plan needs no partials).
  */
 int gqa_decode_workspace_bytes(const gqa_decode_args *args, size_t *bytes);
 

@@ -287,3 +287,20 @@ def test_prefill_total_tokens_and_workspace_rules(lib):
     # The size query skips the caller workspace's own checks.
     assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=1000, h_q=8, h_kv=2, workspace=0x100080,
                                                 workspace_bytes=1)) == need
+
+
+def test_workspace_bytes_reports_a_status(lib):
+    """gqa_decode_workspace_bytes returns a status and writes the size through its
+    pointer: NULL is GQA_ERR_NULL, invalid arguments give their validation status,
+    and neither writes the output.  (num_chunks is explicit, so no device is asked.)"""
+    L = lib
+    a = _args(num_chunks=64)
+    assert L.gqa_decode_workspace_bytes(ctypes.byref(a), None) == B.GQA_ERR_NULL
+    n = ctypes.c_size_t(12345)
+    bad = _args(num_chunks=64, h_q=30)
+    assert L.gqa_decode_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == B.GQA_ERR_SHAPE
+    assert n.value == 12345
+    assert L.gqa_decode_workspace_bytes(None, ctypes.byref(n)) == B.GQA_ERR_NULL
+    assert L.gqa_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == B.GQA_OK
+    st, plan = B.gqa_decode_make_plan(a, 256, 4)
+    assert st == B.GQA_OK and n.value == plan.workspace_bytes
