@@ -33,7 +33,8 @@ GQA_ERR_HIP = 7
 GQA_ERR_ARG = 8
 
 # Every function include/gqa_decode.h, include/gqa_prefill.h and include/gqa_probe.h declare.
-EXPORTS = ("gqa_decode", "gqa_decode_f32", "gqa_decode_f16", "gqa_decode_ex", "gqa_decode_validate",
+EXPORTS = ("gqa_decode", "gqa_decode_f32", "gqa_decode_f16", "gqa_decode_ex", "gqa_decode_noalloc",
+           "gqa_decode_validate",
            "gqa_decode_make_plan", "gqa_decode_workspace_bytes", "gqa_status_str",
            "gqa_last_error_message", "gqa_release", "gqa_prefill", "gqa_prefill_f16", "gqa_prefill_ex",
            "gqa_prefill_validate", "gqa_prefill_workspace_bytes", "gqa_probe_copy", "gqa_probe_read")
@@ -109,6 +110,8 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_f16.restype = ctypes.c_int
     L.gqa_decode_ex.argtypes = [ctypes.POINTER(GqaArgs)]
     L.gqa_decode_ex.restype = ctypes.c_int
+    L.gqa_decode_noalloc.argtypes = [ctypes.POINTER(GqaArgs)]
+    L.gqa_decode_noalloc.restype = ctypes.c_int
     L.gqa_decode_validate.argtypes = [ctypes.POINTER(GqaArgs)]
     L.gqa_decode_validate.restype = ctypes.c_int
     L.gqa_decode_make_plan.argtypes = [ctypes.POINTER(GqaArgs), i32, i32, ctypes.POINTER(GqaPlan)]
@@ -232,6 +235,17 @@ def make_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, in_dtype, o
 
 def gqa_decode_ex(args: GqaArgs) -> int:
     st = lib().gqa_decode_ex(ctypes.byref(args))
+    _check(st)
+    return st
+
+
+GQA_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
+
+
+def gqa_decode_noalloc(args: GqaArgs) -> int:
+    """gqa_decode_ex without allocation: the library's own device scratch array
+    holds the partials (args.workspace must be NULL).  Raises GqaError."""
+    st = lib().gqa_decode_noalloc(ctypes.byref(args))
     _check(st)
     return st
 

@@ -80,25 +80,21 @@ int owned_workspace(int dev, hipStream_t stream, size_t need, void **out) {
     return GQA_OK;
 }
 
-int decode_ex(const gqa_decode_args *a) {
-    gqa::clear_error();
+// Validation and plan of a decode call on the current device.
+int decode_plan(const gqa_decode_args *a, int *dev, gqa_decode_plan *plan) {
     int st = gqa::validate(a);
     if (st != GQA_OK) return st;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    hipError_t e = hipGetDevice(dev);
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
     int num_cus = 0, waves_per_cu = 0;
-    st = device_shape(dev, a->in_dtype, a->out_dtype, a->d_head, &num_cus, &waves_per_cu);
+    st = device_shape(*dev, a->in_dtype, a->out_dtype, a->d_head, &num_cus, &waves_per_cu);
     if (st != GQA_OK) return st;
-    gqa_decode_plan plan;
-    st = gqa::make_plan(a, num_cus, waves_per_cu, &plan);
-    if (st != GQA_OK) return st;
+    return gqa::make_plan(a, num_cus, waves_per_cu, plan);
+}
+
+// Enqueues the sweep and merge kernels of a planned call with its workspace `ws`.
+int decode_launch(const gqa_decode_args *a, const gqa_decode_plan &plan, void *ws) {
     hipStream_t stream = reinterpret_cast<hipStream_t>(a->stream);
-    void *ws = a->workspace;
-    if (!ws) {
-        st = owned_workspace(dev, stream, plan.workspace_bytes, &ws);
-        if (st != GQA_OK) return st;
-    }
     const int G = a->h_q / a->h_kv;
     const gqa::WorkspaceLayout L = gqa::workspace_layout(plan.num_chunks, G * (a->t_q > 0 ? a->t_q : 1), a->d_head);
     gqa::DecodeParams P;
@@ -123,6 +119,7 @@ int decode_ex(const gqa_decode_args *a) {
         ev0 = reinterpret_cast<hipEvent_t>(a->sweep_events[0]);
         ev1 = reinterpret_cast<hipEvent_t>(a->sweep_events[1]);
     }
+    hipError_t e;
     if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess)
         return gqa::fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
     e = gqa::launch_sweep(P, a->in_dtype, a->out_dtype, a->d_head, plan.split_blocks, stream);
@@ -133,6 +130,73 @@ int decode_ex(const gqa_decode_args *a) {
                           plan.merge_slices, stream);
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
     return GQA_OK;
+}
+
+int decode_ex(const gqa_decode_args *a) {
+    gqa::clear_error();
+    int dev = 0;
+    gqa_decode_plan plan;
+    int st = decode_plan(a, &dev, &plan);
+    if (st != GQA_OK) return st;
+    void *ws = a->workspace;
+    if (!ws) {
+        st = owned_workspace(dev, reinterpret_cast<hipStream_t>(a->stream), plan.workspace_bytes, &ws);
+        if (st != GQA_OK) return st;
+    }
+    return decode_launch(a, plan, ws);
+}
+
+// ------------------------------------------------------------------ no-allocation entry point
+//
+// Scratch of gqa_decode_noalloc: the partial triples of a call live in this
+// file-scope device array instead of a workspace, so the call allocates nothing.
+// Every device the library runs it on holds its own copy until the process ends;
+// the array starts zeroed (as every device variable does) and nothing in it has
+// to be zero at the start of a call.  Host code never passes the array's name to
+// a kernel (that would be the host-side stand-in, not a device address): it
+// takes the device address once per device with hipGetSymbolAddress and uses
+// that pointer.
+static __device__ __align__(256) unsigned char scratch[GQA_NOALLOC_SCRATCH_BYTES];
+
+std::map<int, void *> g_scratch;   // device -> address of its `scratch`
+
+int scratch_address(int dev, void **out) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_scratch.find(dev);
+    if (it == g_scratch.end()) {
+        void *ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return gqa::fail(GQA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                             hipGetErrorString(e));
+        it = g_scratch.emplace(dev, ptr).first;
+    }
+    *out = it->second;
+    return GQA_OK;
+}
+
+int decode_noalloc(const gqa_decode_args *a) {
+    gqa::clear_error();
+    if (!a) return gqa::fail(GQA_ERR_NULL, "args is NULL");
+    if (a->workspace || a->workspace_bytes)
+        return gqa::fail(GQA_ERR_ARG, "gqa_decode_noalloc uses its own scratch: workspace must be NULL and "
+                         "workspace_bytes 0");
+    int st = gqa::validate(a);
+    if (st != GQA_OK) return st;
+    int dev = 0;
+    gqa_decode_plan plan;
+    st = decode_plan(a, &dev, &plan);
+    if (st != GQA_OK) return st;
+    if (plan.workspace_bytes > static_cast<size_t>(GQA_NOALLOC_SCRATCH_BYTES))
+        return gqa::fail(GQA_ERR_WORKSPACE,
+                         "the call needs %zu bytes of scratch (%d wavefronts x %d rows x d_head %d), above the "
+                         "%d bytes gqa_decode_noalloc holds; pass a smaller num_chunks or use gqa_decode_ex",
+                         plan.workspace_bytes, plan.num_chunks, (a->h_q / a->h_kv) * (a->t_q > 0 ? a->t_q : 1),
+                         a->d_head, GQA_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    st = scratch_address(dev, &ws);
+    if (st != GQA_OK) return st;
+    return decode_launch(a, plan, ws);
 }
 
 // Resident prefill workgroups per compute unit, cached per (device, variant).
@@ -252,6 +316,14 @@ extern "C" {
 int gqa_decode_ex(const gqa_decode_args *args) {
     try {
         return decode_ex(args);
+    } catch (...) {
+        return gqa::fail(GQA_ERR_HIP, "internal error");
+    }
+}
+
+int gqa_decode_noalloc(const gqa_decode_args *args) {
+    try {
+        return decode_noalloc(args);
     } catch (...) {
         return gqa::fail(GQA_ERR_HIP, "internal error");
     }

@@ -163,6 +163,33 @@ typedef struct gqa_decode_args {
 int gqa_decode_ex(const gqa_decode_args *args);
 
 /*
+ * gqa_decode_noalloc -- gqa_decode_ex for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same operation, kernels and results as gqa_decode_ex with
+ * the same plan; the partial triples go to a scratch array of
+ * GQA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every device it
+ * runs on until the process ends, instead of a workspace.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *
+ * `workspace` must be NULL and `workspace_bytes` 0 (GQA_ERR_ARG otherwise).  A
+ * call whose plan needs more scratch than the array holds -- num_chunks x 2 x
+ * (G * t_q) x (d_head + 2) x 4 bytes, rounded up to 256 -- returns
+ * GQA_ERR_WORKSPACE before anything is enqueued; the automatic plan fits for up
+ * to 16 rows per kv head (G * t_q) at d_head 128 and 32 at d_head 64 on a
+ * 256-compute-unit device, and a smaller num_chunks fits larger shapes.
+ *
+ * Every call on a device shares that device's one scratch array, which keeps the
+ * last call's contents: two calls that may overlap on one device (different
+ * streams, or different threads without ordering) race on it and give
+ * undefined results; calls ordered on one stream are safe.  The first call on a
+ * device looks up the array's device address (and caches the device's compute-
+ * unit count and occupancy, as gqa_decode_ex does): make that first call outside
+ * graph capture.  Other arguments, layouts and errors as gqa_decode_ex.
+ */
+#define GQA_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+int gqa_decode_noalloc(const gqa_decode_args *args);
+
+/*
  * gqa_decode_validate -- the host-side argument checks of gqa_decode_ex alone
  * (pointers, shapes, support, alignment, scale, tuning ranges; the workspace
  * size is checked only when num_chunks is given, since the automatic value needs

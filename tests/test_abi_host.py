@@ -304,3 +304,19 @@ def test_workspace_bytes_reports_a_status(lib):
     assert L.gqa_decode_workspace_bytes(ctypes.byref(a), ctypes.byref(n)) == B.GQA_OK
     st, plan = B.gqa_decode_make_plan(a, 256, 4)
     assert st == B.GQA_OK and n.value == plan.workspace_bytes
+
+
+def test_noalloc_argument_checks_on_the_host(lib):
+    """gqa_decode_noalloc refuses a NULL argument block, a caller workspace and
+    invalid arguments before touching any device."""
+    assert lib.gqa_decode_noalloc(None) == B.GQA_ERR_NULL
+    a = _args(workspace=0x100000, workspace_bytes=1 << 20)
+    assert lib.gqa_decode_noalloc(ctypes.byref(a)) == B.GQA_ERR_ARG
+    assert "workspace" in B.last_error_message()
+    a = _args(workspace_bytes=256)
+    assert lib.gqa_decode_noalloc(ctypes.byref(a)) == B.GQA_ERR_ARG
+    for kw, st in [(dict(batch=0), B.GQA_ERR_SHAPE), (dict(d_head=96), B.GQA_ERR_UNSUPPORTED),
+                   (dict(q=0x10008), B.GQA_ERR_ALIGN), (dict(scale=math.nan), B.GQA_ERR_SCALE),
+                   (dict(num_chunks=-1), B.GQA_ERR_ARG), (dict(q=0), B.GQA_ERR_NULL)]:
+        a = _args(**kw)
+        assert lib.gqa_decode_noalloc(ctypes.byref(a)) == st, kw
