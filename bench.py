@@ -187,7 +187,7 @@ def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
         probe = gqa.make_args(q, k, v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale, code, code,
                               stream=stream, t_q=t_q)
         ws_bytes = gqa.gqa_decode_workspace_bytes(probe)
-        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
         ev_steps = [(hip.event(), hip.event()) for _ in range(steps)]
         timed = [gqa.make_args(q, k, v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale, code, code,
                                0, 0, ws, ws_bytes, stream, sweep_events=e, t_q=t_q) for e in ev_steps]
@@ -249,7 +249,7 @@ def other_workloads(hip, stream, skip: int, steps: int):
         probe = gqa.make_args(d.q, d.k, d.v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale, code, code,
                               stream=stream)
         ws_bytes = gqa.gqa_decode_workspace_bytes(probe)
-        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
         ev_steps = [(hip.event(), hip.event()) for _ in range(steps)]
 
         def args_for(i, events=None):
@@ -402,7 +402,7 @@ def main():
     probe = gqa.make_args(d.q, d.k, d.v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale,
                           dt_code, dt_code, args.num_chunks, args.min_chunk, stream=stream)
     ws_bytes = gqa.gqa_decode_workspace_bytes(probe)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     ev_steps = [(hip.event(), hip.event()) for _ in range(args.steps)]
     ev_all = (hip.event(), hip.event())
 

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "host.h"
@@ -25,7 +26,11 @@ struct OwnedWorkspace {
 std::mutex g_mu;
 std::map<int, int> g_num_cus;                                   // device -> compute units
 std::map<std::pair<int, int>, int> g_waves_per_cu;               // (device, variant) -> waves
-std::map<std::pair<int, uintptr_t>, OwnedWorkspace> g_workspaces; // (device, stream)
+// Library-owned workspaces per (device, stream, kind): decode and prefill keep
+// separate buffers, since the prefill's V copy would overwrite the decode's
+// counters (which must stay zero between calls).
+enum WorkspaceKind { kDecodeWorkspace = 0, kPrefillWorkspace = 1 };
+std::map<std::tuple<int, uintptr_t, int>, OwnedWorkspace> g_workspaces;
 
 int variant_id(int in_dtype, int out_dtype, int D) { return (in_dtype << 3) | (out_dtype << 1) | (D == 128); }
 
@@ -54,9 +59,9 @@ int device_shape(int dev, int in_dtype, int out_dtype, int D, int *num_cus, int 
     return GQA_OK;
 }
 
-int owned_workspace(int dev, hipStream_t stream, size_t need, void **out) {
+int owned_workspace(int dev, hipStream_t stream, int kind, size_t need, void **out) {
     std::lock_guard<std::mutex> lock(g_mu);
-    OwnedWorkspace &w = g_workspaces[std::make_pair(dev, reinterpret_cast<uintptr_t>(stream))];
+    OwnedWorkspace &w = g_workspaces[std::make_tuple(dev, reinterpret_cast<uintptr_t>(stream), kind)];
     if (w.bytes < need) {
         if (w.ptr) {
             // Work already enqueued on this stream may still read the old buffer.
@@ -75,6 +80,13 @@ int owned_workspace(int dev, hipStream_t stream, size_t need, void **out) {
                              hipGetErrorString(e));
         }
         w.bytes = grow;
+        // The decode's fused merge counters must read zero before a call (every call
+        // leaves them so); a new buffer starts zeroed, ordered before the call.
+        if (kind == kDecodeWorkspace) {
+            e = hipMemsetAsync(w.ptr, 0, gqa::kCounterBytes, stream);
+            if (e != hipSuccess)
+                return gqa::fail(GQA_ERR_HIP, "clearing the workspace counters failed: %s", hipGetErrorString(e));
+        }
     }
     *out = w.ptr;
     return GQA_OK;
@@ -96,7 +108,8 @@ int decode_plan(const gqa_decode_args *a, int *dev, gqa_decode_plan *plan) {
 int decode_launch(const gqa_decode_args *a, const gqa_decode_plan &plan, void *ws) {
     hipStream_t stream = reinterpret_cast<hipStream_t>(a->stream);
     const int G = a->h_q / a->h_kv;
-    const gqa::WorkspaceLayout L = gqa::workspace_layout(plan.num_chunks, G * (a->t_q > 0 ? a->t_q : 1), a->d_head);
+    const gqa::WorkspaceLayout L =
+        gqa::workspace_layout(plan.num_chunks, G * (a->t_q > 0 ? a->t_q : 1), a->d_head, plan.fused != 0);
     gqa::DecodeParams P;
     P.q = static_cast<const uint8_t *>(a->q);
     P.k = static_cast<const uint8_t *>(a->k);
@@ -105,6 +118,11 @@ int decode_launch(const gqa_decode_args *a, const gqa_decode_plan &plan, void *w
     P.seq_lens = a->seq_lens;
     P.ws_o = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + L.o_offset);
     P.ws_ml = reinterpret_cast<float2 *>(static_cast<uint8_t *>(ws) + L.ml_offset);
+    P.ws2_o = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + L.o2_offset);
+    P.ws2_ml = reinterpret_cast<float2 *>(static_cast<uint8_t *>(ws) + L.ml2_offset);
+    P.counters = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + L.counter_offset);
+    P.fold_k_log2 = 0;
+    while ((1 << P.fold_k_log2) < plan.fold_fanin) ++P.fold_k_log2;
     P.batch = a->batch;
     P.h_q = a->h_q;
     P.h_kv = a->h_kv;
@@ -122,10 +140,11 @@ int decode_launch(const gqa_decode_args *a, const gqa_decode_plan &plan, void *w
     hipError_t e;
     if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess)
         return gqa::fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
-    e = gqa::launch_sweep(P, a->in_dtype, a->out_dtype, a->d_head, plan.split_blocks, stream);
+    e = gqa::launch_sweep(P, a->in_dtype, a->out_dtype, a->d_head, plan.split_blocks, plan.fused != 0, stream);
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "sweep kernel launch failed: %s", hipGetErrorString(e));
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess)
         return gqa::fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+    if (plan.fused) return GQA_OK;   // the merge ran inside the sweep
     e = gqa::launch_merge(P, a->out_dtype, a->d_head, plan.merge_blocks, plan.merge_threads,
                           plan.merge_slices, stream);
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
@@ -140,7 +159,8 @@ int decode_ex(const gqa_decode_args *a) {
     if (st != GQA_OK) return st;
     void *ws = a->workspace;
     if (!ws) {
-        st = owned_workspace(dev, reinterpret_cast<hipStream_t>(a->stream), plan.workspace_bytes, &ws);
+        st = owned_workspace(dev, reinterpret_cast<hipStream_t>(a->stream), kDecodeWorkspace, plan.workspace_bytes,
+                             &ws);
         if (st != GQA_OK) return st;
     }
     return decode_launch(a, plan, ws);
@@ -246,7 +266,7 @@ int prefill_ex(const gqa_prefill_args *a) {
     if (W.bytes > 0) {
         void *ws = a->workspace;
         if (!ws) {
-            st = owned_workspace(dev, stream, W.bytes, &ws);
+            st = owned_workspace(dev, stream, kPrefillWorkspace, W.bytes, &ws);
             if (st != GQA_OK) return st;
         }
         gqa::VprepParams V;
@@ -465,7 +485,7 @@ void gqa_release(void) {
         const bool have_cur = hipGetDevice(&cur) == hipSuccess;
         for (auto &kv : g_workspaces) {
             if (!kv.second.ptr) continue;
-            if (hipSetDevice(kv.first.first) == hipSuccess) {
+            if (hipSetDevice(std::get<0>(kv.first)) == hipSuccess) {
                 (void)hipDeviceSynchronize();
                 (void)hipFree(kv.second.ptr);
             }

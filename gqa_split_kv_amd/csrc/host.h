@@ -81,14 +81,29 @@ struct PrefillWorkspace {
 PrefillWorkspace prefill_workspace(const gqa_prefill_args *a);
 constexpr int64_t kMaxPrefillRowsHeads = int64_t(1) << 37;   // total_tokens * h_kv limit
 
-// Workspace layout for `num_chunks` wavefronts: two partial-triple slots per
-// wavefront, each R = G * t_q rows of (O[D] fp32) plus (m, l) fp32.
+// Workspace layout for `num_chunks` wavefronts: the fused merge's counters in a
+// fixed reserve at the start (every plan keeps it, so no call's partials ever
+// land on another's counters), then two partial-triple slots per wavefront, each
+// R = G * t_q rows of (O[D] fp32) plus (m, l) fp32, and for the fused merge two
+// more slots per workgroup.
+constexpr size_t kCounterBytes = GQA_DECODE_COUNTER_BYTES;
+constexpr int64_t kCounterWords = static_cast<int64_t>(kCounterBytes / 4);
 struct WorkspaceLayout {
-    size_t o_offset;    // float  [num_chunks][2][R][D]
-    size_t ml_offset;   // float2 [num_chunks][2][R]
+    size_t counter_offset;   // uint32 [levels][num_chunks / kWavesPerBlock][2]  (0)
+    size_t o_offset;         // float  [num_chunks][2][R][D]
+    size_t ml_offset;        // float2 [num_chunks][2][R]
+    size_t o2_offset;        // float  [num_chunks / kWavesPerBlock][2][R][D]   (fused)
+    size_t ml2_offset;       // float2 [num_chunks / kWavesPerBlock][2][R]      (fused)
     size_t bytes;
 };
-WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D);
+WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D, bool fused);
+
+// Fused merge: automatic choice up to this many (sequence, kv head) units, and
+// the bound on the tree's fold volume per node (fan-in K = the largest power of
+// two with K * R * d_head * 4 bytes within it, clamped to [2, 64]).
+constexpr int kFusedMaxUnits = 16;
+constexpr int kFoldBytes = 64 * 1024;
+constexpr int kMaxFanIn = 64;
 
 int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decode_plan *plan);
 

@@ -17,6 +17,11 @@ struct DecodeParams {
     const int32_t *seq_lens;   // [batch]
     float *ws_o;               // [num_chunks][2][R][D]   unnormalised O of a piece
     float2 *ws_ml;             // [num_chunks][2][R]      (m in log2 units, l)
+    // Fused merge only (fused_kernel): the workgroup-level pieces and the tree's counters.
+    float *ws2_o;              // [num_chunks / kWavesPerBlock][2][R][D]
+    float2 *ws2_ml;            // [num_chunks / kWavesPerBlock][2][R]
+    uint32_t *counters;        // [levels][num_chunks / kWavesPerBlock][2], zero before and after a call
+    int32_t fold_k_log2;       // fan-in of the tree: 2^fold_k_log2
     int32_t batch, h_q, h_kv, G;
     int32_t t_q;               // query tokens per sequence
     int32_t R;                 // rows per kv head: G * t_q (row = t * G + g), up to 64
@@ -24,10 +29,11 @@ struct DecodeParams {
     float scale_log2;          // scale * log2(e)
 };
 
-// Enqueues the partial kernel and the merge kernel on `stream`.
 // Enqueues the sweep (partial) kernel: `blocks` workgroups of kThreads.  Dtypes
-// are GQA_DTYPE_* codes.
-hipError_t launch_sweep(const DecodeParams &P, int in_dtype, int out_dtype, int D, int blocks,
+// are GQA_DTYPE_* codes.  With `fused`, the single-kernel form (fused_kernel:
+// the merge runs inside the sweep, no merge kernel follows; blocks =
+// num_chunks / kWavesPerBlock).
+hipError_t launch_sweep(const DecodeParams &P, int in_dtype, int out_dtype, int D, int blocks, bool fused,
                         hipStream_t stream);
 
 // Resident workgroups of the sweep kernel per compute unit.

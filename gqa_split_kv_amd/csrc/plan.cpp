@@ -38,13 +38,36 @@ static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D) {
+WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D, bool fused) {
     WorkspaceLayout L;
     const size_t slots = static_cast<size_t>(num_chunks) * 2 * static_cast<size_t>(rows);
-    L.o_offset = 0;
-    L.ml_offset = round_up(slots * static_cast<size_t>(D) * sizeof(float), 256);
+    L.counter_offset = 0;
+    L.o_offset = kCounterBytes;
+    L.ml_offset = round_up(L.o_offset + slots * static_cast<size_t>(D) * sizeof(float), 256);
     L.bytes = round_up(L.ml_offset + slots * 2 * sizeof(float), 256);
+    L.o2_offset = L.ml2_offset = L.bytes;
+    if (fused) {
+        const size_t slots2 = static_cast<size_t>(num_chunks / kWavesPerBlock) * 2 * static_cast<size_t>(rows);
+        L.o2_offset = L.bytes;
+        L.ml2_offset = round_up(L.o2_offset + slots2 * static_cast<size_t>(D) * sizeof(float), 256);
+        L.bytes = round_up(L.ml2_offset + slots2 * 2 * sizeof(float), 256);
+    }
     return L;
+}
+
+// Fan-in of the fused merge's tree for R rows of d_head: the largest power of two
+// K with K * R * D * 4 <= kFoldBytes, within [2, kMaxFanIn].
+static int fold_fanin(int rows, int D) {
+    int k = 2;
+    while (k < kMaxFanIn && static_cast<int64_t>(2 * k) * rows * D * 4 <= kFoldBytes) k *= 2;
+    return k;
+}
+
+// Tree levels over at most `pieces` pieces per sequence with fan-in k.
+static int fold_levels(int64_t pieces, int k) {
+    int levels = 1;
+    for (int64_t span = k; span < pieces; span *= k) ++levels;
+    return levels;
 }
 
 // Rows of the MFMA N axis per kv head: G query heads x t_q query tokens.
@@ -92,6 +115,54 @@ static int check_basic(const gqa_decode_args *a) {
         return fail(GQA_ERR_ARG, "num_chunks %d out of range [0, %d]", a->num_chunks, kMaxChunks);
     if (a->min_chunk < 0 || a->min_chunk > kMaxMinChunk)
         return fail(GQA_ERR_ARG, "min_chunk %d out of range [0, %d]", a->min_chunk, kMaxMinChunk);
+    if (a->merge < GQA_MERGE_AUTO || a->merge > GQA_MERGE_FUSED)
+        return fail(GQA_ERR_ARG, "merge %d is not GQA_MERGE_AUTO, GQA_MERGE_KERNEL or GQA_MERGE_FUSED", a->merge);
+    return GQA_OK;
+}
+
+// Wavefront count and merge form of a call: `chunks` requested (explicit or
+// automatic) -> the count launched, and whether the merge is fused (with its
+// fan-in and levels).  Returns a status.
+struct Shape {
+    int64_t chunks;
+    bool fused;
+    int fanin, levels;
+};
+
+static int resolve_shape(const gqa_decode_args *a, int64_t chunks, Shape *out) {
+    const int R = rows_per_kv_head(a);
+    const int64_t units = static_cast<int64_t>(a->batch) * a->h_kv;
+    // One wavefront per kv head of every token range: a multiple of h_kv.
+    int64_t plain = chunks / a->h_kv * a->h_kv;
+    if (plain < a->h_kv) plain = a->h_kv;
+    // Fused: whole workgroups of consecutive ranges of one kv head, and no more
+    // wavefronts than the counter reserve serves (levels x 2 counters per workgroup).
+    const int64_t unit = static_cast<int64_t>(a->h_kv) * kWavesPerBlock;
+    const int fanin = fold_fanin(R, a->d_head);
+    auto counters = [&](int64_t n) { return fold_levels(n / unit, fanin) * 2 * (n / kWavesPerBlock); };
+    int64_t fchunks = chunks / unit * unit;
+    if (fchunks < unit) fchunks = unit;
+    const bool capped = counters(fchunks) > kCounterWords;
+    while (fchunks > unit && counters(fchunks) > kCounterWords) fchunks = (fchunks / 2) / unit * unit;
+    if (fchunks < unit) fchunks = unit;
+    const int levels = fold_levels(fchunks / unit, fanin);
+    const bool fits = counters(fchunks) <= kCounterWords;
+    bool fused;
+    if (a->merge == GQA_MERGE_FUSED) {
+        if (!fits)
+            return fail(GQA_ERR_ARG, "the fused merge needs %lld counters for h_kv %d, above the %lld the reserve "
+                        "holds", static_cast<long long>(counters(fchunks)), a->h_kv,
+                        static_cast<long long>(kCounterWords));
+        fused = true;
+    } else if (a->merge == GQA_MERGE_KERNEL) {
+        fused = false;
+    } else {
+        fused = fits && !capped && units <= kFusedMaxUnits;
+    }
+    out->chunks = fused ? fchunks : plain;
+    out->fused = fused;
+    out->fanin = fused ? fanin : 0;
+    out->levels = fused ? levels : 0;
     return GQA_OK;
 }
 
@@ -108,9 +179,10 @@ int validate(const gqa_decode_args *a) {
     int st = check_basic(a);
     if (st != GQA_OK) return st;
     if (a->num_chunks > 0) {
-        int64_t chunks = static_cast<int64_t>(a->num_chunks) / a->h_kv * a->h_kv;
-        if (chunks < a->h_kv) chunks = a->h_kv;
-        const WorkspaceLayout L = workspace_layout(chunks, rows_per_kv_head(a), a->d_head);
+        Shape sh;
+        st = resolve_shape(a, a->num_chunks, &sh);
+        if (st != GQA_OK) return st;
+        const WorkspaceLayout L = workspace_layout(sh.chunks, rows_per_kv_head(a), a->d_head, sh.fused);
         st = check_workspace(a, L.bytes);
         if (st != GQA_OK) return st;
     }
@@ -189,16 +261,25 @@ int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decod
         chunks = static_cast<int64_t>(num_cus) * (waves_per_cu < kAutoWavesPerCu ? waves_per_cu : kAutoWavesPerCu);
         if (chunks > kMaxChunks) chunks = kMaxChunks;
     }
-    // One wavefront per kv head of every token range: a multiple of h_kv.
-    chunks = chunks / a->h_kv * a->h_kv;
-    if (chunks < a->h_kv) chunks = a->h_kv;
+    Shape sh;
+    st = resolve_shape(a, chunks, &sh);
+    if (st != GQA_OK) return st;
+    chunks = sh.chunks;
     if (chunks > kMaxChunks) return fail(GQA_ERR_ARG, "h_kv %d needs more than %d wavefronts", a->h_kv, kMaxChunks);
-    const WorkspaceLayout L = workspace_layout(chunks, rows_per_kv_head(a), a->d_head);
+    const WorkspaceLayout L = workspace_layout(chunks, rows_per_kv_head(a), a->d_head, sh.fused);
     st = check_workspace(a, L.bytes);
     if (st != GQA_OK) return st;
     plan->num_chunks = static_cast<int32_t>(chunks);
     plan->min_chunk = a->min_chunk > 0 ? a->min_chunk : kAutoMinChunk;
     plan->split_blocks = static_cast<int32_t>((chunks + kWavesPerBlock - 1) / kWavesPerBlock);
+    plan->fused = sh.fused ? 1 : 0;
+    plan->fold_fanin = sh.fanin;
+    plan->fold_levels = sh.levels;
+    plan->workspace_bytes = L.bytes;
+    if (sh.fused) {
+        plan->merge_threads = plan->merge_slices = plan->merge_blocks = 0;
+        return GQA_OK;
+    }
     // Expected pieces per sequence: token ranges per sequence on average.
     const int64_t ranges = chunks / a->h_kv;
     const int R = rows_per_kv_head(a);
@@ -208,7 +289,6 @@ int make_plan(const gqa_decode_args *a, int num_cus, int waves_per_cu, gqa_decod
     plan->merge_slices = split ? a->d_head / (4 * kMergeSliceQuads) : 1;
     const int rows_per_block = wide ? 1 : kMergeThreadsNarrow / (a->d_head / 4);
     plan->merge_blocks = a->batch * a->h_kv * ((R + rows_per_block - 1) / rows_per_block) * plan->merge_slices;
-    plan->workspace_bytes = L.bytes;
     return GQA_OK;
 }
 

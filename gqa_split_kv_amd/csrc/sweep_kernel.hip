@@ -331,10 +331,12 @@ __device__ __forceinline__ void store_row(uint8_t *dst, const float *x, int n) {
 // One piece: keys [t0, t1) of (sequence b, kv head j); off = keys before b.  The
 // wavefront takes the kv head's rows as kNT tiles of 16 (rows 16 nt .. 16 nt + 15)
 // and computes each step once per tile on the same loaded keys; w = the
-// wavefront, which indexes the workspace slots.
-template <int kIn, int kOut, int D, int kDepth, int kNT>
-__device__ __forceinline__ void process_piece(const DecodeParams &P, int b, int j, int64_t off,
-                                              int t0, int t1, int len, int w) {
+// wavefront, which indexes the workspace slots.  Returns -1 when the piece was
+// the whole sequence (o written), else the slot its partial triple went to.
+template <int kIn, int kOut, int D, int kDepth, int kNT, bool kLdsSlots = false>
+__device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j, int64_t off,
+                                             int t0, int t1, int len, int w, float *lds_o = nullptr,
+                                             float2 *lds_ml = nullptr) {
     using S = Step<kIn, D>;
     constexpr int VEC = S::VEC;
     const int lane = lane_id();
@@ -458,13 +460,25 @@ swept:
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) out[q * VEC + c] = acc[nt][c][q];
-            if (row_ok[nt]) {
+            if constexpr (kLdsSlots) {
+                // The workgroup's own slots in LDS (16 rows each; w = the wavefront within
+                // the workgroup): row r of slot 2w + slot.
+                if (row_ok[nt]) {
+                    const int lrow = (2 * w + slot) * 16 + r[nt];
+                    float4 *dst = reinterpret_cast<float4 *>(lds_o + lrow * D + 4 * VEC * kg);
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i)
+                        dst[i] = make_float4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+                    if (kg == 0) lds_ml[lrow] = make_float2(m_run[nt], l_tot);
+                }
+            } else if (row_ok[nt]) {
                 const int64_t srow = (static_cast<int64_t>(w) * 2 + slot) * R + r[nt];
                 store_row<kF32>(reinterpret_cast<uint8_t *>(P.ws_o + srow * D + 4 * VEC * kg), out, 4 * VEC);
                 if (kg == 0) P.ws_ml[srow] = make_float2(m_run[nt], l_tot);
             }
         }
     }
+    return (t0 == 0 && t1 == len) ? -1 : (t0 > 0 ? 0 : 1);
 }
 
 template <int kIn, int kOut, int D, int kDepth, int kNT>
@@ -507,8 +521,396 @@ __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
     }
 }
 
+// ------------------------------------------------------------------ fused merge
+//
+// Single-kernel form of the decode for calls whose time is mostly latency (few
+// (sequence, kv head) units): the merge of a sequence's pieces runs inside the
+// sweep kernel, as the page's reduction runs inside its kernel (`_merge_running`
+// applied as partial triples arrive), instead of in a second launch.
+//
+//   * A workgroup sweeps kWavesPerBlock consecutive token ranges of one kv head
+//     (range group cg, head j: workgroup cg * h_kv + j).  Its wavefronts leave
+//     their cut pieces in the workgroup's slots (LDS for up to 16 rows per kv
+//     head, else the workspace); after a barrier the workgroup folds, in token
+//     order, the pieces that belong to one sequence: a sequence that lies inside
+//     the group's ranges gets its o here, and at most two sequences leave a
+//     group-level piece in the workspace (slot 0: begun before the group's first
+//     range; slot 1: continuing past its last), so the cross-workgroup reduction
+//     sees one piece per workgroup and sequence.
+//   * Group-level pieces are reduced by a tree of fixed fan-in K over the pieces
+//     of a sequence in token order: a node's children are K consecutive nodes of
+//     the level below.  Every workgroup that finishes a child increments the
+//     node's counter (a vector atomic at device scope, with release and acquire
+//     ordering), and the one that completes the count -- the last arriver --
+//     folds the children in ascending order, stores the node in its first
+//     child's place and goes up one level; at the root it writes o.  The fold
+//     order is fixed by the tree, not by arrival, so results are bit-identical
+//     from run to run.  The last arriver also puts the counter back to zero, so
+//     the counters read zero before and after every call.
+//   * Empty sequences (no key) get zeros from the workgroups of range group
+//     b mod (number of range groups).
+
+// Running state of one fold over (m, l, O) triples: m in log2 units.
+struct FoldState {
+    float M, L;
+    float4 acc;
+};
+
+__device__ __forceinline__ void fold_in(FoldState &r, float2 ml, float4 o) {
+    const float Mn = fmaxf(r.M, ml.x);
+    // Both sides empty (-inf): exponentiate against 0 so the identity stays NaN-free.
+    const float Mr = Mn == -INFINITY ? 0.f : Mn;
+    const float a = __builtin_amdgcn_exp2f(r.M - Mr);   // 0 while r is empty
+    const float f = __builtin_amdgcn_exp2f(ml.x - Mr);  // 0 for an empty side
+    r.L = r.L * a + ml.y * f;
+    r.acc.x = r.acc.x * a + o.x * f;
+    r.acc.y = r.acc.y * a + o.y * f;
+    r.acc.z = r.acc.z * a + o.z * f;
+    r.acc.w = r.acc.w * a + o.w * f;
+    r.M = Mn;
+}
+
+// Stores four consecutive outputs (d = 4 dq .. 4 dq + 3) of one o row.
+template <int kOut>
+__device__ __forceinline__ void store_out_quad(uint8_t *row, int dq, float4 x) {
+    if constexpr (kOut == kF32)
+        reinterpret_cast<float4 *>(row)[dq] = x;
+    else
+        reinterpret_cast<uint2 *>(row)[dq] = make_uint2(pack2<kOut == kF16>(x.x, x.y), pack2<kOut == kF16>(x.z, x.w));
+}
+
+// The group-level triples travel between workgroups on different XCDs (each with
+// its own L2) through device-coherent accesses: buffer loads and stores with the
+// sc1 cache-policy bit, the form device-scope atomic loads and stores take on
+// this architecture.  A store completes (vmcnt) only once it is visible device
+// wide, and a load with sc1 reads the coherent copy, so no L2 writeback or
+// invalidate is needed: each workgroup waits for its stores before it increments
+// a node's counter, and the last arriver loads the children only after the
+// counter's increment returned.
+constexpr int kCoherent = 16;   // sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws2_rsrc(const void *base) {
+    return make_rsrc(base, 0xffffffffu);   // offsets stay below 2^32: the plan bounds the group-level slots
+}
+
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 x) {
+    const uint4 u = make_uint4(__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, u), r,
+                                           off, 0, kCoherent);
+}
+
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, float2 x) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 u = {__float_as_uint(x.x), __float_as_uint(x.y)};
+    __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, kCoherent);
+}
+
+__device__ __forceinline__ float4 load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent);
+    return make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]), __uint_as_float(u[3]));
+}
+
+__device__ __forceinline__ float2 load_coherent2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherent);
+    return make_float2(__uint_as_float(u[0]), __uint_as_float(u[1]));
+}
+
+// Stores a fold's result for quad (row, dq): into the o row of (sequence b, kv
+// head j), normalised by L, or unnormalised into triple row srow0 + row of the
+// workspace's group-level slots (with (M, L) from the row's dq == 0 thread).
+template <int kOut, int D>
+__device__ __forceinline__ void fold_store(const DecodeParams &P, const FoldState &r, int row, int dq, bool to_o,
+                                           int b, int j, int64_t srow0) {
+    if (to_o) {
+        const int t = row / P.G;
+        const int g = row - t * P.G;
+        uint8_t *orow = P.o + ((static_cast<int64_t>(b) * P.t_q + t) * P.h_q + j * P.G + g) * D *
+                                  (kOut == kF32 ? 4 : 2);
+        const float inv = r.L > 0.f ? 1.0f / r.L : 0.f;   // a query token with no key gives 0
+        store_out_quad<kOut>(orow, dq, make_float4(r.acc.x * inv, r.acc.y * inv, r.acc.z * inv, r.acc.w * inv));
+    } else {
+        const int64_t srow = srow0 + row;
+        store_coherent(ws2_rsrc(P.ws2_o), static_cast<uint32_t>((srow * D + 4 * dq) * 4), r.acc);
+        if (dq == 0) store_coherent(ws2_rsrc(P.ws2_ml), static_cast<uint32_t>(srow * 8), make_float2(r.M, r.L));
+    }
+}
+
+// Folds children i = first, first + step, ... below n of quad (row, dq) into r,
+// in ascending order, with every load of a batch of 16 issued before the folds.
+constexpr int kFoldBatch = 16;
+template <typename Load>
+__device__ __forceinline__ void fold_span(FoldState &r, Load load, int first, int n, int step) {
+    for (int i0 = first; i0 < n; i0 += kFoldBatch * step) {
+        float2 ml[kFoldBatch];
+        float4 ov[kFoldBatch];
+#pragma unroll
+        for (int i = 0; i < kFoldBatch; ++i)
+            if (i0 + i * step < n) load(i0 + i * step, ml[i], ov[i]);
+#pragma unroll
+        for (int i = 0; i < kFoldBatch; ++i)
+            if (i0 + i * step < n) fold_in(r, ml[i], ov[i]);
+    }
+}
+
+// Folds n triples, child i at workspace group-level row index child(i) + row,
+// and stores the result (o rows, or group-level rows srow0 ..).  The workgroup
+// takes the R * D / 4 quads with PL = kThreads / quads threads ("piece lanes")
+// per quad when there are fewer quads than threads: lane l folds children l, l +
+// PL, ..., and the lanes are combined through LDS in ascending order, so the
+// fold order is fixed.  Every load precedes a barrier that precedes every
+// store, so the destination may be the first child's storage.  All threads of
+// the workgroup must call it.
+template <int kOut, int D, typename Child>
+__device__ void fold_children(const DecodeParams &P, FoldState *s_comb, Child child, int n, bool to_o, int b, int j,
+                              int64_t srow0) {
+    constexpr int QD = D / 4;
+    const int tid = static_cast<int>(threadIdx.x);
+    const int quads = P.R * QD;
+    const int PL = quads >= kThreads ? 1 : kThreads / quads;
+    const int iters = (quads + kThreads - 1) / kThreads;
+    for (int it = 0; it < iters; ++it) {
+        const int qd = PL > 1 ? tid % quads : it * kThreads + tid;
+        const int lane = PL > 1 ? tid / quads : 0;
+        const bool active = qd < quads && lane < PL;
+        const int row = qd / QD;
+        const int dq = qd - row * QD;
+        FoldState r = {-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+        if (active) {
+            const auto ro = ws2_rsrc(P.ws2_o);
+            const auto rml = ws2_rsrc(P.ws2_ml);
+            auto load = [&](int i, float2 &ml, float4 &o) {
+                const int64_t srow = child(i) + row;
+                ml = load_coherent2(rml, static_cast<uint32_t>(srow * 8));
+                o = load_coherent4(ro, static_cast<uint32_t>((srow * D + 4 * dq) * 4));
+            };
+            fold_span(r, load, lane, n, PL);
+        }
+        if (PL > 1) s_comb[tid] = r;
+        __syncthreads();   // every child has been read
+        if (active && lane == 0) {
+            for (int l = 1; l < PL; ++l) {
+                const FoldState x = s_comb[qd + l * quads];
+                fold_in(r, make_float2(x.M, x.L), x.acc);
+            }
+            fold_store<kOut, D>(P, r, row, dq, to_o, b, j, srow0);
+        }
+        if (PL > 1) __syncthreads();   // s_comb is free again
+    }
+}
+
+// One wavefront slot's record for the workgroup fold.
+struct SlotMeta {
+    int b, t0, t1, len;
+    int64_t off;
+};
+
+template <int kIn, int kOut, int D, int kDepth, int kNT>
+__global__ __launch_bounds__(kThreads) void fused_kernel(DecodeParams P) {
+    // Up to 16 rows per kv head, the wavefronts' slots live in LDS: slot e =
+    // 2 * wavefront + slot, 16 rows each.
+    constexpr bool kLds = kNT == 1;
+    constexpr int kSlots = 2 * kWavesPerBlock;
+    __shared__ float s_slot_o[kLds ? kSlots * 16 * D : 4];
+    __shared__ float2 s_slot_ml[kLds ? kSlots * 16 : 1];
+    __shared__ FoldState s_comb[kThreads];
+    __shared__ SlotMeta s_meta[kSlots];
+    __shared__ int s_last;
+    const int tid = static_cast<int>(threadIdx.x);
+    const int wave = uniform32(tid / kWave);
+    const int lane = lane_id();
+    const int wg = static_cast<int>(blockIdx.x);
+    const int j = wg % P.h_kv;
+    const int cg = wg / P.h_kv;                          // range group
+    const int n_groups = P.num_chunks / (P.h_kv * kWavesPerBlock);
+    const int w = wg * kWavesPerBlock + wave;            // the wavefront's workspace slots
+    const int c = cg * kWavesPerBlock + wave;            // the wavefront's token range
+    if (lane == 0) {
+        s_meta[2 * wave].b = -1;
+        s_meta[2 * wave + 1].b = -1;
+    }
+    const bool few = P.batch <= kWave;
+    FirstLens fl;
+    if (few) fl.load(P.seq_lens, P.batch);
+    const int64_t total = few ? fl.total() : total_len(P.seq_lens, P.batch);
+    const int64_t chunk = chunk_keys(total, P.num_chunks / P.h_kv, P.min_chunk);
+
+    // ---- zeros for empty sequences b with b mod n_groups == cg (head j's rows); the
+    // workgroup's wavefronts take them in turn.
+    {
+        const int64_t rowq = static_cast<int64_t>(P.R) * (D / 4);   // quads of one (sequence, head)
+        auto zero = [&](int eb) {
+            for (int64_t qd = lane; qd < rowq; qd += kWave) {
+                const int row = static_cast<int>(qd / (D / 4));
+                const int dq = static_cast<int>(qd - static_cast<int64_t>(row) * (D / 4));
+                const FoldState z = {-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+                fold_store<kOut, D>(P, z, row, dq, true, eb, j, 0);
+            }
+        };
+        if (few) {
+            unsigned long long m = __ballot(lane < P.batch && fl.li == 0 && lane % n_groups == cg);
+            for (int idx = 0; m; ++idx) {
+                const int eb = __ffsll(static_cast<long long>(m)) - 1;
+                m &= m - 1;
+                if (idx % kWavesPerBlock == wave) zero(eb);
+            }
+        } else {
+            for (int64_t k0 = 0; cg + k0 * n_groups < P.batch; k0 += kWave) {
+                const int64_t bb = cg + (k0 + lane) * n_groups;
+                unsigned long long m = __ballot(bb < P.batch && P.seq_lens[bb] <= 0);
+                for (int idx = 0; m; ++idx) {
+                    const int src = __ffsll(static_cast<long long>(m)) - 1;
+                    m &= m - 1;
+                    if (idx % kWavesPerBlock == wave) zero(static_cast<int>(cg + (k0 + src) * n_groups));
+                }
+            }
+        }
+    }
+
+    // ---- the wavefront's own range, as in split_kernel
+    int64_t pos = static_cast<int64_t>(c) * chunk;
+    if (pos < total) {
+        const int64_t end = pos + chunk < total ? pos + chunk : total;
+        int b, len;
+        int64_t off;
+        if (few)
+            fl.locate(P.batch, 1, pos, b, off, len);
+        else
+            locate(P.seq_lens, P.batch, 1, pos, b, off, len);
+        while (true) {
+            const int t0 = uniform32(static_cast<int>(pos - off));
+            const int64_t lim = end - off;
+            const int t1 = uniform32(static_cast<int>(lim < len ? lim : len));
+            const int slot = process_piece<kIn, kOut, D, kDepth, kNT, kLds>(
+                P, b, j, off, t0, t1, len, kLds ? wave : w, s_slot_o, s_slot_ml);
+            if (slot >= 0 && lane == 0) s_meta[2 * wave + slot] = SlotMeta{b, t0, t1, len, off};
+            pos = off + t1;
+            if (pos >= end) break;
+            off += len;
+            do {
+                ++b;
+                len = few ? fl.len(b) : uniform32(seq_len_at(P.seq_lens, b));
+            } while (len == 0);
+        }
+    }
+    __syncthreads();
+
+    // ---- workgroup fold of the wavefronts' pieces, sequence by sequence in token order
+    // (slots e = 2 * wavefront + slot are in token order; a sequence's slots are
+    // consecutive among the filled ones).
+    uint32_t filled = 0;
+#pragma unroll
+    for (int e = 0; e < kSlots; ++e) filled |= (s_meta[e].b >= 0 ? 1u : 0u) << e;
+    // group-level pieces left for the cross-workgroup reduction: (sequence, off, len)
+    int gp_b[2] = {0, 0}, gp_len[2] = {0, 0};
+    int64_t gp_off[2] = {0, 0};
+    int ngp = 0;
+    constexpr int QD = D / 4;
+    const int quads = P.R * QD;
+    while (filled) {
+        const int e0 = __builtin_ctz(filled);
+        const SlotMeta first = s_meta[e0];
+        uint32_t members = 0;
+        int elast = e0;
+        for (uint32_t m = filled; m; m &= m - 1) {
+            const int e = __builtin_ctz(m);
+            if (s_meta[e].b != first.b) break;
+            members |= 1u << e;
+            elast = e;
+        }
+        filled &= ~members;
+        const SlotMeta last = s_meta[elast];
+        const bool whole = first.t0 == 0 && last.t1 == last.len;
+        const int slot = first.t0 > 0 ? 0 : 1;
+        const int64_t srow0 = (static_cast<int64_t>(wg) * 2 + slot) * P.R;
+        for (int qd = tid; qd < quads; qd += kThreads) {
+            const int row = qd / QD;
+            const int dq = qd - row * QD;
+            FoldState r = {-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+            for (uint32_t m = members; m; m &= m - 1) {
+                const int e = __builtin_ctz(m);
+                float2 ml;
+                float4 o;
+                if constexpr (kLds) {
+                    const int lrow = e * 16 + row;
+                    ml = s_slot_ml[lrow];
+                    o = reinterpret_cast<const float4 *>(s_slot_o + lrow * D)[dq];
+                } else {
+                    const int64_t srow = (static_cast<int64_t>(wg * kWavesPerBlock + e / 2) * 2 + (e & 1)) * P.R + row;
+                    ml = P.ws_ml[srow];
+                    o = reinterpret_cast<const float4 *>(P.ws_o + srow * D)[dq];
+                }
+                fold_in(r, ml, o);
+            }
+            fold_store<kOut, D>(P, r, row, dq, whole, first.b, j, srow0);
+        }
+        if (!whole) {
+            gp_b[ngp] = first.b;
+            gp_len[ngp] = first.len;
+            gp_off[ngp] = first.off;
+            ++ngp;
+        }
+    }
+
+    // ---- tree reduction of the group-level pieces across workgroups (32-bit
+    // indices: range groups and workgroups number below 2^22)
+    const int kl = P.fold_k_log2;
+    const int64_t chunk_g = chunk * kWavesPerBlock;
+    const int level_stride = 2 * (P.num_chunks / kWavesPerBlock);   // counters per level
+    for (int q = 0; q < ngp; ++q) {
+        const int ca = static_cast<int>(div_nonneg(gp_off[q], chunk_g));
+        const int cb = static_cast<int>(div_nonneg(gp_off[q] + gp_len[q] - 1, chunk_g));
+        int nprev = cb - ca + 1;              // nodes at the level below (pieces at first)
+        int idx = cg - ca;                    // this workgroup's node at that level
+        int sl = 0;                           // log2 of the pieces per node at that level
+        for (int level = 0;; ++level) {
+            const int gidx = idx >> kl;
+            const int first = gidx << kl;
+            const int nchild = min(nprev - first, 1 << kl);
+            const int ncur = (nprev + (1 << kl) - 1) >> kl;
+            const int p0 = first << sl;                      // the node's first piece
+            // storage of piece p: workgroup (ca + p) * h_kv + j, slot 1 for the first piece
+            const int st0 = ((ca + p0) * P.h_kv + j) * 2 + (p0 == 0 ? 1 : 0);
+            if (nchild > 1) {
+                // Every thread's coherent stores of the child are complete (visible device
+                // wide) before the workgroup counts it.
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (tid == 0) {
+                    uint32_t *ctr = P.counters + level * level_stride + st0;
+                    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const int last = old == static_cast<uint32_t>(nchild - 1);
+                    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    s_last = last;
+                }
+                __syncthreads();
+                if (!s_last) break;
+                // child i (node first + i of the level below) is stored with its first piece
+                auto child = [&](int i) {
+                    const int p = (first + i) << sl;
+                    return static_cast<int64_t>((((ca + p) * P.h_kv + j) * 2 + (p == 0 ? 1 : 0)) * P.R);
+                };
+                fold_children<kOut, D>(P, s_comb, child, nchild, ncur == 1, gp_b[q], j,
+                                       static_cast<int64_t>(st0) * P.R);
+            }
+            if (ncur == 1) break;
+            idx = gidx;
+            nprev = ncur;
+            sl += kl;
+        }
+    }
+}
+
 template <int kIn, int kOut, int kNT>
-void launch_iot(const DecodeParams &P, int D, int blocks, hipStream_t stream) {
+void launch_iot(const DecodeParams &P, int D, int blocks, bool fused, hipStream_t stream) {
+    if (fused) {
+        if (D == 128)
+            hipLaunchKernelGGL((fused_kernel<kIn, kOut, 128, kSweepDepth, kNT>), dim3(blocks), dim3(kThreads), 0,
+                               stream, P);
+        else
+            hipLaunchKernelGGL((fused_kernel<kIn, kOut, 64, kSweepDepth, kNT>), dim3(blocks), dim3(kThreads), 0,
+                               stream, P);
+        return;
+    }
     if (D == 128)
         hipLaunchKernelGGL((split_kernel<kIn, kOut, 128, kSweepDepth, kNT>), dim3(blocks), dim3(kThreads), 0, stream,
                            P);
@@ -519,13 +921,13 @@ void launch_iot(const DecodeParams &P, int D, int blocks, hipStream_t stream) {
 // 16-row tiles per wavefront: 1 up to 16 rows per kv head (G * t_q), 2 up to 32,
 // 4 up to 64 (the keys of a step are loaded once for all of them).
 template <int kIn, int kOut>
-hipError_t launch_io(const DecodeParams &P, int D, int blocks, hipStream_t stream) {
+hipError_t launch_io(const DecodeParams &P, int D, int blocks, bool fused, hipStream_t stream) {
     if (P.R <= 16)
-        launch_iot<kIn, kOut, 1>(P, D, blocks, stream);
+        launch_iot<kIn, kOut, 1>(P, D, blocks, fused, stream);
     else if (P.R <= 32)
-        launch_iot<kIn, kOut, 2>(P, D, blocks, stream);
+        launch_iot<kIn, kOut, 2>(P, D, blocks, fused, stream);
     else
-        launch_iot<kIn, kOut, 4>(P, D, blocks, stream);
+        launch_iot<kIn, kOut, 4>(P, D, blocks, fused, stream);
     return hipGetLastError();
 }
 
@@ -541,13 +943,13 @@ hipError_t occupancy_io(int D, int *blocks_per_cu) {
 
 // (in, out) pairs the validation admits: (bf16, bf16), (bf16, f32), (f32, f32),
 // (f16, f16), (f16, f32).
-hipError_t launch_sweep(const DecodeParams &P, int in_dtype, int out_dtype, int D, int blocks,
+hipError_t launch_sweep(const DecodeParams &P, int in_dtype, int out_dtype, int D, int blocks, bool fused,
                         hipStream_t stream) {
-    if (in_dtype == kBf16) return out_dtype == kBf16 ? launch_io<kBf16, kBf16>(P, D, blocks, stream)
-                                                     : launch_io<kBf16, kF32>(P, D, blocks, stream);
-    if (in_dtype == kF16) return out_dtype == kF16 ? launch_io<kF16, kF16>(P, D, blocks, stream)
-                                                   : launch_io<kF16, kF32>(P, D, blocks, stream);
-    return launch_io<kF32, kF32>(P, D, blocks, stream);
+    if (in_dtype == kBf16) return out_dtype == kBf16 ? launch_io<kBf16, kBf16>(P, D, blocks, fused, stream)
+                                                     : launch_io<kBf16, kF32>(P, D, blocks, fused, stream);
+    if (in_dtype == kF16) return out_dtype == kF16 ? launch_io<kF16, kF16>(P, D, blocks, fused, stream)
+                                                   : launch_io<kF16, kF32>(P, D, blocks, fused, stream);
+    return launch_io<kF32, kF32>(P, D, blocks, fused, stream);
 }
 
 hipError_t sweep_occupancy(int in_dtype, int out_dtype, int D, int *blocks_per_cu) {

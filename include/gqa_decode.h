@@ -64,6 +64,15 @@ extern "C" {
 #define GQA_DTYPE_F32 1
 #define GQA_DTYPE_F16 2 /* IEEE binary16 */
 
+/* Merge forms (gqa_decode_args.merge). */
+#define GQA_MERGE_AUTO 0   /* the plan chooses                                        */
+#define GQA_MERGE_KERNEL 1 /* a second kernel merges the pieces of cut sequences       */
+#define GQA_MERGE_FUSED 2  /* one kernel: the pieces are merged inside the sweep       */
+
+/* Bytes at the start of every workspace (and of gqa_decode_noalloc's scratch)
+ * that hold the fused merge's counters; see gqa_decode_args.workspace. */
+#define GQA_DECODE_COUNTER_BYTES (64 * 1024)
+
 /* Status codes. */
 typedef enum gqa_status {
     GQA_OK = 0,
@@ -118,13 +127,34 @@ int gqa_decode_f16(const void *q, const void *k, const void *v, void *o,
  *             1024-key tiles as the split granularity.
  * workspace   Device scratch for the partial triples, at least
  *             gqa_decode_workspace_bytes() bytes, 256-byte aligned, owned by the
- *             caller and not used concurrently by another call.  NULL = a
- *             library-owned buffer per (device, stream), grown with hipMalloc on
- *             demand and freed by gqa_release(); callers that capture HIP graphs
- *             must pass their own, and make one uncaptured call of the same dtypes
- *             and d_head on the device first (it caches the device's compute-unit
- *             count and occupancy); the captured call then enqueues kernel
- *             launches only.
+ *             caller and not used concurrently by another call.  Its first
+ *             GQA_DECODE_COUNTER_BYTES bytes hold the fused merge's counters: they
+ *             must read zero before the first call that uses the workspace (zero
+ *             the buffer once after allocating it, or after using the memory for
+ *             anything else, e.g. a prefill workspace), and every call leaves them
+ *             zero; the rest needs no initialisation.  NULL = a library-owned
+ *             buffer per (device, stream), grown with hipMalloc on demand (its
+ *             counters cleared when it is allocated) and freed by gqa_release();
+ *             callers that capture HIP graphs must pass their own, and make one
+ *             uncaptured call of the same dtypes and d_head on the device first (it
+ *             caches the device's compute-unit count and occupancy); the captured
+ *             call then enqueues kernel launches only.
+ * merge       GQA_MERGE_AUTO (0), GQA_MERGE_KERNEL or GQA_MERGE_FUSED: how the
+ *             pieces of a sequence cut across ranges are merged.  KERNEL: a second
+ *             kernel merges them after the sweep.  FUSED: one kernel; each
+ *             workgroup sweeps 4 consecutive ranges of one kv head (num_chunks is
+ *             then rounded down to a multiple of 4 * h_kv, at least 4 * h_kv),
+ *             folds its wavefronts' pieces per sequence, and the workgroup-level
+ *             pieces of a sequence are reduced by a tree of fixed fan-in whose
+ *             nodes are folded by the last workgroup to arrive (device-scope
+ *             atomic counters), in an order fixed by the tree, so results are the
+ *             same from run to run.  AUTO chooses FUSED for calls of at most 16
+ *             (sequence, kv head) units, where the second launch's latency is a
+ *             large part of the step, unless num_chunks needs more counters than
+ *             the reserve holds.  The fused merge uses levels x num_chunks / 2
+ *             counters (GQA_DECODE_COUNTER_BYTES / 4 at most): FUSED lowers
+ *             num_chunks until they fit, and returns GQA_ERR_ARG only when even
+ *             4 * h_kv wavefronts need more (h_kv above 8,192).
  * sweep_events  See the field's comment; leave NULL outside profiling.
  * t_q         See the field's comment; 0 for the single-token decode.
  */
@@ -157,6 +187,7 @@ typedef struct gqa_decode_args {
      * attends to the keys at positions 0 .. seq_len - t_q + t (causal among the new
      * tokens; a token that sees no key gives 0).  G * t_q must not exceed 64. */
     int32_t t_q;
+    int32_t merge;  /* GQA_MERGE_*, see above */
 } gqa_decode_args;
 
 /* gqa_decode_ex -- the operation with every field of `args` (see above). */
@@ -212,6 +243,9 @@ typedef struct gqa_decode_plan {
     int32_t merge_threads;   /* threads per merge workgroup (256 or 1024)          */
     int32_t merge_slices;    /* d slices per output row in the merge (1 or d / 32) */
     size_t workspace_bytes;  /* partial-triple scratch the call needs              */
+    int32_t fused;           /* 1: one kernel (GQA_MERGE_FUSED), merge_* are 0     */
+    int32_t fold_fanin;      /* fused: children per node of the merge tree         */
+    int32_t fold_levels;     /* fused: counter levels of the tree                  */
 } gqa_decode_plan;
 
 int gqa_decode_make_plan(const gqa_decode_args *args, int32_t num_cus, int32_t waves_per_cu,

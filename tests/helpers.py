@@ -63,15 +63,20 @@ def check_bf16(got_bits: np.ndarray, ref: np.ndarray, what: str = "", slack: flo
     return int(steps[big].max()) if big.any() else 0, r, rel_l2(got, ref)
 
 
+# Merge form the decode helpers request (B.GQA_MERGE_*); a test module may set it
+# per test to run its cases through both the two-kernel and the fused form.
+MERGE = B.GQA_MERGE_AUTO
+
+
 def run_hip(q, k, v, seq_lens, scale, out_dtype=None, num_chunks=0, min_chunk=0, poison=True,
-            workspace=None, stream=None):
+            workspace=None, stream=None, merge=None):
     """Device tensors in; the decode output tensor (synchronised) out."""
     import torch
     out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if poison:
         out.fill_(float("nan"))
     B.decode(q, k, v, seq_lens, scale=scale, out=out, num_chunks=num_chunks, min_chunk=min_chunk,
-             workspace=workspace, stream=stream)
+             workspace=workspace, stream=stream, merge=MERGE if merge is None else merge)
     torch.cuda.synchronize()
     return out
 

@@ -173,15 +173,18 @@ static void plan_grid() {
     const int32_t Gs[] = {1, 4, 8, 16, 33, 64};
     const int32_t tqs[] = {0, 1, 2, 5, 8, 64};
     const int32_t chunks[] = {0, 1, 9, 1000, 1 << 24};
-    int made = 0;
+    const int32_t merges[] = {GQA_MERGE_AUTO, GQA_MERGE_KERNEL, GQA_MERGE_FUSED};
+    int made = 0, fused = 0;
     for (int nc : cus)
         for (int wv : waves)
             for (int32_t batch : batches)
                 for (int32_t hkv : hkvs)
                     for (int32_t G : Gs)
                         for (int32_t tq : tqs)
-                            for (int32_t ch : chunks) {
+                            for (int32_t ch : chunks)
+                            for (int32_t mg : merges) {
                                 gqa_decode_args a = base_args();
+                                a.merge = mg;
                                 a.batch = batch;
                                 a.h_kv = hkv;
                                 a.h_q = static_cast<int32_t>(static_cast<int64_t>(G) * hkv > INT32_MAX ? 0 : G * hkv);
@@ -200,6 +203,32 @@ static void plan_grid() {
                                 const int64_t R = static_cast<int64_t>(G) * (tq > 0 ? tq : 1);
                                 CHECK(p.num_chunks >= hkv && p.num_chunks % hkv == 0, "num_chunks %d h_kv %d",
                                       p.num_chunks, hkv);
+                                CHECK(p.fused == 0 || p.fused == 1, "fused %d", p.fused);
+                                CHECK(mg != GQA_MERGE_KERNEL || p.fused == 0, "kernel merge planned fused");
+                                CHECK(mg != GQA_MERGE_FUSED || p.fused == 1, "fused merge planned as two kernels");
+                                if (p.fused) {
+                                    ++fused;
+                                    const int64_t wgs = p.num_chunks / gqa::kWavesPerBlock;
+                                    CHECK(p.num_chunks % (static_cast<int64_t>(hkv) * gqa::kWavesPerBlock) == 0,
+                                          "fused num_chunks %d not a multiple of 4 h_kv %d", p.num_chunks, hkv);
+                                    CHECK(p.fold_fanin >= 2 && p.fold_fanin <= gqa::kMaxFanIn &&
+                                              (p.fold_fanin & (p.fold_fanin - 1)) == 0,
+                                          "fan-in %d", p.fold_fanin);
+                                    CHECK(static_cast<int64_t>(p.fold_fanin) * R * a.d_head * 4 <= gqa::kFoldBytes ||
+                                              p.fold_fanin == 2, "fold volume of fan-in %d", p.fold_fanin);
+                                    double span = 1;
+                                    for (int l = 0; l < p.fold_levels; ++l) span *= p.fold_fanin;
+                                    CHECK(span >= static_cast<double>(wgs / hkv), "levels %d of fan-in %d cover %g < %lld",
+                                          p.fold_levels, p.fold_fanin, span, static_cast<long long>(wgs / hkv));
+                                    CHECK(static_cast<int64_t>(p.fold_levels) * 2 * wgs <= gqa::kCounterWords,
+                                          "counters %lld", static_cast<long long>(p.fold_levels * 2 * wgs));
+                                    CHECK(p.merge_blocks == 0 && p.merge_threads == 0, "fused plan with a merge kernel");
+                                    const double need = static_cast<double>(gqa::kCounterBytes) +
+                                                        1.25 * p.num_chunks * 2 * R * (a.d_head + 2) * 4;
+                                    CHECK(static_cast<double>(p.workspace_bytes) >= need && p.workspace_bytes % 256 == 0,
+                                          "fused workspace %zu for %g", p.workspace_bytes, need);
+                                    continue;
+                                }
                                 CHECK(p.num_chunks <= (1 << 24), "num_chunks %d above 2^24", p.num_chunks);
                                 if (ch == 0)
                                     CHECK(p.num_chunks <= std::max<int64_t>(hkv, static_cast<int64_t>(nc) * std::min(wv, 4)),
@@ -213,7 +242,7 @@ static void plan_grid() {
                                       "workspace %zu for %g", p.workspace_bytes, need);
                                 CHECK(p.min_chunk > 0, "min_chunk %d", p.min_chunk);
                             }
-    CHECK(made > 1000, "only %d plans were made", made);
+    CHECK(made > 1000 && fused > 100, "only %d plans (%d fused) were made", made, fused);
 }
 
 static void prefill_grid() {

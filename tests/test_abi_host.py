@@ -101,7 +101,8 @@ def test_multi_token_limits(lib):
     st, p1 = B.gqa_decode_make_plan(_args(num_chunks=64), 256, 4)
     st2, p4 = B.gqa_decode_make_plan(_args(num_chunks=64, t_q=4), 256, 4)
     assert st == st2 == B.GQA_OK
-    assert p4.workspace_bytes >= 4 * p1.workspace_bytes - 256
+    C = B.GQA_DECODE_COUNTER_BYTES
+    assert p4.workspace_bytes - C >= 4 * (p1.workspace_bytes - C) - 256
 
 
 def test_more_than_16_rows_plan(lib):
@@ -110,11 +111,14 @@ def test_more_than_16_rows_plan(lib):
     not change, and the workspace grows with the rows."""
     st, p = B.gqa_decode_make_plan(_args(h_q=64, h_kv=8, t_q=4), 256, 4)       # 32 rows
     assert st == B.GQA_OK and p.num_chunks == 1024 and p.split_blocks == 256
-    st, p = B.gqa_decode_make_plan(_args(h_q=48, h_kv=1, t_q=1, num_chunks=11), 256, 4)   # 48 rows
-    assert st == B.GQA_OK and p.num_chunks == 11
+    st, p = B.gqa_decode_make_plan(_args(h_q=48, h_kv=1, t_q=1, num_chunks=11, merge=B.GQA_MERGE_KERNEL), 256, 4)
+    assert st == B.GQA_OK and p.num_chunks == 11 and not p.fused              # 48 rows
+    st, p = B.gqa_decode_make_plan(_args(h_q=48, h_kv=1, t_q=1, num_chunks=11), 256, 4)
+    assert st == B.GQA_OK and p.num_chunks == 8 and p.fused                   # 4 units: fused, 2 workgroups
     st, p64 = B.gqa_decode_make_plan(_args(h_q=64, h_kv=1, num_chunks=64), 256, 4)
     st, p16 = B.gqa_decode_make_plan(_args(h_q=16, h_kv=1, num_chunks=64), 256, 4)
-    assert p64.workspace_bytes >= 4 * p16.workspace_bytes - 256
+    C = B.GQA_DECODE_COUNTER_BYTES
+    assert p64.workspace_bytes - C >= 4 * (p16.workspace_bytes - C) - 256
 
 
 @pytest.mark.parametrize("field", ["q", "k", "v", "o"])
@@ -166,13 +170,14 @@ def test_plan_automatic_and_explicit(lib):
     assert st == B.GQA_OK
     assert (plan.num_chunks, plan.min_chunk, plan.split_blocks) == (8, 1024, 2)   # at least h_kv
     assert plan.merge_slices == 1
-    st, plan = B.gqa_decode_make_plan(_args(batch=1, h_kv=1, h_q=8), 256, 8)
+    kernel = B.GQA_MERGE_KERNEL
+    st, plan = B.gqa_decode_make_plan(_args(batch=1, h_kv=1, h_q=8, merge=kernel), 256, 8)
     assert (st, plan.merge_threads) == (B.GQA_OK, 1024)     # one sequence cut into 1024 ranges
     # ... and only 8 rows: each row's d is split over 4 workgroups
     assert (plan.merge_slices, plan.merge_blocks) == (4, 8 * 4)
     st, plan = B.gqa_decode_make_plan(_args(batch=64, h_kv=1, h_q=8, num_chunks=64 * 64), 256, 8)
     assert (plan.merge_threads, plan.merge_slices, plan.merge_blocks) == (1024, 1, 64 * 8)
-    st, plan = B.gqa_decode_make_plan(_args(num_chunks=7, h_kv=1, h_q=8), 256, 8)
+    st, plan = B.gqa_decode_make_plan(_args(num_chunks=7, h_kv=1, h_q=8, merge=kernel), 256, 8)
     assert (st, plan.num_chunks, plan.split_blocks) == (B.GQA_OK, 7, 2)
     st, plan = B.gqa_decode_make_plan(_args(h_kv=6, h_q=48), 256, 12)
     assert st == B.GQA_OK and plan.num_chunks == 1024 // 6 * 6     # capped at 4 waves per CU
@@ -202,9 +207,11 @@ def test_error_message_is_cleared_on_success(lib):
 
 
 def test_struct_mirrors_match_header_sizes(lib):
-    # gqa_decode_args: 5 pointers, 6 int32 + float, 2 more int32, pointer, size_t, pointer
-    assert ctypes.sizeof(B.GqaArgs) == 5 * 8 + 4 * 4 + 4 + 4 * 4 + 4 + 8 + 8 + 8 + 2 * 8 + 8
-    assert ctypes.sizeof(B.GqaPlan) == 6 * 4 + 8
+    # gqa_decode_args: 5 pointers, 4 int32 + float, 4 more int32, pointer, size_t, pointer,
+    # 2 event pointers, t_q and merge
+    assert ctypes.sizeof(B.GqaArgs) == 5 * 8 + 4 * 4 + 4 + 4 * 4 + 4 + 8 + 8 + 8 + 2 * 8 + 4 + 4
+    # gqa_decode_plan: 6 int32, size_t, 3 int32 (+4 padding)
+    assert ctypes.sizeof(B.GqaPlan) == 6 * 4 + 8 + 3 * 4 + 4
 
 
 # ------------------------------------------------------------------ prefill
@@ -320,3 +327,53 @@ def test_noalloc_argument_checks_on_the_host(lib):
                    (dict(num_chunks=-1), B.GQA_ERR_ARG), (dict(q=0), B.GQA_ERR_NULL)]:
         a = _args(**kw)
         assert lib.gqa_decode_noalloc(ctypes.byref(a)) == st, kw
+
+
+def test_fused_merge_plan(lib):
+    """The fused merge: chosen automatically for at most 16 (sequence, kv head)
+    units; whole workgroups of 4 ranges of one kv head (num_chunks a multiple of
+    4 h_kv); fan-in from the fold volume (K R d 4 bytes <= 64 KiB, 2..64); tree
+    levels from the range groups; the counters' reserve bounds its size."""
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=32, h_kv=8), 256, 4)      # 8 units
+    assert st == B.GQA_OK and p.fused == 1 and p.num_chunks == 1024 and p.split_blocks == 256
+    assert (p.merge_blocks, p.merge_threads) == (0, 0)
+    assert p.fold_fanin == 32 and p.fold_levels == 1                            # R 4: 2 KiB triples; 32 groups
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=8, h_kv=1), 256, 4)        # R 8, 256 range groups
+    assert p.fused and p.fold_fanin == 16 and p.fold_levels == 2
+    st, p = B.gqa_decode_make_plan(_args(batch=4, h_q=32, h_kv=8), 256, 4)       # 32 units: two kernels
+    assert st == B.GQA_OK and p.fused == 0 and p.merge_blocks > 0
+    st, p = B.gqa_decode_make_plan(_args(batch=4, h_q=32, h_kv=8, merge=B.GQA_MERGE_FUSED), 256, 4)
+    assert st == B.GQA_OK and p.fused == 1
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=64, h_kv=1, t_q=1, d_head=128), 256, 4)   # R 64
+    assert p.fused and p.fold_fanin == 2 and p.fold_levels == 8
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=1, h_kv=1, d_head=64), 256, 4)            # R 1, d 64
+    assert p.fused and p.fold_fanin == 64
+    for nc, want in [(1, 32), (33, 32), (100, 96), (4096, 4096)]:               # multiples of 4 h_kv = 32
+        st, p = B.gqa_decode_make_plan(_args(batch=1, num_chunks=nc), 256, 4)
+        assert st == B.GQA_OK and p.fused and p.num_chunks == want, (nc, p.num_chunks)
+    # counters: levels x 2 x num_chunks / 4 within 64 KiB / 4 words
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=8, h_kv=1, num_chunks=1 << 15), 256, 4)
+    assert st == B.GQA_OK and p.fused == 0 and p.num_chunks == 1 << 15   # automatic: too many counters
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=8, h_kv=1, num_chunks=1 << 15, merge=B.GQA_MERGE_FUSED), 256, 4)
+    assert st == B.GQA_OK and p.fused == 1 and p.num_chunks < 1 << 15            # forced: fewer wavefronts
+    assert p.fold_levels * 2 * (p.num_chunks // 4) <= B.GQA_DECODE_COUNTER_BYTES // 4
+    assert p.fold_levels * 2 * (2 * p.num_chunks // 4) > B.GQA_DECODE_COUNTER_BYTES // 4 - 4 * 2 * 16
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=8192, h_kv=8192, merge=B.GQA_MERGE_FUSED), 256, 4)
+    assert st == B.GQA_OK and p.fused and p.num_chunks == 4 * 8192 and p.fold_levels == 1   # 16384 counters
+    a = _args(batch=1, h_q=8200, h_kv=8200, num_chunks=0, merge=B.GQA_MERGE_FUSED)   # 2 x 8200 counters
+    st, _ = B.gqa_decode_make_plan(a, 256, 4)
+    assert st == B.GQA_ERR_ARG and "counters" in B.last_error_message()
+    a.num_chunks = 64
+    assert B.gqa_decode_validate(a) == B.GQA_ERR_ARG
+    assert _validate(merge=3) == B.GQA_ERR_ARG and _validate(merge=-1) == B.GQA_ERR_ARG
+    # workspace: the counter reserve, then the wavefront slots, then (fused) the workgroup slots
+    st, pk = B.gqa_decode_make_plan(_args(batch=1, num_chunks=256, merge=B.GQA_MERGE_KERNEL), 256, 4)
+    st, pf = B.gqa_decode_make_plan(_args(batch=1, num_chunks=256, merge=B.GQA_MERGE_FUSED), 256, 4)
+    slots = 256 * 2 * 4 * (128 + 2) * 4
+    assert pk.workspace_bytes == B.GQA_DECODE_COUNTER_BYTES + slots
+    assert pf.workspace_bytes == B.GQA_DECODE_COUNTER_BYTES + slots + slots // 4
+
+
+def test_args_struct_layout(lib):
+    assert ctypes.sizeof(B.GqaArgs) == 128 and B.GqaArgs.t_q.offset == 120 and B.GqaArgs.merge.offset == 124
+    assert ctypes.sizeof(B.GqaPlan) == 48 and B.GqaPlan.fused.offset == 32

@@ -31,22 +31,24 @@ def _say(*a):
     print(*a, flush=True)
 
 
+@pytest.mark.parametrize("merge", [B.GQA_MERGE_KERNEL, B.GQA_MERGE_FUSED], ids=["kernel", "fused"])
 @pytest.mark.parametrize("t_q", [0, 2])
-def test_decode_graph_replays_equal_eager(t_q):
+def test_decode_graph_replays_equal_eager(t_q, merge):
     import torch
     lens = [3000, 1, 0, 777, 65]
     c = device_case(len(lens), 32, 4, 128, lens, "bf16", seed=41, t_q=t_q)
-    _say("decode graph: lens", lens, "t_q", t_q)
+    _say("decode graph: lens", lens, "t_q", t_q, "merge", merge)
     out = torch.empty(c.q.shape, dtype=torch.float32, device="cuda")
     args = B.make_args(c.q, c.k, c.v, out, c.seq_lens, len(lens), 32, 4, 128, c.scale, B.GQA_DTYPE_BF16,
-                       B.GQA_DTYPE_F32, t_q=t_q)
-    ws = torch.empty(B.gqa_decode_workspace_bytes(args), dtype=torch.uint8, device="cuda")
+                       B.GQA_DTYPE_F32, t_q=t_q, merge=merge)
+    # Zero-filled once: the fused merge's counters must read zero before the first call.
+    ws = torch.zeros(B.gqa_decode_workspace_bytes(args), dtype=torch.uint8, device="cuda")
     # Eager call first: the library caches the device's shape outside the capture.
-    B.decode(c.q, c.k, c.v, c.seq_lens, scale=c.scale, out=out, workspace=ws)
+    B.decode(c.q, c.k, c.v, c.seq_lens, scale=c.scale, out=out, workspace=ws, merge=merge)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        B.decode(c.q, c.k, c.v, c.seq_lens, scale=c.scale, out=out, workspace=ws)
+        B.decode(c.q, c.k, c.v, c.seq_lens, scale=c.scale, out=out, workspace=ws, merge=merge)
     torch.cuda.synchronize()
     qshape = (len(lens), max(t_q, 1), 32, 128)
     for r in range(REPLAYS):
@@ -55,10 +57,11 @@ def test_decode_graph_replays_equal_eager(t_q):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        ref = B.decode(c.q, c.k, c.v, c.seq_lens, scale=c.scale, out_dtype=torch.float32)
+        ref = B.decode(c.q, c.k, c.v, c.seq_lens, scale=c.scale, out_dtype=torch.float32, merge=merge)
         torch.cuda.synchronize()
         assert torch.isfinite(out).all(), "replay %d left unwritten outputs" % r
         assert torch.equal(out, ref), "replay %d differs from the eager call (%s)" % (r, qshape)
+        assert (ws[:B.GQA_DECODE_COUNTER_BYTES].view(torch.int32) == 0).all().item()
     del g
 
 

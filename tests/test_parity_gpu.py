@@ -6,10 +6,13 @@ oracle.gqa_decode_f64 on the same seeded inputs:
   * bf16 results: every element within one bf16 ulp of the nearest-even bf16
     rounding of the oracle, and relative L2 <= 1e-3 against that rounding.
 Outputs are NaN-poisoned before each call so an unwritten element fails.
+Every test runs twice: with the pieces of cut sequences merged by a second
+kernel, and with the merge fused into the sweep kernel.
 """
 import numpy as np
 import pytest
 
+import helpers
 from gqa_split_kv_amd import binding as B
 from gqa_split_kv_amd.inputs import (WORKLOADS, device_workload, host_case, host_workload,
                                      to_host_bits)
@@ -17,6 +20,14 @@ from gqa_split_kv_amd.inputs import (WORKLOADS, device_workload, host_case, host
 from helpers import compare, oracle_of, run_hip, upload
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, params=[B.GQA_MERGE_KERNEL, B.GQA_MERGE_FUSED], ids=["kernel", "fused"])
+def merge_form(request):
+    """The merge form every decode call of the test requests."""
+    helpers.MERGE = request.param
+    yield request.param
+    helpers.MERGE = B.GQA_MERGE_AUTO
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -334,19 +345,53 @@ def test_scale_one_is_the_pages_unscaled_kernel():
 # ------------------------------------------------------------------ boundary behaviour
 
 
-def test_caller_workspace_poisoned_and_reused():
+def test_caller_workspace_poisoned_and_reused(merge_form):
+    """A caller workspace whose partial slots hold NaN (only the counter reserve at
+    its start is zero, as the header asks) gives the oracle's result twice in a
+    row, and the counters read zero again after each call."""
     import torch
     lens = [900, 50, 3000]
     c = host_case(3, 32, 8, 128, lens, "bf16", seed=91)
     ref = oracle_of(c)
     q, k, v, sl = upload(c)
-    args = B.make_args(q, k, v, q, sl, 3, 32, 8, 128, c.scale, 0, 1, num_chunks=300, min_chunk=1)
+    args = B.make_args(q, k, v, q, sl, 3, 32, 8, 128, c.scale, 0, 1, num_chunks=300, min_chunk=1, merge=merge_form)
     nbytes = B.gqa_decode_workspace_bytes(args)
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    ws[:B.GQA_DECODE_COUNTER_BYTES // 4].zero_()
     for _ in range(2):
         o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=300, min_chunk=1,
                     workspace=ws)
         compare(o, ref, "caller workspace")
+        assert (ws[:B.GQA_DECODE_COUNTER_BYTES // 4].view(torch.int32) == 0).all().item()
+
+
+def test_fused_merge_over_thousands_of_pieces_is_deterministic():
+    """One sequence of 48,000 keys cut into 4,000 ranges of 12 keys (1,000
+    workgroup-level pieces, a three-level tree of fan-in 16), and a ragged batch
+    cut as finely: bit-identical outputs over repeated calls, the oracle's result,
+    and counters back at zero after every call."""
+    import torch
+    for lens, h_q, h_kv in (([48000], 8, 1), ([9000, 0, 30000, 5, 9001], 16, 2)):
+        c = host_case(len(lens), h_q, h_kv, 128, lens, "bf16", seed=1000 + len(lens))
+        ref = oracle_of(c)
+        q, k, v, sl = upload(c)
+        nc = 4000 * h_kv
+        args = B.make_args(q, k, v, q, sl, len(lens), h_q, h_kv, 128, c.scale, 0, 1, num_chunks=nc, min_chunk=1,
+                           merge=B.GQA_MERGE_FUSED)
+        st, plan = B.gqa_decode_make_plan(args, 256, 4)
+        assert st == B.GQA_OK and plan.fused and plan.num_chunks == nc and plan.fold_levels == 3, plan.fold_levels
+        ws = torch.zeros(B.gqa_decode_workspace_bytes(args), dtype=torch.uint8, device="cuda")
+        outs = []
+        for rep in range(3):
+            _say("fused merge, lens", lens, "rep", rep)
+            o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=1, workspace=ws,
+                        merge=B.GQA_MERGE_FUSED)
+            outs.append(o)
+            assert (ws[:B.GQA_DECODE_COUNTER_BYTES].view(torch.int32) == 0).all().item()
+        compare(outs[0], ref, "fused, 1000 pieces")
+        assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+        o16 = run_hip(q, k, v, sl, c.scale, num_chunks=nc, min_chunk=1, merge=B.GQA_MERGE_FUSED)
+        compare(o16, ref, "fused, 1000 pieces, bf16 out")
 
 
 def test_too_small_workspace_is_rejected_and_output_untouched():
@@ -356,7 +401,7 @@ def test_too_small_workspace_is_rejected_and_output_untouched():
     ws = torch.zeros(64, dtype=torch.float32, device="cuda")
     o = torch.full((1, 8, 128), 7.0, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(B.GqaError) as ei:
-        B.decode(q, k, v, sl, out=o, num_chunks=10, workspace=ws)
+        B.decode(q, k, v, sl, out=o, num_chunks=10, workspace=ws, merge=helpers.MERGE)
     assert ei.value.status == B.GQA_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert (o == 7.0).all().item()
@@ -370,7 +415,7 @@ def test_invalid_arguments_leave_output_untouched():
     for kw, status in [(dict(h_q=7), B.GQA_ERR_SHAPE), (dict(d_head=96), B.GQA_ERR_UNSUPPORTED),
                        (dict(scale=float("nan")), B.GQA_ERR_SCALE)]:
         base = dict(q=q, k=k, v=v, o=o, seq_lens=sl, batch=1, h_q=8, h_kv=2, d_head=128,
-                    scale=c.scale, in_dtype=0, out_dtype=0)
+                    scale=c.scale, in_dtype=0, out_dtype=0, merge=helpers.MERGE)
         base.update(kw)
         args = B.make_args(**base)
         with pytest.raises(B.GqaError) as ei:
@@ -446,7 +491,7 @@ def test_runs_on_the_given_stream_and_is_deterministic():
         o = torch.full((3, 64, 128), float("nan"), dtype=torch.float32, device="cuda")
         torch.cuda.current_stream().synchronize()
         with torch.cuda.stream(s):
-            B.decode(q, k, v, sl, out=o, stream=s)
+            B.decode(q, k, v, sl, out=o, stream=s, merge=helpers.MERGE)
             ev = torch.cuda.Event()
             ev.record(s)
         ev.synchronize()
@@ -470,3 +515,21 @@ def test_probe_copy_and_read_are_exact(n):
     assert torch.equal(src, dst)
     want = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
     assert int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))) == int(want)
+
+
+def test_decode_after_prefill_on_library_workspaces(merge_form):
+    """Decode and prefill keep separate library-owned workspaces: a prefill's copy
+    of V must not land on the decode's merge counters (which must read zero)."""
+    import torch
+    from gqa_split_kv_amd.inputs import host_prefill_case
+    pc = host_prefill_case(2, 8, 1, 128, [3000, 500], "bf16", seed=1234)
+    pq, pk, pv, psl = upload(pc)
+    B.prefill(pq, pk, pv, psl, scale=pc.scale)
+    lens = [4000, 77]
+    c = host_case(len(lens), 8, 1, 128, lens, "bf16", seed=1235)
+    ref = oracle_of(c)
+    q, k, v, sl = upload(c)
+    for rep in range(2):
+        o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32)
+        compare(o, ref, "decode after prefill, rep %d" % rep)
+        B.prefill(pq, pk, pv, psl, scale=pc.scale)
