@@ -11,19 +11,22 @@ out, fp32 accumulation, synthetic seeded data.
 
 Prints one JSON line:
   value          K/V bytes read once per step / step time (GB/s), whole job
-  us_per_step    mean step time (HIP events around the K timed steps)
+  us_per_step    median step time over 5 repetitions that together make the K
+                 timed steps (HIP events around each), with min and max
   roofline       the sweep kernel: algorithmic K+V bytes per launch / its mean
                  duration (HIP events recorded by the library around that kernel
                  on the launch stream), against MI355X's 8 TB/s HBM peak;
                  traffic = HBM bytes per launch from the committed rocprofv3
                  counter summary if it was taken on the current kernel source
   cpu_baseline   the fp64 CPU oracle on the same inputs, on the host cores
-  decode_variants  the same batch with fp16 q/k/v and with two or four query
-                 tokens per sequence (t_q = 2, 4): step time, GB/s and the sweep
-                 kernel's roofline
+  decode_variants  the same batch with fp16 q/k/v, with two, four or eight query
+                 tokens per sequence (t_q = 2, 4, 8) and with 64 query heads per kv
+                 head (h_q 512): step time, GB/s and the sweep kernel's roofline
   other_workloads  the same step on every other named workload (tiny fp32,
                  8B-shaped, single KV group, long-context stress) at its automatic
-                 plan: step time, GB/s, % of the HBM peak, the sweep kernel's time
+                 plan: median step time and spread, GB/s, % of the HBM peak, the
+                 kernel time by events, and the traced kernel times and HBM traffic
+                 ratio of its committed rocprofv3 summary (profiles/decode_*.md)
   prefill        the causal prefill row at its own workload (one KV group, 32768
                  tokens, h_q 8, d_head 128, bf16): ms per call and TFLOP/s of
                  the algorithmic causal work against the bf16 matrix-core peak,
@@ -116,6 +119,42 @@ def committed_traffic():
     return float(t.group(1)), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-kernel scaled"
 
 
+REPS = 5   # the timed steps are split into this many repetitions: median and spread
+
+
+def split_reps(steps: int, reps: int = REPS):
+    """Sizes of the repetitions that together make exactly `steps` timed steps."""
+    reps = max(1, min(reps, steps))
+    base, extra = divmod(steps, reps)
+    return [base + (1 if i < extra else 0) for i in range(reps)]
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def profile_fields(path: str):
+    """Numbers a committed profile summary records for the current kernel sources:
+    {"kernel_us": ..., "traffic_ratio": ..., ...} from its `name: value` lines, or
+    (None, why) when it is missing or was taken on other sources."""
+    if not os.path.exists(path):
+        return None, "no profile summary committed"
+    text = open(path).read()
+    h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not h:
+        return None, "profile summary unreadable"
+    if h.group(1) != kernel_source_hash():
+        return None, "kernel changed since the profile was taken"
+    out = {}
+    for key in ("kernel_us", "merge_kernel_us", "traffic_bytes_per_launch", "traffic_ratio", "step_gap_us"):
+        m = re.search(r"^%s:\s*([0-9.eE+-]+)\s*$" % key, text, flags=re.M)
+        if m:
+            out[key] = float(m.group(1))
+    return out, os.path.relpath(path, ROOT)
+
+
 def cpu_model() -> str:
     """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
     try:
@@ -179,19 +218,26 @@ def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
          gqa.GQA_DTYPE_BF16, 2),
         ("bf16_t_q4", lambda: (device_queries(w.batch, 4, w.h_q, w.d, "bf16", seed=w.seed + 9), d.k, d.v),
          gqa.GQA_DTYPE_BF16, 4),
+        # 64 rows per kv head, the most the library takes: eight tokens on the same
+        # grouping, and one token with G = 64 query heads per kv head (h_q 512).
+        ("bf16_t_q8", lambda: (device_queries(w.batch, 8, w.h_q, w.d, "bf16", seed=w.seed + 11), d.k, d.v),
+         gqa.GQA_DTYPE_BF16, 8),
+        ("bf16_G64", lambda: (device_queries(w.batch, 1, 64 * w.h_kv, w.d, "bf16", seed=w.seed + 13)[:, 0]
+                              .contiguous(), d.k, d.v), gqa.GQA_DTYPE_BF16, 0),
     ]
     for name, make, code, t_q in forms:
         log("decode variant %s" % name)
         q, k, v = make()
+        h_q = q.shape[-2]
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-        probe = gqa.make_args(q, k, v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale, code, code,
+        probe = gqa.make_args(q, k, v, out, d.seq_lens, w.batch, h_q, w.h_kv, w.d, d.scale, code, code,
                               stream=stream, t_q=t_q)
         ws_bytes = gqa.gqa_decode_workspace_bytes(probe)
         ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
         ev_steps = [(hip.event(), hip.event()) for _ in range(steps)]
-        timed = [gqa.make_args(q, k, v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale, code, code,
+        timed = [gqa.make_args(q, k, v, out, d.seq_lens, w.batch, h_q, w.h_kv, w.d, d.scale, code, code,
                                0, 0, ws, ws_bytes, stream, sweep_events=e, t_q=t_q) for e in ev_steps]
-        warm = gqa.make_args(q, k, v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale, code, code,
+        warm = gqa.make_args(q, k, v, out, d.seq_lens, w.batch, h_q, w.h_kv, w.d, d.scale, code, code,
                              0, 0, ws, ws_bytes, stream, t_q=t_q)
         for _ in range(3):
             gqa.gqa_decode_ex(warm)
@@ -205,7 +251,8 @@ def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
         ms = hip.ms(*ev) / steps
         sweep_ms = sum(hip.ms(a, b) for a, b in ev_steps) / steps
         achieved = kv_bytes / (sweep_ms / 1e3) / 1e9
-        rows[name] = {"t_q": max(t_q, 1), "dtype": "f16" if code == gqa.GQA_DTYPE_F16 else "bf16",
+        rows[name] = {"t_q": max(t_q, 1), "h_q": h_q, "rows_per_kv_head": h_q // w.h_kv * max(t_q, 1),
+                      "dtype": "f16" if code == gqa.GQA_DTYPE_F16 else "bf16",
                       "us_per_step": round(ms * 1e3, 2),
                       "gb_s": round(kv_bytes / (ms / 1e3) / 1e9, 2),
                       "roofline": {"kernel": "split_kernel (key sweep)", "bound": "hbm",
@@ -221,15 +268,22 @@ def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
     return rows
 
 
+def profile_path(workload_name: str) -> str:
+    """The committed rocprofv3 summary (kernel trace and traffic) of one workload."""
+    return os.path.join(ROOT, "profiles", "decode_%s.md" % workload_name)
+
+
 def other_workloads(hip, stream, skip: int, steps: int):
-    """The decode step on every other named workload at its automatic plan: mean
-    step time over `steps` back-to-back calls (HIP events around the loop only),
-    K/V GB/s and its fraction of the HBM peak, and the sweep kernel's own time
-    from a second pass with events around each sweep launch (each event record
-    costs the GPU ~3 us between kernels, which would swamp a ~16 us step, so the
-    step loop has none).  Workloads whose K and V fit in the caches cycle
-    through copies of their inputs totalling about 1 GiB, so every step reads
-    its K and V from HBM."""
+    """The decode step on every other named workload at its automatic plan (with
+    the longest length as the max_seq_len hint): median step time over REPS
+    repetitions of back-to-back calls (HIP events around each repetition only),
+    K/V GB/s and its fraction of the HBM peak; the kernel's own time from a second
+    pass with events around each sweep launch (each event record costs the GPU
+    ~3 us between kernels, which would swamp a ~10 us step, so the step loop has
+    none); and, from the committed rocprofv3 summary of the workload when it was
+    taken on the current kernel sources, the traced kernel times and the HBM
+    traffic ratio.  Workloads whose K and V fit in the caches cycle through copies
+    of their inputs totalling about 1 GiB, so every step reads its K and V from HBM."""
     import torch
     import gqa_split_kv_amd as gqa
     from gqa_split_kv_amd.inputs import WORKLOADS, device_workload
@@ -244,45 +298,67 @@ def other_workloads(hip, stream, skip: int, steps: int):
         sets = [d] + [type(d)(d.q.clone(), d.k.clone(), d.v.clone(), d.seq_lens.clone(), d.seq_lens_host,
                               d.scale, d.dtype) for _ in range(rotate - 1)]
         kv_bytes = w.kv_bytes(d.seq_lens_host)
+        max_len = int(d.seq_lens_host.max())
         code = gqa.GQA_DTYPE_BF16 if w.dtype == "bf16" else gqa.GQA_DTYPE_F32
         out = torch.empty((w.batch, w.h_q, w.d), dtype=d.q.dtype, device="cuda")
         probe = gqa.make_args(d.q, d.k, d.v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale, code, code,
-                              stream=stream)
+                              stream=stream, max_seq_len=max_len)
         ws_bytes = gqa.gqa_decode_workspace_bytes(probe)
+        st, plan = gqa.gqa_decode_make_plan(probe, 256, 4)
         ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
         ev_steps = [(hip.event(), hip.event()) for _ in range(steps)]
 
         def args_for(i, events=None):
             c = sets[i % rotate]
             return gqa.make_args(c.q, c.k, c.v, out, c.seq_lens, w.batch, w.h_q, w.h_kv, w.d, c.scale, code,
-                                 code, 0, 0, ws, ws_bytes, stream, sweep_events=events)
+                                 code, 0, 0, ws, ws_bytes, stream, sweep_events=events, max_seq_len=max_len)
         warm = [args_for(i) for i in range(rotate)]
-        timed = [warm[i % rotate] for i in range(steps)]
         marked = [args_for(i, ev_steps[i]) for i in range(steps)]
         for i in range(max(rotate, 3)):
             gqa.gqa_decode_ex(warm[i % rotate])
         torch.cuda.synchronize()
-        ev = (hip.event(), hip.event())
-        hip.record(ev[0], stream)
-        for a in timed:
-            gqa.gqa_decode_ex(a)
-        hip.record(ev[1], stream)
-        hip.sync(ev[1])
-        ms = hip.ms(*ev) / steps
+        rep_ms = []
+        i0 = 0
+        for n in split_reps(steps):
+            ev = (hip.event(), hip.event())
+            hip.record(ev[0], stream)
+            for i in range(i0, i0 + n):
+                gqa.gqa_decode_ex(warm[i % rotate])
+            hip.record(ev[1], stream)
+            hip.sync(ev[1])
+            rep_ms.append(hip.ms(*ev) / n)
+            hip.destroy(ev[0])
+            hip.destroy(ev[1])
+            i0 += n
+        ms = median(rep_ms)
         for a in marked:
             gqa.gqa_decode_ex(a)
         torch.cuda.synchronize()
         sweep_ms = sum(hip.ms(a, b) for a, b in ev_steps) / steps
         gbs = kv_bytes / (ms / 1e3) / 1e9
-        rows[w.name] = {"dtype": w.dtype, "kv_bytes_per_step": kv_bytes, "rotate": rotate,
-                        "us_per_step": round(ms * 1e3, 2), "gb_s": round(gbs, 2),
-                        "pct_of_peak_hbm": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-                        "sweep_kernel_us": round(sweep_ms * 1e3, 2),
-                        "us_at_hbm_peak": round(kv_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 3)}
-        for e in ev_steps + [ev]:
+        row = {"dtype": w.dtype, "kv_bytes_per_step": kv_bytes, "rotate": rotate,
+               "merge": "fused (one kernel)" if plan.fused else "merge kernel",
+               "us_per_step": round(ms * 1e3, 2), "us_per_step_min": round(min(rep_ms) * 1e3, 2),
+               "us_per_step_max": round(max(rep_ms) * 1e3, 2), "reps": len(rep_ms),
+               "gb_s": round(gbs, 2), "pct_of_peak_hbm": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+               "first_kernel_us_events": round(sweep_ms * 1e3, 2),
+               "us_at_hbm_peak": round(kv_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 3)}
+        prof, note = profile_fields(profile_path(w.name))
+        row["profile"] = note
+        if prof:
+            if "kernel_us" in prof:
+                row["kernel_us_traced"] = prof["kernel_us"]
+                row["roofline"] = {"bound": "hbm", "achieved": round(kv_bytes / prof["kernel_us"] / 1e3, 2),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(kv_bytes / prof["kernel_us"] / 1e3 / HBM_PEAK_GBS, 4)}
+            for key in ("merge_kernel_us", "traffic_ratio", "step_gap_us"):
+                if key in prof:
+                    row[key + ("_traced" if key.endswith("_us") else "")] = prof[key]
+        rows[w.name] = row
+        for e in ev_steps:
             hip.destroy(e[0])
             hip.destroy(e[1])
-        del d, sets, out, ws, warm, timed, marked
+        del d, sets, out, ws, warm, marked
     return rows
 
 
@@ -295,7 +371,8 @@ def prefill_flops(seq_lens, h_q: int, d: int) -> float:
 def prefill_row(hip, stream, steps: int, with_oracle: bool, warmup: int = 10):
     """Times gqa_prefill_ex on the 32K-token single-KV-group workload: `warmup`
     untimed calls per mode first (the matrix-core clocks ramp up over the first
-    few milliseconds of sustained work), then `steps` timed calls."""
+    few milliseconds of sustained work), then `steps` timed calls in REPS
+    repetitions (median and spread of the per-call time)."""
     import torch
     import gqa_split_kv_amd as gqa
     from gqa_split_kv_amd.inputs import PREFILL_32K, device_prefill_case
@@ -314,16 +391,22 @@ def prefill_row(hip, stream, steps: int, with_oracle: bool, warmup: int = 10):
         for _ in range(warmup):
             gqa.gqa_prefill_ex(a)
         torch.cuda.synchronize()
-        ev = (hip.event(), hip.event())
-        hip.record(ev[0], stream)
-        for _ in range(steps):
-            gqa.gqa_prefill_ex(a)
-        hip.record(ev[1], stream)
-        hip.sync(ev[1])
-        ms = hip.ms(*ev) / steps
+        rep_ms = []
+        for n in split_reps(steps):
+            ev = (hip.event(), hip.event())
+            hip.record(ev[0], stream)
+            for _ in range(n):
+                gqa.gqa_prefill_ex(a)
+            hip.record(ev[1], stream)
+            hip.sync(ev[1])
+            rep_ms.append(hip.ms(*ev) / n)
+            hip.destroy(ev[0])
+            hip.destroy(ev[1])
+        ms = median(rep_ms)
         tf = flops / (ms / 1e3) / 1e12
         key = "split_pv" if split else "default"
-        row[key] = {"ms_per_call": round(ms, 4), "tflops": round(tf, 1)}
+        row[key] = {"ms_per_call": round(ms, 4), "ms_min": round(min(rep_ms), 4), "ms_max": round(max(rep_ms), 4),
+                    "reps": len(rep_ms), "tflops": round(tf, 1)}
         if not split:
             row["ms_per_call"] = round(ms, 4)
             row["roofline"] = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tf, 1),
@@ -399,18 +482,21 @@ def main():
     out = torch.empty((w.batch, w.h_q, w.d), dtype=d.q.dtype, device="cuda")
     stream = int(torch.cuda.current_stream().cuda_stream)
     dt_code = gqa.GQA_DTYPE_BF16 if w.dtype == "bf16" else gqa.GQA_DTYPE_F32
+    max_len = int(d.seq_lens_host.max())     # the plan's max_seq_len hint
     probe = gqa.make_args(d.q, d.k, d.v, out, d.seq_lens, w.batch, w.h_q, w.h_kv, w.d, d.scale,
-                          dt_code, dt_code, args.num_chunks, args.min_chunk, stream=stream)
+                          dt_code, dt_code, args.num_chunks, args.min_chunk, stream=stream, max_seq_len=max_len)
     ws_bytes = gqa.gqa_decode_workspace_bytes(probe)
+    _, plan = gqa.gqa_decode_make_plan(probe, 256, 4)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     ev_steps = [(hip.event(), hip.event()) for _ in range(args.steps)]
-    ev_all = (hip.event(), hip.event())
+    reps = split_reps(args.steps)
+    ev_reps = [(hip.event(), hip.event()) for _ in reps]
 
     def step_args(i, events=None):
         s = sets[i % args.rotate]
         return gqa.make_args(s.q, s.k, s.v, out, s.seq_lens, w.batch, w.h_q, w.h_kv, w.d, s.scale,
                              dt_code, dt_code, args.num_chunks, args.min_chunk, ws, ws_bytes, stream,
-                             sweep_events=events)
+                             sweep_events=events, max_seq_len=max_len)
 
     # Argument blocks are built before the timed region, so the loop issues only
     # the library calls (at a few microseconds per step the Python that fills a
@@ -423,18 +509,23 @@ def main():
     torch.cuda.synchronize()
     log("timing %d steps" % args.steps)
     decode_ex = gqa.gqa_decode_ex
+    # The K timed steps run as REPS back-to-back repetitions, each bracketed by its
+    # own pair of events; the step time is the median of the repetitions' means.
     t0 = time.perf_counter()
-    hip.record(ev_all[0], stream)
-    for a in timed_args:
-        decode_ex(a)
-    hip.record(ev_all[1], stream)
+    i0 = 0
+    for (e0, e1), n in zip(ev_reps, reps):
+        hip.record(e0, stream)
+        for a in timed_args[i0:i0 + n]:
+            decode_ex(a)
+        hip.record(e1, stream)
+        i0 += n
     submit = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    hip.sync(ev_all[1])
-    total_ms = hip.ms(*ev_all)
-    sweep_ms = sum(hip.ms(a, b) for a, b in ev_steps) / args.steps
-    ms_per_step = total_ms / args.steps
+    rep_ms = [hip.ms(e0, e1) / n for (e0, e1), n in zip(ev_reps, reps)]
+    sweep_each = [hip.ms(a, b) for a, b in ev_steps]
+    sweep_ms = median(sweep_each)
+    ms_per_step = median(rep_ms)
     value = kv_bytes / (ms_per_step / 1e3) / 1e9
     achieved = kv_bytes / (sweep_ms / 1e3) / 1e9
     traffic, traffic_note = committed_traffic()
@@ -447,6 +538,11 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_min": round(min(rep_ms) * 1e3, 2),
+        "us_per_step_max": round(max(rep_ms) * 1e3, 2),
+        "reps": len(reps),
+        "timing": "median of %d repetitions of back-to-back steps (%s steps each), HIP events" % (
+            len(reps), "/".join(str(n) for n in reps)),
         "pct_of_peak_hbm": round(100.0 * value / HBM_PEAK_GBS, 2),
         "wall_s_timed_region": round(wall, 4),
         "host_us_per_call": round(submit / args.steps * 1e6, 2),
@@ -465,7 +561,7 @@ def main():
             "workspace_bytes": ws_bytes,
         },
         "roofline": {
-            "kernel": "split_kernel (key sweep)",
+            "kernel": "fused_kernel (key sweep and merge)" if plan.fused else "split_kernel (key sweep)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
@@ -481,17 +577,17 @@ def main():
     # Achievable read bandwidth on this machine: the plain read probe over the
     # same K and V bytes, timed the same way.
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")     # GQA_PROBE_SINK_WORDS words
-    reps = 10
+    probe_reps = 10
     for i in range(2):
         gqa.gqa_probe_read(d.k, d.k.numel() * d.k.element_size(), sink, stream)
     ev_p = (hip.event(), hip.event())
     hip.record(ev_p[0], stream)
-    for i in range(reps):
+    for i in range(probe_reps):
         gqa.gqa_probe_read(d.k, d.k.numel() * d.k.element_size(), sink, stream)
         gqa.gqa_probe_read(d.v, d.v.numel() * d.v.element_size(), sink, stream)
     hip.record(ev_p[1], stream)
     hip.sync(ev_p[1])
-    probe_gbs = kv_bytes * reps / (hip.ms(*ev_p) / 1e3) / 1e9
+    probe_gbs = kv_bytes * probe_reps / (hip.ms(*ev_p) / 1e3) / 1e9
     result["roofline"]["probe_read_gbs"] = round(probe_gbs, 1)
     result["roofline"]["frac_of_probe_read"] = round(achieved / probe_gbs, 4)
     if args.copy_probe_mib > 0:

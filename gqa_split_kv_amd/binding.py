@@ -59,6 +59,7 @@ class GqaArgs(ctypes.Structure):
         ("sweep_events", ctypes.c_void_p * 2),
         ("t_q", ctypes.c_int32),
         ("merge", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
     ]
 
 
@@ -223,7 +224,7 @@ def gqa_decode_f16(q, k, v, o, seq_lens, batch: int, h_q: int, h_kv: int, d_head
 
 def make_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, in_dtype, out_dtype,
               num_chunks=0, min_chunk=0, workspace=None, workspace_bytes=0, stream=0,
-              sweep_events=None, t_q=0, merge=GQA_MERGE_AUTO) -> GqaArgs:
+              sweep_events=None, t_q=0, merge=GQA_MERGE_AUTO, max_seq_len=0) -> GqaArgs:
     a = GqaArgs()
     a.q, a.k, a.v, a.o, a.seq_lens = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_lens)
     a.batch, a.h_q, a.h_kv, a.d_head = int(batch), int(h_q), int(h_kv), int(d_head)
@@ -238,6 +239,7 @@ def make_args(q, k, v, o, seq_lens, batch, h_q, h_kv, d_head, scale, in_dtype, o
         a.sweep_events[1] = int(sweep_events[1])
     a.t_q = int(t_q)
     a.merge = int(merge)
+    a.max_seq_len = int(max_seq_len)
     return a
 
 
@@ -348,14 +350,16 @@ def _check_tensors(what: str, q, k, v, seq_lens, out, workspace, batch: int) -> 
 
 
 def decode(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype=None,
-           num_chunks: int = 0, min_chunk: int = 0, workspace=None, stream=None, merge: int = GQA_MERGE_AUTO):
+           num_chunks: int = 0, min_chunk: int = 0, workspace=None, stream=None, merge: int = GQA_MERGE_AUTO,
+           max_seq_len: int = 0):
     """o = GQA decode of q [batch, h_q, d] (or [batch, t_q, h_q, d] for t_q query
     tokens per sequence) against packed k, v [sum(seq_lens), h_kv, d].
 
     q, k and v share one dtype and one CUDA device and are contiguous; seq_lens
     is a contiguous int32 tensor on that device with one length per sequence.
     out_dtype defaults to q's dtype; pass torch.float32 with 16-bit inputs for the
-    fp32 result.  merge is GQA_MERGE_AUTO, GQA_MERGE_KERNEL or GQA_MERGE_FUSED; a
+    fp32 result.  merge is GQA_MERGE_AUTO, GQA_MERGE_KERNEL or GQA_MERGE_FUSED;
+    max_seq_len (0 = unknown) is the plan's hint of the longest sequence; a
     caller workspace must read zero in its first GQA_DECODE_COUNTER_BYTES bytes
     before its first use (torch.zeros).  Raises ValueError/TypeError before any
     device work when the tensors do not fit these rules.  Returns `out`.
@@ -378,7 +382,7 @@ def decode(q, k, v, seq_lens, scale: Optional[float] = None, out=None, out_dtype
         ws_bytes = workspace.numel() * workspace.element_size()
     args = make_args(q, k, v, out, seq_lens, batch, h_q, h_kv, d, scale, _dtype_code(q),
                      _dtype_code(out), num_chunks, min_chunk, workspace, ws_bytes, _stream(stream),
-                     t_q=t_q, merge=merge)
+                     t_q=t_q, merge=merge, max_seq_len=max_seq_len)
     gqa_decode_ex(args)
     return out
 

@@ -48,7 +48,7 @@ constexpr int kMaxChunks = 1 << 24;
 constexpr int kMaxPrefillBlocks = 1 << 20;
 constexpr int kMaxHeadsKv = 1 << 16;   // keeps 16 key rows of lane offsets within 32 bits
 constexpr int kMaxMinChunk = 1 << 30;
-constexpr int kAutoMinChunk = 32;   // default smallest token range
+constexpr int kAutoMinChunk = 64;   // default smallest token range (two 32-key steps)
 // Automatic plan: at most this many sweep wavefronts per compute unit, i.e. one
 // per SIMD.  Measured on MI355X (70B-shaped ragged batch): with the MFMA-based
 // step the SIMD is lightly loaded, one wavefront per SIMD with one step of
@@ -98,9 +98,15 @@ struct WorkspaceLayout {
 };
 WorkspaceLayout workspace_layout(int64_t num_chunks, int rows, int D, bool fused);
 
-// Fused merge: automatic choice up to this many (sequence, kv head) units, and
-// the bound on the tree's fold volume per node (fan-in K = the largest power of
-// two with K * R * d_head * 4 bytes within it, clamped to [2, 64]).
+// Fused merge: chosen automatically for at most this many (sequence, kv head)
+// units when the caller's max_seq_len hint shows that every sequence fits in one
+// workgroup's key span (kWavesPerBlock * min_chunk keys), so that no sequence
+// needs more than one exchange between workgroups; measured on MI355X, the
+// fused form then saves the merge launch (tiny workload 10.6 -> 8.4 us), while
+// for long sequences over few units each level of its tree (a device-coherent
+// store, an atomic and a coherent load, ~3 us) costs as much as the merge kernel.
+// Also the bound on the tree's fold volume per node (fan-in K = the largest power
+// of two with K * R * d_head * 4 bytes within it, clamped to [2, 64]).
 constexpr int kFusedMaxUnits = 16;
 constexpr int kFoldBytes = 64 * 1024;
 constexpr int kMaxFanIn = 64;

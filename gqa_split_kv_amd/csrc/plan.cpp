@@ -115,6 +115,7 @@ static int check_basic(const gqa_decode_args *a) {
         return fail(GQA_ERR_ARG, "num_chunks %d out of range [0, %d]", a->num_chunks, kMaxChunks);
     if (a->min_chunk < 0 || a->min_chunk > kMaxMinChunk)
         return fail(GQA_ERR_ARG, "min_chunk %d out of range [0, %d]", a->min_chunk, kMaxMinChunk);
+    if (a->max_seq_len < 0) return fail(GQA_ERR_ARG, "max_seq_len %d is negative", a->max_seq_len);
     if (a->merge < GQA_MERGE_AUTO || a->merge > GQA_MERGE_FUSED)
         return fail(GQA_ERR_ARG, "merge %d is not GQA_MERGE_AUTO, GQA_MERGE_KERNEL or GQA_MERGE_FUSED", a->merge);
     return GQA_OK;
@@ -157,7 +158,9 @@ static int resolve_shape(const gqa_decode_args *a, int64_t chunks, Shape *out) {
     } else if (a->merge == GQA_MERGE_KERNEL) {
         fused = false;
     } else {
-        fused = fits && !capped && units <= kFusedMaxUnits;
+        const int64_t min_chunk = a->min_chunk > 0 ? a->min_chunk : kAutoMinChunk;
+        fused = fits && !capped && units <= kFusedMaxUnits && a->max_seq_len > 0 &&
+                a->max_seq_len <= kWavesPerBlock * min_chunk;
     }
     out->chunks = fused ? fchunks : plain;
     out->fused = fused;

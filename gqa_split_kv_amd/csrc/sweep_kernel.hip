@@ -796,59 +796,89 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(DecodeParams P) {
 
     // ---- workgroup fold of the wavefronts' pieces, sequence by sequence in token order
     // (slots e = 2 * wavefront + slot are in token order; a sequence's slots are
-    // consecutive among the filled ones).
-    uint32_t filled = 0;
+    // consecutive among the filled ones).  The slot records are read once into
+    // registers and each thread reads all slots of its quad before folding, so the
+    // fold costs one round of LDS reads; every loop over the slots is unrolled.
+    SlotMeta meta[kSlots];
 #pragma unroll
-    for (int e = 0; e < kSlots; ++e) filled |= (s_meta[e].b >= 0 ? 1u : 0u) << e;
+    for (int e = 0; e < kSlots; ++e) meta[e] = s_meta[e];
     // group-level pieces left for the cross-workgroup reduction: (sequence, off, len)
-    int gp_b[2] = {0, 0}, gp_len[2] = {0, 0};
-    int64_t gp_off[2] = {0, 0};
-    int ngp = 0;
+    int gp_b0 = 0, gp_len0 = 0, gp_b1 = 0, gp_len1 = 0, ngp = 0;
+    int64_t gp_off0 = 0, gp_off1 = 0;
+    {
+        int cur = -1, first_t0 = 0;
+        SlotMeta last = meta[0];
+        auto close = [&]() {
+            if (cur >= 0 && !(first_t0 == 0 && last.t1 == last.len)) {
+                if (ngp == 0) {
+                    gp_b0 = cur;
+                    gp_len0 = last.len;
+                    gp_off0 = last.off;
+                } else {
+                    gp_b1 = cur;
+                    gp_len1 = last.len;
+                    gp_off1 = last.off;
+                }
+                ++ngp;
+            }
+        };
+#pragma unroll
+        for (int e = 0; e < kSlots; ++e) {
+            if (meta[e].b >= 0) {
+                if (meta[e].b != cur) {
+                    close();
+                    cur = meta[e].b;
+                    first_t0 = meta[e].t0;
+                }
+                last = meta[e];
+            }
+        }
+        close();
+    }
     constexpr int QD = D / 4;
     const int quads = P.R * QD;
-    while (filled) {
-        const int e0 = __builtin_ctz(filled);
-        const SlotMeta first = s_meta[e0];
-        uint32_t members = 0;
-        int elast = e0;
-        for (uint32_t m = filled; m; m &= m - 1) {
-            const int e = __builtin_ctz(m);
-            if (s_meta[e].b != first.b) break;
-            members |= 1u << e;
-            elast = e;
-        }
-        filled &= ~members;
-        const SlotMeta last = s_meta[elast];
-        const bool whole = first.t0 == 0 && last.t1 == last.len;
-        const int slot = first.t0 > 0 ? 0 : 1;
-        const int64_t srow0 = (static_cast<int64_t>(wg) * 2 + slot) * P.R;
-        for (int qd = tid; qd < quads; qd += kThreads) {
-            const int row = qd / QD;
-            const int dq = qd - row * QD;
-            FoldState r = {-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
-            for (uint32_t m = members; m; m &= m - 1) {
-                const int e = __builtin_ctz(m);
-                float2 ml;
-                float4 o;
-                if constexpr (kLds) {
-                    const int lrow = e * 16 + row;
-                    ml = s_slot_ml[lrow];
-                    o = reinterpret_cast<const float4 *>(s_slot_o + lrow * D)[dq];
-                } else {
-                    const int64_t srow = (static_cast<int64_t>(wg * kWavesPerBlock + e / 2) * 2 + (e & 1)) * P.R + row;
-                    ml = P.ws_ml[srow];
-                    o = reinterpret_cast<const float4 *>(P.ws_o + srow * D)[dq];
-                }
-                fold_in(r, ml, o);
+    for (int qd = tid; qd < quads; qd += kThreads) {
+        const int row = qd / QD;
+        const int dq = qd - row * QD;
+        float2 sml[kSlots];
+        float4 so[kSlots];
+#pragma unroll
+        for (int e = 0; e < kSlots; ++e) {
+            sml[e] = make_float2(-INFINITY, 0.f);
+            so[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (kLds) {
+                const int lrow = e * 16 + row;
+                sml[e] = s_slot_ml[lrow];
+                so[e] = reinterpret_cast<const float4 *>(s_slot_o + lrow * D)[dq];
+            } else if (meta[e].b >= 0) {
+                const int64_t srow = (static_cast<int64_t>(wg * kWavesPerBlock + e / 2) * 2 + (e & 1)) * P.R + row;
+                sml[e] = P.ws_ml[srow];
+                so[e] = reinterpret_cast<const float4 *>(P.ws_o + srow * D)[dq];
             }
-            fold_store<kOut, D>(P, r, row, dq, whole, first.b, j, srow0);
         }
-        if (!whole) {
-            gp_b[ngp] = first.b;
-            gp_len[ngp] = first.len;
-            gp_off[ngp] = first.off;
-            ++ngp;
+        FoldState r = {-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+        int cur = -1, first_t0 = 0;
+        SlotMeta last = meta[0];
+        auto close = [&]() {
+            if (cur < 0) return;
+            const bool whole = first_t0 == 0 && last.t1 == last.len;
+            fold_store<kOut, D>(P, r, row, dq, whole, cur, j,
+                                (static_cast<int64_t>(wg) * 2 + (first_t0 > 0 ? 0 : 1)) * P.R);
+        };
+#pragma unroll
+        for (int e = 0; e < kSlots; ++e) {
+            if (meta[e].b >= 0) {
+                if (meta[e].b != cur) {
+                    close();
+                    cur = meta[e].b;
+                    first_t0 = meta[e].t0;
+                    r = FoldState{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+                }
+                fold_in(r, sml[e], so[e]);
+                last = meta[e];
+            }
         }
+        close();
     }
 
     // ---- tree reduction of the group-level pieces across workgroups (32-bit
@@ -857,8 +887,11 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(DecodeParams P) {
     const int64_t chunk_g = chunk * kWavesPerBlock;
     const int level_stride = 2 * (P.num_chunks / kWavesPerBlock);   // counters per level
     for (int q = 0; q < ngp; ++q) {
-        const int ca = static_cast<int>(div_nonneg(gp_off[q], chunk_g));
-        const int cb = static_cast<int>(div_nonneg(gp_off[q] + gp_len[q] - 1, chunk_g));
+        const int gpb = q == 0 ? gp_b0 : gp_b1;
+        const int64_t gpoff = q == 0 ? gp_off0 : gp_off1;
+        const int gplen = q == 0 ? gp_len0 : gp_len1;
+        const int ca = static_cast<int>(div_nonneg(gpoff, chunk_g));
+        const int cb = static_cast<int>(div_nonneg(gpoff + gplen - 1, chunk_g));
         int nprev = cb - ca + 1;              // nodes at the level below (pieces at first)
         int idx = cg - ca;                    // this workgroup's node at that level
         int sl = 0;                           // log2 of the pieces per node at that level
@@ -889,7 +922,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(DecodeParams P) {
                     const int p = (first + i) << sl;
                     return static_cast<int64_t>((((ca + p) * P.h_kv + j) * 2 + (p == 0 ? 1 : 0)) * P.R);
                 };
-                fold_children<kOut, D>(P, s_comb, child, nchild, ncur == 1, gp_b[q], j,
+                fold_children<kOut, D>(P, s_comb, child, nchild, ncur == 1, gpb, j,
                                        static_cast<int64_t>(st0) * P.R);
             }
             if (ncur == 1) break;

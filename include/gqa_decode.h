@@ -122,7 +122,7 @@ int gqa_decode_f16(const void *q, const void *k, const void *v, void *o,
  *             spans several ranges are merged by a second kernel.  Rounded down to
  *             a multiple of h_kv (at least h_kv).  0 = automatic (compute units x
  *             min(resident wavefronts per compute unit, 4)).  Range: 0..2^24.
- * min_chunk   Smallest range in key rows; 0 = automatic.  Range: 0..2^30.
+ * min_chunk   Smallest range in key rows; 0 = automatic (64).  Range: 0..2^30.
  *             min_chunk = 1024 with a large num_chunks reproduces the page's
  *             1024-key tiles as the split granularity.
  * workspace   Device scratch for the partial triples, at least
@@ -149,9 +149,10 @@ int gqa_decode_f16(const void *q, const void *k, const void *v, void *o,
  *             nodes are folded by the last workgroup to arrive (device-scope
  *             atomic counters), in an order fixed by the tree, so results are the
  *             same from run to run.  AUTO chooses FUSED for calls of at most 16
- *             (sequence, kv head) units, where the second launch's latency is a
- *             large part of the step, unless num_chunks needs more counters than
- *             the reserve holds.  The fused merge uses levels x num_chunks / 2
+ *             (sequence, kv head) units whose max_seq_len hint is at most 4 x
+ *             min_chunk keys (every sequence then meets at most one other
+ *             workgroup), where the second launch is a large part of the step,
+ *             unless num_chunks needs more counters than the reserve holds.  The fused merge uses levels x num_chunks / 2
  *             counters (GQA_DECODE_COUNTER_BYTES / 4 at most): FUSED lowers
  *             num_chunks until they fit, and returns GQA_ERR_ARG only when even
  *             4 * h_kv wavefronts need more (h_kv above 8,192).
@@ -188,6 +189,10 @@ typedef struct gqa_decode_args {
      * tokens; a token that sees no key gives 0).  G * t_q must not exceed 64. */
     int32_t t_q;
     int32_t merge;  /* GQA_MERGE_*, see above */
+    /* Optional hint: no sequence is longer than max_seq_len keys (0 = unknown).
+     * Used only by the automatic merge choice; the kernels read the lengths from
+     * seq_lens, and a wrong hint changes the speed, never the result. */
+    int32_t max_seq_len;
 } gqa_decode_args;
 
 /* gqa_decode_ex -- the operation with every field of `args` (see above). */

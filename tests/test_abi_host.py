@@ -113,8 +113,8 @@ def test_more_than_16_rows_plan(lib):
     assert st == B.GQA_OK and p.num_chunks == 1024 and p.split_blocks == 256
     st, p = B.gqa_decode_make_plan(_args(h_q=48, h_kv=1, t_q=1, num_chunks=11, merge=B.GQA_MERGE_KERNEL), 256, 4)
     assert st == B.GQA_OK and p.num_chunks == 11 and not p.fused              # 48 rows
-    st, p = B.gqa_decode_make_plan(_args(h_q=48, h_kv=1, t_q=1, num_chunks=11), 256, 4)
-    assert st == B.GQA_OK and p.num_chunks == 8 and p.fused                   # 4 units: fused, 2 workgroups
+    st, p = B.gqa_decode_make_plan(_args(h_q=48, h_kv=1, t_q=1, num_chunks=11, max_seq_len=200), 256, 4)
+    assert st == B.GQA_OK and p.num_chunks == 8 and p.fused                   # 4 units, short: fused
     st, p64 = B.gqa_decode_make_plan(_args(h_q=64, h_kv=1, num_chunks=64), 256, 4)
     st, p16 = B.gqa_decode_make_plan(_args(h_q=16, h_kv=1, num_chunks=64), 256, 4)
     C = B.GQA_DECODE_COUNTER_BYTES
@@ -209,7 +209,7 @@ def test_error_message_is_cleared_on_success(lib):
 def test_struct_mirrors_match_header_sizes(lib):
     # gqa_decode_args: 5 pointers, 4 int32 + float, 4 more int32, pointer, size_t, pointer,
     # 2 event pointers, t_q and merge
-    assert ctypes.sizeof(B.GqaArgs) == 5 * 8 + 4 * 4 + 4 + 4 * 4 + 4 + 8 + 8 + 8 + 2 * 8 + 4 + 4
+    assert ctypes.sizeof(B.GqaArgs) == 5 * 8 + 4 * 4 + 4 + 4 * 4 + 4 + 8 + 8 + 8 + 2 * 8 + 4 + 4 + 4 + 4
     # gqa_decode_plan: 6 int32, size_t, 3 int32 (+4 padding)
     assert ctypes.sizeof(B.GqaPlan) == 6 * 4 + 8 + 3 * 4 + 4
 
@@ -334,25 +334,34 @@ def test_fused_merge_plan(lib):
     units; whole workgroups of 4 ranges of one kv head (num_chunks a multiple of
     4 h_kv); fan-in from the fold volume (K R d 4 bytes <= 64 KiB, 2..64); tree
     levels from the range groups; the counters' reserve bounds its size."""
-    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=32, h_kv=8), 256, 4)      # 8 units
+    # automatic: fused only with a max_seq_len hint within 4 x min_chunk (64) keys
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=32, h_kv=8), 256, 4)      # 8 units, no hint
+    assert st == B.GQA_OK and p.fused == 0 and p.min_chunk == 64
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=32, h_kv=8, max_seq_len=257), 256, 4)
+    assert st == B.GQA_OK and p.fused == 0
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=32, h_kv=8, max_seq_len=256), 256, 4)
     assert st == B.GQA_OK and p.fused == 1 and p.num_chunks == 1024 and p.split_blocks == 256
     assert (p.merge_blocks, p.merge_threads) == (0, 0)
     assert p.fold_fanin == 32 and p.fold_levels == 1                            # R 4: 2 KiB triples; 32 groups
-    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=8, h_kv=1), 256, 4)        # R 8, 256 range groups
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=32, h_kv=8, max_seq_len=1000, min_chunk=250), 256, 4)
+    assert p.fused
+    assert _validate(max_seq_len=-1) == B.GQA_ERR_ARG
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=8, h_kv=1, merge=B.GQA_MERGE_FUSED), 256, 4)   # R 8
     assert p.fused and p.fold_fanin == 16 and p.fold_levels == 2
-    st, p = B.gqa_decode_make_plan(_args(batch=4, h_q=32, h_kv=8), 256, 4)       # 32 units: two kernels
+    st, p = B.gqa_decode_make_plan(_args(batch=4, h_q=32, h_kv=8, max_seq_len=100), 256, 4)   # 32 units
     assert st == B.GQA_OK and p.fused == 0 and p.merge_blocks > 0
     st, p = B.gqa_decode_make_plan(_args(batch=4, h_q=32, h_kv=8, merge=B.GQA_MERGE_FUSED), 256, 4)
     assert st == B.GQA_OK and p.fused == 1
-    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=64, h_kv=1, t_q=1, d_head=128), 256, 4)   # R 64
+    F = B.GQA_MERGE_FUSED
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=64, h_kv=1, t_q=1, d_head=128, merge=F), 256, 4)   # R 64
     assert p.fused and p.fold_fanin == 2 and p.fold_levels == 8
-    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=1, h_kv=1, d_head=64), 256, 4)            # R 1, d 64
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=1, h_kv=1, d_head=64, merge=F), 256, 4)            # R 1, d 64
     assert p.fused and p.fold_fanin == 64
     for nc, want in [(1, 32), (33, 32), (100, 96), (4096, 4096)]:               # multiples of 4 h_kv = 32
-        st, p = B.gqa_decode_make_plan(_args(batch=1, num_chunks=nc), 256, 4)
+        st, p = B.gqa_decode_make_plan(_args(batch=1, num_chunks=nc, merge=F), 256, 4)
         assert st == B.GQA_OK and p.fused and p.num_chunks == want, (nc, p.num_chunks)
     # counters: levels x 2 x num_chunks / 4 within 64 KiB / 4 words
-    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=8, h_kv=1, num_chunks=1 << 15), 256, 4)
+    st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=8, h_kv=1, num_chunks=1 << 15, max_seq_len=100), 256, 4)
     assert st == B.GQA_OK and p.fused == 0 and p.num_chunks == 1 << 15   # automatic: too many counters
     st, p = B.gqa_decode_make_plan(_args(batch=1, h_q=8, h_kv=1, num_chunks=1 << 15, merge=B.GQA_MERGE_FUSED), 256, 4)
     assert st == B.GQA_OK and p.fused == 1 and p.num_chunks < 1 << 15            # forced: fewer wavefronts
@@ -375,5 +384,6 @@ def test_fused_merge_plan(lib):
 
 
 def test_args_struct_layout(lib):
-    assert ctypes.sizeof(B.GqaArgs) == 128 and B.GqaArgs.t_q.offset == 120 and B.GqaArgs.merge.offset == 124
+    assert ctypes.sizeof(B.GqaArgs) == 136 and B.GqaArgs.t_q.offset == 120 and B.GqaArgs.merge.offset == 124
+    assert B.GqaArgs.max_seq_len.offset == 128
     assert ctypes.sizeof(B.GqaPlan) == 48 and B.GqaPlan.fused.offset == 32

@@ -50,3 +50,15 @@ def test_traffic_follows_the_kernel_source_hash(tmp_path):
     assert value is None and "changed" in note
     b.TRAFFIC_FILE = str(tmp_path / "missing.md")
     assert b.committed_traffic()[0] is None
+
+
+def test_timed_steps_split_into_repetitions():
+    """The timed region is exactly K steps, split into at most 5 repetitions whose
+    median is reported; fewer steps than repetitions give one step each."""
+    bench = _bench_module()
+    assert bench.split_reps(20) == [4, 4, 4, 4, 4]
+    assert bench.split_reps(7) == [2, 2, 1, 1, 1] and sum(bench.split_reps(7)) == 7
+    assert bench.split_reps(3) == [1, 1, 1]
+    assert bench.split_reps(1) == [1]
+    assert bench.median([3.0, 1.0, 2.0]) == 2.0
+    assert bench.median([4.0, 1.0, 2.0, 3.0]) == 2.5
