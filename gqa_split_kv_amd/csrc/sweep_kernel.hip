@@ -226,17 +226,103 @@ struct Packed16Step {
         const uint4 blo = make_uint4(plo[0], plo[1], plo[2], plo[3]);
 #pragma unroll
         for (int c = 0; c < VEC; ++c) {
-            // A operand of column c: element i = V[key 8kg + i][d = VEC*m + c].
-            uint32_t a[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t x = B.v[2 * w][c >> 1];
-                const uint32_t y = B.v[2 * w + 1][c >> 1];
-                a[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-            }
-            const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
+            const uint4 av = v_operand(B, c);
             acc[c] = mfma16(av, bhi, acc[c]);
             acc[c] = mfma16(av, blo, acc[c]);
+        }
+    }
+    // A operand of P V column c: element i = V[key 8kg + i][d = VEC*m + c].
+    __device__ __forceinline__ static uint4 v_operand(const Buf &B, int c) {
+        uint32_t a[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t x = B.v[2 * w][c >> 1];
+            const uint32_t y = B.v[2 * w + 1][c >> 1];
+            a[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+        }
+        return make_uint4(a[0], a[1], a[2], a[3]);
+    }
+    // The step for kNT 16-row tiles on one load of the keys, in three phases:
+    // every tile's scores (independent MFMA chains) and new row maxima; one
+    // wave-wide test whether any maximum rose (the accumulators are rescaled
+    // only then: elsewhere the factor is exactly 1, or 0 on a still-empty state
+    // whose accumulators are 0, so skipping the rescale changes no bit); then
+    // every tile's weights, split P and products, with each V column's operand
+    // repacked once for all tiles.
+    template <int kNT>
+    __device__ __forceinline__ static void compute_tiles(const Buf &B, const uint4 (&qop)[kNT][NKP], int lo,
+                                                         const int (&hi)[kNT], int kg, float sl2,
+                                                         float (&m_run)[kNT], float (&l_run)[kNT],
+                                                         f32x4_t (&acc)[kNT][VEC]) {
+        constexpr float kOff = kHalf ? 15.f : 0.f;
+        float sv[kNT][8], m_ref[kNT], alpha[kNT];
+        bool moved = false;
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < NKP; ++p) sacc = mfma16(B.k[b][p], qop[nt][p], sacc);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int key = 8 * kg + 4 * b + q;
+                    sv[nt][4 * b + q] = (key >= lo && key < hi[nt]) ? sacc[q] * sl2 : -INFINITY;
+                }
+            }
+            float mx = sv[nt][0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[nt][i]);
+            const float m_new = fmaxf(m_run[nt], max_over_rows(mx));
+            moved |= m_new != m_run[nt];
+            // A row that has seen no key yet keeps the identity: exponentiate against 0.
+            m_ref[nt] = m_new == -INFINITY ? 0.f : m_new;
+            alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - m_ref[nt]);   // 0 while the state is empty
+            m_run[nt] = m_new;
+        }
+        if (__ballot(moved) != 0) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) acc[nt][c] *= alpha[nt];
+        }
+        uint4 bhi[kNT], blo[kNT];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sv[nt][i] = __builtin_amdgcn_exp2f(sv[nt][i] - m_ref[nt] + kOff);
+                sum += sv[nt][i];
+            }
+            l_run[nt] = l_run[nt] * alpha[nt] + sum;
+            uint32_t ph[4], pl[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const f32x2_t pw = {sv[nt][2 * w], sv[nt][2 * w + 1]};
+                if constexpr (kHalf) {
+                    const f16x2_t h = __builtin_convertvector(pw, f16x2_t);
+                    const f32x2_t hf = __builtin_convertvector(h, f32x2_t);
+                    ph[w] = __builtin_bit_cast(uint32_t, h);
+                    pl[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw - hf, f16x2_t));
+                } else {
+                    const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw, bf16x2_t));
+                    const f32x2_t r = {pw[0] - __uint_as_float(hb << 16), pw[1] - __uint_as_float(hb & 0xffff0000u)};
+                    ph[w] = hb;
+                    pl[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+                }
+            }
+            bhi[nt] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+            blo[nt] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+        }
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+            const uint4 av = v_operand(B, c);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                acc[nt][c] = mfma16(av, bhi[nt], acc[nt][c]);
+                acc[nt][c] = mfma16(av, blo[nt], acc[nt][c]);
+            }
         }
     }
 };
@@ -424,10 +510,17 @@ __device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j
             load_step(buf[(ub + kDepth - 1) % kDepth], st + kDepth - 1);
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
             const int hi = min(S::kKeys, span - st * S::kKeys);
+            if constexpr (kIn != kF32 && kNT > 1) {
+                int his[kNT];
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt)
-                S::compute(buf[ub], qop[nt], st == 0 ? lead : 0, min(hi, cap[nt] - st * S::kKeys), kg, sl2,
-                           m_run[nt], l_run[nt], acc[nt]);
+                for (int nt = 0; nt < kNT; ++nt) his[nt] = min(hi, cap[nt] - st * S::kKeys);
+                S::template compute_tiles<kNT>(buf[ub], qop, st == 0 ? lead : 0, his, kg, sl2, m_run, l_run, acc);
+            } else {
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt)
+                    S::compute(buf[ub], qop[nt], st == 0 ? lead : 0, min(hi, cap[nt] - st * S::kKeys), kg, sl2,
+                               m_run[nt], l_run[nt], acc[nt]);
+            }
             if (++st == nstep) goto swept;
         }
     }
@@ -952,13 +1045,15 @@ void launch_iot(const DecodeParams &P, int D, int blocks, bool fused, hipStream_
 }
 
 // 16-row tiles per wavefront: 1 up to 16 rows per kv head (G * t_q), 2 up to 32,
-// 4 up to 64 (the keys of a step are loaded once for all of them).
+// 3 up to 48, 4 up to 64 (the keys of a step are loaded once for all of them).
 template <int kIn, int kOut>
 hipError_t launch_io(const DecodeParams &P, int D, int blocks, bool fused, hipStream_t stream) {
     if (P.R <= 16)
         launch_iot<kIn, kOut, 1>(P, D, blocks, fused, stream);
     else if (P.R <= 32)
         launch_iot<kIn, kOut, 2>(P, D, blocks, fused, stream);
+    else if (P.R <= 48)
+        launch_iot<kIn, kOut, 3>(P, D, blocks, fused, stream);
     else
         launch_iot<kIn, kOut, 4>(P, D, blocks, fused, stream);
     return hipGetLastError();
