@@ -53,7 +53,8 @@ METRIC = "µs/decode step + K/V HBM GB/s (% of peak), GQA h_q=64 h_kv=8 d=128 @3
 # min_chunk and the workspace layout set the traffic per launch), so its counter
 # data is tied to them.
 KERNEL_SRCS = [os.path.join(ROOT, "gqa_split_kv_amd", "csrc", f)
-               for f in ("sweep_kernel.hip", "device_common.h", "kernels.h", "host.h", "plan.cpp", "api.cpp")]
+               for f in ("sweep_kernel.hip", "merge_kernel.hip", "device_common.h", "kernels.h", "host.h", "plan.cpp",
+                         "api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_kernel_70b_ragged_traffic.md")
 
 
@@ -450,6 +451,10 @@ def main():
                     help="timed steps of each other decode form (fp16, t_q = 2) on the same batch; 0 skips")
     ap.add_argument("--workload-steps", type=int, default=50,
                     help="timed steps of the decode on each other named workload; 0 skips")
+    ap.add_argument("--no-step-events", action="store_true",
+                    help="record no HIP events around each sweep launch in the timed loop (for kernel traces, "
+                         "whose gaps between kernels the event records would lengthen); the roofline's kernel "
+                         "time is then not measured")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (profiler calibration)")
     args = ap.parse_args()
@@ -502,7 +507,7 @@ def main():
     # the library calls (at a few microseconds per step the Python that fills a
     # block would otherwise be what is measured).
     warm_args = [step_args(i) for i in range(args.rotate)]
-    timed_args = [step_args(i, ev_steps[i]) for i in range(args.steps)]
+    timed_args = [step_args(i, None if args.no_step_events else ev_steps[i]) for i in range(args.steps)]
     log("warmup %d steps" % args.warmup)
     for i in range(args.warmup):
         gqa.gqa_decode_ex(warm_args[i % args.rotate])
@@ -523,7 +528,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     rep_ms = [hip.ms(e0, e1) / n for (e0, e1), n in zip(ev_reps, reps)]
-    sweep_each = [hip.ms(a, b) for a, b in ev_steps]
+    sweep_each = [hip.ms(a, b) for a, b in ev_steps] if not args.no_step_events else [float("nan")]
     sweep_ms = median(sweep_each)
     ms_per_step = median(rep_ms)
     value = kv_bytes / (ms_per_step / 1e3) / 1e9

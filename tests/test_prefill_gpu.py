@@ -250,15 +250,20 @@ def test_prefill_empty_and_single_token_sequences():
 
 def test_prefill_32k_single_kv_group_sampled_rows():
     """The long-context prefill panel at full size: 32768 tokens, h_q 8, h_kv 1,
-    d 128, bf16; sampled tokens (tile edges, both ends, random) against the oracle
-    one token at a time, plus finiteness of every output."""
+    d 128, bf16; one random token in every 128-token span (256 tokens), the edges
+    of the kernel's 32-token tiles and 64-key steps at both ends and in the middle,
+    against the oracle one token at a time, in both P V modes, plus finiteness of
+    every output."""
     import torch
     w = PREFILL_32K
     c = host_prefill_case(w.batch, w.h_q, w.h_kv, w.d, w.seq_lens(), w.dtype, seed=w.seed)
     q, k, v, sl = upload(c)
     rng = np.random.default_rng(5)
-    rows = sorted(set([0, 1, 31, 32, 33, 1023, 1024, 4095, 16383, 16384, 32735, 32736, 32766, 32767] +
-                      list(rng.integers(0, 32768, size=18))))
+    edges = [0, 1, 31, 32, 33, 63, 64, 65, 1023, 1024, 4095, 16383, 16384, 16385, 32703, 32704, 32735, 32736,
+             32766, 32767]
+    spans = [128 * i + int(rng.integers(0, 128)) for i in range(32768 // 128)]
+    rows = sorted(set(edges + spans))
+    assert len(rows) >= 256
     _say("oracle on", len(rows), "sampled tokens")
     ref = oracle.gqa_prefill_rows_f64(c.q, c.k, c.v, c.seq_lens, c.scale, rows)
     for sp in (0, 1):
