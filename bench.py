@@ -369,11 +369,13 @@ def prefill_flops(seq_lens, h_q: int, d: int) -> float:
     return float(sum(4.0 * d * h_q * S * (S + 1) / 2 for S in seq_lens))
 
 
-def prefill_row(hip, stream, steps: int, with_oracle: bool, warmup: int = 10):
+def prefill_row(hip, stream, steps: int, with_oracle: bool, warmup: int = 10, group_sizes=(16, 32, 64)):
     """Times gqa_prefill_ex on the 32K-token single-KV-group workload: `warmup`
     untimed calls per mode first (the matrix-core clocks ramp up over the first
     few milliseconds of sustained work), then `steps` timed calls in REPS
-    repetitions (median and spread of the per-call time)."""
+    repetitions (median and spread of the per-call time).  Then the default mode
+    at 16, 32 and 64 query heads per kv head on the same length (3 timed calls
+    each, after 2 untimed)."""
     import torch
     import gqa_split_kv_amd as gqa
     from gqa_split_kv_amd.inputs import PREFILL_32K, device_prefill_case
@@ -413,9 +415,39 @@ def prefill_row(hip, stream, steps: int, with_oracle: bool, warmup: int = 10):
             row["roofline"] = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tf, 1),
                                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "kernel_us": round(ms * 1e3, 1)}
+    del c, out
+    # Wider groups on the same sequence length (one kv head): 256 / G tokens per
+    # 256-row tile, so more tiles, each sweeping its own key prefix.
+    row["group_sizes"] = []
+    for G in group_sizes:
+        cg = device_prefill_case(1, G, 1, w.d, [w.seq_len], w.dtype, seed=w.seed + G)
+        og = torch.empty_like(cg.q)
+        fg = prefill_flops(cg.seq_lens_host, G, w.d)
+        a = gqa.make_prefill_args(cg.q, cg.k, cg.v, og, cg.seq_lens, 1, G, 1, w.d, cg.scale,
+                                  gqa.GQA_DTYPE_BF16, gqa.GQA_DTYPE_BF16, 0, stream, 0,
+                                  total_tokens=cg.q.shape[0])
+        for _ in range(2):
+            gqa.gqa_prefill_ex(a)
+        torch.cuda.synchronize()
+        ev = (hip.event(), hip.event())
+        hip.record(ev[0], stream)
+        for _ in range(3):
+            gqa.gqa_prefill_ex(a)
+        hip.record(ev[1], stream)
+        hip.sync(ev[1])
+        ms = hip.ms(*ev) / 3
+        hip.destroy(ev[0])
+        hip.destroy(ev[1])
+        tf = fg / (ms / 1e3) / 1e12
+        row["group_sizes"].append({"G": G, "h_q": G, "h_kv": 1, "seq_len": w.seq_len, "tokens_per_tile": 256 // G,
+                                   "ms_per_call": round(ms, 4), "tflops": round(tf, 1),
+                                   "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        log("prefill G %d: %.3f ms per call, %.1f TFLOP/s" % (G, ms, tf))
+        del cg, og
     if with_oracle:
         import numpy as np
         import oracle
+        c = device_prefill_case(w.batch, w.h_q, w.h_kv, w.d, w.seq_lens(), w.dtype, seed=w.seed)
         from gqa_split_kv_amd.inputs import to_host_bits
         qh, kh, vh = to_host_bits(c.q), to_host_bits(c.k), to_host_bits(c.v)
         S = int(c.seq_lens_host[0])

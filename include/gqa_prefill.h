@@ -31,6 +31,14 @@
  * 4-byte aligned.  Every output row is written by exactly one workgroup (no
  * cross-workgroup reduction).
  *
+ * Cost of wide groups: a tile sweeps its keys in 64-key steps of 256 rows x 64
+ * keys whatever G is, so K/V staging per step, and per flop, does not grow with G;
+ * a G of 32 or 64 only makes more, shorter tiles (8 or 4 tokens), each staging
+ * its own key prefix, and the work grows with h_q like the flops.  Measured on
+ * one 32768-token sequence, one kv head, d_head 128: G 8, 16, 32 and 64 all run
+ * at 1.23-1.25 PFLOP/s (1.79, 3.55, 7.08, 14.13 ms per call).  G not dividing 256
+ * leaves 256 mod G rows of each tile idle.
+ *
  * Workspace: the default precision mode (split_pv = 0) with total_tokens > 0
  * uses one -- V transposed and in fp16, 64 keys of one sequence at a time
  * (nvb = ceil(total_tokens / 64) + batch blocks of d_head x 64 values per kv

@@ -277,6 +277,33 @@ def test_prefill_32k_single_kv_group_sampled_rows():
         _check(o16.index_select(0, idx), ref, "32K bf16 rows split=%d" % sp, sp)
 
 
+@pytest.mark.parametrize("G", [32, 64])
+def test_prefill_wide_groups_long_sequence(G):
+    """32 and 64 query heads per kv head (8 and 4 tokens per 256-row tile) over a
+    4096-token sequence: one random token in every 64-token span, the tile and
+    64-key step edges, against the oracle one token at a time, in both P V modes."""
+    import torch
+    S = 4096
+    c = host_prefill_case(1, G, 1, 128, [S], "bf16", seed=40 + G)
+    q, k, v, sl = upload(c)
+    tt = 256 // G
+    rng = np.random.default_rng(G)
+    edges = [0, 1, tt - 1, tt, tt + 1, 63, 64, 65, 2047, 2048, S - tt - 1, S - tt, S - 65, S - 64, S - 1]
+    spans = [64 * i + int(rng.integers(0, 64)) for i in range(S // 64)]
+    rows = sorted(set(edges + spans))
+    _say("G", G, ": oracle on", len(rows), "sampled tokens")
+    ref = oracle.gqa_prefill_rows_f64(c.q, c.k, c.v, c.seq_lens, c.scale, rows)
+    idx = None
+    for sp in (0, 1):
+        o32 = _run(q, k, v, sl, c.scale, torch.float32, split_pv=sp)
+        assert torch.isfinite(o32).all().item()
+        idx = torch.tensor(rows, device=o32.device)
+        e, r = _check(o32.index_select(0, idx), ref, "G %d fp32 rows split=%d" % (G, sp), sp)
+        _say("  split_pv %d: fp32 max|err| %.3g rel-L2 %.3g" % (sp, e, r))
+        o16 = _run(q, k, v, sl, c.scale, split_pv=sp)
+        _check(o16.index_select(0, idx), ref, "G %d bf16 rows split=%d" % (G, sp), sp)
+
+
 def test_prefill_invalid_arguments_leave_output_untouched():
     import torch
     c = host_prefill_case(2, 8, 2, 64, [5, 7], "bf16", seed=25)
