@@ -238,7 +238,8 @@ struct Packed16Step {
         for (int w = 0; w < 4; ++w) {
             const uint32_t x = B.v[2 * w][c >> 1];
             const uint32_t y = B.v[2 * w + 1][c >> 1];
-            a[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+            // One byte permute per word: bytes (x0, x1, y0, y1) or (x2, x3, y2, y3).
+            a[w] = __builtin_amdgcn_perm(y, x, (c & 1) ? 0x07060302u : 0x05040100u);
         }
         return make_uint4(a[0], a[1], a[2], a[3]);
     }
@@ -248,8 +249,12 @@ struct Packed16Step {
     // only then: elsewhere the factor is exactly 1, or 0 on a still-empty state
     // whose accumulators are 0, so skipping the rescale changes no bit); then
     // every tile's weights, split P and products, with each V column's operand
-    // repacked once for all tiles.
-    template <int kNT>
+    // repacked once for all tiles.  sl2 > 0 (a negative scale is moved into q).
+    //   kMask   scores outside [lo, hi[nt]) are masked; the scores are scaled
+    //           before the maxima and the exponent is (s sl2 - m) + offset.
+    //           Otherwise every key is visible: maxima of the raw scores, then
+    //           scaled, and the exponent one fused s sl2 + (offset - m).
+    template <int kNT, bool kMask>
     __device__ __forceinline__ static void compute_tiles(const Buf &B, const uint4 (&qop)[kNT][NKP], int lo,
                                                          const int (&hi)[kNT], int kg, float sl2,
                                                          float (&m_run)[kNT], float (&l_run)[kNT],
@@ -267,13 +272,17 @@ struct Packed16Step {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int key = 8 * kg + 4 * b + q;
-                    sv[nt][4 * b + q] = (key >= lo && key < hi[nt]) ? sacc[q] * sl2 : -INFINITY;
+                    if constexpr (kMask)
+                        sv[nt][4 * b + q] = (key >= lo && key < hi[nt]) ? sacc[q] * sl2 : -INFINITY;
+                    else
+                        sv[nt][4 * b + q] = sacc[q];
                 }
             }
             float mx = sv[nt][0];
 #pragma unroll
             for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[nt][i]);
-            const float m_new = fmaxf(m_run[nt], max_over_rows(mx));
+            // sl2 > 0: the scaled maximum is the maximum of the raw scores, scaled.
+            const float m_new = fmaxf(m_run[nt], kMask ? max_over_rows(mx) : max_over_rows(mx) * sl2);
             moved |= m_new != m_run[nt];
             // A row that has seen no key yet keeps the identity: exponentiate against 0.
             m_ref[nt] = m_new == -INFINITY ? 0.f : m_new;
@@ -290,9 +299,13 @@ struct Packed16Step {
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
             float sum = 0.f;
+            const float nmu = kOff - m_ref[nt];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                sv[nt][i] = __builtin_amdgcn_exp2f(sv[nt][i] - m_ref[nt] + kOff);
+                if constexpr (kMask)
+                    sv[nt][i] = __builtin_amdgcn_exp2f(sv[nt][i] - m_ref[nt] + kOff);
+                else
+                    sv[nt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][i], sl2, nmu));
                 sum += sv[nt][i];
             }
             l_run[nt] = l_run[nt] * alpha[nt] + sum;
@@ -461,16 +474,30 @@ __device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j
 
     // Q operand: query row (t, g), bytes [64p + 16kg, +16) of it (zero for unused rows):
     // the same d permutation as the K rows, so the contraction covers every d once.
+    // A negative scale negates q instead (exact), so that the steps scale by a
+    // positive factor and the largest scaled score is the largest raw one.
+    const uint32_t qflip = P.scale_log2 < 0.f ? (kIn == kF32 ? 0x80000000u : 0x80008000u) : 0u;
     uint4 qop[kNT][S::NKP];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
         const uint8_t *qrow = P.q + qo_row[nt] * S::ROWB + 16 * kg;
 #pragma unroll
         for (int p = 0; p < S::NKP; ++p) {
-            qop[nt][p] = *reinterpret_cast<const uint4 *>(qrow + 64 * p);
-            if (!row_ok[nt]) qop[nt][p] = make_uint4(0, 0, 0, 0);
+            uint4 x = *reinterpret_cast<const uint4 *>(qrow + 64 * p);
+            x.x ^= qflip;
+            x.y ^= qflip;
+            x.z ^= qflip;
+            x.w ^= qflip;
+            qop[nt][p] = row_ok[nt] ? x : make_uint4(0, 0, 0, 0);
         }
     }
+    // Keys visible to every row of the wavefront: below the smallest causal limit.
+    int capmin = cap[0];
+#pragma unroll
+    for (int nt = 1; nt < kNT; ++nt) capmin = min(capmin, cap[nt]);
+#pragma unroll
+    for (int sh = 1; sh < kWave; sh <<= 1) capmin = min(capmin, __shfl_xor(capmin, sh));
+    capmin = uniform32(capmin);
 
     f32x4_t acc[kNT][VEC];
     float m_run[kNT], l_run[kNT];
@@ -485,7 +512,8 @@ __device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j
     const int64_t row0 = abase * P.h_kv + j;
     const uint8_t *kbase = P.k + row0 * S::ROWB;
     const uint8_t *vbase = P.v + row0 * S::ROWB;
-    const float sl2 = P.scale_log2;
+    // |scale| log2(e), kept above 0 so that a masked (-inf) score stays -inf.
+    const float sl2 = fmaxf(fabsf(P.scale_log2), 1.17549435e-38f);
     const typename S::Lanes lo(rowstride);
 
     // A step at or past nstep gets an empty range: its loads return zeros without
@@ -514,7 +542,13 @@ __device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j
                 int his[kNT];
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) his[nt] = min(hi, cap[nt] - st * S::kKeys);
-                S::template compute_tiles<kNT>(buf[ub], qop, st == 0 ? lead : 0, his, kg, sl2, m_run, l_run, acc);
+                // A step whose keys every row sees needs no mask (taken with four
+                // tiles, where the masking is a measurable share of the vector work).
+                if (kNT >= 4 && (st > 0 || lead == 0) && hi == S::kKeys && capmin - st * S::kKeys >= S::kKeys)
+                    S::template compute_tiles<kNT, false>(buf[ub], qop, 0, his, kg, sl2, m_run, l_run, acc);
+                else
+                    S::template compute_tiles<kNT, true>(buf[ub], qop, st == 0 ? lead : 0, his, kg, sl2, m_run, l_run,
+                                                         acc);
             } else {
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt)

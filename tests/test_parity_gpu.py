@@ -337,6 +337,25 @@ def test_scale_one_is_the_pages_unscaled_kernel():
     compare(o, ref, "scale 1")
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0, -1.3])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_negative_and_zero_scale(scale, dtype):
+    """A negative scale (the kernels negate q and scale by |scale|) and scale 0
+    (every visible key weighs the same), with one to four 16-row tiles per
+    wavefront: 8, 32, 48 and 64 rows per kv head (G 8 with 1, 4, 6 and 8 query
+    tokens), over sequences long enough for steps with no masked key."""
+    import torch
+    lens = [300, 0, 1, 129, 2000, 65]
+    for t_q in (1, 4, 6, 8):
+        c = host_case(len(lens), 16, 2, 128, lens, dtype, seed=500 + t_q, scale=scale, t_q=t_q)
+        ref = oracle_of(c)
+        q, k, v, sl = upload(c)
+        for nc, mc in [(0, 0), (9, 1)]:
+            _say("scale", scale, dtype, "t_q", t_q, "nc", nc)
+            o = run_hip(q, k, v, sl, c.scale, out_dtype=torch.float32, num_chunks=nc, min_chunk=mc)
+            compare(o, ref, "scale=%g %s t_q=%d nc=%d" % (scale, dtype, t_q, nc))
+
+
 # ------------------------------------------------------------------ boundary behaviour
 
 
