@@ -667,8 +667,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel(DecodeParams P) {
 //   * Group-level pieces are reduced by a tree of fixed fan-in K over the pieces
 //     of a sequence in token order: a node's children are K consecutive nodes of
 //     the level below.  Every workgroup that finishes a child increments the
-//     node's counter (a vector atomic at device scope, with release and acquire
-//     ordering), and the one that completes the count -- the last arriver --
+//     node's counter (a relaxed vector atomic at device scope, issued after the
+//     child's device-coherent stores have completed; the last arriver reads the
+//     children with device-coherent loads after the increment returned), and the
+//     one that completes the count -- the last arriver --
 //     folds the children in ascending order, stores the node in its first
 //     child's place and goes up one level; at the root it writes o.  The fold
 //     order is fixed by the tree, not by arrival, so results are bit-identical
