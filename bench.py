@@ -203,11 +203,12 @@ def cpu_baseline(d, w, budget_s: float):
 
 def decode_variants(hip, stream, w, d, kv_bytes: int, steps: int):
     """The decode path's other input forms on the same batch and K/V bytes:
-    fp16 q/k/v (gqa_decode_f16's kernels, fp16 out) and two or four query tokens
-    per sequence (bf16, t_q = 2: every sequence's last two tokens, causal between
-    them, G * t_q = 16 rows per kv head; t_q = 4: 32 rows, two 16-row tiles per
-    wavefront over one load of the keys).  Each is timed like the headline step,
-    with the sweep kernel's own HIP events."""
+    fp16 q/k/v (gqa_decode_f16's kernels, fp16 out); two, four or eight query
+    tokens per sequence (bf16, t_q = 2: every sequence's last two tokens, causal
+    between them, G * t_q = 16 rows per kv head; t_q = 4: 32 rows, two 16-row
+    tiles per wavefront over one load of the keys; t_q = 8: 64 rows, four tiles);
+    and one token on 64 query heads per kv head (h_q 512, 64 rows).  Each is
+    timed like the headline step, with the sweep kernel's own HIP events."""
     import torch
     import gqa_split_kv_amd as gqa
     from gqa_split_kv_amd.inputs import device_queries

@@ -36,7 +36,7 @@
  *             so a call needs no host synchronisation)
  *
  * Supported: d_head in {64, 128}; G = h_q / h_kv in 1..64 (G * t_q <= 64 rows per kv
- * head, swept as one, two or four 16-row tiles per wavefront over one read of the
+ * head, swept as one to four 16-row tiles per wavefront over one read of the
  * keys); (in, out) dtypes
  * (bf16, bf16), (bf16, f32), (f16, f16), (f16, f32) and (f32, f32).  q, k, v, o must be 16-byte aligned,
  * seq_lens 4-byte aligned.
@@ -119,7 +119,8 @@ int gqa_decode_f16(const void *q, const void *k, const void *v, void *o,
  *             is computed on the device from seq_lens, and each range is swept by
  *             h_kv wavefronts, one per kv head.  A range that holds a whole
  *             sequence writes its o rows directly; the pieces of a sequence that
- *             spans several ranges are merged by a second kernel.  Rounded down to
+ *             spans several ranges are merged by a second kernel, or inside the
+ *             sweep kernel (see `merge`).  Rounded down to
  *             a multiple of h_kv (at least h_kv).  0 = automatic (compute units x
  *             min(resident wavefronts per compute unit, 4)).  Range: 0..2^24.
  * min_chunk   Smallest range in key rows; 0 = automatic (64).  Range: 0..2^30.
@@ -263,8 +264,8 @@ int gqa_decode_make_plan(const gqa_decode_args *args, int32_t num_cus, int32_t w
  * NULL, the validation status of the arguments, or GQA_ERR_HIP when the device
  * query fails; *bytes is written only on GQA_OK.  The size comes back through a
  * pointer rather than as the return value because the query can fail in these
- * ways, and a size_t return would have no value that reads unambiguously as an
- * error (0 is a valid size: a call whose plan needs no partials).
+ * ways, and a size_t return would have to reserve a sentinel size for them, which
+ * callers could mistake for a size.
  */
 int gqa_decode_workspace_bytes(const gqa_decode_args *args, size_t *bytes);
 
