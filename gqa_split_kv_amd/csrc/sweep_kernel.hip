@@ -188,6 +188,17 @@ struct Packed16Step {
 #pragma unroll
         for (int i = 0; i < 8; ++i) load_words<VW>(B.v[i], rv, lo.v[i]);
     }
+    // The K half or the V half of load() alone.
+    __device__ __forceinline__ static void load_k(Buf &B, __amdgpu_buffer_rsrc_t rk, const Lanes &lo) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int p = 0; p < NKP; ++p) B.k[b][p] = load16(rk, lo.k[b] + 64 * p);
+    }
+    __device__ __forceinline__ static void load_v(Buf &B, __amdgpu_buffer_rsrc_t rv, const Lanes &lo) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) load_words<VW>(B.v[i], rv, lo.v[i]);
+    }
     __device__ __forceinline__ static void compute(const Buf &B, const uint4 (&qop)[NKP], int lo, int hi,
                                                    int kg, float sl2, float &m_run, float &l_run,
                                                    f32x4_t (&acc)[VEC]) {
@@ -254,11 +265,13 @@ struct Packed16Step {
     //           before the maxima and the exponent is (s sl2 - m) + offset.
     //           Otherwise every key is visible: maxima of the raw scores, then
     //           scaled, and the exponent one fused s sl2 + (offset - m).
-    template <int kNT, bool kMask>
+    // after_qk() runs once every tile's Q K^T products are issued (the caller
+    // loads the next step's keys there, into the registers B.k leaves free).
+    template <int kNT, bool kMask, class AfterQK>
     __device__ __forceinline__ static void compute_tiles(const Buf &B, const uint4 (&qop)[kNT][NKP], int lo,
                                                          const int (&hi)[kNT], int kg, float sl2,
                                                          float (&m_run)[kNT], float (&l_run)[kNT],
-                                                         f32x4_t (&acc)[kNT][VEC]) {
+                                                         f32x4_t (&acc)[kNT][VEC], AfterQK after_qk) {
         constexpr float kOff = kHalf ? 15.f : 0.f;
         float sv[kNT][8], m_ref[kNT], alpha[kNT];
         bool moved = false;
@@ -278,6 +291,11 @@ struct Packed16Step {
                         sv[nt][4 * b + q] = sacc[q];
                 }
             }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        after_qk();
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
             float mx = sv[nt][0];
 #pragma unroll
             for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[nt][i]);
@@ -516,46 +534,78 @@ __device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j
     const float sl2 = fmaxf(fabsf(P.scale_log2), 1.17549435e-38f);
     const typename S::Lanes lo(rowstride);
 
-    // A step at or past nstep gets an empty range: its loads return zeros without
-    // a memory access (the pipeline's prefetches past the piece cost no round trip).
-    auto load_step = [&](typename S::Buf &B, int st) {
+    // Buffer resource over step st's rows of K (or V); a step at or past nstep
+    // gets an empty range, so its loads return zeros without a memory access
+    // (the prefetches past the piece cost no round trip).
+    auto step_rsrc = [&](const uint8_t *base, int st) {
         const int hi = max(0, min(S::kKeys, span - st * S::kKeys));
         const int64_t boff = hi > 0 ? static_cast<int64_t>(st) * S::kKeys * rowstride : 0;
-        const uint32_t bytes = static_cast<uint32_t>(hi * rowstride);
-        S::load(B, buffer_rsrc(kbase + boff, bytes), buffer_rsrc(vbase + boff, bytes), lo);
+        return buffer_rsrc(base + boff, static_cast<uint32_t>(hi * rowstride));
     };
-
-    // Software pipeline over kDepth register buffers: the loads of the next
-    // kDepth-1 steps are in flight while a step is computed.  Every load is
-    // unconditional: prefetches past the last step read an empty range.
-    typename S::Buf buf[kDepth];
+    if constexpr (kIn != kF32 && kNT > 1) {
+        // Several tiles: one K and one V register buffer, each refilled as soon
+        // as its step has used it -- the next step's keys once the Q K^T
+        // products are issued, its values once the P V products are -- so the
+        // loads of step st+1 overlap the rest of step st with no second buffer
+        // (the registers go to the tiles instead).
+        // Unrolled twice with the K buffer named by parity: in a loop that is not
+        // unrolled the compiler waits for every outstanding load (vmcnt(0)) at
+        // the top of each step, V refill included.
+        typename S::Buf bk[2], bv;
+        S::load_k(bk[0], step_rsrc(kbase, 0), lo);
+        S::load_v(bv, step_rsrc(vbase, 0), lo);
+        int st = 0;
+        while (true) {
 #pragma unroll
-    for (int ub = 0; ub + 1 < kDepth; ++ub) load_step(buf[ub], ub);
-    int st = 0;
-    while (true) {
+            for (int ub = 0; ub < 2; ++ub) {
+                typename S::Buf cb;
 #pragma unroll
-        for (int ub = 0; ub < kDepth; ++ub) {
-            load_step(buf[(ub + kDepth - 1) % kDepth], st + kDepth - 1);
-            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
-            const int hi = min(S::kKeys, span - st * S::kKeys);
-            if constexpr (kIn != kF32 && kNT > 1) {
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int p = 0; p < S::NKP; ++p) cb.k[b][p] = bk[ub].k[b][p];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int w = 0; w < S::VW; ++w) cb.v[i][w] = bv.v[i][w];
+                auto next_keys = [&]() { S::load_k(bk[ub ^ 1], step_rsrc(kbase, st + 1), lo); };
+                const int hi = min(S::kKeys, span - st * S::kKeys);
                 int his[kNT];
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) his[nt] = min(hi, cap[nt] - st * S::kKeys);
                 // A step whose keys every row sees needs no mask (taken with four
                 // tiles, where the masking is a measurable share of the vector work).
                 if (kNT >= 4 && (st > 0 || lead == 0) && hi == S::kKeys && capmin - st * S::kKeys >= S::kKeys)
-                    S::template compute_tiles<kNT, false>(buf[ub], qop, 0, his, kg, sl2, m_run, l_run, acc);
+                    S::template compute_tiles<kNT, false>(cb, qop, 0, his, kg, sl2, m_run, l_run, acc, next_keys);
                 else
-                    S::template compute_tiles<kNT, true>(buf[ub], qop, st == 0 ? lead : 0, his, kg, sl2, m_run, l_run,
-                                                         acc);
-            } else {
+                    S::template compute_tiles<kNT, true>(cb, qop, st == 0 ? lead : 0, his, kg, sl2, m_run, l_run,
+                                                         acc, next_keys);
+                __builtin_amdgcn_sched_barrier(0);   // the V refill after the products
+                S::load_v(bv, step_rsrc(vbase, st + 1), lo);
+                if (++st == nstep) goto swept;
+            }
+        }
+    } else {
+        // Software pipeline over kDepth register buffers: the loads of the next
+        // kDepth-1 steps are in flight while a step is computed.  Every load is
+        // unconditional.
+        typename S::Buf buf[kDepth];
+#pragma unroll
+        for (int ub = 0; ub + 1 < kDepth; ++ub)
+            S::load(buf[ub], step_rsrc(kbase, ub), step_rsrc(vbase, ub), lo);
+        int st = 0;
+        while (true) {
+#pragma unroll
+            for (int ub = 0; ub < kDepth; ++ub) {
+                const int pf = st + kDepth - 1;
+                S::load(buf[(ub + kDepth - 1) % kDepth], step_rsrc(kbase, pf), step_rsrc(vbase, pf), lo);
+                __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
+                const int hi = min(S::kKeys, span - st * S::kKeys);
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt)
                     S::compute(buf[ub], qop[nt], st == 0 ? lead : 0, min(hi, cap[nt] - st * S::kKeys), kg, sl2,
                                m_run[nt], l_run[nt], acc[nt]);
+                if (++st == nstep) goto swept;
             }
-            if (++st == nstep) goto swept;
         }
     }
 swept:
