@@ -769,7 +769,10 @@ __device__ __forceinline__ void store_out_quad(uint8_t *row, int dq, float4 x) {
 constexpr int kCoherent = 16;   // sc1
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws2_rsrc(const void *base) {
-    return make_rsrc(base, 0xffffffffu);   // offsets stay below 2^32: the plan bounds the group-level slots
+    // Offsets stay below 2^32: the counter reserve limits a fused launch to
+    // 8192 workgroups, so the group-level slots span at most 8192 x 2 x 64 rows
+    // x 128 floats = 2^29 bytes.
+    return make_rsrc(base, 0xffffffffu);
 }
 
 __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 x) {

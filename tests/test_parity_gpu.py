@@ -231,6 +231,44 @@ def test_multi_token_70b_shaped_ragged_full_size():
     compare(out16, ref, "t_q=2 full size bf16")
 
 
+@pytest.mark.parametrize("form", ["t_q8", "G64"])
+def test_64_rows_70b_shaped_ragged_full_size(form):
+    """The two 64-row forms the benchmark times on the 70B-shaped ragged workload's
+    keys and values (64 sequences of 1K-32K keys), with its query blocks: eight
+    query tokens on 64 query heads (G 8 x t_q 8), and one token on 512 query heads
+    (G 64); automatic plan; the oracle checks 16 of the 64 sequences whole (every
+    fourth, so short and long ones alike) and every output is finite."""
+    import torch
+    import oracle
+    from gqa_split_kv_amd.inputs import device_queries
+    w = WORKLOADS[4]
+    sl_host = w.seq_lens()
+    _say("generating the 70B-shaped ragged workload's K/V and the", form, "queries")
+    d = device_workload(w)
+    if form == "t_q8":
+        q = device_queries(w.batch, 8, w.h_q, w.d, "bf16", seed=w.seed + 11)
+    else:
+        q = device_queries(w.batch, 1, 64 * w.h_kv, w.d, "bf16", seed=w.seed + 13)[:, 0].contiguous()
+    out32 = run_hip(q, d.k, d.v, d.seq_lens, d.scale, out_dtype=torch.float32)
+    out16 = run_hip(q, d.k, d.v, d.seq_lens, d.scale)
+    assert torch.isfinite(out32).all().item() and torch.isfinite(out16.float()).all().item()
+    pick = list(range(0, w.batch, 4))
+    _say("copying the inputs of sequences", pick[0], "...", pick[-1], "to the host and running the oracle")
+    kh, vh = to_host_bits(d.k), to_host_bits(d.v)
+    starts = np.concatenate([[0], np.cumsum(sl_host)])
+    qs, ks, vs = [], [], []
+    for b in pick:
+        qs.append(to_host_bits(q[b:b + 1]))
+        ks.append(kh[starts[b]:starts[b + 1]])
+        vs.append(vh[starts[b]:starts[b + 1]])
+    ref = oracle.gqa_decode_f64(np.concatenate(qs), np.concatenate(ks), np.concatenate(vs),
+                                sl_host[pick].astype(np.int32), d.scale)
+    idx = torch.tensor(pick, device=out32.device)
+    e, r = compare(out32.index_select(0, idx), ref, "%s full size fp32" % form)
+    _say("%s fp32 out: max|err| %.3g rel-L2 %.3g" % (form, e, r))
+    compare(out16.index_select(0, idx), ref, "%s full size bf16" % form)
+
+
 @pytest.mark.parametrize("G,h_kv,t_q", [(8, 2, 4), (16, 1, 3), (8, 1, 8), (32, 2, 1), (64, 1, 1),
                                         (24, 1, 2), (17, 1, 1), (3, 3, 7)])
 @pytest.mark.parametrize("d", [64, 128])
