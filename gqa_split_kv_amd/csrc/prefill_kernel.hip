@@ -207,8 +207,9 @@ struct PrefillTile {
     // i of its rows in sv[nt][h][i].  The contraction over d runs in the outer
     // loop, so the 2 kNT kH accumulators -- the score registers themselves -- form
     // independent chains that the matrix core interleaves (a chain of dependent
-    // products issues at a fraction of the rate), and each piece of the K operand
-    // is read from LDS just before its products.
+    // products issues at a fraction of the rate).  Every K operand read is issued
+    // before the first product (kept there by a scheduling barrier), so the
+    // products wait for one LDS round trip instead of one per d piece.
     __device__ __forceinline__ static void qk(const uint8_t *Kt, const uint32_t (&koff)[2][NKP],
                                               const uint4 (&qop)[kNT][NKP], float (&sv)[kNT][kH][8]) {
         f32x4_t sacc[kNT][kH][2];
@@ -218,21 +219,24 @@ struct PrefillTile {
             for (int h = 0; h < kH; ++h)
 #pragma unroll
                 for (int b = 0; b < 2; ++b) sacc[nt][h][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        uint4 kop[NKP][kH][2];
 #pragma unroll
-        for (int p = 0; p < NKP; ++p) {
-            uint4 kop[kH][2];
+        for (int p = 0; p < NKP; ++p)
 #pragma unroll
             for (int h = 0; h < kH; ++h)
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
-                    kop[h][b] = *reinterpret_cast<const uint4 *>(Kt + h * 32 * LROW + koff[b][p]);
+                    kop[p][h][b] = *reinterpret_cast<const uint4 *>(Kt + h * 32 * LROW + koff[b][p]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < NKP; ++p)
 #pragma unroll
             for (int h = 0; h < kH; ++h)
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-                    for (int b = 0; b < 2; ++b) sacc[nt][h][b] = mfma16<kHalf>(kop[h][b], qop[nt][p], sacc[nt][h][b]);
-        }
+                    for (int b = 0; b < 2; ++b)
+                        sacc[nt][h][b] = mfma16<kHalf>(kop[p][h][b], qop[nt][p], sacc[nt][h][b]);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
@@ -341,11 +345,28 @@ struct PrefillTile {
     //           one 16-byte load per operand at voff[h]; otherwise V rows as
     //           given, read with transpose loads at voff[c & 3].
     //   kRowSum also accumulate the row sums into accl (otherwise row_sums() does).
+    // The fast loop's form (kVT, fp16 P, no row sums) issues every operand read
+    // before the first product, as qk() does.
     template <bool kSplit, bool kVT, bool kRowSum = true>
     __device__ __forceinline__ static void pv(const uint4 (&bhi)[kNT][kH], const uint4 (&blo)[kNT][kH],
                                               const uint8_t *Vt, const uint32_t *voff, f32x4_t (&accl)[kNT],
                                               f32x4_t (&acc)[kNT][VEC]) {
         constexpr bool kPvHalf = kSplit ? kHalf : true;
+        if constexpr (kVT && !kSplit && !kRowSum) {
+            uint4 av[kH][VEC];
+#pragma unroll
+            for (int h = 0; h < kH; ++h)
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) av[h][c] = *reinterpret_cast<const uint4 *>(Vt + c * 16 * kVtRow + voff[h]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int h = 0; h < kH; ++h)
+#pragma unroll
+                for (int c = 0; c < VEC; ++c)
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt) acc[nt][c] = mfma16<true>(av[h][c], bhi[nt][h], acc[nt][c]);
+            return;
+        }
 #pragma unroll
         for (int h = 0; h < kH; ++h) {
 #pragma unroll
