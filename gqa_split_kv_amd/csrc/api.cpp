@@ -171,8 +171,9 @@ int decode_ex(const gqa_decode_args *a) {
 // Scratch of gqa_decode_noalloc: the partial triples of a call live in this
 // file-scope device array instead of a workspace, so the call allocates nothing.
 // Every device the library runs it on holds its own copy until the process ends;
-// the array starts zeroed (as every device variable does) and nothing in it has
-// to be zero at the start of a call.  Host code never passes the array's name to
+// the array starts zeroed (as every device variable does), which is what its
+// leading counter reserve needs, and every call leaves those counters zero; the
+// rest needs no initialisation.  Host code never passes the array's name to
 // a kernel (that would be the host-side stand-in, not a device address): it
 // takes the device address once per device with hipGetSymbolAddress and uses
 // that pointer.

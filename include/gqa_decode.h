@@ -209,11 +209,15 @@ int gqa_decode_ex(const gqa_decode_args *args);
  * nothing (no hipMalloc, no allocating library routine).
  *
  * `workspace` must be NULL and `workspace_bytes` 0 (GQA_ERR_ARG otherwise).  A
- * call whose plan needs more scratch than the array holds -- num_chunks x 2 x
- * (G * t_q) x (d_head + 2) x 4 bytes, rounded up to 256 -- returns
- * GQA_ERR_WORKSPACE before anything is enqueued; the automatic plan fits for up
- * to 16 rows per kv head (G * t_q) at d_head 128 and 32 at d_head 64 on a
- * 256-compute-unit device, and a smaller num_chunks fits larger shapes.
+ * call whose plan needs more scratch than the array holds -- the size
+ * gqa_decode_workspace_bytes() reports for the same arguments: the counter
+ * reserve plus num_chunks x 2 x (G * t_q) x (d_head + 2) x 4 bytes (and a
+ * quarter of that again with the fused merge) -- returns GQA_ERR_WORKSPACE
+ * before anything is enqueued; the automatic plan fits for up to 16 rows per kv
+ * head (G * t_q) at d_head 128 and 32 at d_head 64 on a 256-compute-unit
+ * device, and a smaller num_chunks fits larger shapes.  The array's first
+ * GQA_DECODE_COUNTER_BYTES are the counter reserve: zero when the library is
+ * loaded, and every call leaves them zero.
  *
  * Every call on a device shares that device's one scratch array, which keeps the
  * last call's contents: two calls that may overlap on one device (different
