@@ -256,7 +256,7 @@ struct Packed16Step {
     }
     // The step for kNT 16-row tiles on one load of the keys, in three phases:
     // every tile's scores (independent MFMA chains) and new row maxima; one
-    // wave-wide test whether any maximum rose (the accumulators are rescaled
+    // wave-wide test whether any reference moved (the accumulators are rescaled
     // only then: elsewhere the factor is exactly 1, or 0 on a still-empty state
     // whose accumulators are 0, so skipping the rescale changes no bit); then
     // every tile's weights, split P and products, with each V column's operand
@@ -300,8 +300,15 @@ struct Packed16Step {
 #pragma unroll
             for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[nt][i]);
             // sl2 > 0: the scaled maximum is the maximum of the raw scores, scaled.
-            const float m_new = fmaxf(m_run[nt], kMask ? max_over_rows(mx) : max_over_rows(mx) * sl2);
-            moved |= m_new != m_run[nt];
+            // The reference (m_run) moves only when a row's maximum passes it by more
+            // than kLag (log2 units), so after a piece's first steps the rescale is
+            // rare; the weights are then below 2^kLag, which bf16 holds (fp16 P,
+            // already offset by 2^15, keeps kLag = 0).
+            constexpr float kLag = kHalf ? 0.f : 8.f;
+            const float mxs = kMask ? max_over_rows(mx) : max_over_rows(mx) * sl2;
+            const bool mv = mxs > m_run[nt] + kLag;
+            const float m_new = mv ? fmaxf(m_run[nt], mxs) : m_run[nt];
+            moved |= mv;
             // A row that has seen no key yet keeps the identity: exponentiate against 0.
             m_ref[nt] = m_new == -INFINITY ? 0.f : m_new;
             alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - m_ref[nt]);   // 0 while the state is empty
