@@ -179,16 +179,7 @@ struct Packed16Step {
                 v[i] = static_cast<uint32_t>((8 * kg + i) * rowstride + m * VEC * ES);
         }
     };
-    __device__ __forceinline__ static void load(Buf &B, __amdgpu_buffer_rsrc_t rk,
-                                                __amdgpu_buffer_rsrc_t rv, const Lanes &lo) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int p = 0; p < NKP; ++p) B.k[b][p] = load16(rk, lo.k[b] + 64 * p);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) load_words<VW>(B.v[i], rv, lo.v[i]);
-    }
-    // The K half or the V half of load() alone.
+    // A step's K rows (two 16-key blocks) or V rows into the registers of B.
     __device__ __forceinline__ static void load_k(Buf &B, __amdgpu_buffer_rsrc_t rk, const Lanes &lo) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -198,49 +189,6 @@ struct Packed16Step {
     __device__ __forceinline__ static void load_v(Buf &B, __amdgpu_buffer_rsrc_t rv, const Lanes &lo) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) load_words<VW>(B.v[i], rv, lo.v[i]);
-    }
-    __device__ __forceinline__ static void compute(const Buf &B, const uint4 (&qop)[NKP], int lo, int hi,
-                                                   int kg, float sl2, float &m_run, float &l_run,
-                                                   f32x4_t (&acc)[VEC]) {
-        float sv[8];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int p = 0; p < NKP; ++p) s = mfma16(B.k[b][p], qop[p], s);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-            {
-                const int key = 8 * kg + 4 * b + q;
-                sv[4 * b + q] = (key >= lo && key < hi) ? s[q] * sl2 : -INFINITY;
-            }
-        }
-        softmax_step<8, VEC, kHalf ? 15 : 0>(sv, m_run, l_run, acc);
-        // P = hi + lo in the 16-bit format, packed two keys per word (key 2w low).
-        uint32_t phi[4], plo[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const f32x2_t pw = {sv[2 * w], sv[2 * w + 1]};
-            if constexpr (kHalf) {
-                const f16x2_t h = __builtin_convertvector(pw, f16x2_t);
-                const f32x2_t hf = __builtin_convertvector(h, f32x2_t);
-                phi[w] = __builtin_bit_cast(uint32_t, h);
-                plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw - hf, f16x2_t));
-            } else {
-                const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pw, bf16x2_t));
-                const f32x2_t r = {pw[0] - __uint_as_float(hb << 16), pw[1] - __uint_as_float(hb & 0xffff0000u)};
-                phi[w] = hb;
-                plo[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
-            }
-        }
-        const uint4 bhi = make_uint4(phi[0], phi[1], phi[2], phi[3]);
-        const uint4 blo = make_uint4(plo[0], plo[1], plo[2], plo[3]);
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) {
-            const uint4 av = v_operand(B, c);
-            acc[c] = mfma16(av, bhi, acc[c]);
-            acc[c] = mfma16(av, blo, acc[c]);
-        }
     }
     // A operand of P V column c: element i = V[key 8kg + i][d = VEC*m + c].
     __device__ __forceinline__ static uint4 v_operand(const Buf &B, int c) {
@@ -549,12 +497,13 @@ __device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j
         const int64_t boff = hi > 0 ? static_cast<int64_t>(st) * S::kKeys * rowstride : 0;
         return buffer_rsrc(base + boff, static_cast<uint32_t>(hi * rowstride));
     };
-    if constexpr (kIn != kF32 && kNT > 1) {
-        // Several tiles: one K and one V register buffer, each refilled as soon
-        // as its step has used it -- the next step's keys once the Q K^T
-        // products are issued, its values once the P V products are -- so the
-        // loads of step st+1 overlap the rest of step st with no second buffer
-        // (the registers go to the tiles instead).
+    if constexpr (kIn != kF32) {
+        // 16-bit input: one K and one V register buffer, each refilled as soon as
+        // its step has used it -- the next step's keys once the Q K^T products
+        // are issued, its values once the P V products are -- so the loads of
+        // step st+1 overlap the rest of step st with no second buffer (with
+        // several tiles the registers go to the tiles instead; with one tile
+        // this measured ~1% faster than two full buffers).
         // Unrolled twice with the K buffer named by parity: in a loop that is not
         // unrolled the compiler waits for every outstanding load (vmcnt(0)) at
         // the top of each step, V refill included.
@@ -592,9 +541,9 @@ __device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j
             }
         }
     } else {
-        // Software pipeline over kDepth register buffers: the loads of the next
-        // kDepth-1 steps are in flight while a step is computed.  Every load is
-        // unconditional.
+        // fp32 input: software pipeline over kDepth register buffers, the loads
+        // of the next kDepth-1 steps in flight while a step is computed.  Every
+        // load is unconditional.
         typename S::Buf buf[kDepth];
 #pragma unroll
         for (int ub = 0; ub + 1 < kDepth; ++ub)
