@@ -16,10 +16,12 @@
 //     range read the adjacent kv-head slices of the same rows at the same time
 //     (contiguous DRAM traffic).  A range that covers a whole sequence stores o
 //     itself; a sequence cut across ranges leaves one partial triple per piece
-//     and kv head in a workspace, merged by merge_kernel.
+//     and kv head in a workspace, merged by merge_kernel -- or, in fused_kernel
+//     (below), inside the sweep itself.
 //   * A wavefront sweeps its piece in steps of 32 keys (bf16) or 16 keys (fp32).
 //     Q K^T is v_mfma_f32_16x16x32_bf16 (16x16x4_f32 for fp32 input) with the 16
-//     keys of a block as the M axis and the (up to 16) query heads as the N axis;
+//     keys of a block as the M axis and 16 query rows (heads x query tokens) as
+//     the N axis; up to four such 16-row tiles share each load of the keys;
 //     K rows are loaded straight into the MFMA A-operand layout with 16-byte
 //     buffer loads, so no LDS round trip is needed.  The d axis of the
 //     contraction is permuted (the same permutation on Q and K) so each load
@@ -51,7 +53,7 @@ using namespace dev;
 #ifndef GQA_SWEEP_DEPTH
 #define GQA_SWEEP_DEPTH 2
 #endif
-constexpr int kSweepDepth = GQA_SWEEP_DEPTH;   // register buffers in the sweep pipeline
+constexpr int kSweepDepth = GQA_SWEEP_DEPTH;   // register buffers of the fp32 sweep pipeline
 // Cache policy of the K/V stream loads (buffer-instruction cache-policy bits).
 // K and V are read exactly once, so they are loaded non-temporally (nt) and do
 // not displace the partials, q and seq_lens from the caches.
