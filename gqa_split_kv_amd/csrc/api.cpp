@@ -131,6 +131,7 @@ int decode_launch(const gqa_decode_args *a, const gqa_decode_plan &plan, void *w
     P.R = G * P.t_q;
     P.num_chunks = plan.num_chunks;
     P.min_chunk = plan.min_chunk;
+    P.expect_len = a->batch == 1 && a->max_seq_len > 0 ? a->max_seq_len : 0;
     P.scale_log2 = static_cast<float>(static_cast<double>(a->scale) * 1.4426950408889634074);
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     if (a->sweep_events[0] && a->sweep_events[1]) {

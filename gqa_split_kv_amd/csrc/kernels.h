@@ -26,6 +26,7 @@ struct DecodeParams {
     int32_t t_q;               // query tokens per sequence
     int32_t R;                 // rows per kv head: G * t_q (row = t * G + g), up to 64
     int32_t num_chunks, min_chunk;
+    int32_t expect_len;        // one sequence: the length the caller's bound predicts, else 0
     float scale_log2;          // scale * log2(e)
 };
 

@@ -48,7 +48,9 @@ __device__ __forceinline__ void store_quad(uint8_t *row, int eq, float4 x) {
 }
 
 // Folds a batch of pieces into a running (M, L, acc) with the merge rule: the new
-// maximum, both sides rescaled by 2^(old - new), sums added.
+// maximum, both sides rescaled by 2^(old - new), sums added.  Every multiply-add
+// is written as one fused operation (nothing is left to contraction), so each
+// inlined copy of the merge rounds alike.
 struct Running {
     float M, L;
     float4 acc;
@@ -60,11 +62,11 @@ __device__ __forceinline__ void fold(Running &r, float m, float l, float4 o) {
     const float Mr = Mn == -INFINITY ? 0.f : Mn;
     const float a = __builtin_amdgcn_exp2f(r.M - Mr);   // 0 when r is empty
     const float f = __builtin_amdgcn_exp2f(m - Mr);     // 0 for an empty side
-    r.L = r.L * a + l * f;
-    r.acc.x = r.acc.x * a + o.x * f;
-    r.acc.y = r.acc.y * a + o.y * f;
-    r.acc.z = r.acc.z * a + o.z * f;
-    r.acc.w = r.acc.w * a + o.w * f;
+    r.L = __builtin_fmaf(r.L, a, l * f);
+    r.acc.x = __builtin_fmaf(r.acc.x, a, o.x * f);
+    r.acc.y = __builtin_fmaf(r.acc.y, a, o.y * f);
+    r.acc.z = __builtin_fmaf(r.acc.z, a, o.z * f);
+    r.acc.w = __builtin_fmaf(r.acc.w, a, o.w * f);
     r.M = Mn;
 }
 
@@ -82,51 +84,44 @@ __device__ __forceinline__ Running shfl_xor_running(const Running &r, int mask) 
 // Workgroup layout: kRows rows x PL piece lanes x kQuads element quads (one d
 // slice of 4 kQuads elements; D / (4 kQuads) slices per row); a row is one
 // (query token, query head) of the kv head, row = t * G + g.
-template <int kOut, int D, int kThreadsM, int kRows, int kQuads>
-__global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
-    constexpr int TP = kQuads * kRows;               // threads per piece lane
-    constexpr int PL = kThreadsM / TP;               // piece lanes
-    constexpr int kSlices = D / (4 * kQuads);
-    constexpr int kBatch = 8;                        // pieces in flight per thread
-    constexpr int kWaves = kThreadsM / kWave;
-    static_assert(PL >= 1 && PL * TP == kThreadsM && kSlices * 4 * kQuads == D, "layout");
+template <int kThreadsM, int kRows, int kQuads>
+struct MergeLayout {
+    static constexpr int TP = kQuads * kRows;        // threads per piece lane
+    static constexpr int PL = kThreadsM / TP;        // piece lanes
+    static constexpr int kWaves = kThreadsM / kWave;
+    static_assert(PL >= 1 && PL * TP == kThreadsM, "layout");
     static_assert(PL == 1 || TP <= kWave, "piece lanes are folded within and across wavefronts");
-    __shared__ Running s_run[PL > 1 ? kWaves : 1][PL > 1 ? TP : 1];
+    // LDS of the fold across wavefronts: lanes [0, TP) of every wavefront.
+    static constexpr int kRunRows = PL > 1 ? kWaves : 1;
+    static constexpr int kRunCols = PL > 1 ? TP : 1;
+};
 
-    const int G = P.G;
+// Merges the pieces of (sequence b, kv head j) for the thread's row g and element
+// quad eq, given the sequence's length, the total over the batch and the keys
+// before it, and stores o.  With kCheck (one sequence whose length was
+// predicted), the pieces are read at once and the stored length `got` (as read:
+// a negative value never equals the positive prediction), read before them, is
+// compared with the prediction before anything is stored: on a mismatch
+// every wavefront returns false having stored nothing (the slots read lie inside
+// the workspace either way).  Otherwise returns true.
+template <int kOut, int D, int kThreadsM, int kRows, int kQuads, bool kCheck>
+__device__ __forceinline__ bool merge_pieces(const DecodeParams &P,
+                                             Running (*s_run)[MergeLayout<kThreadsM, kRows, kQuads>::kRunCols],
+                                             int j, int g, int eq, bool active, uint8_t *orow, int len,
+                                             int64_t total, int64_t ustart, int got) {
+    using Lay = MergeLayout<kThreadsM, kRows, kQuads>;
+    constexpr int TP = Lay::TP;
+    constexpr int PL = Lay::PL;
+    constexpr int kBatch = 8;                        // pieces in flight per thread
     const int R = P.R;
-    const int groups = (R + kRows - 1) / kRows;
-    const int blk = static_cast<int>(blockIdx.x) / kSlices;
-    const int slice = static_cast<int>(blockIdx.x) - blk * kSlices;
-    const int unit = blk / groups;
-    const int r0 = (blk - unit * groups) * kRows;
-    const int b = unit / P.h_kv;
-    const int j = unit - b * P.h_kv;
     const int tid = static_cast<int>(threadIdx.x);
-    const int eq = slice * kQuads + tid % kQuads;    // element quad within the row
-    const int hh = (tid / kQuads) % kRows;
     const int pl = tid / TP;
-    const int g = r0 + hh;                           // row within the kv head
-    const bool active = g < R;
-    const int tq = (active ? g : R - 1) / G;
-    const int gh = (active ? g : R - 1) - tq * G;
-    // Up to 64 sequences: one read of seq_lens gives the length, total and prefix.
-    const bool few = P.batch <= kWave;
-    FirstLens fl;
-    if (few) fl.load(P.seq_lens, P.batch);
-    const int len = few ? fl.len(b) : uniform32(seq_len_at(P.seq_lens, b));
-    uint8_t *orow = P.o + ((static_cast<int64_t>(b) * P.t_q + tq) * P.h_q + j * G + gh) * D *
-                              (kOut == kF32 ? 4 : 2);
-    if (len == 0) {
-        if (pl == 0 && active) store_quad<kOut>(orow, eq, make_float4(0.f, 0.f, 0.f, 0.f));
-        return;
-    }
-    const int64_t total = few ? fl.total() : total_len(P.seq_lens, P.batch);
     const int64_t chunk = chunk_keys(total, P.num_chunks / P.h_kv, P.min_chunk);
-    const int64_t ustart = few ? fl.prefix(b) : prefix_len(P.seq_lens, b);
     const int64_t ca = ustart / chunk;   // token ranges holding this sequence
     const int64_t cb = (ustart + len - 1) / chunk;
-    if (ca == cb) return;                // written whole by the sweep kernel
+    // The prediction held: the same test in every wavefront (each read the length).
+    auto confirmed = [&]() { return !kCheck || uniform32(got) == len; };
+    if (ca == cb) return confirmed();    // written whole by the sweep kernel
 
     Running r = {-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
     if (active) {
@@ -156,15 +151,16 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
 #pragma unroll
             for (int i = 0; i < kBatch; ++i) {
                 const float f = __builtin_amdgcn_exp2f(ml[i].x - mbr);   // 0 for the padding
-                bt.L += f * ml[i].y;
-                bt.acc.x += f * ov[i].x;
-                bt.acc.y += f * ov[i].y;
-                bt.acc.z += f * ov[i].z;
-                bt.acc.w += f * ov[i].w;
+                bt.L = __builtin_fmaf(f, ml[i].y, bt.L);
+                bt.acc.x = __builtin_fmaf(f, ov[i].x, bt.acc.x);
+                bt.acc.y = __builtin_fmaf(f, ov[i].y, bt.acc.y);
+                bt.acc.z = __builtin_fmaf(f, ov[i].z, bt.acc.z);
+                bt.acc.w = __builtin_fmaf(f, ov[i].w, bt.acc.w);
             }
             fold(r, bt.M, bt.L, bt.acc);
         }
     }
+    if (!confirmed()) return false;      // before any barrier or store: uniform over the workgroup
     if constexpr (PL > 1) {
         // Piece lanes of one wavefront sit TP lanes apart: fold them pairwise.
 #pragma unroll
@@ -176,9 +172,9 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
         const int ln = tid % kWave;
         if (ln < TP) s_run[wv][ln] = r;
         __syncthreads();
-        if (wv != 0 || ln >= TP) return;
+        if (wv != 0 || ln >= TP) return true;
 #pragma unroll
-        for (int i = 1; i < kWaves; ++i) {
+        for (int i = 1; i < Lay::kWaves; ++i) {
             const Running x = s_run[i][ln];
             fold(r, x.M, x.L, x.acc);
         }
@@ -187,6 +183,57 @@ __global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
         const float inv = r.L > 0.f ? 1.0f / r.L : 0.f;   // a query token with no key gives 0
         store_quad<kOut>(orow, eq, make_float4(r.acc.x * inv, r.acc.y * inv, r.acc.z * inv, r.acc.w * inv));
     }
+    return true;
+}
+
+template <int kOut, int D, int kThreadsM, int kRows, int kQuads>
+__global__ __launch_bounds__(kThreadsM) void merge_kernel(DecodeParams P) {
+    using Lay = MergeLayout<kThreadsM, kRows, kQuads>;
+    constexpr int kSlices = D / (4 * kQuads);
+    static_assert(kSlices * 4 * kQuads == D, "layout");
+    __shared__ Running s_run[Lay::kRunRows][Lay::kRunCols];
+
+    const int G = P.G;
+    const int R = P.R;
+    const int groups = (R + kRows - 1) / kRows;
+    const int blk = static_cast<int>(blockIdx.x) / kSlices;
+    const int slice = static_cast<int>(blockIdx.x) - blk * kSlices;
+    const int unit = blk / groups;
+    const int r0 = (blk - unit * groups) * kRows;
+    const int b = unit / P.h_kv;
+    const int j = unit - b * P.h_kv;
+    const int tid = static_cast<int>(threadIdx.x);
+    const int eq = slice * kQuads + tid % kQuads;    // element quad within the row
+    const int hh = (tid / kQuads) % kRows;
+    const int pl = tid / Lay::TP;
+    const int g = r0 + hh;                           // row within the kv head
+    const bool active = g < R;
+    const int tq = (active ? g : R - 1) / G;
+    const int gh = (active ? g : R - 1) - tq * G;
+    uint8_t *orow = P.o + ((static_cast<int64_t>(b) * P.t_q + tq) * P.h_q + j * G + gh) * D *
+                              (kOut == kF32 ? 4 : 2);
+    if (P.expect_len > 0) {
+        // One sequence, its length predicted by the caller's bound: the piece loads
+        // need not wait for the read of seq_lens (a buffer load, so that it stays a
+        // vector load, waited for only where the length is compared).  A wrong
+        // prediction continues below with the length as stored.
+        const int got = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(P.seq_lens, 4), 0, 0, 0));
+        if (merge_pieces<kOut, D, kThreadsM, kRows, kQuads, true>(P, s_run, j, g, eq, active, orow, P.expect_len,
+                                                                   P.expect_len, 0, got))
+            return;
+    }
+    // Up to 64 sequences: one read of seq_lens gives the length, total and prefix.
+    const bool few = P.batch <= kWave;
+    FirstLens fl;
+    if (few) fl.load(P.seq_lens, P.batch);
+    const int len = few ? fl.len(b) : uniform32(seq_len_at(P.seq_lens, b));
+    if (len == 0) {
+        if (pl == 0 && active) store_quad<kOut>(orow, eq, make_float4(0.f, 0.f, 0.f, 0.f));
+        return;
+    }
+    const int64_t total = few ? fl.total() : total_len(P.seq_lens, P.batch);
+    const int64_t ustart = few ? fl.prefix(b) : prefix_len(P.seq_lens, b);
+    merge_pieces<kOut, D, kThreadsM, kRows, kQuads, false>(P, s_run, j, g, eq, active, orow, len, total, ustart, 0);
 }
 
 template <int kOut, int D>

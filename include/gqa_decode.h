@@ -191,8 +191,12 @@ typedef struct gqa_decode_args {
     int32_t t_q;
     int32_t merge;  /* GQA_MERGE_*, see above */
     /* Optional hint: no sequence is longer than max_seq_len keys (0 = unknown).
-     * Used only by the automatic merge choice; the kernels read the lengths from
-     * seq_lens, and a wrong hint changes the speed, never the result. */
+     * Used by the automatic merge choice, and with batch 1 by the merge kernel,
+     * which reads the pieces for a length of exactly max_seq_len while it reads
+     * seq_lens and checks the two before it stores (one memory round trip less
+     * when they agree).  The kernels take the lengths from seq_lens: a wrong hint
+     * changes the speed, never the result, and with the merge form fixed the
+     * result is bit-identical with and without it. */
     int32_t max_seq_len;
 } gqa_decode_args;
 

@@ -69,14 +69,15 @@ MERGE = B.GQA_MERGE_AUTO
 
 
 def run_hip(q, k, v, seq_lens, scale, out_dtype=None, num_chunks=0, min_chunk=0, poison=True,
-            workspace=None, stream=None, merge=None):
+            workspace=None, stream=None, merge=None, max_seq_len=0):
     """Device tensors in; the decode output tensor (synchronised) out."""
     import torch
     out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if poison:
         out.fill_(float("nan"))
     B.decode(q, k, v, seq_lens, scale=scale, out=out, num_chunks=num_chunks, min_chunk=min_chunk,
-             workspace=workspace, stream=stream, merge=MERGE if merge is None else merge)
+             workspace=workspace, stream=stream, merge=MERGE if merge is None else merge,
+             max_seq_len=max_seq_len)
     torch.cuda.synchronize()
     return out
 

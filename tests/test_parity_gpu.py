@@ -160,6 +160,33 @@ def test_edge_lengths(lens):
                 assert (o[b] == 0).all().item()
 
 
+@pytest.mark.parametrize("h_q,h_kv,d,t_q,dtype", [(32, 8, 128, 0, "bf16"), (8, 1, 128, 0, "bf16"),
+                                                  (16, 2, 128, 4, "bf16"), (8, 1, 64, 0, "f32")])
+def test_single_sequence_length_bound(h_q, h_kv, d, t_q, dtype):
+    """One sequence with the caller's max_seq_len bound: the merge reads its pieces
+    for the length the bound predicts and falls back when the stored length differs
+    (bound above the length, a bound below it, an empty or negative length).  Each
+    result matches the oracle and, bit for bit, the same call without a bound."""
+    import torch
+    out_dtype = torch.float32
+    for L in [1, 33, 1000, 8192, 0, -3]:
+        c = host_case(1, h_q, h_kv, d, [L], dtype, seed=L + 1000 * h_kv + t_q, t_q=t_q)
+        ref = oracle_of(c)
+        q, k, v, sl = upload(c)
+        for nc, mc in [(0, 0), (4096, 1), (64, 1)]:
+            _say("h_q", h_q, "h_kv", h_kv, "d", d, "t_q", t_q, dtype, "len", L, "no bound", "nc", nc, "mc", mc)
+            base = run_hip(q, k, v, sl, c.scale, out_dtype=out_dtype, num_chunks=nc, min_chunk=mc)
+            for hint in sorted({max(L, 0), max(L, 0) + 1, 2 * max(L, 0) + 7, max(L - 1, 0), 5}):
+                _say("  bound", hint)
+                o = run_hip(q, k, v, sl, c.scale, out_dtype=out_dtype, num_chunks=nc, min_chunk=mc,
+                            max_seq_len=hint)
+                compare(o, ref, "len=%d bound=%d nc=%d mc=%d" % (L, hint, nc, mc))
+                # (the merge form is forced here, so the bound cannot change the plan)
+                assert torch.equal(o, base), "len=%d bound=%d nc=%d mc=%d" % (L, hint, nc, mc)
+                if L <= 0:
+                    assert (o == 0).all().item()
+
+
 @pytest.mark.parametrize("nc,mc", [(1, 1), (2, 1), (3, 7), (64, 1), (4096, 1), (100000, 1),
                                    (7, 1024), (1 << 20, 16), (0, 17)])
 def test_forced_chunking_ragged_batch(nc, mc):
