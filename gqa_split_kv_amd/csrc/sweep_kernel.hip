@@ -447,25 +447,58 @@ __device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j
         cap[nt] = len - P.t_q + t + 1 - static_cast<int>(abase - off);
     }
 
-    // Q operand: query row (t, g), bytes [64p + 16kg, +16) of it (zero for unused rows):
-    // the same d permutation as the K rows, so the contraction covers every d once.
-    // A negative scale negates q instead (exact), so that the steps scale by a
-    // positive factor and the largest scaled score is the largest raw one.
-    const uint32_t qflip = P.scale_log2 < 0.f ? (kIn == kF32 ? 0x80000000u : 0x80008000u) : 0u;
+    // Q operand: query row (t, g), bytes [64p + 16kg, +16) of it: the same d
+    // permutation as the K rows, so the contraction covers every d once.  Lanes of
+    // unused rows (past R) hold a copy of row R - 1: their scores are finite and
+    // never stored, and with no select on the loaded value the loads stay
+    // unconditional and go out together.  A negative scale negates q instead
+    // (exact), so that the steps scale by a positive factor and the largest scaled
+    // score is the largest raw one.
     uint4 qop[kNT][S::NKP];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
         const uint8_t *qrow = P.q + qo_row[nt] * S::ROWB + 16 * kg;
 #pragma unroll
-        for (int p = 0; p < S::NKP; ++p) {
-            uint4 x = *reinterpret_cast<const uint4 *>(qrow + 64 * p);
-            x.x ^= qflip;
-            x.y ^= qflip;
-            x.z ^= qflip;
-            x.w ^= qflip;
-            qop[nt][p] = row_ok[nt] ? x : make_uint4(0, 0, 0, 0);
-        }
+        for (int p = 0; p < S::NKP; ++p) qop[nt][p] = *reinterpret_cast<const uint4 *>(qrow + 64 * p);
     }
+
+    const int64_t row0 = abase * P.h_kv + j;
+    const uint8_t *kbase = P.k + row0 * S::ROWB;
+    const uint8_t *vbase = P.v + row0 * S::ROWB;
+    const typename S::Lanes lo(rowstride);
+    // Buffer resource over step st's rows of K (or V); a step at or past nstep
+    // gets an empty range, so its loads return zeros without a memory access
+    // (the prefetches past the piece cost no round trip).
+    auto step_rsrc = [&](const uint8_t *base, int st) {
+        const int hi = max(0, min(S::kKeys, span - st * S::kKeys));
+        const int64_t boff = hi > 0 ? static_cast<int64_t>(st) * S::kKeys * rowstride : 0;
+        return buffer_rsrc(base + boff, static_cast<uint32_t>(hi * rowstride));
+    };
+    // The first step's K and V (16-bit input: the refilled buffers below; fp32: the
+    // first kDepth - 1 steps of its pipeline) go out with the Q loads, before any
+    // of them is used: the scheduling barrier keeps the rest of the set-up (and
+    // the register moves of Q) behind them, so a piece starts with one round trip.
+    typename S::Buf bk[2], bv;
+    typename S::Buf buf[kDepth];
+    if constexpr (kIn != kF32) {
+        S::load_k(bk[0], step_rsrc(kbase, 0), lo);
+        S::load_v(bv, step_rsrc(vbase, 0), lo);
+    } else {
+#pragma unroll
+        for (int ub = 0; ub + 1 < kDepth; ++ub)
+            S::load(buf[ub], step_rsrc(kbase, ub), step_rsrc(vbase, ub), lo);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t qflip = P.scale_log2 < 0.f ? (kIn == kF32 ? 0x80000000u : 0x80008000u) : 0u;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int p = 0; p < S::NKP; ++p) {
+            qop[nt][p].x ^= qflip;
+            qop[nt][p].y ^= qflip;
+            qop[nt][p].z ^= qflip;
+            qop[nt][p].w ^= qflip;
+        }
     // Keys visible to every row of the wavefront: below the smallest causal limit.
     int capmin = cap[0];
 #pragma unroll
@@ -484,21 +517,8 @@ __device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j
         l_run[nt] = 0.f;
     }
 
-    const int64_t row0 = abase * P.h_kv + j;
-    const uint8_t *kbase = P.k + row0 * S::ROWB;
-    const uint8_t *vbase = P.v + row0 * S::ROWB;
     // |scale| log2(e), kept above 0 so that a masked (-inf) score stays -inf.
     const float sl2 = fmaxf(fabsf(P.scale_log2), 1.17549435e-38f);
-    const typename S::Lanes lo(rowstride);
-
-    // Buffer resource over step st's rows of K (or V); a step at or past nstep
-    // gets an empty range, so its loads return zeros without a memory access
-    // (the prefetches past the piece cost no round trip).
-    auto step_rsrc = [&](const uint8_t *base, int st) {
-        const int hi = max(0, min(S::kKeys, span - st * S::kKeys));
-        const int64_t boff = hi > 0 ? static_cast<int64_t>(st) * S::kKeys * rowstride : 0;
-        return buffer_rsrc(base + boff, static_cast<uint32_t>(hi * rowstride));
-    };
     if constexpr (kIn != kF32) {
         // 16-bit input: one K and one V register buffer, each refilled as soon as
         // its step has used it -- the next step's keys once the Q K^T products
@@ -509,9 +529,6 @@ __device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j
         // Unrolled twice with the K buffer named by parity: in a loop that is not
         // unrolled the compiler waits for every outstanding load (vmcnt(0)) at
         // the top of each step, V refill included.
-        typename S::Buf bk[2], bv;
-        S::load_k(bk[0], step_rsrc(kbase, 0), lo);
-        S::load_v(bv, step_rsrc(vbase, 0), lo);
         int st = 0;
         while (true) {
 #pragma unroll
@@ -546,10 +563,6 @@ __device__ __forceinline__ int process_piece(const DecodeParams &P, int b, int j
         // fp32 input: software pipeline over kDepth register buffers, the loads
         // of the next kDepth-1 steps in flight while a step is computed.  Every
         // load is unconditional.
-        typename S::Buf buf[kDepth];
-#pragma unroll
-        for (int ub = 0; ub + 1 < kDepth; ++ub)
-            S::load(buf[ub], step_rsrc(kbase, ub), step_rsrc(vbase, ub), lo);
         int st = 0;
         while (true) {
 #pragma unroll
