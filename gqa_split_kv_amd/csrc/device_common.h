@@ -138,7 +138,9 @@ struct FirstLens {
     __device__ void load(const int32_t *seq_lens, int batch) {
         const int i = lane_id();
         li = (i < batch) ? seq_len_at(seq_lens, i) : 0;
-        incl = inclusive_scan64(li);
+        // One sequence: every lane's inclusive prefix is lane 0's length (no scan).
+        incl = batch == 1 ? static_cast<int64_t>(__builtin_amdgcn_readlane(static_cast<int>(li), 0))
+                          : inclusive_scan64(li);
     }
     __device__ int64_t total() const { return lane64(incl, kWave - 1); }
     __device__ int len(int b) const { return static_cast<int>(lane64(li, b)); }      // b < 64
