@@ -47,6 +47,7 @@ def _say(*a):
 
 
 def test_tiny_fp32_workload():
+    import torch
     w = WORKLOADS[1]
     c = host_workload(w)
     ref = oracle_of(c)
@@ -56,6 +57,8 @@ def test_tiny_fp32_workload():
         out = run_hip(q, k, v, sl, c.scale, num_chunks=nc, min_chunk=mc)
         e, r = compare(out, ref, "cfg1 nc=%d mc=%d" % (nc, mc))
         assert e < 1e-5 and r < 1e-5, (e, r)   # fp32 in and out: fp32-level agreement
+        hinted = run_hip(q, k, v, sl, c.scale, num_chunks=nc, min_chunk=mc, max_seq_len=int(c.seq_lens.max()))
+        assert torch.equal(hinted, out), "cfg1 with the length bound"
 
 
 @pytest.mark.parametrize("cfg", [2, 3])
@@ -73,6 +76,10 @@ def test_single_sequence_bf16_workloads(cfg):
         assert e < 1e-4 and r < 1e-4, (e, r)
         out16 = run_hip(q, k, v, sl, c.scale, num_chunks=nc, min_chunk=mc)
         compare(out16, ref, "cfg%d bf16 out" % cfg)
+        # The benchmark's call: the longest length as the max_seq_len bound (the merge
+        # then reads the pieces before the length arrives); the same bits.
+        hinted = run_hip(q, k, v, sl, c.scale, num_chunks=nc, min_chunk=mc, max_seq_len=int(c.seq_lens.max()))
+        assert torch.equal(hinted, out16), "cfg%d with the length bound" % cfg
 
 
 def _full_size(cfg):
