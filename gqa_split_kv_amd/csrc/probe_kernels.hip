@@ -3,11 +3,13 @@
 // rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes) and a device read (the
 // achievable read bandwidth of the HBM on this machine, the practical ceiling
 // of the decode sweep).  The copy is grid-stride with four 16-byte loads in
-// flight per lane and 8 workgroups per compute unit.  The read gives every
-// wavefront one contiguous slab and streams it with non-temporal 16-byte buffer
-// loads, eight 1 KiB wavefront loads in flight, two wavefronts per SIMD (the
-// fastest plain read measured on MI355X: ~7.06 TB/s, where a grid-stride read
-// with the same policy reached ~5.7 TB/s).
+// flight per lane and 8 workgroups per compute unit.  The read is grid-stride
+// over 8 KiB chunks, one wavefront per SIMD, each chunk read as eight 1 KiB
+// non-temporal wavefront loads in flight: the fastest of the plain reads
+// measured on MI355X over a 4 GiB buffer (7.27 TB/s; a contiguous slab per
+// wavefront 7.19 TB/s at one and 7.00 at two wavefronts per SIMD; 16 KiB or
+// more in flight per wavefront, or loads without the non-temporal policy,
+// slower).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,29 +36,27 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const uint4 *__restrict_
 }
 
 constexpr int kReadUnroll = 8;
-constexpr int kReadWavesPerCu = 8;
+constexpr int kReadWavesPerCu = 4;
 constexpr int kReadCpol = 2;   // non-temporal, the policy the decode sweep uses for K/V
+constexpr size_t kReadChunk = kReadUnroll * 1024;   // bytes per wavefront per round
 
-// Wavefront w reads the 16-byte units [w per, min((w + 1) per, n16)) of src
-// (per: a multiple of 64, at most 2^27 units so that a slab's byte count fits a
-// buffer resource), 1 KiB per wavefront load.
-__global__ __launch_bounds__(kThreads) void read_kernel(const uint8_t *__restrict__ src, size_t n16, size_t per,
+// Wavefront w of W reads the chunks w, w + W, w + 2W, ... of kReadChunk bytes of
+// src (the last one cut at `bytes`), 1 KiB per wavefront load.
+__global__ __launch_bounds__(kThreads) void read_kernel(const uint8_t *__restrict__ src, size_t bytes,
                                                         uint32_t *sink) {
     const int lane = static_cast<int>(threadIdx.x) & 63;
+    const size_t waves = static_cast<size_t>(gridDim.x) * (kThreads / 64);
     const size_t w = static_cast<size_t>(blockIdx.x) * (kThreads / 64) + threadIdx.x / 64;
-    const size_t beg = w * per;
     uint32_t acc = 0;
-    if (beg < n16) {
-        const size_t end = beg + per < n16 ? beg + per : n16;
-        const uint32_t bytes = static_cast<uint32_t>((end - beg) * 16);
-        const auto r = gqa::dev::make_rsrc(src + beg * 16, bytes);
-        for (uint32_t off = static_cast<uint32_t>(lane) * 16; off < bytes; off += kReadUnroll * 1024) {
-            uint4 x[kReadUnroll];   // loads past the slab's end read zero
+    for (size_t beg = w * kReadChunk; beg < bytes; beg += waves * kReadChunk) {
+        const size_t left = bytes - beg;
+        const auto r = gqa::dev::make_rsrc(src + beg, static_cast<uint32_t>(left < kReadChunk ? left : kReadChunk));
+        uint4 x[kReadUnroll];   // loads past the chunk's range read zero
 #pragma unroll
-            for (int u = 0; u < kReadUnroll; ++u) x[u] = gqa::dev::buffer_load16<kReadCpol>(r, off + u * 1024);
+        for (int u = 0; u < kReadUnroll; ++u)
+            x[u] = gqa::dev::buffer_load16<kReadCpol>(r, static_cast<uint32_t>(lane) * 16 + u * 1024);
 #pragma unroll
-            for (int u = 0; u < kReadUnroll; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
-        }
+        for (int u = 0; u < kReadUnroll; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) acc ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc), d));
@@ -91,18 +91,18 @@ int gqa_probe_copy(const void *src, void *dst, size_t bytes, void *stream) {
 int gqa_probe_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
     if (!src || !sink) return 1;
     if ((reinterpret_cast<uintptr_t>(src) | bytes) % 16 || reinterpret_cast<uintptr_t>(sink) % 4) return 4;
-    const size_t n16 = bytes / 16;
-    if (n16 == 0) return 0;
+    if (bytes == 0) return 0;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 7;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 7;
-    const size_t waves = static_cast<size_t>(cus) * kReadWavesPerCu;
-    size_t per = ((n16 + waves - 1) / waves + 63) & ~static_cast<size_t>(63);
-    if (per > (static_cast<size_t>(1) << 27)) per = static_cast<size_t>(1) << 27;
-    const size_t grid = ((n16 + per - 1) / per + kThreads / 64 - 1) / (kThreads / 64);
-    if (grid > 0x7fffffffu) return 7;
-    hipLaunchKernelGGL(read_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                       reinterpret_cast<hipStream_t>(stream), static_cast<const uint8_t *>(src), n16, per, sink);
+    // One workgroup of kReadWavesPerCu wavefronts per compute unit (fewer for a
+    // buffer of fewer chunks).
+    const size_t chunks = (bytes + kReadChunk - 1) / kReadChunk;
+    const size_t want = (chunks + kThreads / 64 - 1) / (kThreads / 64);
+    const size_t cap = static_cast<size_t>(cus) * kReadWavesPerCu / (kThreads / 64);
+    const unsigned grid = static_cast<unsigned>(want < cap ? want : cap);
+    hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream),
+                       static_cast<const uint8_t *>(src), bytes, sink);
     return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 
