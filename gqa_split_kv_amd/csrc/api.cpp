@@ -265,6 +265,7 @@ int prefill_ex(const gqa_prefill_args *a) {
     P.vt = nullptr;
     P.vflags = nullptr;
     P.nvb = 0;
+    P.queue = nullptr;
     if (W.bytes > 0) {
         void *ws = a->workspace;
         if (!ws) {
@@ -279,11 +280,13 @@ int prefill_ex(const gqa_prefill_args *a) {
         V.batch = a->batch;
         V.h_kv = a->h_kv;
         V.nvb = W.nvb;
+        V.queue = reinterpret_cast<unsigned long long *>(static_cast<uint8_t *>(ws) + W.queue_offset);
         e = gqa::launch_vprep(V, a->in_dtype, a->d_head, stream);
         if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "V copy kernel launch failed: %s", hipGetErrorString(e));
         P.vt = V.vt;
         P.vflags = V.flags;
         P.nvb = W.nvb;
+        P.queue = V.queue;
     }
     e = gqa::launch_prefill(P, a->in_dtype, a->out_dtype, a->d_head, blocks, stream);
     if (e != hipSuccess) return gqa::fail(GQA_ERR_HIP, "prefill kernel launch failed: %s", hipGetErrorString(e));

@@ -75,6 +75,7 @@ int validate_prefill(const gqa_prefill_args *a, bool check_workspace = true);
 // (and nvb = 0) when the call makes no copy (split_pv = 1 or total_tokens = 0).
 struct PrefillWorkspace {
     size_t flags_offset;
+    size_t queue_offset;   // the tile queue's counter (zeroed by the V copy kernel)
     size_t bytes;
     int64_t nvb;
 };

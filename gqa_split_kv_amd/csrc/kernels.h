@@ -59,6 +59,9 @@ struct PrefillParams {
     const uint8_t *vt;         // [h_kv][nvb][D][64] fp16: V^T of every sequence's 64-key steps, or null
     const uint8_t *vflags;     // [h_kv][nvb] 1 = that step's V is not fit for fp16 (bf16 input)
     int64_t nvb;               // step blocks per kv head in vt (0: no copy)
+    // Tile queue: the next work item to take, zeroed by the V copy kernel before
+    // the prefill kernel starts; null = the fixed snake order (no workspace).
+    unsigned long long *queue;
 };
 
 // Transposed fp16 copy of V for the prefill's fast loop (vprep_kernel).
@@ -69,6 +72,7 @@ struct VprepParams {
     const int32_t *seq_lens;   // [batch]
     int32_t batch, h_kv;
     int64_t nvb;               // >= sum over sequences of ceil(len / 64)
+    unsigned long long *queue; // set to 0 (the prefill's tile queue)
 };
 
 // Enqueues vprep_kernel over h_kv * nvb workgroups.

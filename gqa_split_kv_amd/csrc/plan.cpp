@@ -193,12 +193,13 @@ int validate(const gqa_decode_args *a) {
 }
 
 PrefillWorkspace prefill_workspace(const gqa_prefill_args *a) {
-    PrefillWorkspace W = {0, 0, 0};
+    PrefillWorkspace W = {0, 0, 0, 0};
     if (a->split_pv != 0 || a->total_tokens <= 0) return W;
     W.nvb = (a->total_tokens + kPrefillStepKeys - 1) / kPrefillStepKeys + a->batch;
     const size_t blocks = static_cast<size_t>(W.nvb) * static_cast<size_t>(a->h_kv);
     W.flags_offset = round_up(blocks * static_cast<size_t>(a->d_head) * kPrefillStepKeys * 2, 256);
-    W.bytes = round_up(W.flags_offset + blocks, 256);
+    W.queue_offset = round_up(W.flags_offset + blocks, 256);
+    W.bytes = W.queue_offset + 256;
     return W;
 }
 

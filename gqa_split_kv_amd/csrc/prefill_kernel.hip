@@ -49,10 +49,13 @@
 //     recomputing that step with moved references when one appears).  Weights
 //     are then below 2^16 (the exponent offset 2^7 keeps small weights inside
 //     fp16's range), and the common factor cancels in O / l.
-//   * Tiles are handed out in a fixed snake order over a persistent grid: the
-//     tiles of a (sequence, kv head) are enumerated last token first (longest
-//     first), and workgroup w takes tiles w, 2g-1-w, 2g+w, ... (g = grid size),
-//     which evens out the causal triangle's work.
+//   * Tiles are handed out over a persistent grid: the tiles of a (sequence, kv
+//     head) are enumerated last token first (longest first), and workgroup w
+//     takes tiles w, 2g-1-w, 2g+w, ... (g = grid size, a snake that evens out
+//     the causal triangle's work), except that the last round's tiles come
+//     from a counter in the workspace (zeroed by the V copy kernel), so that
+//     compute units that ran faster take more of them.  Without a workspace
+//     (split_pv = 1) the whole order is fixed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -708,13 +711,33 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     __shared__ __align__(16) uint8_t k1s[T::kSlotBytes];
     __shared__ __align__(16) uint8_t v0s[T::kSlotBytes];
     __shared__ __align__(16) uint8_t v1s[T::kSlotBytes];
+    __shared__ int64_t s_item;
     const int tt = kPrefillRows / P.G;
     const int64_t items = count_items(P.seq_lens, P.batch, tt, P.h_kv);
     const int64_t g = gridDim.x;
     const int64_t w = blockIdx.x;
-    for (int64_t r = 0; r * g < items; ++r) {
-        const int64_t it = r * g + ((r & 1) ? g - 1 - w : w);   // snake order
-        if (it >= items) continue;
+    // Every round but the last in the fixed snake order (the workgroups of a round
+    // sweep neighbouring tiles of a sequence at about the same pace, so their K/V
+    // reads meet in the cache); the last round's items -- the shortest tiles --
+    // from the workspace's counter, longest first, so that workgroups on compute
+    // units that ran faster take more of them.  One loop with one call of run():
+    // a second inlined copy of the tile sweep costs registers in its inner loops.
+    const int64_t rounds = (items + g - 1) / g;
+    const int64_t first_dyn = P.queue && rounds > 1 ? (rounds - 1) * g : items;
+    for (int64_t r = 0;; ++r) {
+        int64_t it;
+        if (r * g < first_dyn) {
+            it = r * g + ((r & 1) ? g - 1 - w : w);   // snake order
+            if (it >= first_dyn) continue;
+        } else {
+            if (first_dyn >= items) break;
+            if (threadIdx.x == 0)
+                s_item = first_dyn + static_cast<int64_t>(atomicAdd(P.queue, 1ull));   // relaxed; selects work only
+            __syncthreads();
+            it = s_item;
+            __syncthreads();   // every thread has read it before thread 0 takes the next
+            if (it >= items) break;   // each workgroup's last take is past the end
+        }
         int b, len;
         int64_t off, local, steps;
         locate_item(P.seq_lens, P.batch, tt, P.h_kv, it, b, off, len, local, steps);
@@ -743,6 +766,7 @@ __global__ __launch_bounds__(kVprepThreads) void vprep_kernel(VprepParams p) {
     __shared__ __align__(16) uint8_t tile[K * kPitch];
     __shared__ unsigned wmax[kVprepThreads / kWave];
     const int64_t idx = blockIdx.x;
+    if (idx == 0 && threadIdx.x == 0) *p.queue = 0;   // the prefill kernel's tile queue starts at item 0
     const int j = static_cast<int>(idx / p.nvb);
     const int64_t blk = idx - static_cast<int64_t>(j) * p.nvb;
     int b, len;

@@ -42,7 +42,8 @@
  * Workspace: the default precision mode (split_pv = 0) with total_tokens > 0
  * uses one -- V transposed and in fp16, 64 keys of one sequence at a time
  * (nvb = ceil(total_tokens / 64) + batch blocks of d_head x 64 values per kv
- * head), and one flag byte per block and kv head, both rewritten by every call
+ * head), one flag byte per block and kv head, and the 8-byte counter of the
+ * queue the workgroups take their tiles from, all rewritten by every call
  * (nothing needs initialising).  gqa_prefill_workspace_bytes() gives its size.
  * With workspace NULL the library uses its own, per (device, stream), grown
  * with hipMalloc (not capturable in a HIP graph; freed by gqa_release()); a

@@ -270,15 +270,15 @@ def test_prefill_total_tokens_and_workspace_rules(lib):
     assert _pvalidate(total_tokens=(1 << 34) + 1, h_q=64, h_kv=8) == B.GQA_ERR_ARG
     # Workspace: V transposed in 64-key blocks, nvb = ceil(total / 64) + batch
     # blocks per kv head of d x 64 fp16 values, then one flag byte per block and
-    # kv head, each part rounded up to 256 bytes.
+    # kv head, then the tile queue's counter, each part rounded up to 256 bytes.
     a = _pargs(total_tokens=1000, h_q=8, h_kv=2)
     nvb = 16 + 1
-    assert B.gqa_prefill_workspace_bytes(a) == 2 * nvb * 128 * 64 * 2 + 256
-    assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=129, d_head=64, batch=3)) == (3 + 3) * 64 * 64 * 2 + 256
+    assert B.gqa_prefill_workspace_bytes(a) == 2 * nvb * 128 * 64 * 2 + 256 + 256
+    assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=129, d_head=64, batch=3)) == (3 + 3) * 64 * 64 * 2 + 256 + 256
     assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=1000, split_pv=1)) == 0
     assert B.gqa_prefill_workspace_bytes(_pargs(total_tokens=0)) == 0
     assert B.gqa_prefill_workspace_bytes(
-        _pargs(total_tokens=1000, in_dtype=B.GQA_DTYPE_F16, out_dtype=B.GQA_DTYPE_F16)) == 2 * 0 + 17 * 128 * 64 * 2 + 256
+        _pargs(total_tokens=1000, in_dtype=B.GQA_DTYPE_F16, out_dtype=B.GQA_DTYPE_F16)) == 17 * 128 * 64 * 2 + 256 + 256
     # The V copy's grid (nvb x h_kv workgroups) must stay below 2^31.
     assert _pvalidate(total_tokens=1 << 36, h_q=8, h_kv=2) == B.GQA_ERR_ARG and "2^31" in B.last_error_message()
     assert _pvalidate(total_tokens=1 << 36, h_q=8, h_kv=1) == B.GQA_OK

@@ -209,7 +209,8 @@ def test_prefill_caller_workspace_poisoned_and_reused():
                              B.GQA_DTYPE_BF16, total_tokens=1234)
     need = B.gqa_prefill_workspace_bytes(a0)
     nvb = -(-1234 // 64) + 3                          # 64-key blocks: ceil(total / 64) + batch
-    assert need == 2 * nvb * 128 * 64 * 2 + 256       # transposed copy + one flag byte per block and head
+    # transposed copy, one flag byte per block and head, the tile queue's counter
+    assert need == 2 * nvb * 128 * 64 * 2 + 256 + 256
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     for c in cases:
         q, k, v, sl = upload(c)
