@@ -65,22 +65,26 @@ def test_decode_graph_replays_equal_eager(t_q, merge):
     del g
 
 
-@pytest.mark.parametrize("split_pv", [0, 1])
-def test_prefill_graph_replays_equal_eager(split_pv):
+@pytest.mark.parametrize("split_pv,num_blocks", [(0, 0), (1, 0), (0, 16)])
+def test_prefill_graph_replays_equal_eager(split_pv, num_blocks):
+    """With 16 workgroups the 60 tiles take four rounds, the last from the tile
+    queue's counter, which every replay's V copy must zero again."""
     import torch
     lens = [1500, 77, 300]
     c = device_prefill_case(len(lens), 8, 1, 128, lens, "bf16", seed=43)
-    _say("prefill graph: lens", lens, "split_pv", split_pv)
+    _say("prefill graph: lens", lens, "split_pv", split_pv, "num_blocks", num_blocks)
     out = torch.empty(c.q.shape, dtype=torch.float32, device="cuda")
     total = c.q.shape[0]
     args = B.make_prefill_args(c.q, c.k, c.v, out, c.seq_lens, len(lens), 8, 1, 128, c.scale, B.GQA_DTYPE_BF16,
                                B.GQA_DTYPE_F32, split_pv=split_pv, total_tokens=total)
     ws = torch.empty(max(B.gqa_prefill_workspace_bytes(args), 1), dtype=torch.uint8, device="cuda")
-    B.prefill(c.q, c.k, c.v, c.seq_lens, scale=c.scale, out=out, split_pv=split_pv, workspace=ws)
+    B.prefill(c.q, c.k, c.v, c.seq_lens, scale=c.scale, out=out, split_pv=split_pv, workspace=ws,
+              num_blocks=num_blocks)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        B.prefill(c.q, c.k, c.v, c.seq_lens, scale=c.scale, out=out, split_pv=split_pv, workspace=ws)
+        B.prefill(c.q, c.k, c.v, c.seq_lens, scale=c.scale, out=out, split_pv=split_pv, workspace=ws,
+                  num_blocks=num_blocks)
     torch.cuda.synchronize()
     for r in range(REPLAYS):
         # New queries and new values (the replay must rebuild the transposed V copy).
