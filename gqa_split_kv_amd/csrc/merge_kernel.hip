@@ -23,7 +23,10 @@
 // wide (one row, all of d, 32 piece lanes at d 128) for long sequences cut into
 // many; split (one row, 32 elements of d, 128 piece lanes) for a few units cut
 // into very many pieces, where the wide layout would leave most of the GPU idle.
-// Also writes zeros for an empty sequence.
+// Also writes zeros for an empty sequence.  With a single sequence and a length
+// bound from the caller, the pieces are read for a length of exactly the bound
+// while seq_lens is read, and the two lengths are compared before any store (a
+// mismatch takes the general path; the result is the same either way).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
