@@ -54,7 +54,7 @@ METRIC = "µs/decode step + K/V HBM GB/s (% of peak), GQA h_q=64 h_kv=8 d=128 @3
 # data is tied to them.
 KERNEL_SRCS = [os.path.join(ROOT, "gqa_split_kv_amd", "csrc", f)
                for f in ("sweep_kernel.hip", "merge_kernel.hip", "device_common.h", "kernels.h", "host.h", "plan.cpp",
-                         "api.cpp")]
+                         "api.cpp")] + [os.path.join(ROOT, "gqa_split_kv_amd", "build.py")]   # with the compile flags
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_kernel_70b_ragged_traffic.md")
 
 

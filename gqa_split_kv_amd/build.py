@@ -24,6 +24,9 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 DEVICE_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+# The sweep kernel's instruction schedule: LLVM's max-ilp strategy measured
+# 0.25-0.7% faster than the default on every decode form (bit-identical code paths).
+SWEEP_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall"]
 
 
@@ -41,7 +44,8 @@ def build(verbose: bool = False) -> str:
     for name in ("sweep_kernel", "merge_kernel"):
         src = os.path.join(CSRC, name + ".hip")
         obj = os.path.join(BUILD, name + ".o")
-        _run([HIPCC, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *NO_PACKED_FP32, *DEVICE_FLAGS,
+        extra = SWEEP_FLAGS if name == "sweep_kernel" else []
+        _run([HIPCC, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *NO_PACKED_FP32, *DEVICE_FLAGS, *extra,
               "-c", src, "-o", obj], verbose)
         objs.append(obj)
     # Prefill kernel: its accumulators live in AGPRs (no VGPR-form MFMA).
